@@ -1,0 +1,461 @@
+"""Pins for the CPU oracle: each check rests on something other than the
+oracle's own formulas.
+
+* torch's float8_e4m3fn dtype: an independent implementation of the OCP E4M3
+  format (decode of all 256 codes; round-to-nearest-even cast of in-range
+  values).
+* brute-force nearest search over all E4M3 values in exact rational
+  arithmetic (Python ``fractions``), ties resolved to the even code.
+* hand-worked 32-element blocks (derivations in the comments).
+* closed forms and invariants: the scale characterisation
+  2^8 <= amax * 2^-X < 2^9, exact round trips of small integers and powers
+  of two, the round-trip error bound, scale invariance, transposition.
+* exact integer arithmetic for dbias and the GEMM.
+"""
+
+import math
+import random
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def bf16_bits(values):
+    """Exact float values (representable in BF16) -> BF16 bit patterns."""
+    f = np.asarray(values, dtype=np.float32)
+    bits = (f.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(((bits.astype(np.uint32)) << 16).view(np.float32), f), "not exact in BF16"
+    return bits
+
+
+def block_row(values):
+    """One 32-element rowwise block (rest zero) as a [1, 32] BF16 array."""
+    v = list(values) + [0.0] * (32 - len(values))
+    return bf16_bits(np.array(v, dtype=np.float64).reshape(1, 32))
+
+
+# ----------------------------------------------------------- E4M3 / E8M0
+
+def torch_e4m3_values():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_e4m3_decode_matches_torch_for_all_codes():
+    ours = oracle.e4m3_decode(np.arange(256))
+    ref = torch_e4m3_values()
+    nan_o, nan_r = np.isnan(ours), np.isnan(ref)
+    assert np.array_equal(nan_o, nan_r)
+    assert list(np.nonzero(nan_o)[0]) == [0x7F, 0xFF]
+    assert np.array_equal(ours[~nan_o], ref[~nan_r])
+    # signed zero is kept as a distinct code
+    assert math.copysign(1.0, ours[0x80]) == -1.0
+
+
+def test_e4m3_landmarks():
+    d = oracle.e4m3_decode
+    assert d(0x7E) == 448.0 and d(0xFE) == -448.0
+    assert d(0x08) == 2.0 ** -6          # smallest normal
+    assert d(0x01) == 2.0 ** -9          # smallest subnormal
+    assert d(0x07) == 7 * 2.0 ** -9      # largest subnormal
+    assert d(0x38) == 1.0
+    pos = oracle.e4m3_decode(np.arange(0x7F))
+    assert np.all(np.diff(pos) > 0)      # codes 0..0x7E are strictly increasing
+    assert np.isfinite(oracle.e4m3_decode(np.arange(256))).sum() == 254
+
+
+def test_e8m0_decode_is_the_shifted_exponent():
+    # "frost(gemm): Add Rubin kernel pipelines", ue8m0 readback nitpick: the
+    # byte shifted into the fp32 exponent field is the scale value.
+    for b in range(1, 255):
+        as_f32 = np.array([b << 23], dtype=np.uint32).view(np.float32)[0]
+        assert oracle.e8m0_decode(b) == float(as_f32)
+    # Byte 0: OCP gives 2^-127 (the page's readback would give 0.0).
+    assert oracle.e8m0_decode(0) == 2.0 ** -127
+    assert np.isnan(oracle.e8m0_decode(255))
+
+
+POS_CODES = [(c, Fraction(float(v))) for c, v in enumerate(torch_e4m3_values()[:0x7F])]
+
+
+def brute_force_encode(v: Fraction, negative: bool) -> int:
+    """Nearest E4M3 value by exhaustive search; ties go to the even code;
+    magnitudes from 448 up saturate to 448; the sign bit is always kept."""
+    a = abs(v)
+    if a >= 448:
+        code = 0x7E
+    else:
+        best = None
+        for c, val in POS_CODES:
+            d = abs(val - a)
+            if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+                best = (d, c)
+        code = best[1]
+    return code | (0x80 if negative else 0)
+
+
+def _encode_cases():
+    vals = []
+    pos = [float(v) for _, v in POS_CODES]
+    for a, b in zip(pos[:-1], pos[1:]):
+        mid = (a + b) / 2
+        vals += [a, mid, math.nextafter(mid, 0.0), math.nextafter(mid, 1e9), b]
+    vals += [447.0, 448.0, 449.0, 463.0, 464.0, 465.0, 479.0, 480.0, 500.0, 511.0, 1e30]
+    vals += [2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -11, 2.0 ** -40, 0.0]
+    rng = random.Random(7)
+    for _ in range(3000):
+        vals.append(rng.uniform(0, 512) * 2.0 ** rng.randint(-12, 0))
+    out = []
+    for v in vals:
+        out += [v, -v]
+    out.append(-0.0)
+    return out
+
+
+def test_e4m3_encode_matches_brute_force_nearest_even():
+    cases = _encode_cases()
+    got = oracle.e4m3_encode(np.array(cases))
+    for v, g in zip(cases, got):
+        want = brute_force_encode(Fraction(v), math.copysign(1.0, v) < 0)
+        assert int(g) == want, (v, hex(int(g)), hex(want))
+
+
+def test_e4m3_encode_matches_torch_cast_on_all_bf16_scalings():
+    # Every finite BF16 pattern, scaled by powers of two; torch's cast is RNE
+    # and agrees with saturation wherever |v| <= 448.
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]
+    x = oracle.bf16_value(bits)
+    for k in (-133, -127, -100, -40, -9, -6, 0, 3, 8, 40, 119, 127):
+        v = np.ldexp(x, k)
+        with np.errstate(over="ignore"):
+            f32 = v.astype(np.float32)
+        keep = np.isfinite(f32) & (np.abs(v) <= 448.0) & (f32.astype(np.float64) == v)
+        ours = oracle.e4m3_encode(v[keep])
+        ref = torch.from_numpy(f32[keep]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(ours, ref), k
+        # out of range: saturation keeps the sign
+        big = np.abs(v) > 448.0
+        if big.any():
+            sat = oracle.e4m3_encode(v[big])
+            assert np.all((sat & 0x7F) == 0x7E)
+            assert np.array_equal(sat >> 7, (v[big] < 0).astype(np.uint8))
+
+
+# ----------------------------------------------------- hand-worked blocks
+
+# Each row: block values (rest of the 32 are zero), expected scale byte,
+# expected codes of the listed values, expected dequantized values.
+WORKED = [
+    # amax 5 -> floor(log2 5) = 2 -> X = -6 -> byte 121.  x*64: 64 -> 1.0*2^6;
+    # -0.30078125*64 = -19.25 -> 10*2 = 20 (0xDA); 160 = 1.25*2^7; 192 = 1.5*2^7;
+    # 2^-4 = 1.0*2^-4 (exp field 3); 320 = 1.25*2^8.
+    ([1.0, -0.30078125, 2.5, 0.0, 3.0, 2.0 ** -10, 5.0], 0x79,
+     [0x68, 0xDA, 0x72, 0x00, 0x74, 0x18, 0x7A],
+     [1.0, -0.3125, 2.5, 0.0, 3.0, 2.0 ** -10, 5.0]),
+    # amax 7.5 -> X = -6; 7.5*64 = 480 saturates to 448 -> 7.0.
+    ([7.5, 1.0], 0x79, [0x7E, 0x68], [7.0, 1.0]),
+    # amax 500 -> floor(log2) = 8 -> X = 0 -> byte 127; 448 exact; 500 saturates.
+    ([448.0, 1.0, 500.0], 0x7F, [0x7E, 0x38, 0x7E], [448.0, 1.0, 448.0]),
+    # amax 1 -> X = -8 -> byte 119; x*256: 2^-8 -> 2 * 2^-9; 2^-10 is a tie
+    # between 0 and 2^-9 -> even (0); 3*2^-11 = 0.75 * 2^-9 -> 1 * 2^-9.
+    ([1.0, 2.0 ** -16, 2.0 ** -18, 3 * 2.0 ** -19], 0x77,
+     [0x78, 0x02, 0x00, 0x01], [1.0, 2.0 ** -16, 0.0, 2.0 ** -17]),
+    # all-subnormal block: 2^-130 -> X = -138 clamps to -127 (byte 0);
+    # 2^-130 * 2^127 = 2^-3 (exp field 4) -> dequantizes exactly.
+    ([2.0 ** -130] * 32, 0x00, [0x20] * 32, [2.0 ** -130] * 32),
+    # all zero -> byte 0
+    ([0.0] * 32, 0x00, [0x00] * 32, [0.0] * 32),
+]
+
+
+@pytest.mark.parametrize("case", range(len(WORKED)))
+def test_worked_block(case):
+    vals, byte, codes, deq = WORKED[case]
+    x = block_row(vals)
+    q, s = oracle.quantize_rowwise(x)
+    assert s[0, 0] == byte
+    assert list(q[0, :len(codes)]) == codes
+    assert np.all(q[0, len(vals):] == 0)
+    d = oracle.dequantize(q, s)[0, :len(deq)]
+    assert list(d) == deq
+
+
+def test_worked_block_max_bf16():
+    # max BF16 = (2 - 2^-7) * 2^127 -> floor(log2) = 127 -> X = 119 -> byte 246;
+    # scaled value 510 saturates to 448 -> 448 * 2^119; 1.0 * 2^-119 -> +0.
+    x = np.zeros((1, 32), dtype=np.uint16)
+    x[0, 0] = workloads.BF16_MAX_BITS
+    x[0, 1:] = 0x3F80
+    q, s = oracle.quantize_rowwise(x)
+    assert s[0, 0] == 0xF6
+    assert q[0, 0] == 0x7E and np.all(q[0, 1:] == 0)
+    assert oracle.dequantize(q, s)[0, 0] == 448.0 * 2.0 ** 119
+
+
+def test_signed_zero_and_negative_underflow_keep_sign():
+    x = block_row([-0.0, 1.0, -(2.0 ** -20), 2.0 ** -20])
+    q, s = oracle.quantize_rowwise(x)
+    assert s[0, 0] == 0x77
+    assert q[0, 0] == 0x80 and q[0, 2] == 0x80 and q[0, 3] == 0x00
+    xz = block_row([-0.0])
+    qz, sz = oracle.quantize_rowwise(xz)
+    assert sz[0, 0] == 0 and qz[0, 0] == 0x80
+
+
+def test_scaled_tie_encodings():
+    # encoder on pre-scaled values: ties to even at both ends of the range
+    v = np.array([2.0 ** -10, 3 * 2.0 ** -10, 17.0, 19.0, 464.0, 465.0, 240.0, 248.0])
+    assert list(oracle.e4m3_encode(v)) == [0x00, 0x02, 0x58, 0x5A, 0x7E, 0x7E, 0x77, 0x78]
+
+
+# --------------------------------------------------- closed-form invariants
+
+def _random_blocks(n, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, 32)).astype(np.float32)
+    x *= np.ldexp(np.float32(1), rng.integers(-140, 120, size=(n, 1))).astype(np.float32)
+    bits = workloads.f32_to_bf16_bits(x)
+    bits[(bits & 0x7F80) == 0x7F80] = 0x3F80
+    sub = rng.random((n, 32)) < 0.05
+    bits[sub] = (rng.integers(0, 2, sub.sum()).astype(np.uint16) << 15) | \
+        rng.integers(0, 128, sub.sum()).astype(np.uint16)
+    bits[rng.random(n) < 0.02] = 0
+    return bits
+
+
+def test_scale_characterisation():
+    bits = _random_blocks(20000, 1)
+    q, s = oracle.quantize_rowwise(bits)
+    x = oracle.bf16_value(bits)
+    amax = np.abs(x).max(axis=1)
+    X = s[:, 0].astype(np.int64) - 127
+    scaled = np.ldexp(amax, -X)
+    nz = amax > 0
+    clamped = nz & (amax < 2.0 ** -119)
+    free = nz & ~clamped
+    assert np.all((scaled[free] >= 256) & (scaled[free] < 512))
+    assert np.all(s[clamped, 0] == 0) and np.all(scaled[clamped] < 256)
+    assert np.all(s[~nz, 0] == 0)
+    assert clamped.sum() > 0 and free.sum() > 0 and (~nz).sum() > 0
+
+
+def test_round_trip_bound():
+    bits = _random_blocks(20000, 2)
+    q, s = oracle.quantize_rowwise(bits)
+    x = oracle.bf16_value(bits)
+    d = oracle.dequantize(q, s)
+    X = np.repeat(s.astype(np.int64) - 127, 32, axis=1)
+    v = np.ldexp(np.abs(x), -X)                 # scaled magnitude
+    err = np.abs(x - d)
+    sat = v >= 448
+    normal = (v >= 2.0 ** -6) & ~sat
+    sub = (v < 2.0 ** -6)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(normal, np.abs(x), 1.0)))
+    assert np.all(err[normal] <= np.ldexp(1.0, (e[normal] - 4).astype(np.int64)))
+    assert np.all(err[sub] <= np.ldexp(1.0, X[sub] - 10))
+    assert np.all(np.abs(d[sat]) == np.ldexp(448.0, X[sat]))
+    assert np.all(err[sat] < np.abs(x[sat]) / 8)
+    assert np.array_equal(np.signbit(d), np.signbit(x))
+
+
+def test_small_integers_and_powers_of_two_round_trip_exactly():
+    rng = np.random.default_rng(3)
+    for k in (-100, -20, 0, 7, 60, 110):
+        ints = rng.integers(-14, 15, size=(64, 32)).astype(np.float64)
+        ints[:, 0] = rng.choice([-14, 14, 9, -8, 1, 3], size=64)
+        x = bf16_bits(np.ldexp(ints, k))
+        q, s = oracle.quantize_rowwise(x)
+        assert np.array_equal(oracle.dequantize(q, s), np.ldexp(ints, k))
+        pw = np.ldexp(1.0, k - np.arange(18))
+        xp = block_row(list(pw))
+        qp, sp = oracle.quantize_rowwise(xp)
+        assert np.array_equal(oracle.dequantize(qp, sp)[0, :18], pw)
+    # 15 needs 480 at the chosen scale and saturates to 14
+    q, s = oracle.quantize_rowwise(block_row([15.0, 1.0]))
+    assert oracle.dequantize(q, s)[0, 0] == 14.0
+    # 2^-18 below the top power sits on the 2^-10 tie and goes to zero
+    q, s = oracle.quantize_rowwise(block_row([1.0, 2.0 ** -18]))
+    assert q[0, 1] == 0
+
+
+def test_scale_invariance():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((512, 64)).astype(np.float32)
+    bits = workloads.f32_to_bf16_bits(x)
+    q0, s0 = oracle.quantize_rowwise(bits)
+    for k in (-30, -1, 1, 17, 60):
+        bk = workloads.f32_to_bf16_bits(np.ldexp(oracle.bf16_value(bits), k).astype(np.float32))
+        qk, sk = oracle.quantize_rowwise(bk)
+        assert np.array_equal(qk, q0)
+        assert np.array_equal(sk.astype(int), s0.astype(int) + k)
+
+
+def test_colwise_is_rowwise_of_transpose():
+    bits = workloads.wide_range_bf16((96, 160), 5, n_maxbf16=3, n_subnormal=40,
+                                     n_subnormal_blocks=2)
+    qT, sT = oracle.quantize_colwise(bits)
+    qr, sr = oracle.quantize_rowwise(np.ascontiguousarray(bits.T))
+    assert np.array_equal(qT, qr) and np.array_equal(sT, sr)
+    assert qT.shape == (160, 96) and sT.shape == (160, 3)
+
+
+def test_quantize_block_by_brute_force():
+    # whole-block check in exact rationals: X is the unique integer with
+    # 2^8 <= amax * 2^-X < 2^9 (clamped to >= -127), codes by nearest search
+    bits = _random_blocks(300, 6)
+    q, s = oracle.quantize_rowwise(bits)
+    for i in range(bits.shape[0]):
+        vals = [Fraction(float(v)) for v in oracle.bf16_value(bits[i])]
+        amax = max(abs(v) for v in vals)
+        if amax == 0:
+            X = -127
+            want_byte = 0
+        else:
+            X = -140
+            while not (amax / Fraction(2) ** X < 512):
+                X += 1
+            X = max(X, -127)
+            want_byte = X + 127
+        assert s[i, 0] == want_byte
+        for j, v in enumerate(vals):
+            neg = bits[i, j] >> 15 == 1
+            assert q[i, j] == brute_force_encode(v / Fraction(2) ** X, neg), (i, j)
+
+
+def test_dbias_exact_on_integers():
+    rng = np.random.default_rng(8)
+    ints = rng.integers(-256, 257, size=(96, 64))
+    x = bf16_bits(ints.astype(np.float64))
+    got = oracle.dbias(x)
+    want = ints.sum(axis=0)
+    assert np.array_equal(got.astype(np.int64), want)
+
+
+def test_dbias_is_rounded_once():
+    # 2^24 followed by 4096 ones: the exact sum 2^24 + 4096 is a float32, but a
+    # float32 running sum would stay at 2^24 (2^24 + 1 ties to even).
+    col = np.ones(4097)
+    col[0] = 2.0 ** 24
+    x = bf16_bits(np.stack([col, -col], axis=1))
+    got = oracle.dbias(x)
+    assert got[0] == 2.0 ** 24 + 4096 and got[1] == -(2.0 ** 24 + 4096)
+
+
+def test_dbias_matches_correctly_rounded_sum():
+    bits = workloads.student_t_bf16((128, 64), 9)
+    got = oracle.dbias(bits)
+    x = oracle.bf16_value(bits)
+    for c in range(64):
+        exact = np.float32(math.fsum(x[:, c]))
+        assert got[c] == exact
+
+
+# ------------------------------------------------------------------ GEMM
+
+def test_gemm_identity_gives_transposed_dequantized_b():
+    a = bf16_bits(np.eye(256))
+    b = workloads.normal_bf16((256, 256), 1)
+    qa, sa = oracle.quantize_rowwise(a)
+    qb, sb = oracle.quantize_rowwise(b)
+    c = oracle.gemm_tn(qa, sa, qb, sb)
+    assert np.array_equal(c, oracle.dequantize(qb, sb).T)
+
+
+def test_gemm_all_ones():
+    x = bf16_bits(np.ones((64, 256)))
+    q, s = oracle.quantize_rowwise(x)
+    assert np.all(oracle.gemm_tn(q, s, q, s) == 256.0)
+
+
+def test_gemm_small_integers_exact():
+    rng = np.random.default_rng(10)
+    A = rng.integers(-14, 15, size=(96, 384))
+    B = rng.integers(-14, 15, size=(64, 384))
+    qa, sa = oracle.quantize_rowwise(bf16_bits(A.astype(np.float64)))
+    qb, sb = oracle.quantize_rowwise(bf16_bits(B.astype(np.float64)))
+    c = oracle.gemm_tn(qa, sa, qb, sb)
+    assert np.array_equal(c, (A @ B.T).astype(np.float64))
+
+
+def test_gemm_tiny_brute_force_rationals():
+    rng = np.random.default_rng(11)
+    M, N, K = 4, 5, 96
+    qa = rng.integers(0, 256, size=(M, K)).astype(np.uint8)
+    qb = rng.integers(0, 256, size=(N, K)).astype(np.uint8)
+    qa[(qa & 0x7F) == 0x7F] = 0x30
+    qb[(qb & 0x7F) == 0x7F] = 0x31
+    sa = rng.integers(100, 150, size=(M, K // 32)).astype(np.uint8)
+    sb = rng.integers(100, 150, size=(N, K // 32)).astype(np.uint8)
+    vals = {c: Fraction(float(v)) for c, v in enumerate(torch_e4m3_values()) if not math.isnan(v)}
+    c = oracle.gemm_tn(qa, sa, qb, sb)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(vals[int(qa[m, k])] * Fraction(2) ** (int(sa[m, k // 32]) - 127) *
+                        vals[int(qb[n, k])] * Fraction(2) ** (int(sb[n, k // 32]) - 127)
+                        for k in range(K))
+            mag = sum(abs(vals[int(qa[m, k])] * vals[int(qb[n, k])]) *
+                      Fraction(2) ** (int(sa[m, k // 32]) + int(sb[n, k // 32]) - 254)
+                      for k in range(K))
+            assert abs(Fraction(c[m, n]) - exact) <= mag * Fraction(K, 2 ** 52)
+
+
+def test_gemm_scale_byte_doubles_one_row_block():
+    rng = np.random.default_rng(12)
+    qa = oracle.quantize_rowwise(workloads.normal_bf16((64, 256), 3))
+    qb = oracle.quantize_rowwise(workloads.normal_bf16((32, 256), 4))
+    base = oracle.gemm_tn(*qa, *qb)
+    sa2 = qa[1].copy()
+    sa2[5, :] += 1            # every block of row 5 scaled by 2
+    c2 = oracle.gemm_tn(qa[0], sa2, *qb)
+    assert np.array_equal(c2[5], 2 * base[5])
+    assert np.array_equal(np.delete(c2, 5, 0), np.delete(base, 5, 0))
+    _ = rng
+
+
+# ------------------------------------------------------------ scale packing
+
+def test_pack_scales_hand_example():
+    s = np.arange(16, dtype=np.uint8).reshape(2, 8)     # dim 2, K = 256
+    p = oracle.pack_scales(s)
+    assert p.shape == (2, 2)
+    assert [hex(int(w)) for w in p.reshape(-1)] == ["0x3020100", "0xb0a0908", "0x7060504", "0xf0e0d0c"]
+
+
+def test_pack_scales_is_a_permutation():
+    rng = np.random.default_rng(13)
+    s = rng.integers(0, 256, size=(96, 64)).astype(np.uint8)
+    p = oracle.pack_scales(s)
+    back = p.view(np.uint8).reshape(16, 96, 4).transpose(1, 0, 2).reshape(96, 64)
+    assert np.array_equal(back, s)
+
+
+# ---------------------------------------------------------------- grouped
+
+def test_grouped_gemm_single_group_is_dense():
+    x = oracle.quantize_rowwise(workloads.normal_bf16((96, 256), 1))
+    w = oracle.quantize_rowwise(workloads.normal_bf16((64, 256), 2))
+    g = oracle.grouped_gemm_tn(x[0], x[1], w[0][None], w[1][None], [0, 96])
+    assert np.array_equal(g, oracle.gemm_tn(*x, *w))
+
+
+def test_grouped_gemm_ragged_with_empty_groups():
+    xq, xs = oracle.quantize_rowwise(workloads.normal_bf16((160, 128), 1))
+    ws = [oracle.quantize_rowwise(workloads.normal_bf16((64, 128), 10 + g)) for g in range(4)]
+    qw = np.stack([w[0] for w in ws])
+    sw = np.stack([w[1] for w in ws])
+    off = workloads.offsets_from_counts([0, 64, 0, 96])
+    out = oracle.grouped_gemm_tn(xq, xs, qw, sw, off)
+    assert np.array_equal(out[:64], oracle.gemm_tn(xq[:64], xs[:64], qw[1], sw[1]))
+    assert np.array_equal(out[64:], oracle.gemm_tn(xq[64:], xs[64:], qw[3], sw[3]))
+    part = workloads.offsets_from_counts([32, 32, 0, 32])     # rows 96.. in no group
+    out2 = oracle.grouped_gemm_tn(xq, xs, qw, sw, part)
+    assert np.all(np.isnan(out2[96:])) and not np.any(np.isnan(out2[:96]))
