@@ -1,0 +1,216 @@
+/*
+ * mxfp8.h - C ABI of the MI355X (gfx950) MXFP8 library.
+ *
+ * MXFP8 block-scaled quantization (BF16 -> E4M3 codes + one E8M0 scale per
+ * 32 consecutive elements along the reduction direction, rowwise and
+ * columnwise, optional fused dbias) and the block-scaled MXFP8 GEMM
+ * (fp32 accumulation, BF16 output; dense and ragged grouped).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers on the device that owns
+ *    `stream`.  The caller allocates and owns every buffer (inputs, outputs,
+ *    workspace); the library never allocates, frees or synchronises, and
+ *    never reads device data on the host.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *    Work is enqueued asynchronously; a returned MXFP8_OK means "validated
+ *    and launched", not "finished".
+ *  - Sizes are int64_t element counts; matrices are row-major.
+ *  - Arguments are validated on the host BEFORE anything is launched; an
+ *    invalid call returns an error code and enqueues nothing.  Unsupported
+ *    requests are rejected, never silently changed.  There is no fallback
+ *    path.  Launch failures return MXFP8_ERR_HIP (the HIP error code is
+ *    available from mxfp8_last_hip_error()).
+ *  - Empty problems (a zero dimension) are valid no-ops, except that
+ *    outputs that are mathematically defined (a dbias over zero rows, a GEMM
+ *    with K = 0) are written as zeros.
+ *
+ * Numerics (OCP MX reading of the pages: the block size, E8M0 scales, E4M3
+ * data and the rowwise / columnwise / dbias options come from the page
+ * "[Common] Experimental CuTeDSL MXFP8 backends in C++ via TVM-FFI",
+ * config-struct review and Greptile summary; the scale rule is OCP MX):
+ *  - block amax over 32 BF16 values; shared exponent X = floor(log2 amax) - 8
+ *    clamped to [-127, 127]; scale byte = X + 127 (0 for an all-zero block);
+ *  - code = E4M3(x * 2^-X) rounded to nearest even, saturated to +-448, sign
+ *    of zero kept;
+ *  - dequantized value = E4M3 value * 2^(byte - 127).
+ */
+#ifndef MXFP8_H
+#define MXFP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mxfp8_status {
+    MXFP8_OK = 0,
+    MXFP8_ERR_NULL = 1,        /* a required pointer is NULL                       */
+    MXFP8_ERR_SHAPE = 2,       /* negative size or a divisibility rule violated     */
+    MXFP8_ERR_MISALIGNED = 3,  /* pointer / leading dimension alignment violated    */
+    MXFP8_ERR_FLAGS = 4,       /* unknown flag bits or no copy requested            */
+    MXFP8_ERR_WORKSPACE = 5,   /* DBIAS workspace missing or too small              */
+    MXFP8_ERR_HIP = 6,         /* the HIP runtime reported an error at launch       */
+    MXFP8_ERR_LIMIT = 7        /* a size exceeds what one launch grid can cover     */
+} mxfp8_status;
+
+/* Flags of mxfp8_quantize (the rowwise / colwise / with_dbias options of the
+ * quantization config in "[Common] Experimental CuTeDSL MXFP8 backends in C++
+ * via TVM-FFI", review of the config key). */
+#define MXFP8_ROWWISE 1u /* blocks along rows:    q_row[rows][cols], s_row[rows][cols/32]    */
+#define MXFP8_COLWISE 2u /* blocks along columns, stored transposed:
+                            q_colT[cols][rows], s_colT[cols][rows/32]                       */
+#define MXFP8_DBIAS 4u   /* dbias[cols] = fp32 column sums of the BF16 input                 */
+
+/* Human-readable name of a status code (static storage). */
+const char *mxfp8_status_string(mxfp8_status s);
+
+/* HIP error code (hipError_t as int) of the last MXFP8_ERR_HIP returned on
+ * the calling thread; 0 if none. */
+int mxfp8_last_hip_error(void);
+
+/* ------------------------------------------------------------------------
+ * Quantization
+ *
+ * Defining passage: MXFP8 quantization with rowwise and/or columnwise output
+ * and an optional fused dbias whose partial sums go to a caller workspace and
+ * are then reduced ("[Common] Experimental CuTeDSL MXFP8 backends in C++ via
+ * TVM-FFI", Greptile summary and config struct); columnwise storage is the
+ * materialised transpose ("Experimental FlyDSL GEMM backend for TE PyTorch
+ * (BF16/FP16/FP32/FP8/MXFP8)", commit notes on TN/NN/NT storage selection).
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of workspace mxfp8_quantize needs for `flags` at this shape (0 when
+ * DBIAS is not requested). */
+size_t mxfp8_quantize_workspace_bytes(int64_t rows, int64_t cols, uint32_t flags);
+
+/*
+ * x       BF16 input [rows][ld_x] (row-major, only the first `cols` of each
+ *         row are read).  16-byte aligned; ld_x >= cols and ld_x % 8 == 0.
+ * rows    >= 0; a multiple of 32 when MXFP8_COLWISE is set.
+ * cols    >= 0; a multiple of 32.
+ * flags   a non-empty combination of MXFP8_ROWWISE / MXFP8_COLWISE, plus
+ *         MXFP8_DBIAS optionally.
+ * q_row   ROWWISE: E4M3 codes [rows][cols], 16-byte aligned.   Else ignored.
+ * s_row   ROWWISE: E8M0 scales [rows][cols/32].                Else ignored.
+ * q_colT  COLWISE: E4M3 codes [cols][rows], 16-byte aligned.   Else ignored.
+ * s_colT  COLWISE: E8M0 scales [cols][rows/32].                Else ignored.
+ * dbias   DBIAS: fp32 [cols], 4-byte aligned.                  Else ignored.
+ * workspace, workspace_bytes
+ *         DBIAS: device scratch of at least
+ *         mxfp8_quantize_workspace_bytes(rows, cols, flags) bytes, 16-byte
+ *         aligned, used for per-row-tile partial sums (the result is
+ *         deterministic: no atomics).  Else ignored.
+ * Errors: NULL (a required pointer is NULL), SHAPE, MISALIGNED, FLAGS,
+ *         WORKSPACE, LIMIT, HIP.  Inputs with NaN/Inf are outside the
+ *         contract (the codes are then unspecified; nothing faults).
+ */
+mxfp8_status mxfp8_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                            uint32_t flags,
+                            uint8_t *q_row, uint8_t *s_row,
+                            uint8_t *q_colT, uint8_t *s_colT,
+                            float *dbias,
+                            void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/* ------------------------------------------------------------------------
+ * Scale packing
+ *
+ * Defining passage: one fused launch per GEMM operand converts the E8M0
+ * scales into the MFMA-ready [K/128, dim] packed word layout, from rowwise
+ * or columnwise scale storage with its actual strides ("Experimental FlyDSL
+ * GEMM backend for TE PyTorch (BF16/FP16/FP32/FP8/MXFP8)", commit notes on
+ * the fused scale-pack kernel).
+ *
+ * Layout: packed is uint32 [k/128][dim]; byte j (little-endian) of word
+ * (t, r) is the scale of K-block 4t + j of row r, i.e. of
+ * K = [128t + 32j, 128t + 32j + 32).
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of the packed layout for a [dim][k] operand: 4 * (k/128) * dim. */
+size_t mxfp8_packed_scale_bytes(int64_t dim, int64_t k);
+
+/*
+ * s       E8M0 scales [dim][ld_s] bytes (K-block index fastest), 4-byte
+ *         aligned; ld_s >= k/32 and ld_s % 4 == 0.
+ * dim     >= 0 rows of the operand (M for A, N -- or G*N stacked -- for B).
+ * k       >= 0, a multiple of 128.
+ * packed  uint32 [k/128][dim], 4-byte aligned; must not overlap s.
+ * Errors: NULL, SHAPE, MISALIGNED, LIMIT, HIP.
+ */
+mxfp8_status mxfp8_pack_scales(const uint8_t *s, int64_t dim, int64_t k, int64_t ld_s,
+                               uint32_t *packed, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Block-scaled GEMM (TN)
+ *
+ * Defining passage: MXFP8 x MXFP8 -> BF16 on the gfx950 scaled FP8 MFMA,
+ * with only alpha = 1 and beta = 0 supported (no accumulate, bias or output
+ * epilogue), TN layout with both operands K-major ("Experimental FlyDSL GEMM
+ * backend for TE PyTorch (BF16/FP16/FP32/FP8/MXFP8)", Summary and the review
+ * of the epilogue validation).
+ *
+ *   C[m][n] = bf16_rne( sum_k dq(A)[m][k] * dq(B)[n][k] ),  fp32 accumulation.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * a         E4M3 codes A [M][K] (row-major, K contiguous), 16-byte aligned.
+ * a_packed  packed scales of A, uint32 [K/128][M] (mxfp8_pack_scales layout).
+ * b         E4M3 codes B [N][K], 16-byte aligned.
+ * b_packed  packed scales of B, uint32 [K/128][N].
+ * c         BF16 output [M][ldc], 16-byte aligned; ldc >= N, ldc % 8 == 0.
+ * M >= 0; N >= 0 and N % 32 == 0; K >= 0 and K % 128 == 0.
+ * K == 0 writes zeros.  The output must not overlap the inputs.
+ * Overflow beyond BF16 range gives +-inf, like the fp32->BF16 rounding.
+ * Errors: NULL, SHAPE, MISALIGNED, LIMIT, HIP.
+ */
+mxfp8_status mxfp8_gemm(const uint8_t *a, const uint32_t *a_packed,
+                        const uint8_t *b, const uint32_t *b_packed,
+                        void *c, int64_t ldc,
+                        int64_t M, int64_t N, int64_t K, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Grouped (ragged expert) GEMM
+ *
+ * Defining passages: per group g the A operand's row base moves to the
+ * group's first row and its row extent shrinks to the group size ("frost
+ * (gemm): Add Rubin kernel pipelines", review of the MoE grouped template);
+ * expert boundaries are int32 offsets that stay on the device, empty groups
+ * are legal and an empty total is a no-op, one launch per call, no host
+ * synchronisation and no workspace ("gemm(cutedsl): add standalone Lightning
+ * W4A16 grouped GEMM", PR body and review of the zero-token case).
+ *
+ *   for g < G, for m in [offsets[g], offsets[g+1]):
+ *       C[m][n] = bf16_rne( sum_k dq(A)[m][k] * dq(B_g)[n][k] ).
+ * ------------------------------------------------------------------------ */
+
+/*
+ * a          E4M3 codes [M_total][K], 16-byte aligned.
+ * a_packed   uint32 [K/128][M_total].
+ * b          E4M3 codes of the G experts [G][N][K], 16-byte aligned.
+ * b_packed   uint32 [K/128][G*N]: the experts' scales stacked as G*N rows and
+ *            packed in one mxfp8_pack_scales call (expert g, row n is packed
+ *            row g*N + n).
+ * offsets    DEVICE int32 [G+1]: offsets[0] = 0, non-decreasing,
+ *            offsets[G] <= M_total.  Rows of C outside every group are not
+ *            written.  Values are read on the device only; out-of-range or
+ *            decreasing offsets are clamped (such groups become empty) so no
+ *            access leaves the buffers.
+ * G          1 <= G <= 65536.
+ * c          BF16 [M_total][ldc]; ldc >= N, ldc % 8 == 0.
+ * M_total >= 0; N >= 0 and N % 32 == 0; K >= 0 and K % 128 == 0.
+ * Errors: NULL, SHAPE, MISALIGNED, LIMIT, HIP.
+ */
+mxfp8_status mxfp8_grouped_gemm(const uint8_t *a, const uint32_t *a_packed,
+                                const uint8_t *b, const uint32_t *b_packed,
+                                const int32_t *offsets, int32_t G,
+                                void *c, int64_t ldc,
+                                int64_t M_total, int64_t N, int64_t K, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP8_H */

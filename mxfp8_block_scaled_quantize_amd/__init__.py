@@ -1,0 +1,192 @@
+"""Python binding of libmxfp8 (MXFP8 quantize + block-scaled GEMM on gfx950).
+
+The ``mxfp8_*`` functions mirror the C ABI of ``include/mxfp8.h`` one to one:
+they only marshal arguments (torch tensors -> device pointers, torch streams
+-> hipStream_t) and raise :class:`MXFP8Error` on a non-OK status.  Every step
+of the computation runs in the HIP kernels of ``libmxfp8.so``; there is no
+CPU fallback, and importing functions that need the library raises when it
+has not been built.  PyTorch is used for device memory and streams only.
+
+The small helpers below them (``quantize``, ``pack_scales``, ``gemm``,
+``grouped_gemm``) allocate outputs with torch and call the same entry points.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxfp8.so")
+
+MXFP8_ROWWISE = 1
+MXFP8_COLWISE = 2
+MXFP8_DBIAS = 4
+
+STATUS_NAMES = {0: "MXFP8_OK", 1: "MXFP8_ERR_NULL", 2: "MXFP8_ERR_SHAPE", 3: "MXFP8_ERR_MISALIGNED",
+                4: "MXFP8_ERR_FLAGS", 5: "MXFP8_ERR_WORKSPACE", 6: "MXFP8_ERR_HIP", 7: "MXFP8_ERR_LIMIT"}
+
+EXPORTED = ("mxfp8_status_string", "mxfp8_last_hip_error", "mxfp8_quantize_workspace_bytes",
+            "mxfp8_quantize", "mxfp8_packed_scale_bytes", "mxfp8_pack_scales", "mxfp8_gemm",
+            "mxfp8_grouped_gemm")
+
+
+class MXFP8Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().mxfp8_status_string(status).decode()
+        if status == 6:
+            msg += " (hipError %d)" % lib().mxfp8_last_hip_error()
+        super().__init__("%s: %s" % (where, msg))
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmxfp8.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libmxfp8.so is not built (run mxfp8_block_scaled_quantize_amd.build.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, U32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+    L.mxfp8_status_string.restype = ctypes.c_char_p
+    L.mxfp8_status_string.argtypes = [ctypes.c_int]
+    L.mxfp8_last_hip_error.restype = ctypes.c_int
+    L.mxfp8_last_hip_error.argtypes = []
+    L.mxfp8_quantize_workspace_bytes.restype = SZ
+    L.mxfp8_quantize_workspace_bytes.argtypes = [I64, I64, U32]
+    L.mxfp8_quantize.restype = ctypes.c_int
+    L.mxfp8_quantize.argtypes = [P, I64, I64, I64, U32, P, P, P, P, P, P, SZ, P]
+    L.mxfp8_packed_scale_bytes.restype = SZ
+    L.mxfp8_packed_scale_bytes.argtypes = [I64, I64]
+    L.mxfp8_pack_scales.restype = ctypes.c_int
+    L.mxfp8_pack_scales.argtypes = [P, I64, I64, I64, P, P]
+    L.mxfp8_gemm.restype = ctypes.c_int
+    L.mxfp8_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
+    L.mxfp8_grouped_gemm.restype = ctypes.c_int
+    L.mxfp8_grouped_gemm.argtypes = [P, P, P, P, P, I32, P, I64, I64, I64, I64, P]
+    _lib = L
+    return L
+
+
+def _p(t):
+    """Device pointer of a tensor (or an int address, or None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _s(stream):
+    """hipStream_t of a torch stream (None -> torch's current stream)."""
+    if isinstance(stream, int):
+        return stream
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MXFP8Error(status, where)
+
+
+# ------------------------------------------------------------ C ABI mirror
+
+def mxfp8_status_string(status: int) -> str:
+    return lib().mxfp8_status_string(status).decode()
+
+
+def mxfp8_last_hip_error() -> int:
+    return lib().mxfp8_last_hip_error()
+
+
+def mxfp8_quantize_workspace_bytes(rows: int, cols: int, flags: int) -> int:
+    return lib().mxfp8_quantize_workspace_bytes(rows, cols, flags)
+
+
+def mxfp8_quantize(x, rows, cols, ld_x, flags, q_row=None, s_row=None, q_colT=None, s_colT=None,
+                   dbias=None, workspace=None, workspace_bytes=0, stream=None):
+    _check(lib().mxfp8_quantize(_p(x), rows, cols, ld_x, flags, _p(q_row), _p(s_row), _p(q_colT),
+                                _p(s_colT), _p(dbias), _p(workspace), workspace_bytes, _s(stream)),
+           "mxfp8_quantize")
+
+
+def mxfp8_packed_scale_bytes(dim: int, k: int) -> int:
+    return lib().mxfp8_packed_scale_bytes(dim, k)
+
+
+def mxfp8_pack_scales(s, dim, k, ld_s, packed, stream=None):
+    _check(lib().mxfp8_pack_scales(_p(s), dim, k, ld_s, _p(packed), _s(stream)), "mxfp8_pack_scales")
+
+
+def mxfp8_gemm(a, a_packed, b, b_packed, c, ldc, M, N, K, stream=None):
+    _check(lib().mxfp8_gemm(_p(a), _p(a_packed), _p(b), _p(b_packed), _p(c), ldc, M, N, K, _s(stream)),
+           "mxfp8_gemm")
+
+
+def mxfp8_grouped_gemm(a, a_packed, b, b_packed, offsets, G, c, ldc, M_total, N, K, stream=None):
+    _check(lib().mxfp8_grouped_gemm(_p(a), _p(a_packed), _p(b), _p(b_packed), _p(offsets), G, _p(c), ldc,
+                                    M_total, N, K, _s(stream)), "mxfp8_grouped_gemm")
+
+
+# ------------------------------------------------------ allocating helpers
+
+def quantize(x, rowwise=True, colwise=False, dbias=False, stream=None):
+    """Quantize a BF16 [rows, cols] CUDA tensor; returns a dict of outputs."""
+    import torch
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    R, C = x.shape
+    dev = x.device
+    flags = (MXFP8_ROWWISE if rowwise else 0) | (MXFP8_COLWISE if colwise else 0) | (MXFP8_DBIAS if dbias else 0)
+    out = {}
+    if rowwise:
+        out["q_row"] = torch.empty((R, C), dtype=torch.uint8, device=dev)
+        out["s_row"] = torch.empty((R, C // 32), dtype=torch.uint8, device=dev)
+    if colwise:
+        out["q_colT"] = torch.empty((C, R), dtype=torch.uint8, device=dev)
+        out["s_colT"] = torch.empty((C, R // 32), dtype=torch.uint8, device=dev)
+    ws = None
+    nws = mxfp8_quantize_workspace_bytes(R, C, flags)
+    if dbias:
+        out["dbias"] = torch.empty((C,), dtype=torch.float32, device=dev)
+    if nws:
+        ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
+    mxfp8_quantize(x, R, C, x.stride(0), flags, out.get("q_row"), out.get("s_row"), out.get("q_colT"),
+                   out.get("s_colT"), out.get("dbias"), ws, nws, stream)
+    return out
+
+
+def pack_scales(s, stream=None):
+    """E8M0 scales uint8 [dim, K/32] -> packed int32 words [K/128, dim]."""
+    import torch
+    assert s.dtype == torch.uint8 and s.dim() == 2 and s.stride(1) == 1
+    dim, kb = s.shape
+    out = torch.empty((kb // 4, dim), dtype=torch.int32, device=s.device)
+    mxfp8_pack_scales(s, dim, kb * 32, s.stride(0), out, stream)
+    return out
+
+
+def gemm(a, a_packed, b, b_packed, stream=None):
+    """C = dq(A) dq(B)^T in BF16 for E4M3 codes a [M, K], b [N, K]."""
+    import torch
+    M, K = a.shape
+    N = b.shape[0]
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    mxfp8_gemm(a, a_packed, b, b_packed, c, N, M, N, K, stream)
+    return c
+
+
+def grouped_gemm(a, a_packed, b, b_packed, offsets, out=None, stream=None):
+    """Ragged grouped GEMM; b is [G, N, K]; rows outside every group keep `out`'s values."""
+    import torch
+    M, K = a.shape
+    G, N, _ = b.shape
+    c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    mxfp8_grouped_gemm(a, a_packed, b, b_packed, offsets, G, c, c.stride(0), M, N, K, stream)
+    return c

@@ -1,0 +1,145 @@
+// C ABI of the MXFP8 library: host-side validation, then one launch sequence
+// on the caller's stream.  See include/mxfp8.h for the contract.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mxfp8.h"
+#include "launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxGrid = 0x7FFFFFFF;  // one-dimensional grid limit
+constexpr int64_t kMaxDim = int64_t(1) << 40; // keeps every element offset well inside int64
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+mxfp8_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MXFP8_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return MXFP8_ERR_HIP;
+}
+
+mxfp8_status check_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint32_t flags,
+                            const uint8_t* q_row, const uint8_t* s_row, const uint8_t* q_colT,
+                            const uint8_t* s_colT, const float* dbias, const void* ws, size_t ws_bytes) {
+  if (flags & ~(MXFP8_ROWWISE | MXFP8_COLWISE | MXFP8_DBIAS)) return MXFP8_ERR_FLAGS;
+  if (!(flags & (MXFP8_ROWWISE | MXFP8_COLWISE))) return MXFP8_ERR_FLAGS;
+  if (rows < 0 || cols < 0 || ld_x < cols) return MXFP8_ERR_SHAPE;
+  if (rows > kMaxDim || ld_x > kMaxDim || (rows > 0 && ld_x > kMaxDim / rows)) return MXFP8_ERR_LIMIT;
+  if (cols % 32) return MXFP8_ERR_SHAPE;
+  if ((flags & MXFP8_COLWISE) && rows % 32) return MXFP8_ERR_SHAPE;
+  const bool any = rows > 0 && cols > 0;
+  if (any && !x) return MXFP8_ERR_NULL;
+  if (any && (flags & MXFP8_ROWWISE) && (!q_row || !s_row)) return MXFP8_ERR_NULL;
+  if (any && (flags & MXFP8_COLWISE) && (!q_colT || !s_colT)) return MXFP8_ERR_NULL;
+  if ((flags & MXFP8_DBIAS) && cols > 0 && !dbias) return MXFP8_ERR_NULL;
+  if (any) {
+    if (!aligned(x, 16) || ld_x % 8) return MXFP8_ERR_MISALIGNED;
+    if ((flags & MXFP8_ROWWISE) && !aligned(q_row, 16)) return MXFP8_ERR_MISALIGNED;
+    if ((flags & MXFP8_COLWISE) && !aligned(q_colT, 16)) return MXFP8_ERR_MISALIGNED;
+  }
+  if ((flags & MXFP8_DBIAS) && cols > 0 && !aligned(dbias, 4)) return MXFP8_ERR_MISALIGNED;
+  if (mx::quantize_row_tiles(rows) * mx::quantize_col_tiles(cols) > kMaxGrid) return MXFP8_ERR_LIMIT;
+  const size_t need = mxfp8_quantize_workspace_bytes(rows, cols, flags);
+  if (need > 0) {
+    if (!ws || ws_bytes < need) return MXFP8_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return MXFP8_ERR_MISALIGNED;
+  }
+  return MXFP8_OK;
+}
+
+mxfp8_status check_gemm_common(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
+                               const void* c, int64_t ldc, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return MXFP8_ERR_SHAPE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim || ldc > kMaxDim) return MXFP8_ERR_LIMIT;
+  if (N % 32 || K % 128 || ldc < N) return MXFP8_ERR_SHAPE;
+  if (M == 0 || N == 0) return MXFP8_OK;
+  if (!c) return MXFP8_ERR_NULL;
+  if (K > 0 && (!a || !ap || !b || !bp)) return MXFP8_ERR_NULL;
+  if (!aligned(c, 16) || ldc % 8) return MXFP8_ERR_MISALIGNED;
+  if (K > 0 && (!aligned(a, 16) || !aligned(b, 16) || !aligned(ap, 4) || !aligned(bp, 4)))
+    return MXFP8_ERR_MISALIGNED;
+  return MXFP8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mxfp8_status_string(mxfp8_status s) {
+  switch (s) {
+    case MXFP8_OK: return "MXFP8_OK";
+    case MXFP8_ERR_NULL: return "MXFP8_ERR_NULL: a required pointer is NULL";
+    case MXFP8_ERR_SHAPE: return "MXFP8_ERR_SHAPE: negative size or divisibility rule violated";
+    case MXFP8_ERR_MISALIGNED: return "MXFP8_ERR_MISALIGNED: pointer or leading dimension misaligned";
+    case MXFP8_ERR_FLAGS: return "MXFP8_ERR_FLAGS: unknown flag bits or no copy requested";
+    case MXFP8_ERR_WORKSPACE: return "MXFP8_ERR_WORKSPACE: workspace missing or too small";
+    case MXFP8_ERR_HIP: return "MXFP8_ERR_HIP: the HIP runtime reported an error";
+    case MXFP8_ERR_LIMIT: return "MXFP8_ERR_LIMIT: problem too large for one launch grid";
+  }
+  return "unknown mxfp8_status";
+}
+
+int mxfp8_last_hip_error(void) { return g_last_hip_error; }
+
+size_t mxfp8_quantize_workspace_bytes(int64_t rows, int64_t cols, uint32_t flags) {
+  if (!(flags & MXFP8_DBIAS) || rows <= 0 || cols <= 0) return 0;
+  return (size_t)mx::quantize_row_tiles(rows) * (size_t)cols * sizeof(float);
+}
+
+mxfp8_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint32_t flags,
+                            uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT, float* dbias,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  const mxfp8_status st =
+      check_quantize(x, rows, cols, ld_x, flags, q_row, s_row, q_colT, s_colT, dbias, workspace, workspace_bytes);
+  if (st != MXFP8_OK) return st;
+  if (cols == 0) return MXFP8_OK;
+  if (rows == 0 && !(flags & MXFP8_DBIAS)) return MXFP8_OK;
+  return hip_status(mx::launch_quantize(static_cast<const uint16_t*>(x), rows, cols, ld_x, flags, q_row, s_row,
+                                        q_colT, s_colT, dbias, static_cast<float*>(workspace),
+                                        static_cast<hipStream_t>(stream)));
+}
+
+size_t mxfp8_packed_scale_bytes(int64_t dim, int64_t k) {
+  if (dim <= 0 || k <= 0) return 0;
+  return (size_t)(k / 128) * (size_t)dim * 4u;
+}
+
+mxfp8_status mxfp8_pack_scales(const uint8_t* s, int64_t dim, int64_t k, int64_t ld_s, uint32_t* packed,
+                               void* stream) {
+  if (dim < 0 || k < 0 || k % 128 || ld_s < k / 32) return MXFP8_ERR_SHAPE;
+  if (dim > kMaxDim || ld_s > kMaxDim || k > kMaxDim) return MXFP8_ERR_LIMIT;
+  if (dim == 0 || k == 0) return MXFP8_OK;
+  if (!s || !packed) return MXFP8_ERR_NULL;
+  if (!aligned(s, 4) || ld_s % 4 || !aligned(packed, 4)) return MXFP8_ERR_MISALIGNED;
+  if (mx::pack_scales_blocks(dim, k) > kMaxGrid) return MXFP8_ERR_LIMIT;
+  return hip_status(mx::launch_pack_scales(s, dim, k, ld_s, packed, static_cast<hipStream_t>(stream)));
+}
+
+mxfp8_status mxfp8_gemm(const uint8_t* a, const uint32_t* a_packed, const uint8_t* b, const uint32_t* b_packed,
+                        void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream) {
+  const mxfp8_status st = check_gemm_common(a, a_packed, b, b_packed, c, ldc, M, N, K);
+  if (st != MXFP8_OK) return st;
+  if (M == 0 || N == 0) return MXFP8_OK;
+  if (mx::gemm_blocks(M, N, 0, false) > kMaxGrid) return MXFP8_ERR_LIMIT;
+  return hip_status(mx::launch_gemm(a, a_packed, b, b_packed, static_cast<uint16_t*>(c), ldc, M, N, K, nullptr, 0,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+mxfp8_status mxfp8_grouped_gemm(const uint8_t* a, const uint32_t* a_packed, const uint8_t* b,
+                                const uint32_t* b_packed, const int32_t* offsets, int32_t G, void* c, int64_t ldc,
+                                int64_t M_total, int64_t N, int64_t K, void* stream) {
+  if (G < 1 || G > 65536) return MXFP8_ERR_SHAPE;
+  const mxfp8_status st = check_gemm_common(a, a_packed, b, b_packed, c, ldc, M_total, N, K);
+  if (st != MXFP8_OK) return st;
+  if (M_total == 0 || N == 0) return MXFP8_OK;
+  if (!offsets) return MXFP8_ERR_NULL;
+  if (!aligned(offsets, 4)) return MXFP8_ERR_MISALIGNED;
+  if (mx::gemm_blocks(M_total, N, G, true) > kMaxGrid) return MXFP8_ERR_LIMIT;
+  return hip_status(mx::launch_gemm(a, a_packed, b, b_packed, static_cast<uint16_t*>(c), ldc, M_total, N, K,
+                                    offsets, G, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,28 @@
+// Internal launchers (host side) of the gfx950 kernels.  The public C ABI in
+// include/mxfp8.h validates every argument before calling these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+int64_t quantize_row_tiles(int64_t R);
+int64_t quantize_col_tiles(int64_t C);
+
+hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint32_t flags,
+                           uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT,
+                           float* dbias, float* dbias_part, hipStream_t stream);
+
+hipError_t launch_pack_scales(const uint8_t* s, int64_t dim, int64_t k, int64_t ld_s, uint32_t* packed,
+                              hipStream_t stream);
+int64_t pack_scales_blocks(int64_t dim, int64_t k);
+
+// Dense (offsets == nullptr) or grouped GEMM.  b_rows_total is the number of
+// rows of the packed B scale matrix (N dense, G*N grouped).
+hipError_t launch_gemm(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
+                       uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                       const int32_t* offsets, int32_t G, hipStream_t stream);
+int64_t gemm_blocks(int64_t M, int64_t N, int32_t G, bool grouped);
+
+}  // namespace mx

@@ -1,0 +1,140 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/mxfp8.h declares, and rejects invalid arguments on the host before
+anything is launched (these calls never reach the HIP runtime)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp8_block_scaled_quantize_amd as mx
+from mxfp8_block_scaled_quantize_amd import build as mxbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp8.h")
+
+OK, NULL, SHAPE, MISALIGNED, FLAGS, WORKSPACE, HIP, LIMIT = range(8)
+ROW, COL, DB = 1, 2, 4
+A16 = 0x10000  # fake, 16-byte aligned "device" addresses: never dereferenced
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mx.LIB_PATH):
+        mxbuild.build()
+    return mx.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxfp8_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("mxfp8_quantize", "mxfp8_pack_scales", "mxfp8_gemm", "mxfp8_grouped_gemm"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert names and set(names) == set(mx.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+    so = ctypes.CDLL(mx.LIB_PATH)
+    for n in names:
+        getattr(so, n)
+
+
+def test_status_strings(L):
+    for code, name in mx.STATUS_NAMES.items():
+        assert mx.mxfp8_status_string(code).startswith(name)
+    assert "unknown" in mx.mxfp8_status_string(99)
+
+
+def test_workspace_and_packed_sizes(L):
+    assert L.mxfp8_quantize_workspace_bytes(300, 256, ROW | DB) == 3 * 256 * 4
+    assert L.mxfp8_quantize_workspace_bytes(300, 256, ROW) == 0
+    assert L.mxfp8_quantize_workspace_bytes(0, 256, ROW | DB) == 0
+    assert L.mxfp8_packed_scale_bytes(96, 512) == 4 * 96 * 4
+    assert L.mxfp8_packed_scale_bytes(0, 512) == 0
+
+
+def q(L, x=A16, rows=64, cols=64, ld=64, flags=ROW, qr=A16, sr=A16, qc=A16, sc=A16, db=A16, ws=A16, wsb=1 << 20):
+    return L.mxfp8_quantize(x, rows, cols, ld, flags, qr, sr, qc, sc, db, ws, wsb, None)
+
+
+def test_quantize_validation(L):
+    assert q(L, flags=0) == FLAGS
+    assert q(L, flags=8 | ROW) == FLAGS
+    assert q(L, flags=DB) == FLAGS
+    assert q(L, cols=48, ld=48) == SHAPE
+    assert q(L, rows=-1) == SHAPE
+    assert q(L, ld=32) == SHAPE
+    assert q(L, rows=48, flags=COL) == SHAPE
+    assert q(L, x=None) == NULL
+    assert q(L, qr=None) == NULL
+    assert q(L, sr=None) == NULL
+    assert q(L, flags=COL, qc=None) == NULL
+    assert q(L, flags=ROW | DB, db=None) == NULL
+    assert q(L, x=A16 + 2) == MISALIGNED
+    assert q(L, ld=68) == MISALIGNED
+    assert q(L, qr=A16 + 8) == MISALIGNED
+    assert q(L, flags=COL, qc=A16 + 4) == MISALIGNED
+    assert q(L, flags=ROW | DB, db=A16 + 2) == MISALIGNED
+    assert q(L, flags=ROW | DB, ws=None) == WORKSPACE
+    assert q(L, flags=ROW | DB, wsb=64 * 4 - 1) == WORKSPACE
+    assert q(L, flags=ROW | DB, ws=A16 + 4) == MISALIGNED
+    # empty problems are no-ops that launch nothing
+    assert q(L, rows=0, x=None, qr=None, sr=None) == OK
+    assert q(L, cols=0, ld=0, x=None, qr=None, sr=None) == OK
+
+
+def test_quantize_grid_limit(L):
+    assert q(L, rows=1 << 36, cols=1 << 20, ld=1 << 20) == LIMIT
+    assert q(L, rows=1 << 41, cols=64, ld=64) == LIMIT
+
+
+def test_pack_validation(L):
+    P = L.mxfp8_pack_scales
+    assert P(A16, 64, 100, 4, A16, None) == SHAPE
+    assert P(A16, 64, 256, 4, A16, None) == SHAPE          # ld_s < k/32
+    assert P(A16, -1, 256, 8, A16, None) == SHAPE
+    assert P(None, 64, 256, 8, A16, None) == NULL
+    assert P(A16, 64, 256, 8, None, None) == NULL
+    assert P(A16 + 1, 64, 256, 8, A16, None) == MISALIGNED
+    assert P(A16, 64, 256, 10, A16, None) == MISALIGNED
+    assert P(A16, 0, 256, 8, None, None) == OK
+
+
+def test_gemm_validation(L):
+    G = L.mxfp8_gemm
+    assert G(A16, A16, A16, A16, A16, 64, 64, 64, 100, None) == SHAPE      # K % 128
+    assert G(A16, A16, A16, A16, A16, 48, 64, 48, 128, None) == SHAPE      # N % 32
+    assert G(A16, A16, A16, A16, A16, 32, 64, 64, 128, None) == SHAPE      # ldc < N
+    assert G(A16, A16, A16, A16, A16, 64, -1, 64, 128, None) == SHAPE
+    assert G(None, A16, A16, A16, A16, 64, 64, 64, 128, None) == NULL
+    assert G(A16, None, A16, A16, A16, 64, 64, 64, 128, None) == NULL
+    assert G(A16, A16, A16, A16, None, 64, 64, 64, 128, None) == NULL
+    assert G(A16 + 8, A16, A16, A16, A16, 64, 64, 64, 128, None) == MISALIGNED
+    assert G(A16, A16 + 2, A16, A16, A16, 64, 64, 64, 128, None) == MISALIGNED
+    assert G(A16, A16, A16, A16, A16 + 2, 64, 64, 64, 128, None) == MISALIGNED
+    assert G(A16, A16, A16, A16, A16, 68, 64, 64, 128, None) == MISALIGNED  # ldc % 8
+    assert G(None, None, None, None, None, 64, 0, 64, 128, None) == OK
+
+
+def test_grouped_gemm_validation(L):
+    G = L.mxfp8_grouped_gemm
+    assert G(A16, A16, A16, A16, A16, 0, A16, 64, 64, 64, 128, None) == SHAPE
+    assert G(A16, A16, A16, A16, A16, 70000, A16, 64, 64, 64, 128, None) == SHAPE
+    assert G(A16, A16, A16, A16, None, 4, A16, 64, 64, 64, 128, None) == NULL
+    assert G(A16, A16, A16, A16, A16 + 2, 4, A16, 64, 64, 64, 128, None) == MISALIGNED
+    assert G(A16, A16, A16, A16, None, 4, None, 64, 0, 64, 128, None) == OK
+
+
+def test_binding_raises_on_error(L):
+    with pytest.raises(mx.MXFP8Error) as ei:
+        mx.mxfp8_quantize(A16, 64, 48, 64, ROW, A16, A16, stream=0)
+    assert ei.value.status == SHAPE and "SHAPE" in str(ei.value)

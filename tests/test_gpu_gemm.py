@@ -1,0 +1,275 @@
+"""GPU parity of mxfp8_pack_scales (bit-exact), mxfp8_gemm and
+mxfp8_grouped_gemm against the CPU oracle (BF16 outputs within
+|gpu - ref| <= 8e-3 |ref| + 1e-3 sqrt(K) rms(ref); exact where the exact
+result is a BF16 value)."""
+
+import numpy as np
+import pytest
+
+import mxfp8_block_scaled_quantize_amd as mx
+import oracle
+import workloads
+from gpu_util import (bf16_to_f64, gemm_tolerance_check, log, need_gpu, sample_indices, to_dev,
+                      to_dev_bf16, to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+def quantize_on_gpu(bits, colwise=False):
+    """Rowwise (or transposed columnwise) MXFP8 copy made by the GPU path,
+    with its packed scales; all device tensors."""
+    need_gpu()
+    x = to_dev_bf16(bits)
+    out = mx.quantize(x, rowwise=not colwise, colwise=colwise)
+    q, s = (out["q_colT"], out["s_colT"]) if colwise else (out["q_row"], out["s_row"])
+    return q, s, mx.pack_scales(s)
+
+
+def gemm_gpu(qa, pa, qb, pb, ldc=None, canary=False):
+    torch = need_gpu()
+    M, K = qa.shape
+    N = qb.shape[0]
+    ldc = N if ldc is None else ldc
+    G = 1024 if canary else 0
+    full = torch.full((M * ldc + 2 * G,), -12345, dtype=torch.int16, device="cuda")
+    c = full[G:G + M * ldc].view(torch.bfloat16)
+    mx.mxfp8_gemm(qa, pa, qb, pb, c, ldc, M, N, K)
+    torch.cuda.synchronize()
+    h = to_host(full.view(torch.bfloat16))
+    if canary:
+        assert np.all(h[:G] == np.uint16(-12345 & 0xFFFF)) and np.all(h[-G:] == np.uint16(-12345 & 0xFFFF))
+        inner = h[G:G + M * ldc].reshape(M, ldc)
+        assert np.all(inner[:, N:] == np.uint16(-12345 & 0xFFFF)), "columns beyond N written"
+    return h[G:G + M * ldc].reshape(M, ldc)[:, :N]
+
+
+# ------------------------------------------------------------- packing
+
+@pytest.mark.parametrize("dim,K", [(32, 128), (96, 512), (1000, 4096), (64, 128 * 67)])
+def test_pack_scales_bit_exact(dim, K):
+    torch = need_gpu()
+    rng = np.random.default_rng(dim + K)
+    s = rng.integers(0, 256, size=(dim, K // 32)).astype(np.uint8)
+    log("pack dim=%d K=%d" % (dim, K))
+    got = to_host(mx.pack_scales(to_dev(s)))
+    assert np.array_equal(got, oracle.pack_scales(s))
+    # strided source (ld_s > K/32)
+    wide = np.zeros((dim, K // 32 + 12), dtype=np.uint8)
+    wide[:, :K // 32] = s
+    ws = to_dev(wide)
+    out = torch.empty((K // 128, dim), dtype=torch.int32, device="cuda")
+    mx.mxfp8_pack_scales(ws, dim, K, wide.shape[1], out)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(out), oracle.pack_scales(s))
+
+
+# -------------------------------------------------------- dense GEMM
+
+def check_dense(a_bits, b_bits, label, rows=None, cols=None, ldc=None, canary=False):
+    qa, sa, pa = quantize_on_gpu(a_bits)
+    qb, sb, pb = quantize_on_gpu(b_bits)
+    K = a_bits.shape[1]
+    log("%s M=%d N=%d K=%d" % (label, a_bits.shape[0], b_bits.shape[0], K))
+    c = gemm_gpu(qa, pa, qb, pb, ldc=ldc, canary=canary)
+    # oracle on its own quantization of the same inputs
+    oqa, osa = oracle.quantize_rowwise(a_bits)
+    oqb, osb = oracle.quantize_rowwise(b_bits)
+    ref = oracle.gemm_tn(oqa, osa, oqb, osb, rows=rows, cols=cols)
+    mag = oracle.gemm_tn_abs(oqa, osa, oqb, osb, rows=rows, cols=cols)
+    sub = c if rows is None else c[np.ix_(rows, cols)]
+    return gemm_tolerance_check(sub, ref, K, mag, label), sub, ref
+
+
+def test_tiny_config():
+    d = workloads.tiny()
+    check_dense(d["A"], d["B"], "tiny", canary=True)
+
+
+@pytest.mark.parametrize("M,N,K", [(32, 32, 128), (96, 224, 384), (160, 96, 1024), (1000, 320, 256),
+                                   (7, 64, 128), (256, 4096, 128), (130, 160, 2048)])
+def test_ragged_gemm_shapes(M, N, K):
+    a = workloads.normal_bf16((M, K), M + K)
+    b = workloads.normal_bf16((N, K), N + 3 * K, std=0.5)
+    check_dense(a, b, "ragged", ldc=N + 24, canary=True)
+
+
+def test_identity_gives_dequantized_b_exactly():
+    a = (np.eye(256, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    b = workloads.normal_bf16((256, 256), 1)
+    qa, sa, pa = quantize_on_gpu(a)
+    qb, sb, pb = quantize_on_gpu(b)
+    log("identity")
+    c = gemm_gpu(qa, pa, qb, pb)
+    want = oracle.dequantize(*oracle.quantize_rowwise(b)).T
+    assert np.array_equal(bf16_to_f64(c), want)
+
+
+def test_small_integers_exact():
+    rng = np.random.default_rng(10)
+    A = rng.integers(-14, 15, size=(192, 640))
+    B = rng.integers(-14, 15, size=(160, 640))
+    ab = (A.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    bb = (B.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    qa, sa, pa = quantize_on_gpu(ab)
+    qb, sb, pb = quantize_on_gpu(bb)
+    log("integers")
+    c = gemm_gpu(qa, pa, qb, pb)
+    exact = (A @ B.T).astype(np.float64)
+    # every |sum| < 2^16 here; BF16 keeps 8 significant bits: compare against
+    # the round-to-nearest-even BF16 of the exact integer
+    want = bf16_to_f64(workloads.f32_to_bf16_bits(exact.astype(np.float32)))
+    assert np.array_equal(bf16_to_f64(c), want)
+
+
+def test_one_scale_byte_doubles_exactly_its_block():
+    # P8: bump one E8M0 byte of A (row 37, K-block 5) by one: only row 37
+    # changes, and only through K [160, 192).  A tile spanning several MFMA
+    # blocks (256 x 256 x 512) catches scale-layout mistakes.
+    torch = need_gpu()
+    a = workloads.normal_bf16((256, 512), 21)
+    b = workloads.normal_bf16((256, 512), 22)
+    qa, sa, pa = quantize_on_gpu(a)
+    qb, sb, pb = quantize_on_gpu(b)
+    base = gemm_gpu(qa, pa, qb, pb)
+    sa2 = sa.clone()
+    sa2[37, 5] += 1
+    pa2 = mx.pack_scales(sa2)
+    log("one-hot scale")
+    c2 = gemm_gpu(qa, pa2, qb, pb)
+    assert np.array_equal(np.delete(c2, 37, 0), np.delete(base, 37, 0))
+    oqa, osa = oracle.quantize_rowwise(a)
+    oqb, osb = oracle.quantize_rowwise(b)
+    osa2 = osa.copy()
+    osa2[37, 5] += 1
+    ref = oracle.gemm_tn(oqa, osa2, oqb, osb, rows=[37])
+    gemm_tolerance_check(c2[37:38], ref, 512, label="bumped row")
+    delta = oracle.gemm_tn(oqa[:, 160:192], osa[:, 5:6], oqb[:, 160:192], osb[:, 5:6], rows=[37])
+    assert np.abs(delta).max() > 0
+    _ = torch
+
+
+def test_k_zero_writes_zeros():
+    torch = need_gpu()
+    c = torch.full((64, 96), 3.0, dtype=torch.bfloat16, device="cuda")
+    mx.mxfp8_gemm(None, None, None, None, c, 96, 64, 96, 0)
+    torch.cuda.synchronize()
+    assert torch.all(c == 0).item()
+
+
+# --------------------------------------------------------- grouped GEMM
+
+def grouped_case(M, N, K, counts, seed, canary_rows=True):
+    torch = need_gpu()
+    G = len(counts)
+    x = workloads.normal_bf16((M, K), seed)
+    w = workloads.normal_bf16((G, N, K), seed + 1, std=0.02)
+    off = workloads.offsets_from_counts(counts)
+    qx, sx, px = quantize_on_gpu(x)
+    wq = quantize_on_gpu(w.reshape(G * N, K))
+    qw = wq[0].view(G, N, K)
+    pw = wq[2]
+    out = torch.full((M, N), -7.0, dtype=torch.bfloat16, device="cuda")
+    log("grouped M=%d N=%d K=%d counts=%s" % (M, N, K, list(counts)))
+    mx.grouped_gemm(qx, px, qw, pw, to_dev(off), out=out)
+    torch.cuda.synchronize()
+    c = to_host(out)
+    oqx, osx = oracle.quantize_rowwise(x)
+    oq = [oracle.quantize_rowwise(w[g]) for g in range(G)]
+    qwo = np.stack([q for q, _ in oq])
+    swo = np.stack([s for _, s in oq])
+    covered = np.zeros(M, dtype=bool)
+    covered[off[0]:off[-1]] = True
+    rows = np.nonzero(covered)[0]
+    ref = oracle.grouped_gemm_tn(oqx, osx, qwo, swo, off, rows=rows)
+    gemm_tolerance_check(c[rows], ref, K, label="grouped")
+    if canary_rows:
+        assert np.all(bf16_to_f64(c[~covered]) == -7.0), "rows outside the groups were written"
+
+
+def test_grouped_uniform_counts():
+    grouped_case(1024, 256, 512, [128] * 8, 3)
+
+
+def test_grouped_ragged_and_empty():
+    grouped_case(2048, 320, 384, [0, 320, 0, 0, 736, 32, 960, 0], 5)
+
+
+def test_grouped_unaligned_counts_and_uncovered_tail():
+    grouped_case(1200, 96, 256, [5, 0, 131, 257, 600], 6)   # rows 993.. belong to no group
+
+
+def test_grouped_single_group_matches_dense():
+    grouped_case(512, 128, 256, [512], 7)
+
+
+def test_grouped_empty_total():
+    torch = need_gpu()
+    off = to_dev(np.zeros(5, dtype=np.int32))
+    c = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    mx.mxfp8_grouped_gemm(None, None, None, None, off, 4, c, 64, 0, 64, 128)
+
+
+# ------------------------------------------------------ full workload sizes
+
+@pytest.mark.slow
+def test_full_dense_linear_sampled():
+    d = workloads.dense_linear()
+    rows = sample_indices(8192, 48, 1)
+    cols = sample_indices(14336, 48, 2)
+    check_dense(d["X"], d["W"], "dense 8192x14336x4096", rows=rows, cols=cols)
+
+
+@pytest.mark.slow
+def test_full_dense_square_sampled():
+    d = workloads.dense_square()
+    rows = sample_indices(8192, 40, 3)
+    cols = sample_indices(8192, 40, 4)
+    check_dense(d["A"], d["B"], "dense 8192^3", rows=rows, cols=cols)
+
+
+@pytest.mark.slow
+def test_full_backward_wgrad_sampled():
+    d = workloads.backward()
+    qa, sa, pa = quantize_on_gpu(d["dY"], colwise=True)    # [4096][16384]
+    qb, sb, pb = quantize_on_gpu(d["X"], colwise=True)     # [4096][16384]
+    log("wgrad 4096x4096x16384")
+    c = gemm_gpu(qa, pa, qb, pb)
+    rows = sample_indices(4096, 40, 5)
+    cols = sample_indices(4096, 40, 6)
+    oqa, osa = oracle.quantize_colwise(d["dY"])
+    oqb, osb = oracle.quantize_colwise(d["X"])
+    ref = oracle.gemm_tn(oqa, osa, oqb, osb, rows=rows, cols=cols)
+    gemm_tolerance_check(c[np.ix_(rows, cols)], ref, 16384, label="wgrad")
+
+
+@pytest.mark.slow
+def test_full_stress_sampled():
+    d = workloads.stress()
+    a = d["A"]
+    # include the rows that carry max-BF16 values (overflow exclusion applies)
+    hot = np.unique(np.nonzero((a & 0x7FFF) == workloads.BF16_MAX_BITS)[0])[:8]
+    rows = np.unique(np.concatenate([sample_indices(32768, 32, 7), hot]))
+    cols = sample_indices(8192, 32, 8)
+    n_ex, _, _ = check_dense(a, d["B"], "stress 32768x8192x8192", rows=rows, cols=cols)
+    log("stress: %d entries excluded for overflow" % n_ex)
+
+
+@pytest.mark.slow
+def test_full_moe_sampled():
+    torch = need_gpu()
+    d = workloads.moe()
+    x, w, off = d["X"], d["W"], d["offsets"]
+    G, N, K = w.shape
+    qx, sx, px = quantize_on_gpu(x)
+    wq = quantize_on_gpu(w.reshape(G * N, K))
+    log("moe grouped 16384x14336x4096 counts=%s" % np.diff(off).tolist())
+    c = mx.grouped_gemm(qx, px, wq[0].view(G, N, K), wq[2], to_dev(off))
+    torch.cuda.synchronize()
+    rows = sample_indices(16384, 48, 9)
+    cols = sample_indices(N, 32, 10)
+    ch = to_host(c)[np.ix_(rows, cols)]
+    oqx, osx = oracle.quantize_rowwise(x)
+    ws = [oracle.quantize_rowwise(w[g]) for g in range(G)]
+    ref = oracle.grouped_gemm_tn(oqx, osx, np.stack([q for q, _ in ws]), np.stack([s for _, s in ws]), off,
+                                 rows=rows, cols=cols)
+    gemm_tolerance_check(ch, ref, K, label="moe")

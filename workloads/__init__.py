@@ -39,9 +39,13 @@ BF16_MAX_BITS = 0x7F7F  # largest finite BF16 magnitude, about 3.39e38
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to BF16 (nearest, ties to even) -> uint16 bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return u.astype(np.uint16)
+    u = x.view(np.uint32)
+    lsb = u >> 16
+    lsb &= 1
+    lsb += 0x7FFF
+    lsb += u          # finite floats stay below 2^32 (largest is 0xFF7FFFFF + 0x8000)
+    lsb >>= 16
+    return lsb.astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
