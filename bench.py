@@ -34,8 +34,10 @@ def parse():
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=8192,
-                   help="rows of X in the CPU-oracle sample")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="minimum CPU-oracle time: whole oracle steps are repeated until reached")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run one plain 256 MiB device copy (reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -112,6 +114,12 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     events = []
     torch.cuda.synchronize()
@@ -176,15 +184,15 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(lin, args.cpu_rows)
+        result["cpu_baseline"] = cpu_baseline(host, args.cpu_seconds)
 
     print(json.dumps(result))
 
 
-def cpu_baseline(lin, m_rows):
-    """The CPU oracle on a bounded sample of the same work: quantize the first
-    m_rows rows of X and all of W, dequantize, fp64 GEMM m_rows x 14336 x 4096.
-    Reported as GEMM TFLOP/s of that sample, like ``value``."""
+def cpu_baseline(host, min_seconds):
+    """The CPU oracle on the same step: rowwise quantize of X, W, A, B, scale
+    packing, and the two GEMMs in fp64; whole steps are repeated until
+    min_seconds have passed.  Reported as GEMM TFLOP/s, like ``value``."""
     import numpy as np
     import oracle
     try:
@@ -192,22 +200,24 @@ def cpu_baseline(lin, m_rows):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas_threads = 1
-    x = np.ascontiguousarray(lin["X"][:m_rows])
-    w = lin["W"]
+    flops = 2.0 * (8192 * 14336 * 4096 + 8192 * 8192 * 8192)
+    steps = 0
     t0 = time.perf_counter()
-    qx, sx = oracle.quantize_rowwise(x)
-    qw, sw = oracle.quantize_rowwise(w)
-    px = oracle.pack_scales(sx)
-    pw = oracle.pack_scales(sw)
-    c = oracle.gemm_tn(qx, sx, qw, sw)
-    t1 = time.perf_counter()
-    _ = (px, pw, c)
-    flops = 2.0 * m_rows * w.shape[0] * w.shape[1]
-    return {"value": round(flops / (t1 - t0) / 1e12, 5), "unit": "TFLOP/s",
+    while True:
+        q = {name: oracle.quantize_rowwise(bits) for name, bits in host.items()}
+        _ = [oracle.pack_scales(s) for _, s in q.values()]
+        for a, b in (("X", "W"), ("A", "B")):
+            c = oracle.gemm_tn(*q[a], *q[b])
+            del c
+        steps += 1
+        t1 = time.perf_counter()
+        if t1 - t0 >= min_seconds:
+            break
+    return {"value": round(steps * flops / (t1 - t0) / 1e12, 5), "unit": "TFLOP/s",
             "cores": int(max(oracle.num_threads(), blas_threads)), "kind": "oracle",
-            "seconds": round(t1 - t0, 2),
-            "sample": "rows 0..%d of X[8192x4096] with all of W[14336x4096]: oracle rowwise quantize of both, "
-                      "scale packing, fp64 GEMM %dx14336x4096" % (m_rows - 1, m_rows)}
+            "seconds": round(t1 - t0, 2), "steps": steps,
+            "sample": "%d whole step(s) of the same workload on the host: oracle rowwise quantize of X, W, A, B, "
+                      "scale packing, fp64 GEMMs 8192x14336x4096 and 8192x8192x8192" % steps}
 
 
 if __name__ == "__main__":

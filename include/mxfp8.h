@@ -161,7 +161,7 @@ mxfp8_status mxfp8_pack_scales(const uint8_t *s, int64_t dim, int64_t k, int64_t
  * b         E4M3 codes B [N][K], 16-byte aligned.
  * b_packed  packed scales of B, uint32 [K/128][N].
  * c         BF16 output [M][ldc], 16-byte aligned; ldc >= N, ldc % 8 == 0.
- * M >= 0; N >= 0 and N % 32 == 0; K >= 0 and K % 128 == 0.
+ * M >= 0; N >= 0 and N % 32 == 0; K >= 0, K % 128 == 0 and K <= 2^22.
  * K == 0 writes zeros.  The output must not overlap the inputs.
  * Overflow beyond BF16 range gives +-inf, like the fp32->BF16 rounding.
  * Errors: NULL, SHAPE, MISALIGNED, LIMIT, HIP.
@@ -200,7 +200,7 @@ mxfp8_status mxfp8_gemm(const uint8_t *a, const uint32_t *a_packed,
  *            access leaves the buffers.
  * G          1 <= G <= 65536.
  * c          BF16 [M_total][ldc]; ldc >= N, ldc % 8 == 0.
- * M_total >= 0; N >= 0 and N % 32 == 0; K >= 0 and K % 128 == 0.
+ * M_total >= 0; N >= 0 and N % 32 == 0; K >= 0, K % 128 == 0 and K <= 2^22.
  * Errors: NULL, SHAPE, MISALIGNED, LIMIT, HIP.
  */
 mxfp8_status mxfp8_grouped_gemm(const uint8_t *a, const uint32_t *a_packed,

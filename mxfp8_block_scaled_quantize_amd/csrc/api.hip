@@ -12,6 +12,7 @@ thread_local int g_last_hip_error = 0;
 
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;  // one-dimensional grid limit
 constexpr int64_t kMaxDim = int64_t(1) << 40; // keeps every element offset well inside int64
+constexpr int64_t kMaxGemmK = int64_t(1) << 22; // a 256-row operand tile stays below 2^31 bytes
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -54,6 +55,7 @@ mxfp8_status check_gemm_common(const uint8_t* a, const uint32_t* ap, const uint8
                                const void* c, int64_t ldc, int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K < 0) return MXFP8_ERR_SHAPE;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim || ldc > kMaxDim) return MXFP8_ERR_LIMIT;
+  if (K > kMaxGemmK) return MXFP8_ERR_LIMIT;
   if (N % 32 || K % 128 || ldc < N) return MXFP8_ERR_SHAPE;
   if (M == 0 || N == 0) return MXFP8_OK;
   if (!c) return MXFP8_ERR_NULL;

@@ -123,6 +123,7 @@ def test_gemm_validation(L):
     assert G(A16, A16, A16, A16, A16 + 2, 64, 64, 64, 128, None) == MISALIGNED
     assert G(A16, A16, A16, A16, A16, 68, 64, 64, 128, None) == MISALIGNED  # ldc % 8
     assert G(None, None, None, None, None, 64, 0, 64, 128, None) == OK
+    assert G(A16, A16, A16, A16, A16, 64, 64, 64, (1 << 22) + 128, None) == LIMIT
 
 
 def test_grouped_gemm_validation(L):
