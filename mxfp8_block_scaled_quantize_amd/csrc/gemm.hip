@@ -44,6 +44,8 @@ constexpr int SB_OFF = SA_OFF + BM * 4;
 constexpr int SLOT_BYTES = SB_OFF + BN * 4;          // 34 KB
 constexpr int LDS_BYTES = NSLOT * SLOT_BYTES;        // 136 KB
 constexpr int GROUP_M = 4;              // row tiles per L2 group
+constexpr int C_LDS_STRIDE = 2 * BN + 16;            // BF16 output tile row in LDS, padded (528 B)
+static_assert(BM * C_LDS_STRIDE <= LDS_BYTES, "output tile must fit in the ring");
 constexpr uint32_t RSRC_FLAGS = 0x00020000u;         // raw buffer, 32-bit data format
 
 template <int N>
@@ -232,9 +234,18 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
     if (st + 4 < nk) issue_step(st + 4, EVEN);
-    if (st + 1 < nk)
-      read_frags(st + 1, ic<1 - decltype(SET)::value>{}, ic<!even>{}, ic<1 - decltype(T2)::value>{});
+    // Fragments of st+1 are read unconditionally (after the last step they
+    // read a stale slot and are never used) so that the reads and the MFMAs
+    // share one basic block and can be interleaved: one MFMA, then up to two
+    // LDS reads, keeping the MFMA pipe fed while the LDS queue drains.
+    read_frags(st + 1, ic<1 - decltype(SET)::value>{}, ic<!even>{}, ic<1 - decltype(T2)::value>{});
     mfma_step(SET, T2, OP);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // scale shifts
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+    }
   };
 
   if (nk > 0) {
@@ -256,27 +267,43 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
     }
   }
 
-  // ---- epilogue: fp32 -> BF16 (RNE); lane pairs swap values so each lane
-  // stores two adjacent columns of one row as one 32-bit word.
-  const bool odd = lane & 1;
-  const int64_t row_base = m_lo + wm * 128 + 4 * lg;
-  const int64_t col_base = n0 + wn * 128 + lr;
+  // ---- epilogue: fp32 -> BF16 (RNE) into a padded row-major LDS tile (the
+  // ring is free once every wave is past its last step), then 16-byte
+  // stores that cover whole 512-byte row segments of C.  Lane pairs swap
+  // values so each LDS write is one 32-bit word (two adjacent columns).
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  {
+    const bool odd = lane & 1;
+    const int rb = wm * 128 + 4 * lg;
+    const int cb = wn * 128 + lr - (odd ? 1 : 0);
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int64_t col = col_base + 32 * j;
-    if (n0 + wn * 128 + 32 * j >= N) continue;     // N % 32 == 0: whole 32-column blocks
-    const int64_t cst = odd ? col - 1 : col;
+    for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+      for (int j = 0; j < 4; j++)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const uint32_t a = f32_to_bf16_rne(acc[i][j][r]);
-        const uint32_t b = f32_to_bf16_rne(acc[i][j][r + 1]);
-        const uint32_t x = odd ? a : b;
-        const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);  // lane ^ 1
-        const uint32_t word = odd ? (y | (b << 16)) : (a | (y << 16));
-        const int64_t row = row_base + 32 * i + 8 * (r >> 2) + (r & 3) + (odd ? 1 : 0);
-        if (row < m_hi) *reinterpret_cast<uint32_t*>(Cm + row * ldc + cst) = word;
+        for (int r = 0; r < 16; r += 2) {
+          const uint32_t a = f32_to_bf16_rne(acc[i][j][r]);
+          const uint32_t b = f32_to_bf16_rne(acc[i][j][r + 1]);
+          const uint32_t x = odd ? a : b;
+          const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);  // lane ^ 1
+          const uint32_t word = odd ? (y | (b << 16)) : (a | (y << 16));
+          const int row = rb + 32 * i + 8 * (r >> 2) + (r & 3) + (odd ? 1 : 0);
+          *(__attribute__((address_space(3))) uint32_t*)(smem + row * C_LDS_STRIDE + 2 * (cb + 32 * j)) = word;
+        }
+  }
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  {
+    const int ch = tid & 31;           // 16-byte chunk of a 512-byte tile row
+    const int64_t col = n0 + 8 * ch;
+    if (col < N) {
+#pragma unroll 8
+      for (int k = 0; k < 32; k++) {
+        const int row = (tid >> 5) + 8 * k;
+        const int64_t grow = m_lo + row;
+        const u32x4 v = *(lds_u32x4*)(smem + row * C_LDS_STRIDE + 16 * ch);
+        if (grow < m_hi) store_nt16(Cm + grow * ldc + col, make_uint4(v.x, v.y, v.z, v.w));
       }
     }
   }
