@@ -41,6 +41,34 @@ def parse():
     return p.parse_args()
 
 
+def gemm_source_hash():
+    """Hash of the sources that define the GEMM kernel (profile traffic is tied to it)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("mxfp8_block_scaled_quantize_amd/csrc/gemm.hip", "mxfp8_block_scaled_quantize_amd/csrc/mx_device.h"):
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(kernel_key):
+    """HBM-side bytes per launch from the rocprofv3 summaries in profiles/, or None
+    when no summary was taken for the current GEMM sources."""
+    src = gemm_source_hash()
+    pdir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(pdir):
+        return None
+    for name in sorted(os.listdir(pdir)):
+        with open(os.path.join(pdir, name)) as fh:
+            for line in fh:
+                parts = line.split()
+                if len(parts) >= 5 and parts[0] == "traffic" and " ".join(parts[1:3]) == kernel_key \
+                        and parts[3] == "src=" + src:
+                    kv = dict(p.split("=", 1) for p in parts[4:] if "=" in p)
+                    return int(kv["read_bytes"]) + int(kv["write_bytes"]), name
+    return None
+
+
 def quant_bytes(rows, cols):
     """Algorithmic bytes of a rowwise quantize: read 2 B, write 1 + 1/32 B per element."""
     return rows * cols * (2 + 1 + 1.0 / 32)
@@ -157,9 +185,13 @@ def main():
     dom_t = avg[("gemm", "XW")]
     dom_flops = gemm_flops["XW"]
     achieved = dom_flops / (dom_t * 1e-3) / 1e12
+    prof = profiled_traffic("gemm 8192x14336x4096")
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": prof[0] if prof else None,
                 "kernel": "mxfp8 gemm 8192x14336x4096", "ms": round(dom_t, 4)}
+    if prof:
+        roofline["traffic_unit"] = "bytes per launch (HBM side, calibrated FETCH_SIZE + WRITE_SIZE)"
+        roofline["traffic_source"] = "profiles/" + prof[1]
 
     result = {
         "metric": METRIC,

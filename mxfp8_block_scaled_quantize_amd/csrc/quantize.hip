@@ -4,7 +4,8 @@
 // owns rows [32w, 32w + 32) of the tile; lane (rg = lane / 16, cg = lane % 16)
 // owns the 8 x 8 sub-block rows 32w + 8rg + [0, 8), columns 8cg + [0, 8), read
 // with eight 16-byte loads (each load instruction of a wave covers four rows
-// of 256 contiguous bytes).
+// of 256 contiguous bytes).  Plain (cached) loads measured faster here than
+// non-temporal ones; the transposed copy is stored non-temporally.
 //
 //  - rowwise 32-blocks are 4 consecutive lanes (a DPP quad) in one row;
 //  - columnwise 32-blocks are the 4 lanes cg, cg+16, cg+32, cg+48 of a wave
@@ -43,9 +44,30 @@ __global__ __launch_bounds__(Q_THREADS) void quantize_tile_kernel(
   const int w = tid >> 6;
   const int cg = lane & 15;
   const int rg = lane >> 4;
-  const int64_t tile = blockIdx.x;
-  const int64_t tr = tile / tiles_c;
-  const int64_t tc = tile - tr * tiles_c;
+  int64_t tr, tc;
+  if (ROW && !COL) {
+    // Rowwise only: workgroup ids are dealt round-robin to the 8 XCDs; remap
+    // them so each XCD walks its own share in groups of 8 x 8 tiles.  The 8
+    // column tiles of a group write 8 x 4 = 32 contiguous scale bytes per row
+    // from one L2, instead of 4-byte pieces from 8 different L2s.
+    const int64_t ntile = gridDim.x;
+    const int64_t bid = blockIdx.x;
+    const int64_t full = (ntile / 8) * 8;
+    const int64_t lid = bid < full ? (bid & 7) * (full >> 3) + (bid >> 3) : bid;
+    const int64_t tiles_r = ntile / tiles_c;
+    const int64_t per_band = 8 * tiles_c;                          // tiles in 8 row tiles
+    const int64_t band = lid / per_band;
+    const int64_t hb = (tiles_r - 8 * band) < 8 ? (tiles_r - 8 * band) : 8;
+    const int64_t inb = lid - band * per_band;
+    const int64_t grp = inb / (8 * hb);
+    const int64_t wg = (tiles_c - 8 * grp) < 8 ? (tiles_c - 8 * grp) : 8;
+    const int64_t ing = inb - grp * 8 * hb;
+    tr = 8 * band + ing / wg;
+    tc = 8 * grp + ing % wg;
+  } else {
+    tr = (int64_t)blockIdx.x / tiles_c;
+    tc = (int64_t)blockIdx.x - tr * tiles_c;
+  }
   const int64_t r0 = tr * QT_R;
   const int64_t c0 = tc * QT_C;
   const int64_t rb = r0 + 32 * w + 8 * rg;  // first row of this lane
@@ -56,7 +78,7 @@ __global__ __launch_bounds__(Q_THREADS) void quantize_tile_kernel(
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     if (cval && rb + i < R)
-      v[i] = load_nt16(x + (rb + i) * ldx + cb);
+      v[i] = *reinterpret_cast<const uint4*>(x + (rb + i) * ldx + cb);
     else
       v[i] = make_uint4(0u, 0u, 0u, 0u);
   }
@@ -169,6 +191,49 @@ __global__ __launch_bounds__(Q_THREADS) void quantize_tile_kernel(
   }
 }
 
+// Rowwise copy of a contiguous input (ld_x == cols): blocks never cross rows
+// (cols % 32 == 0), so the tensor is one flat stream of 32-element blocks and
+// the scales [rows][cols/32] are the flat block index.  Each wave quantizes
+// FL_ELEMS contiguous elements: load u of lane l covers elements
+// 512u + 8l + [0, 8), i.e. every load instruction reads 1 KB contiguous, each
+// DPP quad holds one block, codes go out (non-temporally) as 512-byte runs and
+// the wave's 32 scale bytes are contiguous.  Two loads per lane measured best
+// (more waves in flight than with four or eight).
+constexpr int FL_LOADS = 2;
+constexpr int64_t FL_ELEMS = 512 * FL_LOADS;  // per wave
+
+__global__ __launch_bounds__(Q_THREADS) void quantize_rowwise_flat_kernel(const uint16_t* __restrict__ x,
+                                                                         int64_t total,
+                                                                         uint8_t* __restrict__ q,
+                                                                         uint8_t* __restrict__ s) {
+  const int lane = threadIdx.x & 63;
+  const int64_t base = ((int64_t)blockIdx.x * (Q_THREADS / 64) + (threadIdx.x >> 6)) * FL_ELEMS;
+  uint4 v[FL_LOADS];
+#pragma unroll
+  for (int u = 0; u < FL_LOADS; u++) {
+    const int64_t e = base + 512 * u + 8 * lane;
+    v[u] = e < total ? *reinterpret_cast<const uint4*>(x + e) : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int u = 0; u < FL_LOADS; u++) {
+    const int64_t e = base + 512 * u + 8 * lane;
+    uint32_t m = pk_max_u16(pk_max_u16(abs_bits2(v[u].x), abs_bits2(v[u].y)),
+                            pk_max_u16(abs_bits2(v[u].z), abs_bits2(v[u].w)));
+    m = max(m & 0xFFFFu, m >> 16);
+    m = quad_max(m);
+    const uint32_t byte = scale_byte_from_amax(m);
+    const float sc = inv_scale(byte);
+    uint2 o;
+    o.x = cvt4_e4m3(bf_lo(v[u].x) * sc, bf_hi(v[u].x) * sc, bf_lo(v[u].y) * sc, bf_hi(v[u].y) * sc);
+    o.y = cvt4_e4m3(bf_lo(v[u].z) * sc, bf_hi(v[u].z) * sc, bf_lo(v[u].w) * sc, bf_hi(v[u].w) * sc);
+    if (e < total) {  // total % 32 == 0: a quad is entirely in or out
+      __builtin_nontemporal_store(o.x, reinterpret_cast<uint32_t*>(q + e));
+      __builtin_nontemporal_store(o.y, reinterpret_cast<uint32_t*>(q + e) + 1);
+      if ((lane & 3) == 0) s[e >> 5] = (uint8_t)byte;
+    }
+  }
+}
+
 // dbias[c] = sum over row tiles of the partial sums, in four interleaved
 // chains combined pairwise (a fixed order: the result is deterministic).
 __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float* __restrict__ part, int64_t tiles,
@@ -203,6 +268,14 @@ hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
   const bool row = flags & 1u, col = flags & 2u, db = flags & 4u;
   const int64_t tr = quantize_row_tiles(R), tc = quantize_col_tiles(C);
   const int64_t tiles = tr * tc;
+  if (row && !col && !db && ldx == C) {
+    const int64_t total = R * C;
+    const int64_t blocks = (total + FL_ELEMS * (Q_THREADS / 64) - 1) / (FL_ELEMS * (Q_THREADS / 64));
+    if (blocks > 0)
+      hipLaunchKernelGGL(quantize_rowwise_flat_kernel, dim3((unsigned)blocks), dim3(Q_THREADS), 0, stream, x, total,
+                         q_row, s_row);
+    return hipGetLastError();
+  }
   if (tiles > 0) {
     const dim3 grid((unsigned)tiles), block(Q_THREADS);
 #define MX_Q_LAUNCH(RW, CL, DB)                                                                   \
