@@ -5,22 +5,27 @@
 // Operand layout of V_MFMA_SCALE_F32_32X32X64_F8F6F4 with E4M3 on both sides,
 // as measured on gfx950: lane l holds row (l % 32) of the 32-row block; its
 // bytes 0..15 are K = 16*(l/32) + [0,16) and bytes 16..31 are
-// K = 32 + 16*(l/32) + [0,16) of the 64-wide K step.  The scale operand of
-// lane l (byte chosen by op_sel) scales row (l % 32), K-block (l / 32) of the
-// step.  Result register i of lane l is row 8*(i/4) + 4*(l/32) + (i%4),
-// column l % 32.
+// K = 32 + 16*(l/32) + [0,16) of the 64-wide K step.  Bytes 0..15 of every
+// lane are scaled by the scale operand of lane (l % 32) and bytes 16..31 by
+// that of lane 32 + (l % 32) (byte chosen by op_sel): lane l supplies the
+// scale of K-block l / 32.  Result register i of lane l is row
+// 8*(i/4) + 4*(l/32) + (i%4), column l % 32.
 //
 // Tiling: one workgroup of 4 waves computes a 256 x 256 tile; wave (wm, wn)
-// owns 128 x 128 = 4 x 4 MFMA blocks (256 fp32 accumulators per lane).  K is
-// consumed in 64-byte steps through a 4-slot LDS ring (34 KB per slot: A and
-// B 256 x 64 bytes each, plus the packed scale words of a 128-wide K slab).
-// Slots are filled by buffer->LDS DMA (16 bytes per lane, rows past the end
-// of the matrix read as zero) issued four steps ahead; operand fragments of
-// step s+1 are read from LDS while the MFMAs of step s run.  16-byte chunks
-// of each 64-byte LDS row are XOR-swizzled by (row >> 2) & 3, which makes
-// every fragment read conflict free.  Workgroup ids are remapped so that the
-// tiles resident on one XCD (ids are dealt round-robin to the 8 XCDs) form
-// compact groups of 4 row tiles, sharing A and B in that XCD's L2.
+// owns 128 x 128 = 4 x 4 MFMA blocks (256 fp32 accumulators per lane, in
+// AGPRs).  K moves in 128-byte steps through a 2-slot LDS ring (66 KB per
+// slot: A and B 256 x 128 bytes, plus the step's packed scale words), filled
+// by buffer->LDS DMA of whole 128-byte row segments (rows past the end of the
+// operand read as zero).  A step runs as two 64-wide halves with their own
+// fragment registers: the first half's MFMAs overlap the LDS reads of the
+// second half; then one barrier makes step t+1 resident and frees this
+// step's slot; the second half's MFMAs overlap the DMA of step t+2 and the
+// LDS reads of step t+1.  The DMA is branch-free (a step past the end gets
+// zero-length buffer ranges) so the scheduler can interleave it with the
+// MFMAs.  16-byte chunks of each 128-byte LDS row are XOR-swizzled by
+// (row >> 1) & 7, which makes the fragment reads conflict free.  Workgroup ids
+// are remapped so the tiles resident on one XCD (ids are dealt round-robin to
+// the 8 XCDs) form groups of 4 row tiles sharing A and B in that XCD's L2.
 #include "mx_device.h"
 #include "launch.h"
 
@@ -35,8 +40,8 @@ typedef __attribute__((address_space(3))) const uint32_t lds_u32;
 
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int BK = 64;                  // K bytes per pipeline step
-constexpr int NSLOT = 4;
+constexpr int BK = 128;                 // K bytes per pipeline step
+constexpr int NSLOT = 2;
 constexpr int A_BYTES = BM * BK;        // 16 KB
 constexpr int B_BYTES = BN * BK;        // 16 KB
 constexpr int SA_OFF = A_BYTES + B_BYTES;
@@ -46,6 +51,7 @@ constexpr int LDS_BYTES = NSLOT * SLOT_BYTES;        // 136 KB
 constexpr int GROUP_M = 4;              // row tiles per L2 group
 constexpr int C_LDS_STRIDE = 2 * BN + 16;            // BF16 output tile row in LDS, padded (528 B)
 static_assert(BM * C_LDS_STRIDE <= LDS_BYTES, "output tile must fit in the ring");
+static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 constexpr uint32_t RSRC_FLAGS = 0x00020000u;         // raw buffer, 32-bit data format
 
 template <int N>
@@ -71,7 +77,7 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA targets stay scalar
   const int wm = wave >> 1, wn = wave & 1;
 
   // ---- tile selection: XCD-aware remap, then groups of GROUP_M row tiles
@@ -115,102 +121,109 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
   const int rows_a = (int)((m_hi - m_lo) < BM ? (m_hi - m_lo) : BM);
   const int rows_b = (int)((N - n0) < BN ? (N - n0) : BN);
 
-  // ---- DMA sources.  Data: raw buffers over the tile's rows (out-of-range rows read 0).
-  const __amdgpu_buffer_rsrc_t rs_a =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(A + m_lo * K), 0, (int)((int64_t)rows_a * K), RSRC_FLAGS);
-  const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(B + (b_row0 + n0) * K), 0, (int)((int64_t)rows_b * K), RSRC_FLAGS);
-  // lane's 4 DMA row/chunk offsets (same for A and B): LDS rows 16*(4w+i) + lane/4, slot lane%4
-  uint32_t dma_off[4];
+  // ---- DMA addressing (same for A and B).  Data goes through raw buffers
+  // over the tile's rows, so rows past the end of the operand read as zero.
+  // DMA instruction i of wave w covers LDS rows 8(8w+i) + lane/8, chunk slot
+  // lane%8; the swizzle (row>>1)&7 = (4(i&1) + lane/16) & 7 only depends on
+  // the parity of i.
+  uint32_t dma_base[2];
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int r = 16 * (4 * wave + i) + (lane >> 2);
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
-    dma_off[i] = (uint32_t)r * (uint32_t)K + 16u * (uint32_t)c;
+  for (int e = 0; e < 2; e++) {
+    const int r = 64 * wave + (lane >> 3);
+    const int c = (lane & 7) ^ ((4 * e + (lane >> 4)) & 7);
+    dma_base[e] = (uint32_t)r * (uint32_t)K + 16u * (uint32_t)c;
   }
   // scale words: wave w brings rows 64w + lane (clamped into the valid rows)
   const int sra = (64 * wave + lane) < rows_a ? (64 * wave + lane) : rows_a - 1;
   const int srb = (64 * wave + lane) < rows_b ? (64 * wave + lane) : rows_b - 1;
-  const uint32_t* sa_src = Ap + m_lo + sra;
-  const uint32_t* sb_src = Bp + b_row0 + n0 + srb;
 
-  const int nk = (int)(K / BK);  // even: K % 128 == 0
+  const int nk = (int)(K / BK);
 
-  // DMA of one K step into its ring slot: 8 data loads per lane, plus the
-  // scale words of the 128-wide slab on even steps (2 more loads per lane).
-  auto issue_step = [&](int s, auto EVEN) {
-    lds_u8* base = smem + (s & (NSLOT - 1)) * SLOT_BYTES;
-    const uint32_t k0 = (uint32_t)s * BK;
+  // DMA of one 128-wide K step into its slot: 16 data loads per lane (8 rows x
+  // 128 B per instruction) plus the step's two scale words, 18 per lane.  It is
+  // branch-free: a step past the end gets zero-length buffer ranges, so its
+  // loads touch no memory and write zeros to a slot nobody reads.
+  const uint32_t a_rec = (uint32_t)((int64_t)rows_a * K);
+  const uint32_t b_rec = (uint32_t)((int64_t)rows_b * K);
+  auto issue_step = [&](int s) {
+    const bool valid = s < nk;
+    lds_u8* base = smem + (s & 1) * SLOT_BYTES;
+    const uint32_t k0 = valid ? (uint32_t)s * BK : 0u;
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(A + m_lo * K), 0, (int)(valid ? a_rec : 0u), RSRC_FLAGS);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(B + (b_row0 + n0) * K), 0, (int)(valid ? b_rec : 0u), RSRC_FLAGS);
+    const int64_t sv = valid ? s : 0;
+    const __amdgpu_buffer_rsrc_t rsa =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Ap + sv * M + m_lo), 0, valid ? rows_a * 4 : 0, RSRC_FLAGS);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Bp + sv * brows + b_row0 + n0), 0, valid ? rows_b * 4 : 0, RSRC_FLAGS);
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_void*)(base + 1024 * (4 * wave + i)), 16,
-                                               dma_off[i] + k0, 0, 0, 0);
+    for (int i = 0; i < 8; i++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(base + 1024 * (8 * wave + i)), 16,
+                                               dma_base[i & 1] + (uint32_t)(8 * i) * (uint32_t)K + k0, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(base + A_BYTES + 1024 * (4 * wave + i)), 16,
-                                               dma_off[i] + k0, 0, 0, 0);
-    if constexpr (decltype(EVEN)::value) {
-      const int64_t t = s >> 1;
-      __builtin_amdgcn_global_load_lds((const void*)(sa_src + t * M), (lds_void*)(base + SA_OFF + 256 * wave), 4,
-                                       0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(sb_src + t * brows), (lds_void*)(base + SB_OFF + 256 * wave),
-                                       4, 0, 0);
-    }
+    for (int i = 0; i < 8; i++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(base + A_BYTES + 1024 * (8 * wave + i)), 16,
+                                               dma_base[i & 1] + (uint32_t)(8 * i) * (uint32_t)K + k0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(base + SA_OFF + 256 * wave), 4, 4u * (uint32_t)sra, 0,
+                                             0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(base + SB_OFF + 256 * wave), 4, 4u * (uint32_t)srb, 0,
+                                             0, 0);
   };
 
-  // ---- fragment addressing inside a slot
+  // Fragment of lane (row lr, group lg) for K half h: bytes 0..15 are
+  // K = 64h + 16lg + [0,16) and bytes 16..31 are K = 64h + 32 + 16lg + [0,16):
+  // the MFMA scales bytes 0..15 of every lane with the scale of lane lr and
+  // bytes 16..31 with that of lane 32 + lr.
   const int lr = lane & 31;
   const int lg = lane >> 5;
-  const int swz = (lane >> 2) & 3;
+  const int swz = (lr >> 1) & 7;
   const int a_row_off = (wm * 128 + lr) * BK;
   const int b_row_off = A_BYTES + (wn * 128 + lr) * BK;
-  const int c0 = 16 * (lg ^ swz);
-  const int c1 = 16 * ((2 + lg) ^ swz);
+  const uint32_t sh = 8u * (uint32_t)lg;
 
   v8i fa[2][4], fb[2][4];
-  uint32_t sa[2][4], sb[2][4];
+  uint32_t sa[4], sb[4], na[4], nb[4];   // scale words of the current / next step
   v16f acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
     for (int j = 0; j < 4; j++) acc[i][j] = v16f{};
 
-  // LDS -> registers: operand fragments of step s into register set SET; on
-  // even steps also the slab's scale words into scale set T2.  At use the
-  // words are shifted right by 8 * (lane / 32), so that byte 0 is this lane's
-  // K block of the even step and byte 2 that of the odd step.
-  const uint32_t sh = 8u * (uint32_t)lg;
-  auto read_frags = [&](int s, auto SET, auto EVEN, auto T2) {
+  auto slot_base = [&](int s) { return smem + (s & 1) * SLOT_BYTES; };
+  auto read_frags = [&](int s, auto H, auto SET) {
+    constexpr int h = decltype(H)::value;
     constexpr int set = decltype(SET)::value;
-    const lds_u8* base = smem + (s & (NSLOT - 1)) * SLOT_BYTES;
+    const lds_u8* base = slot_base(s);
+    const int p0 = 16 * ((4 * h + lg) ^ swz);       // K = 64h + 16lg + [0,16)  (scale block 2h)
+    const int p1 = 16 * ((4 * h + 2 + lg) ^ swz);   // K = 64h + 32 + 16lg + [0,16) (block 2h+1)
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const u32x4 lo = *(lds_u32x4*)(base + a_row_off + i * 32 * BK + c0);
-      const u32x4 hi = *(lds_u32x4*)(base + a_row_off + i * 32 * BK + c1);
+      const u32x4 lo = *(lds_u32x4*)(base + a_row_off + i * 32 * BK + p0);
+      const u32x4 hi = *(lds_u32x4*)(base + a_row_off + i * 32 * BK + p1);
       fa[set][i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      const u32x4 blo = *(lds_u32x4*)(base + b_row_off + i * 32 * BK + c0);
-      const u32x4 bhi = *(lds_u32x4*)(base + b_row_off + i * 32 * BK + c1);
+      const u32x4 blo = *(lds_u32x4*)(base + b_row_off + i * 32 * BK + p0);
+      const u32x4 bhi = *(lds_u32x4*)(base + b_row_off + i * 32 * BK + p1);
       fb[set][i] = v8i{(int)blo.x, (int)blo.y, (int)blo.z, (int)blo.w, (int)bhi.x, (int)bhi.y, (int)bhi.z, (int)bhi.w};
     }
-    if constexpr (decltype(EVEN)::value) {
-      constexpr int t2 = decltype(T2)::value;
+  };
+  auto read_scales = [&](int s, uint32_t* ra, uint32_t* rb) {
+    const lds_u8* base = slot_base(s);
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        sa[t2][i] = *(lds_u32*)(base + SA_OFF + 4 * (wm * 128 + 32 * i + lr));
-        sb[t2][i] = *(lds_u32*)(base + SB_OFF + 4 * (wn * 128 + 32 * i + lr));
-      }
+    for (int i = 0; i < 4; i++) {
+      ra[i] = *(lds_u32*)(base + SA_OFF + 4 * (wm * 128 + 32 * i + lr));
+      rb[i] = *(lds_u32*)(base + SB_OFF + 4 * (wn * 128 + 32 * i + lr));
     }
   };
-
-  auto mfma_step = [&](auto SET, auto T2, auto OPSEL) {
+  auto mfma_half = [&](auto SET, auto OPSEL) {
     constexpr int set = decltype(SET)::value;
-    constexpr int t2 = decltype(T2)::value;
     constexpr int op = decltype(OPSEL)::value;
     int xa[4], xb[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      xa[i] = (int)(sa[t2][i] >> sh);
-      xb[i] = (int)(sb[t2][i] >> sh);
+      xa[i] = (int)(sa[i] >> sh);
+      xb[i] = (int)(sb[i] >> sh);
     }
 #pragma unroll
     for (int i = 0; i < 4; i++)
@@ -220,53 +233,49 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
                                                                     xa[i], op, xb[j]);
   };
 
-  // One pipeline step st (register set SET, scale set T2, op_sel OP): make
-  // step st+1 resident (the DMA of steps st+2, st+3 may stay in flight: 18
-  // loads per lane, one even and one odd step), refill the slot of step st
-  // with step st+4, read the fragments of st+1, multiply step st.
-  auto substep = [&](int st, auto SET, auto T2, auto OP, auto EVEN) {
-    constexpr bool even = decltype(EVEN)::value;
-    if (st + 1 < nk) {
-      if (st + 3 < nk) wait_vmcnt<18>();
-      else if (st + 2 < nk) wait_vmcnt<even ? 10 : 8>();
-      else wait_vmcnt<0>();
-    }
-    wait_lgkm0();
-    __builtin_amdgcn_s_barrier();
-    if (st + 4 < nk) issue_step(st + 4, EVEN);
-    // Fragments of st+1 are read unconditionally (after the last step they
-    // read a stale slot and are never used) so that the reads and the MFMAs
-    // share one basic block and can be interleaved: one MFMA, then up to two
-    // LDS reads, keeping the MFMA pipe fed while the LDS queue drains.
-    read_frags(st + 1, ic<1 - decltype(SET)::value>{}, ic<!even>{}, ic<1 - decltype(T2)::value>{});
-    mfma_step(SET, T2, OP);
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // scale shifts
-#pragma unroll
-    for (int i = 0; i < 16; i++) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
-    }
-  };
-
   if (nk > 0) {
-    // prologue: steps 0..3 in flight, step 0 resident, its fragments read
-    issue_step(0, ic<1>{});
-    if (1 < nk) issue_step(1, ic<0>{});
-    if (2 < nk) issue_step(2, ic<1>{});
-    if (3 < nk) issue_step(3, ic<0>{});
-    if (nk >= 4) wait_vmcnt<8 + 10 + 8>();
-    else wait_vmcnt<0>();
+    issue_step(0);
+    issue_step(1);
+    wait_vmcnt<18>();
     __builtin_amdgcn_s_barrier();
-    read_frags(0, ic<0>{}, ic<1>{}, ic<0>{});
-
-    for (int s = 0; s < nk; s += 4) {
-      substep(s, ic<0>{}, ic<0>{}, ic<0>{}, ic<1>{});
-      if (s + 1 < nk) substep(s + 1, ic<1>{}, ic<0>{}, ic<2>{}, ic<0>{});
-      if (s + 2 < nk) substep(s + 2, ic<0>{}, ic<1>{}, ic<0>{}, ic<1>{});
-      if (s + 3 < nk) substep(s + 3, ic<1>{}, ic<1>{}, ic<2>{}, ic<0>{});
+    read_frags(0, ic<0>{}, ic<0>{});
+    read_scales(0, sa, sb);
+    // One K step per iteration: first half from register set 0 while the
+    // second half's fragments load; then make step t+1 resident, refill this
+    // step's slot with step t+2, and run the second half while the first-half
+    // fragments and the scales of step t+1 load.
+    for (int t = 0; t < nk; t++) {
+      read_frags(t, ic<1>{}, ic<1>{});
+      mfma_half(ic<0>{}, ic<0>{});
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if (t + 1 < nk) wait_vmcnt<0>();
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+      issue_step(t + 2);
+      read_frags(t + 1, ic<0>{}, ic<0>{});
+      read_scales(t + 1, na, nb);
+      mfma_half(ic<1>{}, ic<2>{});
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // DMA
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        sa[i] = na[i];
+        sb[i] = nb[i];
+      }
     }
   }
 
+  wait_vmcnt<0>();   // the tail's empty DMA must land before the ring is reused
   // ---- epilogue: fp32 -> BF16 (RNE) into a padded row-major LDS tile (the
   // ring is free once every wave is past its last step), then 16-byte
   // stores that cover whole 512-byte row segments of C.  Lane pairs swap
@@ -325,10 +334,9 @@ hipError_t launch_gemm(const uint8_t* a, const uint32_t* ap, const uint8_t* b, c
   if (blocks == 0) return hipSuccess;
   static bool attr_done[2] = {false, false};
   if (!attr_done[grouped]) {
-    hipError_t e = grouped ? hipFuncSetAttribute((const void*)gemm_kernel<true>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES)
-                           : hipFuncSetAttribute((const void*)gemm_kernel<false>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    const void* fn = grouped ? reinterpret_cast<const void*>(&gemm_kernel<true>)
+                             : reinterpret_cast<const void*>(&gemm_kernel<false>);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_done[grouped] = true;
   }
