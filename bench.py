@@ -1,17 +1,22 @@
 """Benchmark of the MXFP8 hot path on one MI355X.
 
-One step is the dense linear-layer workload: X BF16[8192x4096] ~ N(0,1) and
-W BF16[14336x4096] ~ N(0,0.02), plus the square A, B BF16[8192x8192]:
-rowwise MXFP8 quantize of all four, scale packing, then the TN GEMMs
-8192x14336x4096 and 8192x8192x8192 with BF16 output.  Inputs are resident in
-HBM before timing starts.
+Default workload (the one whose JSON line is the benchmark): the dense linear
+layer.  One step = rowwise MXFP8 quantize of X BF16[8192x4096] ~ N(0,1),
+W BF16[14336x4096] ~ N(0,0.02) and the square A, B BF16[8192x8192], scale
+packing of all four, then the TN GEMMs 8192x14336x4096 and 8192x8192x8192
+with BF16 output.  Inputs are resident in HBM before timing starts.
 
-Printed: one JSON line.  ``value`` is the end-to-end GEMM throughput of the
-step (GEMM FLOPs / wall time of the whole step, quantize and packing
-included).  ``roofline`` is the dominant kernel (the GEMM at 8192x14336x4096)
-against the FP8 MFMA peak, timed with HIP events on its stream;
-``quantize`` reports the rowwise quantizer against HBM peak;
-``cpu_baseline`` is the CPU oracle on a bounded sample of the same work.
+``value`` is the end-to-end GEMM throughput of the step (GEMM FLOPs / wall
+time of the whole step, quantize and packing included).  ``roofline`` is the
+dominant kernel (the GEMM at 8192x14336x4096) against the FP8 MFMA peak, timed
+with HIP events recorded on its launch stream; ``quantize`` reports each
+quantizer launch against the HBM peak; ``cpu_baseline`` is the CPU oracle on
+the same work.
+
+``--workload backward|moe|stress`` measures the other workloads the same way:
+row+col+dbias quantize and the wgrad GEMM on the columnwise copies; the ragged
+grouped MoE GEMM; the wide-range 32768x8192x8192 GEMM.  They are reporting
+aids next to the default line.
 """
 
 import argparse
@@ -33,6 +38,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="dense", choices=["dense", "backward", "moe", "stress"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU-oracle time: whole oracle steps are repeated until reached")
@@ -62,16 +68,120 @@ def profiled_traffic(kernel_key):
         with open(os.path.join(pdir, name)) as fh:
             for line in fh:
                 parts = line.split()
-                if len(parts) >= 5 and parts[0] == "traffic" and " ".join(parts[1:3]) == kernel_key \
-                        and parts[3] == "src=" + src:
-                    kv = dict(p.split("=", 1) for p in parts[4:] if "=" in p)
+                if len(parts) >= 5 and parts[0] == "traffic" and parts[1] == kernel_key and parts[2] == "src=" + src:
+                    kv = dict(p.split("=", 1) for p in parts[3:] if "=" in p)
                     return int(kv["read_bytes"]) + int(kv["write_bytes"]), name
     return None
 
 
-def quant_bytes(rows, cols):
-    """Algorithmic bytes of a rowwise quantize: read 2 B, write 1 + 1/32 B per element."""
-    return rows * cols * (2 + 1 + 1.0 / 32)
+def quant_bytes(rows, cols, copies, dbias=False):
+    """Algorithmic bytes of a quantize: read 2 B per element, write 1 + 1/32 B
+    per element and copy, plus 4 B per column for dbias."""
+    return rows * cols * (2 + copies * (1 + 1.0 / 32)) + (4 * cols if dbias else 0)
+
+
+class Op:
+    """One launch of the step: kind (quantize / pack / gemm), label, callable
+    taking the stream, algorithmic work (bytes for quantize / pack, FLOPs for
+    gemm)."""
+
+    def __init__(self, kind, label, fn, work):
+        self.kind, self.label, self.fn, self.work = kind, label, fn, work
+
+
+def build_ops(workload, dev):
+    """Upload the workload's inputs, allocate outputs and return the step's launches."""
+    import numpy as np
+    import torch
+
+    import mxfp8_block_scaled_quantize_amd as mx
+    import workloads
+
+    def upload(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    ops, keep = [], []
+
+    def quantize_op(label, bits, flags):
+        R, C = bits.shape
+        b = {"x": upload(bits)}
+        if flags & mx.MXFP8_ROWWISE:
+            b["q"] = torch.empty((R, C), dtype=torch.uint8, device=dev)
+            b["s"] = torch.empty((R, C // 32), dtype=torch.uint8, device=dev)
+            b["p"] = torch.empty((C // 128, R), dtype=torch.int32, device=dev)
+        if flags & mx.MXFP8_COLWISE:
+            b["qT"] = torch.empty((C, R), dtype=torch.uint8, device=dev)
+            b["sT"] = torch.empty((C, R // 32), dtype=torch.uint8, device=dev)
+            b["pT"] = torch.empty((R // 128, C), dtype=torch.int32, device=dev)
+        if flags & mx.MXFP8_DBIAS:
+            b["db"] = torch.empty((C,), dtype=torch.float32, device=dev)
+        nws = mx.mxfp8_quantize_workspace_bytes(R, C, flags)
+        b["ws"] = torch.empty((max(nws, 16),), dtype=torch.uint8, device=dev) if nws else None
+        keep.append(b)
+        copies = int(bool(flags & mx.MXFP8_ROWWISE)) + int(bool(flags & mx.MXFP8_COLWISE))
+        ops.append(Op("quantize", label, lambda st: mx.mxfp8_quantize(
+            b["x"], R, C, C, flags, b.get("q"), b.get("s"), b.get("qT"), b.get("sT"), b.get("db"),
+            b["ws"], nws, stream=st), quant_bytes(R, C, copies, bool(flags & mx.MXFP8_DBIAS))))
+        # packing reads the byte scales and writes the same bytes as words
+        if flags & mx.MXFP8_ROWWISE:
+            ops.append(Op("pack", label + " row", lambda st: mx.mxfp8_pack_scales(
+                b["s"], R, C, C // 32, b["p"], stream=st), 2.0 * R * C / 32))
+        if flags & mx.MXFP8_COLWISE:
+            ops.append(Op("pack", label + " col", lambda st: mx.mxfp8_pack_scales(
+                b["sT"], C, R, R // 32, b["pT"], stream=st), 2.0 * R * C / 32))
+        return b
+
+    def gemm_op(a, pa, b, pb, M, N, K):
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        keep.append(c)
+        label = "%dx%dx%d" % (M, N, K)
+        ops.append(Op("gemm", label, lambda st: mx.mxfp8_gemm(a, pa, b, pb, c, N, M, N, K, stream=st),
+                      2.0 * M * N * K))
+        return label
+
+    ROW, COL, DB = mx.MXFP8_ROWWISE, mx.MXFP8_COLWISE, mx.MXFP8_DBIAS
+    host = None
+    if workload == "dense":
+        lin, sq = workloads.dense_linear(), workloads.dense_square()
+        host = {"X": lin["X"], "W": lin["W"], "A": sq["A"], "B": sq["B"]}
+        bx = quantize_op("X[8192x4096]", lin["X"], ROW)
+        bw = quantize_op("W[14336x4096]", lin["W"], ROW)
+        ba = quantize_op("A[8192x8192]", sq["A"], ROW)
+        bb = quantize_op("B[8192x8192]", sq["B"], ROW)
+        dominant = gemm_op(bx["q"], bx["p"], bw["q"], bw["p"], 8192, 14336, 4096)
+        gemm_op(ba["q"], ba["p"], bb["q"], bb["p"], 8192, 8192, 8192)
+        desc = ("dense linear layer: rowwise MXFP8 quantize of X[8192x4096], W[14336x4096], A[8192x8192], "
+                "B[8192x8192] + scale packing + TN GEMMs 8192x14336x4096 and 8192x8192x8192, BF16 out")
+    elif workload == "backward":
+        d = workloads.backward()
+        bd = quantize_op("dY[16384x4096] row+col+dbias", d["dY"], ROW | COL | DB)
+        bx = quantize_op("X[16384x4096] col", d["X"], COL)
+        dominant = gemm_op(bd["qT"], bd["pT"], bx["qT"], bx["pT"], 4096, 4096, 16384)
+        desc = ("backward: dY[16384x4096] = 0.1*t(3) with 1% zero 32x32 tiles, rowwise+columnwise quantize with "
+                "fused dbias; X[16384x4096] columnwise; wgrad TN GEMM 4096x4096x16384 on the transposed copies")
+    elif workload == "stress":
+        d = workloads.stress()
+        ba = quantize_op("A[32768x8192] row+col", d["A"], ROW | COL)
+        bb = quantize_op("B[8192x8192]", d["B"], ROW)
+        dominant = gemm_op(ba["q"], ba["p"], bb["q"], bb["p"], 32768, 8192, 8192)
+        desc = ("wide-range stress: A[32768x8192] (2^u block scales, max BF16, subnormals) rowwise+columnwise, "
+                "B[8192x8192] rowwise, TN GEMM 32768x8192x8192")
+    else:  # moe
+        d = workloads.moe()
+        G, N, K = d["W"].shape
+        Mt = d["X"].shape[0]
+        bx = quantize_op("X[%dx%d]" % (Mt, K), d["X"], ROW)
+        bw = quantize_op("W[%dx%dx%d]" % (G, N, K), d["W"].reshape(G * N, K), ROW)
+        off = torch.from_numpy(d["offsets"]).to(dev)
+        c = torch.empty((Mt, N), dtype=torch.bfloat16, device=dev)
+        keep.extend([c, off])
+        tokens = int(d["offsets"][-1] - d["offsets"][0])
+        dominant = "grouped %dx%dx%d G=%d" % (Mt, N, K, G)
+        ops.append(Op("gemm", dominant, lambda st: mx.mxfp8_grouped_gemm(
+            bx["q"], bx["p"], bw["q"], bw["p"], off, G, c, N, Mt, N, K, stream=st), 2.0 * tokens * N * K))
+        desc = ("grouped MoE: X[%dx%d] and W[%d][%dx%d] rowwise, ragged grouped GEMM over %d experts with "
+                "token counts %s" % (Mt, K, G, N, K, G, np.diff(d["offsets"]).tolist()))
+    return ops, keep, dominant, desc, host
 
 
 def main():
@@ -85,7 +195,6 @@ def main():
     import torch
 
     import mxfp8_block_scaled_quantize_amd as mx
-    import workloads
 
     if not os.path.exists(mx.LIB_PATH):
         from mxfp8_block_scaled_quantize_amd import build as mxbuild
@@ -94,50 +203,21 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    lin = workloads.dense_linear()
-    sq = workloads.dense_square()
-    host = {"X": lin["X"], "W": lin["W"], "A": sq["A"], "B": sq["B"]}
-    bufs = {}
-    for name, bits in host.items():
-        R, C = bits.shape
-        x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
-        bufs[name] = {
-            "x": x, "R": R, "C": C,
-            "q": torch.empty((R, C), dtype=torch.uint8, device=dev),
-            "s": torch.empty((R, C // 32), dtype=torch.uint8, device=dev),
-            "p": torch.empty((C // 128, R), dtype=torch.int32, device=dev),
-        }
-    gemms = [("X", "W"), ("A", "B")]
-    outs = [torch.empty((bufs[a]["R"], bufs[b]["R"]), dtype=torch.bfloat16, device=dev) for a, b in gemms]
+    ops, keep, dominant, desc, host = build_ops(args.workload, dev)
     torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        for name, b in bufs.items():
-            if ev is not None:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-            mx.mxfp8_quantize(b["x"], b["R"], b["C"], b["C"], mx.MXFP8_ROWWISE, b["q"], b["s"], stream=stream)
-            if ev is not None:
-                e1 = torch.cuda.Event(enable_timing=True)
-                e1.record(stream)
-            mx.mxfp8_pack_scales(b["s"], b["R"], b["C"], b["C"] // 32, b["p"], stream=stream)
-            if ev is not None:
-                e2 = torch.cuda.Event(enable_timing=True)
-                e2.record(stream)
-                ev.append(("quantize", name, e0, e1))
-                ev.append(("pack", name, e1, e2))
-        for (an, bn), c in zip(gemms, outs):
-            a, b = bufs[an], bufs[bn]
-            if ev is not None:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-            mx.mxfp8_gemm(a["q"], a["p"], b["q"], b["p"], c, b["R"], a["R"], b["R"], a["C"], stream=stream)
-            if ev is not None:
-                e1 = torch.cuda.Event(enable_timing=True)
-                e1.record(stream)
-                ev.append(("gemm", an + bn, e0, e1))
+        for op in ops:
+            if ev is None:
+                op.fn(stream)
+                continue
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            op.fn(stream)
+            e1.record(stream)
+            ev.append((op, e0, e1))
 
     for _ in range(args.warmup):
         step()
@@ -159,36 +239,32 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     dur = {}
-    for kind, name, e0, e1 in events:
-        dur.setdefault((kind, name), []).append(e0.elapsed_time(e1))
+    for op, e0, e1 in events:
+        dur.setdefault(id(op), []).append(e0.elapsed_time(e1))
     avg = {k: float(np.mean(v)) for k, v in dur.items()}
 
-    gemm_flops = {an + bn: 2.0 * bufs[an]["R"] * bufs[bn]["R"] * bufs[an]["C"] for an, bn in gemms}
-    total_flops = sum(gemm_flops.values())
+    total_flops = sum(op.work for op in ops if op.kind == "gemm")
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
-    gemm_report = {}
-    for key, fl in gemm_flops.items():
-        t = avg[("gemm", key)]
-        tf = fl / (t * 1e-3) / 1e12
-        M, N, K = bufs[key[0]]["R"], bufs[key[1]]["R"], bufs[key[0]]["C"]
-        gemm_report["%dx%dx%d" % (M, N, K)] = {"ms": round(t, 4), "tflops": round(tf, 1),
-                                              "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
-    quant_report = {}
-    for name, b in bufs.items():
-        t = avg[("quantize", name)]
-        gbs = quant_bytes(b["R"], b["C"]) / (t * 1e-3) / 1e9
-        quant_report["%s[%dx%d]" % (name, b["R"], b["C"])] = {
-            "ms": round(t, 4), "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "pack_ms": round(avg[("pack", name)], 4)}
+    gemm_report, quant_report, pack_report = {}, {}, {}
+    for op in ops:
+        t = avg[id(op)]
+        if op.kind == "gemm":
+            tf = op.work / (t * 1e-3) / 1e12
+            gemm_report[op.label] = {"ms": round(t, 4), "tflops": round(tf, 1),
+                                     "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
+        else:
+            gbs = op.work / (t * 1e-3) / 1e9
+            rep = quant_report if op.kind == "quantize" else pack_report
+            rep[op.label] = {"ms": round(t, 4), "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
-    dom_t = avg[("gemm", "XW")]
-    dom_flops = gemm_flops["XW"]
-    achieved = dom_flops / (dom_t * 1e-3) / 1e12
-    prof = profiled_traffic("gemm 8192x14336x4096")
+    dom = [op for op in ops if op.kind == "gemm" and op.label == dominant][0]
+    dom_t = avg[id(dom)]
+    achieved = dom.work / (dom_t * 1e-3) / 1e12
+    prof = profiled_traffic("gemm:" + dominant.replace(" ", ":"))
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": prof[0] if prof else None,
-                "kernel": "mxfp8 gemm 8192x14336x4096", "ms": round(dom_t, 4)}
+                "kernel": "mxfp8 gemm " + dominant, "ms": round(dom_t, 4)}
     if prof:
         roofline["traffic_unit"] = "bytes per launch (HBM side, calibrated FETCH_SIZE + WRITE_SIZE)"
         roofline["traffic_source"] = "profiles/" + prof[1]
@@ -206,16 +282,13 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8_e4m3",
         "data": "synthetic",
-        "config": {"workload": "dense linear layer: rowwise MXFP8 quantize of X[8192x4096], W[14336x4096], "
-                               "A[8192x8192], B[8192x8192] + scale packing + TN GEMMs 8192x14336x4096 and "
-                               "8192x8192x8192, BF16 out",
-                   "global_batch": 8192, "gemm_flops_per_step": total_flops},
+        "config": {"workload": desc, "gemm_flops_per_step": total_flops},
         "roofline": roofline,
         "gemm": gemm_report,
         "quantize": quant_report,
+        "pack": pack_report,
     }
-
-    if not args.no_cpu_baseline:
+    if host is not None and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(host, args.cpu_seconds)
 
     print(json.dumps(result))
@@ -225,7 +298,6 @@ def cpu_baseline(host, min_seconds):
     """The CPU oracle on the same step: rowwise quantize of X, W, A, B, scale
     packing, and the two GEMMs in fp64; whole steps are repeated until
     min_seconds have passed.  Reported as GEMM TFLOP/s, like ``value``."""
-    import numpy as np
     import oracle
     try:
         from threadpoolctl import threadpool_info

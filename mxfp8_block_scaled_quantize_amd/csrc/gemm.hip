@@ -208,29 +208,26 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
       fb[set][i] = v8i{(int)blo.x, (int)blo.y, (int)blo.z, (int)blo.w, (int)bhi.x, (int)bhi.y, (int)bhi.z, (int)bhi.w};
     }
   };
+  // Scale words of step s, shifted right by 8 * (lane / 32) right away (the
+  // same shift serves both halves; op_sel then picks byte 0 or 2), one half
+  // before the MFMAs that use them.
   auto read_scales = [&](int s, uint32_t* ra, uint32_t* rb) {
     const lds_u8* base = slot_base(s);
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      ra[i] = *(lds_u32*)(base + SA_OFF + 4 * (wm * 128 + 32 * i + lr));
-      rb[i] = *(lds_u32*)(base + SB_OFF + 4 * (wn * 128 + 32 * i + lr));
+      ra[i] = *(lds_u32*)(base + SA_OFF + 4 * (wm * 128 + 32 * i + lr)) >> sh;
+      rb[i] = *(lds_u32*)(base + SB_OFF + 4 * (wn * 128 + 32 * i + lr)) >> sh;
     }
   };
   auto mfma_half = [&](auto SET, auto OPSEL) {
     constexpr int set = decltype(SET)::value;
     constexpr int op = decltype(OPSEL)::value;
-    int xa[4], xb[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      xa[i] = (int)(sa[i] >> sh);
-      xb[i] = (int)(sb[i] >> sh);
-    }
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
       for (int j = 0; j < 4; j++)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[set][i], fb[set][j], acc[i][j], 0, 0, op,
-                                                                    xa[i], op, xb[j]);
+                                                                    (int)sa[i], op, (int)sb[j]);
   };
 
   if (nk > 0) {
@@ -247,7 +244,6 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
     for (int t = 0; t < nk; t++) {
       read_frags(t, ic<1>{}, ic<1>{});
       mfma_half(ic<0>{}, ic<0>{});
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
 #pragma unroll
       for (int i = 0; i < 16; i++) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -260,7 +256,6 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
       read_frags(t + 1, ic<0>{}, ic<0>{});
       read_scales(t + 1, na, nb);
       mfma_half(ic<1>{}, ic<2>{});
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
 #pragma unroll
       for (int i = 0; i < 16; i++) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
