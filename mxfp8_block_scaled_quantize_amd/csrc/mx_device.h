@@ -8,21 +8,28 @@ namespace mx {
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
 
-// Streaming (non-temporal) 16-byte global accesses for data touched once.
-__device__ __forceinline__ uint4 load_nt16(const void* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
+// Streaming (non-temporal) global stores for data written once.
 __device__ __forceinline__ void store_nt16(void* p, uint4 d) {
   const u32x4 v = {d.x, d.y, d.z, d.w};
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
+__device__ __forceinline__ void store_nt8(void* p, uint2 d) {
+  __builtin_nontemporal_store(d.x, reinterpret_cast<uint32_t*>(p));
+  __builtin_nontemporal_store(d.y, reinterpret_cast<uint32_t*>(p) + 1);
+}
 
-// Packed per-halfword unsigned max (v_pk_max_u16).  Non-negative BF16 values
-// order like their bit patterns, so |x| max is an integer max on bits & 0x7FFF.
+// Packed per-halfword unsigned max / min (v_pk_max_u16 / v_pk_min_u16).
+// Non-negative BF16 values order like their bit patterns, so |x| max is an
+// integer max on bits & 0x7FFF.
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
                                                                 __builtin_bit_cast(u16x2, b)));
 }
 
@@ -34,26 +41,47 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 
 // E8M0 byte of a block from the 15-bit magnitude pattern of its amax.
 // floor(log2 amax) - 8 + 127 is (biased exponent field - 8); subnormal or zero
-// amax (exponent field 0) and anything below 2^-119 clamp to byte 0.
+// amax (exponent field 0) and anything below 2^-118 clamp to byte 0.
 __device__ __forceinline__ uint32_t scale_byte_from_amax(uint32_t amax_bits) {
   int e = (int)(amax_bits >> 7);
   return (uint32_t)(e > 8 ? e - 8 : 0);
 }
 
-// 2^-(byte-127) as fp32: always a normal number for bytes 0..246.
-__device__ __forceinline__ float inv_scale(uint32_t byte) {
-  return __uint_as_float((254u - byte) << 23);
+// BF16 magnitude pattern of 448 * 2^(byte - 127), the largest value a block
+// with this scale byte encodes (1.75 * 2^(byte - 119): exponent field
+// byte + 8, mantissa 0x60).  Always a normal finite BF16 for bytes 0..246.
+__device__ __forceinline__ uint32_t sat_limit_bits(uint32_t byte) { return ((byte + 8u) << 7) | 0x60u; }
+
+// Clamp the magnitudes of two BF16 values to the packed limits, keeping the
+// signs.  RNE sends (448, 464] * 2^X to 448 * 2^X anyway, so clamping to
+// 448 * 2^X changes no code except that values the convert would turn into
+// NaN (above 464 * 2^X) saturate.
+__device__ __forceinline__ uint32_t clamp_bf16x2(uint32_t w, uint32_t lim2) {
+  return (w & 0x80008000u) | pk_min_u16(abs_bits2(w), lim2);
 }
 
-// v_cvt_pk_fp8_f32 rounds to nearest even and handles E4M3 subnormals, but it
-// turns magnitudes above 464 into NaN: clamp to the saturation value first.
-__device__ __forceinline__ float sat448(float v) { return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); }
+// Four BF16 values (two dwords, already clamped) -> four E4M3 bytes of
+// x / 2^(byte - 127).  v_cvt_scalef32_pk_fp8_bf16 divides by two to the power
+// of the exponent field of its fp32 scale operand (the fp32 with bits
+// byte << 23, i.e. the E8M0 scale itself, byte 0 included) and rounds to
+// nearest even with E4M3 subnormals; this was measured on every BF16 pattern
+// for every scale byte 0..254.
+__device__ __forceinline__ uint32_t cvt4_scaled(uint32_t c0, uint32_t c1, uint32_t byte) {
+  const float f = __uint_as_float(byte << 23);
+  i16x2 r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, c0), f, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, c1), f, true);
+  return __builtin_bit_cast(uint32_t, r);
+}
 
-// Four fp32 values (already multiplied by the inverse scale) -> four E4M3 bytes.
-__device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d) {
-  int r = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
-  r = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), r, true);
-  return (uint32_t)r;
+// Eight consecutive BF16 values of one block -> eight E4M3 codes.
+__device__ __forceinline__ uint2 quantize8(uint4 v, uint32_t byte) {
+  uint32_t lim = sat_limit_bits(byte);
+  lim |= lim << 16;
+  uint2 o;
+  o.x = cvt4_scaled(clamp_bf16x2(v.x, lim), clamp_bf16x2(v.y, lim), byte);
+  o.y = cvt4_scaled(clamp_bf16x2(v.z, lim), clamp_bf16x2(v.w, lim), byte);
+  return o;
 }
 
 // Cross-lane max inside a quad of lanes via DPP quad permutes.

@@ -1,74 +1,59 @@
 // MXFP8 quantization kernels for gfx950.
 //
-// One workgroup (256 threads = 4 wave64) owns a 128 x 128 BF16 tile.  Wave w
-// owns rows [32w, 32w + 32) of the tile; lane (rg = lane / 16, cg = lane % 16)
-// owns the 8 x 8 sub-block rows 32w + 8rg + [0, 8), columns 8cg + [0, 8), read
-// with eight 16-byte loads (each load instruction of a wave covers four rows
-// of 256 contiguous bytes).  Plain (cached) loads measured faster here than
-// non-temporal ones; the transposed copy is stored non-temporally.
+// Tile kernel: one workgroup of QW waves owns a (32 * QW) x 128 BF16 tile.
+// Wave w owns rows [32w, 32w + 32) of the tile; lane (rg = lane / 16,
+// cg = lane % 16) owns the 8 x 8 sub-block rows 32w + 8rg + [0, 8), columns
+// 8cg + [0, 8), read with eight 16-byte loads (each load instruction of a wave
+// covers four rows of 256 contiguous bytes).
 //
 //  - rowwise 32-blocks are 4 consecutive lanes (a DPP quad) in one row;
 //  - columnwise 32-blocks are the 4 lanes cg, cg+16, cg+32, cg+48 of a wave
 //    (8 rows each), so every colwise block is reduced inside one wave;
-//  - the columnwise codes are converted column-major in registers (pairs of
-//    rows of one column per convert), written to a transposed 16 KB LDS tile
-//    and streamed out as full 128-byte rows of q_colT;
+//  - conversion is exact integer scale selection (amax on BF16 bit patterns),
+//    a clamp of the BF16 magnitudes to 448 * 2^X, and the hardware scaled
+//    convert, which divides by 2^X and rounds to nearest even;
+//  - the columnwise codes are built column-major in registers (a byte permute
+//    pairs two rows of one column per convert), written to a transposed LDS
+//    tile and streamed out as full (32 * QW)-byte rows of q_colT;
+//  - the scale bytes of a tile are gathered in LDS and stored as one word per
+//    row (rowwise) and one QW-byte group per column (columnwise) instead of
+//    single bytes;
 //  - dbias partial sums are reduced lane -> wave -> workgroup and written once
 //    per (row tile, column); a second kernel sums the row tiles.
 //
-// The arithmetic is exact integer scale selection (amax on BF16 bit patterns)
-// and exact power-of-two scaling in fp32, followed by the hardware
-// round-to-nearest-even E4M3 convert after clamping to +-448.
+// Flat kernel: the rowwise copy of a contiguous input is one stream of
+// 32-element blocks (see quantize_rowwise_flat_kernel).
 #include "mx_device.h"
 #include "launch.h"
 
 namespace mx {
 
-constexpr int QT_R = 128;
-constexpr int QT_C = 128;
-constexpr int Q_THREADS = 256;
+constexpr int QT_C = 128;            // tile columns
+constexpr int QT_R_MIN = 128;        // rows of the smallest tile (4 waves)
 
-template <bool ROW, bool COL, bool DBIAS>
-__global__ __launch_bounds__(Q_THREADS) void quantize_tile_kernel(
+template <bool ROW, bool COL, bool DBIAS, int QW, bool NT_QROW, bool NT_COLT>
+__global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
     const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
     uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
     uint8_t* __restrict__ q_colT, uint8_t* __restrict__ s_colT,
     float* __restrict__ dbias_part, int64_t tiles_c) {
-  // Transposed FP8 tile: [column][row] bytes, 8-byte row units XOR-swizzled
-  // by the column group to spread the transposing writes over the banks.
-  __shared__ __attribute__((aligned(16))) uint8_t lds_t[COL ? QT_C * QT_R : 16];
-  __shared__ float lds_db[DBIAS ? 4 * QT_C : 1];
+  constexpr int TR = 32 * QW;   // tile rows
+  constexpr int NT = 64 * QW;   // threads
+  // Transposed FP8 tile [column][row]; 8-byte row units XOR-swizzled by the
+  // column group to spread the transposing writes over the banks.
+  __shared__ __attribute__((aligned(16))) uint8_t lds_t[COL ? QT_C * TR : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sc[COL ? QT_C * QW : 16];  // [column][wave]
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sr[ROW ? TR * 4 : 16];     // [row][block]
+  __shared__ float lds_db[DBIAS ? QW * QT_C : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int cg = lane & 15;
   const int rg = lane >> 4;
-  int64_t tr, tc;
-  if (ROW && !COL) {
-    // Rowwise only: workgroup ids are dealt round-robin to the 8 XCDs; remap
-    // them so each XCD walks its own share in groups of 8 x 8 tiles.  The 8
-    // column tiles of a group write 8 x 4 = 32 contiguous scale bytes per row
-    // from one L2, instead of 4-byte pieces from 8 different L2s.
-    const int64_t ntile = gridDim.x;
-    const int64_t bid = blockIdx.x;
-    const int64_t full = (ntile / 8) * 8;
-    const int64_t lid = bid < full ? (bid & 7) * (full >> 3) + (bid >> 3) : bid;
-    const int64_t tiles_r = ntile / tiles_c;
-    const int64_t per_band = 8 * tiles_c;                          // tiles in 8 row tiles
-    const int64_t band = lid / per_band;
-    const int64_t hb = (tiles_r - 8 * band) < 8 ? (tiles_r - 8 * band) : 8;
-    const int64_t inb = lid - band * per_band;
-    const int64_t grp = inb / (8 * hb);
-    const int64_t wg = (tiles_c - 8 * grp) < 8 ? (tiles_c - 8 * grp) : 8;
-    const int64_t ing = inb - grp * 8 * hb;
-    tr = 8 * band + ing / wg;
-    tc = 8 * grp + ing % wg;
-  } else {
-    tr = (int64_t)blockIdx.x / tiles_c;
-    tc = (int64_t)blockIdx.x - tr * tiles_c;
-  }
-  const int64_t r0 = tr * QT_R;
+  const int64_t tr = (int64_t)blockIdx.x / tiles_c;
+  const int64_t tc = (int64_t)blockIdx.x - tr * tiles_c;
+  const int64_t r0 = tr * TR;
   const int64_t c0 = tc * QT_C;
   const int64_t rb = r0 + 32 * w + 8 * rg;  // first row of this lane
   const int64_t cb = c0 + 8 * cg;           // first column of this lane
@@ -84,7 +69,6 @@ __global__ __launch_bounds__(Q_THREADS) void quantize_tile_kernel(
   }
 
   if (ROW) {
-    const int64_t ncb = C >> 5;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       uint32_t m = pk_max_u16(pk_max_u16(abs_bits2(v[i].x), abs_bits2(v[i].y)),
@@ -92,15 +76,13 @@ __global__ __launch_bounds__(Q_THREADS) void quantize_tile_kernel(
       m = max(m & 0xFFFFu, m >> 16);
       m = quad_max(m);
       const uint32_t byte = scale_byte_from_amax(m);
-      const float sc = inv_scale(byte);
-      uint2 o;
-      o.x = cvt4_e4m3(bf_lo(v[i].x) * sc, bf_hi(v[i].x) * sc, bf_lo(v[i].y) * sc, bf_hi(v[i].y) * sc);
-      o.y = cvt4_e4m3(bf_lo(v[i].z) * sc, bf_hi(v[i].z) * sc, bf_lo(v[i].w) * sc, bf_hi(v[i].w) * sc);
+      const uint2 o = quantize8(v[i], byte);
       const int64_t r = rb + i;
       if (cval && r < R) {
-        *reinterpret_cast<uint2*>(q_row + r * C + cb) = o;
-        if ((cg & 3) == 0) s_row[r * ncb + (cb >> 5)] = (uint8_t)byte;
+        if (NT_QROW) store_nt8(q_row + r * C + cb, o);
+        else *reinterpret_cast<uint2*>(q_row + r * C + cb) = o;
       }
+      if ((cg & 3) == 0) lds_sr[(32 * w + 8 * rg + i) * 4 + (cg >> 2)] = (uint8_t)byte;
     }
   }
 
@@ -123,27 +105,35 @@ __global__ __launch_bounds__(Q_THREADS) void quantize_tile_kernel(
       cm[j] = pk_max_u16(cm[j], (uint32_t)__shfl_xor((int)cm[j], 16, 64));
       cm[j] = pk_max_u16(cm[j], (uint32_t)__shfl_xor((int)cm[j], 32, 64));
     }
-    const bool wval = (r0 + 32 * w) < R;  // R % 32 == 0: the wave's 32 rows are all valid or not
-    const int64_t nrb = R >> 5;
+    // Dword j of every row holds columns 2j (low half) and 2j + 1 (high half):
+    // clamp both halves with their own column's limit.
+    uint32_t cbyte[8], cw[8][4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      cbyte[2 * j] = scale_byte_from_amax(cm[j] & 0xFFFFu);
+      cbyte[2 * j + 1] = scale_byte_from_amax(cm[j] >> 16);
+      const uint32_t lim2 = sat_limit_bits(cbyte[2 * j]) | (sat_limit_bits(cbyte[2 * j + 1]) << 16);
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const uint32_t d = j == 0 ? v[i].x : j == 1 ? v[i].y : j == 2 ? v[i].z : v[i].w;
+        cw[i][j] = clamp_bf16x2(d, lim2);
+      }
+    }
     const int u = 4 * w + rg;             // 8-row unit of this lane inside the tile
     const int swz = 2 * (cg & 7);         // even XOR keeps 16-byte pairs of units adjacent
 #pragma unroll
     for (int k = 0; k < 8; k++) {
-      const uint32_t amax = (k & 1) ? (cm[k >> 1] >> 16) : (cm[k >> 1] & 0xFFFFu);
-      const uint32_t byte = scale_byte_from_amax(amax);
-      const float sc = inv_scale(byte);
-      float e[8];
+      // rows 2p and 2p + 1 of column k side by side: bytes 0-1 / 2-3 of each dword
+      const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t d[4];
 #pragma unroll
-      for (int i = 0; i < 8; i++) {
-        const uint32_t d = (k >> 1) == 0 ? v[i].x : (k >> 1) == 1 ? v[i].y : (k >> 1) == 2 ? v[i].z : v[i].w;
-        e[i] = ((k & 1) ? bf_hi(d) : bf_lo(d)) * sc;
-      }
+      for (int p = 0; p < 4; p++) d[p] = __builtin_amdgcn_perm(cw[2 * p + 1][k >> 1], cw[2 * p][k >> 1], sel);
       uint2 o;
-      o.x = cvt4_e4m3(e[0], e[1], e[2], e[3]);
-      o.y = cvt4_e4m3(e[4], e[5], e[6], e[7]);
+      o.x = cvt4_scaled(d[0], d[1], cbyte[k]);
+      o.y = cvt4_scaled(d[2], d[3], cbyte[k]);
       const int cl = 8 * cg + k;
-      *reinterpret_cast<uint2*>(lds_t + cl * QT_R + 8 * (u ^ swz)) = o;
-      if (rg == 0 && cval && wval) s_colT[(cb + k) * nrb + ((r0 >> 5) + w)] = (uint8_t)byte;
+      *reinterpret_cast<uint2*>(lds_t + cl * TR + 8 * (u ^ swz)) = o;
+      if (rg == 0) lds_sc[cl * QW + w] = (uint8_t)cbyte[k];
     }
   }
 
@@ -167,26 +157,70 @@ __global__ __launch_bounds__(Q_THREADS) void quantize_tile_kernel(
     }
   }
 
-  if (COL || DBIAS) __syncthreads();
+  __syncthreads();
 
   if (COL) {
-    // Thread t streams 16-byte chunk (t % 8) of transposed rows t/8 + 32j.
+    // Transposed rows are TR bytes: CH 16-byte chunks each.
+    constexpr int CH = TR / 16;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int cl = (tid >> 3) + 32 * j;
-      const int ch = tid & 7;
+    for (int j = 0; j < (QT_C * CH) / NT; j++) {
+      const int t = tid + NT * j;
+      const int cl = t / CH;
+      const int ch = t % CH;
       const int swz = 2 * ((cl >> 3) & 7);
-      const uint4 d = *reinterpret_cast<const uint4*>(lds_t + cl * QT_R + 8 * ((2 * ch) ^ swz));
+      const uint4 d = *reinterpret_cast<const uint4*>(lds_t + cl * TR + 8 * ((2 * ch) ^ swz));
       const int64_t col = c0 + cl;
       const int64_t row = r0 + 16 * ch;
-      if (col < C && row < R) store_nt16(q_colT + col * R + row, d);
+      if (col < C && row < R) {
+        if (NT_COLT) store_nt16(q_colT + col * R + row, d);
+        else *reinterpret_cast<uint4*>(q_colT + col * R + row) = d;
+      }
+    }
+    // The QW scale bytes of a column: QW consecutive row blocks of s_colT.
+    if (tid < QT_C) {
+      const int64_t col = c0 + tid;
+      const int64_t nrb = R >> 5;
+      const int64_t b0 = r0 >> 5;
+      if (col < C) {
+        uint8_t* dst = s_colT + col * nrb + b0;
+        const bool whole = b0 + QW <= nrb && (reinterpret_cast<uintptr_t>(dst) & (QW - 1)) == 0;
+        if (QW == 8 && whole) {
+          *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(lds_sc + tid * QW);
+        } else if (QW == 4 && whole) {
+          *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(lds_sc + tid * QW);
+        } else {
+          for (int j = 0; j < QW && b0 + j < nrb; j++) dst[j] = lds_sc[tid * QW + j];
+        }
+      }
     }
   }
-
+  if (ROW && tid >= NT - TR) {
+    // The 4 scale bytes of a row of the tile (one per 32-column block).
+    const int rl = tid - (NT - TR);
+    const int64_t row = r0 + rl;
+    if (row < R) {
+      const int64_t ncb = C >> 5;
+      const uint32_t word = *reinterpret_cast<const uint32_t*>(lds_sr + 4 * rl);
+      uint8_t* dst = s_row + row * ncb + 4 * tc;
+      const int64_t nb = ncb - 4 * tc;
+      if (nb >= 4 && (reinterpret_cast<uintptr_t>(dst) & 3) == 0) {
+        *reinterpret_cast<uint32_t*>(dst) = word;
+      } else {
+        for (int j = 0; j < 4 && j < nb; j++) dst[j] = (uint8_t)(word >> (8 * j));
+      }
+    }
+  }
   if (DBIAS) {
     if (tid < QT_C && c0 + tid < C) {
-      const float s = ((lds_db[tid] + lds_db[QT_C + tid]) + lds_db[2 * QT_C + tid]) + lds_db[3 * QT_C + tid];
-      dbias_part[tr * C + c0 + tid] = s;
+      // pairwise over the waves (QW is 4 or 8)
+      float t[QW];
+#pragma unroll
+      for (int q = 0; q < QW; q++) t[q] = lds_db[q * QT_C + tid];
+#pragma unroll
+      for (int h = QW / 2; h >= 1; h /= 2)
+#pragma unroll
+        for (int q = 0; q < h; q++) t[q] = t[q] + t[q + h];
+      dbias_part[tr * C + c0 + tid] = t[0];
     }
   }
 }
@@ -199,15 +233,16 @@ __global__ __launch_bounds__(Q_THREADS) void quantize_tile_kernel(
 // DPP quad holds one block, codes go out (non-temporally) as 512-byte runs and
 // the wave's 32 scale bytes are contiguous.  Two loads per lane measured best
 // (more waves in flight than with four or eight).
+constexpr int FL_THREADS = 256;
 constexpr int FL_LOADS = 2;
 constexpr int64_t FL_ELEMS = 512 * FL_LOADS;  // per wave
 
-__global__ __launch_bounds__(Q_THREADS) void quantize_rowwise_flat_kernel(const uint16_t* __restrict__ x,
-                                                                         int64_t total,
-                                                                         uint8_t* __restrict__ q,
-                                                                         uint8_t* __restrict__ s) {
+__global__ __launch_bounds__(FL_THREADS) void quantize_rowwise_flat_kernel(const uint16_t* __restrict__ x,
+                                                                          int64_t total,
+                                                                          uint8_t* __restrict__ q,
+                                                                          uint8_t* __restrict__ s) {
   const int lane = threadIdx.x & 63;
-  const int64_t base = ((int64_t)blockIdx.x * (Q_THREADS / 64) + (threadIdx.x >> 6)) * FL_ELEMS;
+  const int64_t base = ((int64_t)blockIdx.x * (FL_THREADS / 64) + (threadIdx.x >> 6)) * FL_ELEMS;
   uint4 v[FL_LOADS];
 #pragma unroll
   for (int u = 0; u < FL_LOADS; u++) {
@@ -222,36 +257,43 @@ __global__ __launch_bounds__(Q_THREADS) void quantize_rowwise_flat_kernel(const 
     m = max(m & 0xFFFFu, m >> 16);
     m = quad_max(m);
     const uint32_t byte = scale_byte_from_amax(m);
-    const float sc = inv_scale(byte);
-    uint2 o;
-    o.x = cvt4_e4m3(bf_lo(v[u].x) * sc, bf_hi(v[u].x) * sc, bf_lo(v[u].y) * sc, bf_hi(v[u].y) * sc);
-    o.y = cvt4_e4m3(bf_lo(v[u].z) * sc, bf_hi(v[u].z) * sc, bf_lo(v[u].w) * sc, bf_hi(v[u].w) * sc);
+    const uint2 o = quantize8(v[u], byte);
     if (e < total) {  // total % 32 == 0: a quad is entirely in or out
-      __builtin_nontemporal_store(o.x, reinterpret_cast<uint32_t*>(q + e));
-      __builtin_nontemporal_store(o.y, reinterpret_cast<uint32_t*>(q + e) + 1);
+      store_nt8(q + e, o);
       if ((lane & 3) == 0) s[e >> 5] = (uint8_t)byte;
     }
   }
 }
 
-// dbias[c] = sum over row tiles of the partial sums, in four interleaved
-// chains combined pairwise (a fixed order: the result is deterministic).
-__global__ __launch_bounds__(256) void dbias_reduce_kernel(const float* __restrict__ part, int64_t tiles,
-                                                           int64_t C, float* __restrict__ out) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= C) return;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  int64_t t = 0;
-  for (; t + 4 <= tiles; t += 4) {
-    a0 += part[(t + 0) * C + c];
-    a1 += part[(t + 1) * C + c];
-    a2 += part[(t + 2) * C + c];
-    a3 += part[(t + 3) * C + c];
+// dbias[c] = sum over row tiles of the partial sums.  A workgroup owns 32
+// columns; its 8 thread groups sum the row tiles g, g + 8, g + 16, ... of a
+// column and the 8 sums are combined pairwise (a fixed order: the result is
+// deterministic).
+constexpr int DB_COLS = 32;
+constexpr int DB_PARTS = 8;
+
+__global__ __launch_bounds__(DB_COLS * DB_PARTS) void dbias_reduce_kernel(const float* __restrict__ part,
+                                                                          int64_t tiles, int64_t C,
+                                                                          float* __restrict__ out) {
+  __shared__ float lds[DB_PARTS][DB_COLS];
+  const int cl = threadIdx.x % DB_COLS;
+  const int g = threadIdx.x / DB_COLS;
+  const int64_t c = (int64_t)blockIdx.x * DB_COLS + cl;
+  float s = 0.0f;
+  if (c < C)
+    for (int64_t t = g; t < tiles; t += DB_PARTS) s += part[t * C + c];
+  lds[g][cl] = s;
+  __syncthreads();
+  if (g == 0 && c < C) {
+    float q[DB_PARTS];
+#pragma unroll
+    for (int p = 0; p < DB_PARTS; p++) q[p] = lds[p][cl];
+#pragma unroll
+    for (int h = DB_PARTS / 2; h >= 1; h /= 2)
+#pragma unroll
+      for (int p = 0; p < h; p++) q[p] = q[p] + q[p + h];
+    out[c] = q[0];
   }
-  if (t < tiles) a0 += part[t * C + c];
-  if (t + 1 < tiles) a1 += part[(t + 1) * C + c];
-  if (t + 2 < tiles) a2 += part[(t + 2) * C + c];
-  out[c] = (a0 + a1) + (a2 + a3);
 }
 
 __global__ __launch_bounds__(256) void fill_zero_f32_kernel(float* __restrict__ out, int64_t n) {
@@ -259,44 +301,61 @@ __global__ __launch_bounds__(256) void fill_zero_f32_kernel(float* __restrict__ 
   if (i < n) out[i] = 0.0f;
 }
 
-int64_t quantize_row_tiles(int64_t R) { return (R + QT_R - 1) / QT_R; }
+int64_t quantize_row_tiles(int64_t R) { return (R + QT_R_MIN - 1) / QT_R_MIN; }
 int64_t quantize_col_tiles(int64_t C) { return (C + QT_C - 1) / QT_C; }
+
+// Tile configuration per copy set (measured on MI355X with the stress,
+// backward and columnwise-only shapes): 8 waves with non-temporal rowwise
+// codes and cached transposed codes when both copies are written; 4 waves with
+// non-temporal transposed codes for the columnwise copy alone.
+template <bool ROW, bool COL, bool DBIAS>
+static hipError_t launch_tiles(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q_row,
+                               uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT, float* dbias_part,
+                               int64_t* row_tiles, hipStream_t stream) {
+  constexpr int QW = (ROW || !COL) ? 8 : 4;
+  constexpr bool NT_QROW = true;
+  constexpr bool NT_COLT = !ROW;
+  const int64_t tr = (R + 32 * QW - 1) / (32 * QW);
+  const int64_t tc = quantize_col_tiles(C);
+  *row_tiles = tr;
+  if (tr * tc == 0) return hipSuccess;
+  hipLaunchKernelGGL((quantize_tile_kernel<ROW, COL, DBIAS, QW, NT_QROW, NT_COLT>), dim3((unsigned)(tr * tc)),
+                     dim3(64 * QW), 0, stream, x, R, C, ldx, q_row, s_row, q_colT, s_colT, dbias_part, tc);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint32_t flags,
                            uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT,
                            float* dbias, float* dbias_part, hipStream_t stream) {
   const bool row = flags & 1u, col = flags & 2u, db = flags & 4u;
-  const int64_t tr = quantize_row_tiles(R), tc = quantize_col_tiles(C);
-  const int64_t tiles = tr * tc;
   if (row && !col && !db && ldx == C) {
     const int64_t total = R * C;
-    const int64_t blocks = (total + FL_ELEMS * (Q_THREADS / 64) - 1) / (FL_ELEMS * (Q_THREADS / 64));
+    const int64_t per_block = FL_ELEMS * (FL_THREADS / 64);
+    const int64_t blocks = (total + per_block - 1) / per_block;
     if (blocks > 0)
-      hipLaunchKernelGGL(quantize_rowwise_flat_kernel, dim3((unsigned)blocks), dim3(Q_THREADS), 0, stream, x, total,
+      hipLaunchKernelGGL(quantize_rowwise_flat_kernel, dim3((unsigned)blocks), dim3(FL_THREADS), 0, stream, x, total,
                          q_row, s_row);
     return hipGetLastError();
   }
-  if (tiles > 0) {
-    const dim3 grid((unsigned)tiles), block(Q_THREADS);
-#define MX_Q_LAUNCH(RW, CL, DB)                                                                   \
-  hipLaunchKernelGGL((quantize_tile_kernel<RW, CL, DB>), grid, block, 0, stream, x, R, C, ldx, q_row, \
-                     s_row, q_colT, s_colT, dbias_part, tc)
-    if (row && col && db) MX_Q_LAUNCH(true, true, true);
-    else if (row && col) MX_Q_LAUNCH(true, true, false);
-    else if (row && db) MX_Q_LAUNCH(true, false, true);
-    else if (row) MX_Q_LAUNCH(true, false, false);
-    else if (col && db) MX_Q_LAUNCH(false, true, true);
-    else MX_Q_LAUNCH(false, true, false);
+  int64_t tiles_r = 0;
+  hipError_t e;
+#define MX_Q_LAUNCH(RW, CL, DB) \
+  launch_tiles<RW, CL, DB>(x, R, C, ldx, q_row, s_row, q_colT, s_colT, dbias_part, &tiles_r, stream)
+  if (row && col && db) e = MX_Q_LAUNCH(true, true, true);
+  else if (row && col) e = MX_Q_LAUNCH(true, true, false);
+  else if (row && db) e = MX_Q_LAUNCH(true, false, true);
+  else if (row) e = MX_Q_LAUNCH(true, false, false);
+  else if (col && db) e = MX_Q_LAUNCH(false, true, true);
+  else e = MX_Q_LAUNCH(false, true, false);
 #undef MX_Q_LAUNCH
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  if (e != hipSuccess) return e;
   if (db && C > 0) {
-    const dim3 grid((unsigned)((C + 255) / 256)), block(256);
-    if (tiles > 0)
-      hipLaunchKernelGGL(dbias_reduce_kernel, grid, block, 0, stream, dbias_part, tr, C, dbias);
+    const dim3 grid((unsigned)((C + DB_COLS - 1) / DB_COLS));
+    if (tiles_r > 0)
+      hipLaunchKernelGGL(dbias_reduce_kernel, grid, dim3(DB_COLS * DB_PARTS), 0, stream, dbias_part, tiles_r, C,
+                         dbias);
     else
-      hipLaunchKernelGGL(fill_zero_f32_kernel, grid, block, 0, stream, dbias, C);
+      hipLaunchKernelGGL(fill_zero_f32_kernel, dim3((unsigned)((C + 255) / 256)), dim3(256), 0, stream, dbias, C);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -81,10 +81,11 @@ def check_against_oracle(bits, flags, res, label):
 
 def dbias_depth(R):
     """Length of the longest fp32 addition chain of the GPU dbias: 8 rows per
-    lane, 2 cross-lane steps, 3 across the waves of a 128-row tile, then four
-    interleaved chains over the row tiles combined pairwise."""
+    lane, 2 cross-lane steps, 3 pairwise levels across the (up to 8) waves of
+    a row tile, then 8 interleaved chains over the row tiles (tiles of at
+    least 128 rows) combined pairwise in 3 levels."""
     tiles = (R + 127) // 128
-    return 8 + 2 + 3 + (tiles + 3) // 4 + 2
+    return 8 + 2 + 3 + (tiles + 7) // 8 + 3
 
 
 def check_dbias(bits, got, label):
