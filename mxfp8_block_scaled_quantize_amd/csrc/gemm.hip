@@ -60,6 +60,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Workgroup barrier that the compiler may not move LDS (or any memory)
+// accesses across.  The hardware side (which loads and DMAs must have landed)
+// is handled by the explicit waits in front of each use.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int V>
 struct ic {
@@ -234,7 +242,7 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
     issue_step(0);
     issue_step(1);
     wait_vmcnt<18>();
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
     read_frags(0, ic<0>{}, ic<0>{});
     read_scales(0, sa, sb);
     // One K step per iteration: first half from register set 0 while the
@@ -251,7 +259,7 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
       }
       if (t + 1 < nk) wait_vmcnt<0>();
       wait_lgkm0();
-      __builtin_amdgcn_s_barrier();
+      lds_barrier();
       issue_step(t + 2);
       read_frags(t + 1, ic<0>{}, ic<0>{});
       read_scales(t + 1, na, nb);
@@ -271,35 +279,43 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
   }
 
   wait_vmcnt<0>();   // the tail's empty DMA must land before the ring is reused
-  // ---- epilogue: fp32 -> BF16 (RNE) into a padded row-major LDS tile (the
-  // ring is free once every wave is past its last step), then 16-byte
-  // stores that cover whole 512-byte row segments of C.  Lane pairs swap
-  // values so each LDS write is one 32-bit word (two adjacent columns).
+  // ---- epilogue: fp32 -> BF16 (RNE, v_cvt_pk_bf16_f32) into a padded
+  // row-major LDS tile (the ring is free once every wave is past its last
+  // step), then 16-byte stores that cover whole 512-byte row segments of C.
+  // Registers r, r+1 of a lane are rows R, R+1 of one column; lane pairs
+  // (columns c, c+1) trade halves so each LDS write is one 32-bit word of two
+  // adjacent columns: the even lane writes row R, the odd lane row R+1.
   wait_lgkm0();
-  __builtin_amdgcn_s_barrier();
+  lds_barrier();
   {
     const bool odd = lane & 1;
     const int rb = wm * 128 + 4 * lg;
     const int cb = wn * 128 + lr - (odd ? 1 : 0);
+    const uint32_t send_shift = odd ? 0u : 16u;                   // odd sends row R, even sends row R+1
+    const uint32_t sel = odd ? 0x03020504u : 0x05040100u;         // (partner, own) halves -> word
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 4; i++) {
 #pragma unroll
       for (int j = 0; j < 4; j++)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const uint32_t a = f32_to_bf16_rne(acc[i][j][r]);
-          const uint32_t b = f32_to_bf16_rne(acc[i][j][r + 1]);
-          const uint32_t x = odd ? a : b;
-          const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);  // lane ^ 1
-          const uint32_t word = odd ? (y | (b << 16)) : (a | (y << 16));
+          const bf16x2 h = {(__bf16)acc[i][j][r], (__bf16)acc[i][j][r + 1]};
+          const uint32_t pk = __builtin_bit_cast(uint32_t, h);   // row R low, row R+1 high
+          const uint32_t send = __builtin_amdgcn_alignbit(pk, pk, send_shift);
+          const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, true);  // lane ^ 1
+          const uint32_t word = __builtin_amdgcn_perm(y, pk, sel);
           const int row = rb + 32 * i + 8 * (r >> 2) + (r & 3) + (odd ? 1 : 0);
           *(__attribute__((address_space(3))) uint32_t*)(smem + row * C_LDS_STRIDE + 2 * (cb + 32 * j)) = word;
         }
+      __builtin_amdgcn_sched_barrier(0);   // bounds the registers the batched AGPR reads take
+    }
   }
   wait_lgkm0();
-  __builtin_amdgcn_s_barrier();
+  lds_barrier();
   {
-    const int ch = tid & 31;           // 16-byte chunk of a 512-byte tile row
+    // 16-byte chunk of a 512-byte tile row (tid & 31, re-derived from the lane
+    // id so the value is not kept live through the conversion above)
+    const int ch = (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & 31);
     const int64_t col = n0 + 8 * ch;
     if (col < N) {
 #pragma unroll 8

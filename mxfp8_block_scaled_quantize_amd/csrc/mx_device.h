@@ -92,11 +92,4 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
   return v > t ? v : t;
 }
 
-// fp32 -> bf16 round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 }  // namespace mx
