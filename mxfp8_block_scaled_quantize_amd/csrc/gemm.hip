@@ -20,12 +20,16 @@
 // fragment registers: the first half's MFMAs overlap the LDS reads of the
 // second half; then one barrier makes step t+1 resident and frees this
 // step's slot; the second half's MFMAs overlap the DMA of step t+2 and the
-// LDS reads of step t+1.  The DMA is branch-free (a step past the end gets
-// zero-length buffer ranges) so the scheduler can interleave it with the
-// MFMAs.  16-byte chunks of each 128-byte LDS row are XOR-swizzled by
-// (row >> 1) & 7, which makes the fragment reads conflict free.  Workgroup ids
-// are remapped so the tiles resident on one XCD (ids are dealt round-robin to
-// the 8 XCDs) form groups of 4 row tiles sharing A and B in that XCD's L2.
+// LDS reads of step t+1.  Each MFMA is issued together with one 16-byte LDS
+// read and (second half) one DMA, in a fixed order pinned by scheduling
+// barriers; reads come in the order the next MFMAs consume them.  Two steps
+// are unrolled so both slots sit at constant LDS offsets (an odd step count
+// runs one extra all-zero step).  The scale words are laid out in LDS so
+// that the four a lane needs are one 16-byte read.  16-byte chunks of each
+// 128-byte LDS row are XOR-swizzled by (row >> 1) & 7, which makes the
+// fragment reads conflict free.  Workgroup ids are remapped so the tiles
+// resident on one XCD (ids are dealt round-robin to the 8 XCDs) form groups of
+// 4 row tiles sharing A and B in that XCD's L2.
 #include "mx_device.h"
 #include "launch.h"
 
@@ -33,10 +37,10 @@ namespace mx {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
-typedef __attribute__((address_space(3))) const uint32_t lds_u32;
 
 constexpr int BM = 256;
 constexpr int BN = 256;
@@ -134,16 +138,25 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
   // DMA instruction i of wave w covers LDS rows 8(8w+i) + lane/8, chunk slot
   // lane%8; the swizzle (row>>1)&7 = (4(i&1) + lane/16) & 7 only depends on
   // the parity of i.
-  uint32_t dma_base[2];
+  // DMA instruction i of wave w covers LDS rows 8(8w + i) + lane/8, chunk
+  // slot lane%8; the swizzle (row >> 1) & 7 is (4i + lane/16) & 7.  The step's
+  // K offset goes into the scalar offset field.
+  uint32_t dma_off[8];
 #pragma unroll
-  for (int e = 0; e < 2; e++) {
-    const int r = 64 * wave + (lane >> 3);
-    const int c = (lane & 7) ^ ((4 * e + (lane >> 4)) & 7);
-    dma_base[e] = (uint32_t)r * (uint32_t)K + 16u * (uint32_t)c;
+  for (int i = 0; i < 8; i++) {
+    const int r = 64 * wave + 8 * i + (lane >> 3);
+    const int c = (lane & 7) ^ ((4 * i + (lane >> 4)) & 7);
+    dma_off[i] = (uint32_t)r * (uint32_t)K + 16u * (uint32_t)c;
   }
-  // scale words: wave w brings rows 64w + lane (clamped into the valid rows)
-  const int sra = (64 * wave + lane) < rows_a ? (64 * wave + lane) : rows_a - 1;
-  const int srb = (64 * wave + lane) < rows_b ? (64 * wave + lane) : rows_b - 1;
+  // Scale words are stored so that the four words a lane needs (rows
+  // 32i + lr of its wave's 128-row half, i = 0..3) are one 16-byte LDS read:
+  // word position p = 128 * half + 4 * lr + i holds row 128 * half + 32i + lr.
+  // Wave w brings positions 64w + lane (rows past the end are clamped into the
+  // valid rows: their data rows are zero, so any scale will do).
+  const int sp = 64 * wave + lane;
+  const int srow = (sp & ~127) + 32 * (sp & 3) + ((sp & 127) >> 2);
+  const int sra = srow < rows_a ? srow : rows_a - 1;
+  const int srb = srow < rows_b ? srow : rows_b - 1;
 
   const int nk = (int)(K / BK);
 
@@ -153,31 +166,39 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
   // loads touch no memory and write zeros to a slot nobody reads.
   const uint32_t a_rec = (uint32_t)((int64_t)rows_a * K);
   const uint32_t b_rec = (uint32_t)((int64_t)rows_b * K);
-  auto issue_step = [&](int s) {
+  const __amdgpu_buffer_rsrc_t ra_v = __builtin_amdgcn_make_buffer_rsrc((void*)(A + m_lo * K), 0, (int)a_rec, RSRC_FLAGS);
+  const __amdgpu_buffer_rsrc_t rb_v =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(B + (b_row0 + n0) * K), 0, (int)b_rec, RSRC_FLAGS);
+  const __amdgpu_buffer_rsrc_t r_none = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, 0, RSRC_FLAGS);
+  // DMA piece q of step s into SLOT: 0..7 A rows, 8..15 B rows, 16/17 the
+  // scale words of A / B.  A step past the end gets zero-length buffer ranges.
+  auto dma_piece = [&](int s, auto SLOT, int q) {
+    lds_u8* base = smem + decltype(SLOT)::value * SLOT_BYTES;
     const bool valid = s < nk;
-    lds_u8* base = smem + (s & 1) * SLOT_BYTES;
-    const uint32_t k0 = valid ? (uint32_t)s * BK : 0u;
-    const __amdgpu_buffer_rsrc_t ra =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(A + m_lo * K), 0, (int)(valid ? a_rec : 0u), RSRC_FLAGS);
-    const __amdgpu_buffer_rsrc_t rb =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(B + (b_row0 + n0) * K), 0, (int)(valid ? b_rec : 0u), RSRC_FLAGS);
+    const int k0 = valid ? s * BK : 0;
     const int64_t sv = valid ? s : 0;
-    const __amdgpu_buffer_rsrc_t rsa =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Ap + sv * M + m_lo), 0, valid ? rows_a * 4 : 0, RSRC_FLAGS);
-    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(Bp + sv * brows + b_row0 + n0), 0, valid ? rows_b * 4 : 0, RSRC_FLAGS);
+    if (q < 8) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(valid ? ra_v : r_none, (lds_void*)(base + 1024 * (8 * wave + q)), 16,
+                                               dma_off[q], k0, 0, 0);
+    } else if (q < 16) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(valid ? rb_v : r_none,
+                                               (lds_void*)(base + A_BYTES + 1024 * (8 * wave + q - 8)), 16,
+                                               dma_off[q - 8], k0, 0, 0);
+    } else if (q == 16) {
+      const __amdgpu_buffer_rsrc_t rsa =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(Ap + sv * M + m_lo), 0, valid ? rows_a * 4 : 0, RSRC_FLAGS);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(base + SA_OFF + 256 * wave), 4, 4u * (uint32_t)sra, 0,
+                                               0, 0);
+    } else {
+      const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(Bp + sv * brows + b_row0 + n0), 0, valid ? rows_b * 4 : 0, RSRC_FLAGS);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(base + SB_OFF + 256 * wave), 4, 4u * (uint32_t)srb, 0,
+                                               0, 0);
+    }
+  };
+  auto issue_step = [&](int s, auto SLOT) {
 #pragma unroll
-    for (int i = 0; i < 8; i++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(base + 1024 * (8 * wave + i)), 16,
-                                               dma_base[i & 1] + (uint32_t)(8 * i) * (uint32_t)K + k0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(base + A_BYTES + 1024 * (8 * wave + i)), 16,
-                                               dma_base[i & 1] + (uint32_t)(8 * i) * (uint32_t)K + k0, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(base + SA_OFF + 256 * wave), 4, 4u * (uint32_t)sra, 0,
-                                             0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(base + SB_OFF + 256 * wave), 4, 4u * (uint32_t)srb, 0,
-                                             0, 0);
+    for (int q = 0; q < 18; q++) dma_piece(s, SLOT, q);
   };
 
   // Fragment of lane (row lr, group lg) for K half h: bytes 0..15 are
@@ -199,11 +220,10 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
 #pragma unroll
     for (int j = 0; j < 4; j++) acc[i][j] = v16f{};
 
-  auto slot_base = [&](int s) { return smem + (s & 1) * SLOT_BYTES; };
-  auto read_frags = [&](int s, auto H, auto SET) {
+  auto read_frags = [&](auto SLOT, auto H, auto SET) {
     constexpr int h = decltype(H)::value;
     constexpr int set = decltype(SET)::value;
-    const lds_u8* base = slot_base(s);
+    const lds_u8* base = smem + decltype(SLOT)::value * SLOT_BYTES;
     const int p0 = 16 * ((4 * h + lg) ^ swz);       // K = 64h + 16lg + [0,16)  (scale block 2h)
     const int p1 = 16 * ((4 * h + 2 + lg) ^ swz);   // K = 64h + 32 + 16lg + [0,16) (block 2h+1)
 #pragma unroll
@@ -216,65 +236,94 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
       fb[set][i] = v8i{(int)blo.x, (int)blo.y, (int)blo.z, (int)blo.w, (int)bhi.x, (int)bhi.y, (int)bhi.z, (int)bhi.w};
     }
   };
-  // Scale words of step s, shifted right by 8 * (lane / 32) right away (the
-  // same shift serves both halves; op_sel then picks byte 0 or 2), one half
-  // before the MFMAs that use them.
-  auto read_scales = [&](int s, uint32_t* ra, uint32_t* rb) {
-    const lds_u8* base = slot_base(s);
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      ra[i] = *(lds_u32*)(base + SA_OFF + 4 * (wm * 128 + 32 * i + lr)) >> sh;
-      rb[i] = *(lds_u32*)(base + SB_OFF + 4 * (wn * 128 + 32 * i + lr)) >> sh;
+  // One 16-byte piece q of the fragments: frag q/2 (A blocks 0..3, then B
+  // blocks 0..3), low (K block 2h) or high (block 2h+1) half.
+  auto read_piece = [&](auto SLOT, auto H, auto SET, int qq) {
+    // order: A0, B0..B3, A1..A3 (the operands of MFMA (i, j) in i-major order)
+    constexpr int order[16] = {0, 1, 8, 9, 10, 11, 12, 13, 14, 15, 2, 3, 4, 5, 6, 7};
+    const int q = order[qq];
+    constexpr int h = decltype(H)::value;
+    constexpr int set = decltype(SET)::value;
+    const lds_u8* base = smem + decltype(SLOT)::value * SLOT_BYTES;
+    const int f = q >> 1;
+    const int p = (q & 1) ? 16 * ((4 * h + 2 + lg) ^ swz) : 16 * ((4 * h + lg) ^ swz);
+    const int off = (f < 4 ? a_row_off + f * 32 * BK : b_row_off + (f - 4) * 32 * BK) + p;
+    const v4i v = __builtin_bit_cast(v4i, *(lds_u32x4*)(base + off));
+    if (f < 4) {
+      if (q & 1) fa[set][f].hi = v; else fa[set][f].lo = v;
+    } else {
+      if (q & 1) fb[set][f - 4].hi = v; else fb[set][f - 4].lo = v;
     }
   };
-  auto mfma_half = [&](auto SET, auto OPSEL) {
+  // The four scale words of a step (one 16-byte read each for A and B), read
+  // one half before the MFMAs that use them.  They are shifted right by
+  // 8 * (lane / 32) when the step starts (the same shift serves both halves;
+  // op_sel then picks byte 0 or 2): lane l supplies the scale of K-block l / 32.
+  auto read_scales = [&](auto SLOT, uint32_t* ra, uint32_t* rb) {
+    const lds_u8* base = smem + decltype(SLOT)::value * SLOT_BYTES;
+    const u32x4 a4 = *(lds_u32x4*)(base + SA_OFF + 16 * (wm * 32 + lr));
+    const u32x4 b4 = *(lds_u32x4*)(base + SB_OFF + 16 * (wn * 32 + lr));
+    ra[0] = a4.x; ra[1] = a4.y; ra[2] = a4.z; ra[3] = a4.w;
+    rb[0] = b4.x; rb[1] = b4.y; rb[2] = b4.z; rb[3] = b4.w;
+  };
+  auto mfma_one = [&](auto SET, auto OPSEL, int q) {
     constexpr int set = decltype(SET)::value;
     constexpr int op = decltype(OPSEL)::value;
+    const int i = q >> 2, j = q & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[set][i], fb[set][j], acc[i][j], 0, 0, op,
+                                                                (int)sa[i], op, (int)sb[j]);
+  };
+  // One K step: first half from register set 0 while the second half's
+  // fragments load; then make step t+1 resident, refill this step's slot with
+  // step t+2, and run the second half while the first-half fragments and the
+  // scales of step t+1 load.  Slots alternate, so two steps are unrolled and
+  // every LDS address is a constant offset.
+  auto kstep = [&](int t, auto SLOT) {
+    constexpr int slot = decltype(SLOT)::value;
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int q = 0; q < 16; q++) {
+      mfma_one(ic<0>{}, ic<0>{}, q);
+      read_piece(SLOT, ic<1>{}, ic<1>{}, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vmcnt<0>();
+    wait_lgkm0();
+    lds_barrier();
+    dma_piece(t + 2, SLOT, 16);
+    dma_piece(t + 2, SLOT, 17);
+    read_scales(ic<1 - slot>{}, na, nb);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[set][i], fb[set][j], acc[i][j], 0, 0, op,
-                                                                    (int)sa[i], op, (int)sb[j]);
+    for (int q = 0; q < 16; q++) {
+      mfma_one(ic<1>{}, ic<2>{}, q);
+      read_piece(ic<1 - slot>{}, ic<0>{}, ic<0>{}, q);
+      dma_piece(t + 2, SLOT, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      sa[i] = na[i] >> sh;
+      sb[i] = nb[i] >> sh;
+    }
   };
 
   if (nk > 0) {
-    issue_step(0);
-    issue_step(1);
+    issue_step(0, ic<0>{});
+    issue_step(1, ic<1>{});
     wait_vmcnt<18>();
     lds_barrier();
-    read_frags(0, ic<0>{}, ic<0>{});
-    read_scales(0, sa, sb);
-    // One K step per iteration: first half from register set 0 while the
-    // second half's fragments load; then make step t+1 resident, refill this
-    // step's slot with step t+2, and run the second half while the first-half
-    // fragments and the scales of step t+1 load.
-    for (int t = 0; t < nk; t++) {
-      read_frags(t, ic<1>{}, ic<1>{});
-      mfma_half(ic<0>{}, ic<0>{});
+    read_frags(ic<0>{}, ic<0>{}, ic<0>{});
+    read_scales(ic<0>{}, sa, sb);
 #pragma unroll
-      for (int i = 0; i < 16; i++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      if (t + 1 < nk) wait_vmcnt<0>();
-      wait_lgkm0();
-      lds_barrier();
-      issue_step(t + 2);
-      read_frags(t + 1, ic<0>{}, ic<0>{});
-      read_scales(t + 1, na, nb);
-      mfma_half(ic<1>{}, ic<2>{});
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // DMA
-      }
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        sa[i] = na[i];
-        sb[i] = nb[i];
-      }
+    for (int i = 0; i < 4; i++) {
+      sa[i] >>= sh;
+      sb[i] >>= sh;
+    }
+    // An odd step count runs one extra all-zero step (its DMA ranges are
+    // empty, so its codes and scales read as zero and add nothing).
+    for (int t = 0; t < nk; t += 2) {
+      kstep(t, ic<0>{});
+      kstep(t + 1, ic<1>{});
     }
   }
 
@@ -287,7 +336,11 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
   // adjacent columns: the even lane writes row R, the odd lane row R+1.
   wait_lgkm0();
   lds_barrier();
+  // Lane-derived values are re-derived from the lane id here so that none of
+  // them stays live (or spills) across the main loop.
+  const int elane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   {
+    const int lane = elane, lr = elane & 31, lg = elane >> 5;
     const bool odd = lane & 1;
     const int rb = wm * 128 + 4 * lg;
     const int cb = wn * 128 + lr - (odd ? 1 : 0);
@@ -320,7 +373,7 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
     if (col < N) {
 #pragma unroll 8
       for (int k = 0; k < 32; k++) {
-        const int row = (tid >> 5) + 8 * k;
+        const int row = 2 * wave + (elane >> 5) + 8 * k;   // tid / 32 + 8k
         const int64_t grow = m_lo + row;
         const u32x4 v = *(lds_u32x4*)(smem + row * C_LDS_STRIDE + 16 * ch);
         if (grow < m_hi) store_nt16(Cm + grow * ldc + col, make_uint4(v.x, v.y, v.z, v.w));

@@ -86,7 +86,7 @@ def test_tiny_config():
 
 
 @pytest.mark.parametrize("M,N,K", [(32, 32, 128), (96, 224, 384), (160, 96, 1024), (1000, 320, 256),
-                                   (7, 64, 128), (256, 4096, 128), (130, 160, 2048)])
+                                   (7, 64, 128), (256, 4096, 128), (130, 160, 2048), (288, 288, 1152)])
 def test_ragged_gemm_shapes(M, N, K):
     a = workloads.normal_bf16((M, K), M + K)
     b = workloads.normal_bf16((N, K), N + 3 * K, std=0.5)
