@@ -171,6 +171,25 @@ mxfp8_status mxfp8_gemm(const uint8_t *a, const uint32_t *a_packed,
                         void *c, int64_t ldc,
                         int64_t M, int64_t N, int64_t K, void *stream);
 
+/* Flags of mxfp8_gemm_ex / mxfp8_grouped_gemm_ex. */
+#define MXFP8_GEMM_ACCUMULATE 1u /* C = bf16_rne( float(C) + sum_k dq(A) dq(B) ): beta = 1 */
+
+/*
+ * mxfp8_gemm with options.  Defining passage: the accumulate option that the
+ * FlyDSL backend still rejects (wgrad accumulation into an existing gradient,
+ * "Experimental FlyDSL GEMM backend for TE PyTorch (BF16/FP16/FP32/FP8/MXFP8)",
+ * review of the epilogue validation and of the fallback exceptions).
+ * flags   0 or MXFP8_GEMM_ACCUMULATE.  With ACCUMULATE, C is read and the sum
+ *         is rounded once (fp32 accumulator + the old BF16 value, then BF16
+ *         round-to-nearest-even); K == 0 leaves C unchanged.
+ * Other arguments and errors as mxfp8_gemm; unknown flag bits -> FLAGS.
+ * mxfp8_gemm(...) is mxfp8_gemm_ex(..., 0, stream).
+ */
+mxfp8_status mxfp8_gemm_ex(const uint8_t *a, const uint32_t *a_packed,
+                           const uint8_t *b, const uint32_t *b_packed,
+                           void *c, int64_t ldc,
+                           int64_t M, int64_t N, int64_t K, uint32_t flags, void *stream);
+
 /* ------------------------------------------------------------------------
  * Grouped (ragged expert) GEMM
  *
@@ -208,6 +227,14 @@ mxfp8_status mxfp8_grouped_gemm(const uint8_t *a, const uint32_t *a_packed,
                                 const int32_t *offsets, int32_t G,
                                 void *c, int64_t ldc,
                                 int64_t M_total, int64_t N, int64_t K, void *stream);
+
+/* mxfp8_grouped_gemm with options (flags as mxfp8_gemm_ex; rows outside every
+ * group are neither read nor written). */
+mxfp8_status mxfp8_grouped_gemm_ex(const uint8_t *a, const uint32_t *a_packed,
+                                   const uint8_t *b, const uint32_t *b_packed,
+                                   const int32_t *offsets, int32_t G,
+                                   void *c, int64_t ldc,
+                                   int64_t M_total, int64_t N, int64_t K, uint32_t flags, void *stream);
 
 #ifdef __cplusplus
 }

@@ -22,13 +22,14 @@ LIB_PATH = os.path.join(_HERE, "libmxfp8.so")
 MXFP8_ROWWISE = 1
 MXFP8_COLWISE = 2
 MXFP8_DBIAS = 4
+MXFP8_GEMM_ACCUMULATE = 1
 
 STATUS_NAMES = {0: "MXFP8_OK", 1: "MXFP8_ERR_NULL", 2: "MXFP8_ERR_SHAPE", 3: "MXFP8_ERR_MISALIGNED",
                 4: "MXFP8_ERR_FLAGS", 5: "MXFP8_ERR_WORKSPACE", 6: "MXFP8_ERR_HIP", 7: "MXFP8_ERR_LIMIT"}
 
 EXPORTED = ("mxfp8_status_string", "mxfp8_last_hip_error", "mxfp8_quantize_workspace_bytes",
             "mxfp8_quantize", "mxfp8_packed_scale_bytes", "mxfp8_pack_scales", "mxfp8_gemm",
-            "mxfp8_grouped_gemm")
+            "mxfp8_grouped_gemm", "mxfp8_gemm_ex", "mxfp8_grouped_gemm_ex")
 
 
 class MXFP8Error(RuntimeError):
@@ -68,6 +69,10 @@ def lib() -> ctypes.CDLL:
     L.mxfp8_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
     L.mxfp8_grouped_gemm.restype = ctypes.c_int
     L.mxfp8_grouped_gemm.argtypes = [P, P, P, P, P, I32, P, I64, I64, I64, I64, P]
+    L.mxfp8_gemm_ex.restype = ctypes.c_int
+    L.mxfp8_gemm_ex.argtypes = [P, P, P, P, P, I64, I64, I64, I64, U32, P]
+    L.mxfp8_grouped_gemm_ex.restype = ctypes.c_int
+    L.mxfp8_grouped_gemm_ex.argtypes = [P, P, P, P, P, I32, P, I64, I64, I64, I64, U32, P]
     _lib = L
     return L
 
@@ -135,6 +140,16 @@ def mxfp8_grouped_gemm(a, a_packed, b, b_packed, offsets, G, c, ldc, M_total, N,
                                     M_total, N, K, _s(stream)), "mxfp8_grouped_gemm")
 
 
+def mxfp8_gemm_ex(a, a_packed, b, b_packed, c, ldc, M, N, K, flags, stream=None):
+    _check(lib().mxfp8_gemm_ex(_p(a), _p(a_packed), _p(b), _p(b_packed), _p(c), ldc, M, N, K, flags, _s(stream)),
+           "mxfp8_gemm_ex")
+
+
+def mxfp8_grouped_gemm_ex(a, a_packed, b, b_packed, offsets, G, c, ldc, M_total, N, K, flags, stream=None):
+    _check(lib().mxfp8_grouped_gemm_ex(_p(a), _p(a_packed), _p(b), _p(b_packed), _p(offsets), G, _p(c), ldc,
+                                       M_total, N, K, flags, _s(stream)), "mxfp8_grouped_gemm_ex")
+
+
 # ------------------------------------------------------ allocating helpers
 
 def quantize(x, rowwise=True, colwise=False, dbias=False, stream=None):
@@ -172,21 +187,29 @@ def pack_scales(s, stream=None):
     return out
 
 
-def gemm(a, a_packed, b, b_packed, stream=None):
-    """C = dq(A) dq(B)^T in BF16 for E4M3 codes a [M, K], b [N, K]."""
+def gemm(a, a_packed, b, b_packed, out=None, accumulate=False, stream=None):
+    """C = dq(A) dq(B)^T in BF16 for E4M3 codes a [M, K], b [N, K]; with
+    accumulate=True the product is added to `out` (beta = 1)."""
     import torch
     M, K = a.shape
     N = b.shape[0]
-    c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
-    mxfp8_gemm(a, a_packed, b, b_packed, c, N, M, N, K, stream)
+    if accumulate and out is None:
+        raise ValueError("accumulate=True needs out")
+    c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    assert c.dtype == torch.bfloat16 and c.shape == (M, N) and c.stride(1) == 1
+    mxfp8_gemm_ex(a, a_packed, b, b_packed, c, c.stride(0), M, N, K, MXFP8_GEMM_ACCUMULATE if accumulate else 0,
+                  stream)
     return c
 
 
-def grouped_gemm(a, a_packed, b, b_packed, offsets, out=None, stream=None):
+def grouped_gemm(a, a_packed, b, b_packed, offsets, out=None, accumulate=False, stream=None):
     """Ragged grouped GEMM; b is [G, N, K]; rows outside every group keep `out`'s values."""
     import torch
     M, K = a.shape
     G, N, _ = b.shape
+    if accumulate and out is None:
+        raise ValueError("accumulate=True needs out")
     c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
-    mxfp8_grouped_gemm(a, a_packed, b, b_packed, offsets, G, c, c.stride(0), M, N, K, stream)
+    mxfp8_grouped_gemm_ex(a, a_packed, b, b_packed, offsets, G, c, c.stride(0), M, N, K,
+                          MXFP8_GEMM_ACCUMULATE if accumulate else 0, stream)
     return c

@@ -78,7 +78,7 @@ struct ic {
   static constexpr int value = V;
 };
 
-template <bool GROUPED>
+template <bool GROUPED, bool ACC>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
                  const uint8_t* __restrict__ B, const uint32_t* __restrict__ Bp,
@@ -339,6 +339,22 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
   // Lane-derived values are re-derived from the lane id here so that none of
   // them stays live (or spills) across the main loop.
   const int elane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  if (ACC) {
+    // Accumulate: stage the current C tile in the LDS tile (same layout and
+    // thread mapping as the stores below; rows / columns outside C read as 0).
+    const int ch = elane & 31;
+    const int64_t col = n0 + 8 * ch;
+#pragma unroll 8
+    for (int k = 0; k < 32; k++) {
+      const int row = 2 * wave + (elane >> 5) + 8 * k;
+      const int64_t grow = m_lo + row;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (col < N && grow < m_hi) v = *reinterpret_cast<const u32x4*>(Cm + grow * ldc + col);
+      *(__attribute__((address_space(3))) u32x4*)(smem + row * C_LDS_STRIDE + 16 * ch) = v;
+    }
+    wait_lgkm0();
+    lds_barrier();
+  }
   {
     const int lane = elane, lr = elane & 31, lg = elane >> 5;
     const bool odd = lane & 1;
@@ -352,13 +368,28 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
       for (int j = 0; j < 4; j++)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const bf16x2 h = {(__bf16)acc[i][j][r], (__bf16)acc[i][j][r + 1]};
+          const int row = rb + 32 * i + 8 * (r >> 2) + (r & 3) + (odd ? 1 : 0);
+          __attribute__((address_space(3))) uint32_t* slot_word =
+              (__attribute__((address_space(3))) uint32_t*)(smem + row * C_LDS_STRIDE + 2 * (cb + 32 * j));
+          float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
+          if (ACC) {
+            // The word at this lane's address holds the old C of its row for
+            // columns c, c+1; the partner holds the other row.  Trade halves
+            // the same way as below so each lane gets rows R, R+1 of its column.
+            const uint32_t w_old = *slot_word;
+            const uint32_t y_old =
+                (uint32_t)__builtin_amdgcn_mov_dpp((int)__builtin_amdgcn_alignbit(w_old, w_old, send_shift), 0xB1,
+                                                   0xF, 0xF, true);
+            const uint32_t c_r = odd ? y_old : w_old;                 // row R of this column in the low half
+            const uint32_t c_r1 = odd ? (w_old >> 16) : y_old;         // row R+1 of this column in the low half
+            v0 += __uint_as_float(c_r << 16);
+            v1 += __uint_as_float(c_r1 << 16);
+          }
+          const bf16x2 h = {(__bf16)v0, (__bf16)v1};
           const uint32_t pk = __builtin_bit_cast(uint32_t, h);   // row R low, row R+1 high
           const uint32_t send = __builtin_amdgcn_alignbit(pk, pk, send_shift);
           const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, true);  // lane ^ 1
-          const uint32_t word = __builtin_amdgcn_perm(y, pk, sel);
-          const int row = rb + 32 * i + 8 * (r >> 2) + (r & 3) + (odd ? 1 : 0);
-          *(__attribute__((address_space(3))) uint32_t*)(smem + row * C_LDS_STRIDE + 2 * (cb + 32 * j)) = word;
+          *slot_word = __builtin_amdgcn_perm(y, pk, sel);
         }
       __builtin_amdgcn_sched_barrier(0);   // bounds the registers the batched AGPR reads take
     }
@@ -388,29 +419,34 @@ int64_t gemm_blocks(int64_t M, int64_t N, int32_t G, bool grouped) {
   return tm * tn;
 }
 
+template <bool GROUPED, bool ACC>
+static hipError_t launch_gemm_t(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
+                                uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, const int32_t* offsets,
+                                int32_t G, int64_t tiles_m, int64_t tiles_n, hipStream_t stream) {
+  static bool attr_done = false;
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<GROUPED, ACC>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  hipLaunchKernelGGL((gemm_kernel<GROUPED, ACC>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), LDS_BYTES, stream,
+                     a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
                        uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                       const int32_t* offsets, int32_t G, hipStream_t stream) {
+                       const int32_t* offsets, int32_t G, bool accumulate, hipStream_t stream) {
   const bool grouped = offsets != nullptr;
   const int64_t tiles_n = (N + BN - 1) / BN;
   const int64_t tiles_m = (M + BM - 1) / BM + (grouped ? (int64_t)G : 0);
-  const int64_t blocks = tiles_m * tiles_n;
-  if (blocks == 0) return hipSuccess;
-  static bool attr_done[2] = {false, false};
-  if (!attr_done[grouped]) {
-    const void* fn = grouped ? reinterpret_cast<const void*>(&gemm_kernel<true>)
-                             : reinterpret_cast<const void*>(&gemm_kernel<false>);
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_done[grouped] = true;
-  }
+  if (tiles_m * tiles_n == 0) return hipSuccess;
   if (grouped)
-    hipLaunchKernelGGL(gemm_kernel<true>, dim3((unsigned)blocks), dim3(256), LDS_BYTES, stream, a, ap, b, bp, c,
-                       ldc, M, N, K, offsets, G, tiles_m, tiles_n);
-  else
-    hipLaunchKernelGGL(gemm_kernel<false>, dim3((unsigned)blocks), dim3(256), LDS_BYTES, stream, a, ap, b, bp, c,
-                       ldc, M, N, K, offsets, G, tiles_m, tiles_n);
-  return hipGetLastError();
+    return accumulate ? launch_gemm_t<true, true>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, stream)
+                      : launch_gemm_t<true, false>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, stream);
+  return accumulate ? launch_gemm_t<false, true>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, stream)
+                    : launch_gemm_t<false, false>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, stream);
 }
 
 }  // namespace mx

@@ -135,6 +135,17 @@ def test_grouped_gemm_validation(L):
     assert G(A16, A16, A16, A16, None, 4, None, 64, 0, 64, 128, None) == OK
 
 
+def test_gemm_ex_flags(L):
+    G = L.mxfp8_gemm_ex
+    assert G(A16, A16, A16, A16, A16, 64, 64, 64, 128, 2, None) == FLAGS
+    assert G(A16, A16, A16, A16, A16, 64, 64, 64, 100, 1, None) == SHAPE   # the dense checks still apply
+    assert G(None, None, None, None, None, 64, 0, 64, 128, 1, None) == OK
+    GG = L.mxfp8_grouped_gemm_ex
+    assert GG(A16, A16, A16, A16, A16, 4, A16, 64, 64, 64, 128, 4, None) == FLAGS
+    assert GG(A16, A16, A16, A16, A16, 0, A16, 64, 64, 64, 128, 1, None) == SHAPE
+    assert GG(A16, A16, A16, A16, None, 4, None, 64, 0, 64, 128, 1, None) == OK
+
+
 def test_binding_raises_on_error(L):
     with pytest.raises(mx.MXFP8Error) as ei:
         mx.mxfp8_quantize(A16, 64, 48, 64, ROW, A16, A16, stream=0)

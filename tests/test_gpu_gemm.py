@@ -156,9 +156,67 @@ def test_k_zero_writes_zeros():
     assert torch.all(c == 0).item()
 
 
+# ------------------------------------------------ accumulate (beta = 1)
+
+@pytest.mark.parametrize("M,N,K", [(96, 224, 384), (300, 288, 1152), (512, 512, 2048)])
+def test_gemm_accumulate(M, N, K):
+    """C = C_old + A B^T, rounded once: compared with the oracle product plus the
+    old values; columns beyond N (ldc padding) keep their canary."""
+    torch = need_gpu()
+    a = workloads.normal_bf16((M, K), M + 7 * K)
+    b = workloads.normal_bf16((N, K), N + 11 * K, std=0.05)
+    c_old = workloads.normal_bf16((M, N), M * N + 1, std=4.0)
+    qa, sa, pa = quantize_on_gpu(a)
+    qb, sb, pb = quantize_on_gpu(b)
+    ldc = N + 40
+    full = np.full((M, ldc), 0x3F80, dtype=np.uint16)        # 1.0 in the padding
+    full[:, :N] = c_old
+    cd = to_dev_bf16(full)
+    log("accumulate M=%d N=%d K=%d" % (M, N, K))
+    mx.mxfp8_gemm_ex(qa, pa, qb, pb, cd, ldc, M, N, K, mx.MXFP8_GEMM_ACCUMULATE)
+    torch.cuda.synchronize()
+    got = to_host(cd)
+    assert np.all(got[:, N:] == 0x3F80), "ldc padding written"
+    oqa, osa = oracle.quantize_rowwise(a)
+    oqb, osb = oracle.quantize_rowwise(b)
+    ref = oracle.gemm_tn(oqa, osa, oqb, osb) + bf16_to_f64(c_old)
+    gemm_tolerance_check(got[:, :N], ref, K, label="accumulate")
+
+
+def test_gemm_accumulate_exact_on_integers():
+    """Small integers: every partial sum is exact in fp32, so C_old + A B^T must be
+    the exact integer rounded once to BF16."""
+    torch = need_gpu()
+    rng = np.random.default_rng(21)
+    M, N, K = 128, 96, 256
+    ai = rng.integers(-3, 4, size=(M, K)).astype(np.float32)
+    bi = rng.integers(-3, 4, size=(N, K)).astype(np.float32)
+    ci = rng.integers(-40, 41, size=(M, N)).astype(np.float32)
+    a = workloads.f32_to_bf16_bits(ai)
+    b = workloads.f32_to_bf16_bits(bi)
+    c_old = workloads.f32_to_bf16_bits(ci)
+    qa, sa, pa = quantize_on_gpu(a)
+    qb, sb, pb = quantize_on_gpu(b)
+    cd = to_dev_bf16(c_old)
+    mx.gemm(qa, pa, qb, pb, out=cd, accumulate=True)
+    torch.cuda.synchronize()
+    exact = ai.astype(np.int64) @ bi.astype(np.int64).T + ci.astype(np.int64)
+    want = workloads.f32_to_bf16_bits(exact.astype(np.float32))
+    assert np.array_equal(to_host(cd), want)
+
+
+def test_gemm_accumulate_k_zero_keeps_c():
+    torch = need_gpu()
+    c_old = workloads.normal_bf16((64, 96), 5)
+    cd = to_dev_bf16(c_old)
+    mx.mxfp8_gemm_ex(None, None, None, None, cd, 96, 64, 96, 0, mx.MXFP8_GEMM_ACCUMULATE)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(cd), c_old)
+
+
 # --------------------------------------------------------- grouped GEMM
 
-def grouped_case(M, N, K, counts, seed, canary_rows=True):
+def grouped_case(M, N, K, counts, seed, canary_rows=True, accumulate=False):
     torch = need_gpu()
     G = len(counts)
     x = workloads.normal_bf16((M, K), seed)
@@ -168,9 +226,13 @@ def grouped_case(M, N, K, counts, seed, canary_rows=True):
     wq = quantize_on_gpu(w.reshape(G * N, K))
     qw = wq[0].view(G, N, K)
     pw = wq[2]
-    out = torch.full((M, N), -7.0, dtype=torch.bfloat16, device="cuda")
-    log("grouped M=%d N=%d K=%d counts=%s" % (M, N, K, list(counts)))
-    mx.grouped_gemm(qx, px, qw, pw, to_dev(off), out=out)
+    c_old = workloads.normal_bf16((M, N), seed + 2, std=2.0) if accumulate else None
+    if accumulate:
+        out = to_dev_bf16(c_old)
+    else:
+        out = torch.full((M, N), -7.0, dtype=torch.bfloat16, device="cuda")
+    log("grouped M=%d N=%d K=%d counts=%s accumulate=%d" % (M, N, K, list(counts), accumulate))
+    mx.grouped_gemm(qx, px, qw, pw, to_dev(off), out=out, accumulate=accumulate)
     torch.cuda.synchronize()
     c = to_host(out)
     oqx, osx = oracle.quantize_rowwise(x)
@@ -181,8 +243,12 @@ def grouped_case(M, N, K, counts, seed, canary_rows=True):
     covered[off[0]:off[-1]] = True
     rows = np.nonzero(covered)[0]
     ref = oracle.grouped_gemm_tn(oqx, osx, qwo, swo, off, rows=rows)
+    if accumulate:
+        ref = ref + bf16_to_f64(c_old[rows])
     gemm_tolerance_check(c[rows], ref, K, label="grouped")
-    if canary_rows:
+    if canary_rows and accumulate:
+        assert np.array_equal(c[~covered], c_old[~covered]), "rows outside the groups were written"
+    elif canary_rows:
         assert np.all(bf16_to_f64(c[~covered]) == -7.0), "rows outside the groups were written"
 
 
@@ -196,6 +262,10 @@ def test_grouped_ragged_and_empty():
 
 def test_grouped_unaligned_counts_and_uncovered_tail():
     grouped_case(1200, 96, 256, [5, 0, 131, 257, 600], 6)   # rows 993.. belong to no group
+
+
+def test_grouped_accumulate():
+    grouped_case(1200, 96, 256, [5, 0, 131, 257, 600], 8, accumulate=True)
 
 
 def test_grouped_single_group_matches_dense():
