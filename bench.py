@@ -13,10 +13,11 @@ with HIP events recorded on its launch stream; ``quantize`` reports each
 quantizer launch against the HBM peak; ``cpu_baseline`` is the CPU oracle on
 the same work.
 
-``--workload backward|moe|stress`` measures the other workloads the same way:
-row+col+dbias quantize and the wgrad GEMM on the columnwise copies; the ragged
-grouped MoE GEMM; the wide-range 32768x8192x8192 GEMM.  They are reporting
-aids next to the default line.
+``--workload backward|moe|stress|linear`` measures the other workloads the
+same way: row+col+dbias quantize and the wgrad GEMM on the columnwise copies;
+the ragged grouped MoE GEMM; the wide-range 32768x8192x8192 GEMM; one MXFP8
+linear-layer training step (fprop, dgrad, wgrad accumulated into a BF16 main
+gradient).  They are reporting aids next to the default line.
 """
 
 import argparse
@@ -38,7 +39,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="dense", choices=["dense", "backward", "moe", "stress"])
+    p.add_argument("--workload", default="dense", choices=["dense", "backward", "moe", "stress", "linear"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU-oracle time: whole oracle steps are repeated until reached")
@@ -131,11 +132,12 @@ def build_ops(workload, dev):
                 b["sT"], C, R, R // 32, b["pT"], stream=st), 2.0 * R * C / 32))
         return b
 
-    def gemm_op(a, pa, b, pb, M, N, K):
-        c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    def gemm_op(a, pa, b, pb, M, N, K, accumulate=False, name=""):
+        c = torch.zeros((M, N), dtype=torch.bfloat16, device=dev)
         keep.append(c)
-        label = "%dx%dx%d" % (M, N, K)
-        ops.append(Op("gemm", label, lambda st: mx.mxfp8_gemm(a, pa, b, pb, c, N, M, N, K, stream=st),
+        label = name + "%dx%dx%d" % (M, N, K)
+        flags = mx.MXFP8_GEMM_ACCUMULATE if accumulate else 0
+        ops.append(Op("gemm", label, lambda st: mx.mxfp8_gemm_ex(a, pa, b, pb, c, N, M, N, K, flags, stream=st),
                       2.0 * M * N * K))
         return label
 
@@ -166,6 +168,21 @@ def build_ops(workload, dev):
         dominant = gemm_op(ba["q"], ba["p"], bb["q"], bb["p"], 32768, 8192, 8192)
         desc = ("wide-range stress: A[32768x8192] (2^u block scales, max BF16, subnormals) rowwise+columnwise, "
                 "B[8192x8192] rowwise, TN GEMM 32768x8192x8192")
+    elif workload == "linear":
+        lin = workloads.dense_linear()
+        T, K = lin["X"].shape
+        N = lin["W"].shape[0]
+        dy = workloads.normal_bf16((T, N), 4)
+        bx = quantize_op("X[%dx%d] row+col" % (T, K), lin["X"], ROW | COL)
+        bw = quantize_op("W[%dx%d] row+col" % (N, K), lin["W"], ROW | COL)
+        dominant = gemm_op(bx["q"], bx["p"], bw["q"], bw["p"], T, N, K, name="fprop ")
+        bd = quantize_op("dY[%dx%d] row+col" % (T, N), dy, ROW | COL)
+        gemm_op(bd["q"], bd["p"], bw["qT"], bw["pT"], T, K, N, name="dgrad ")
+        gemm_op(bd["qT"], bd["pT"], bx["qT"], bx["pT"], N, K, T, accumulate=True, name="wgrad+= ")
+        desc = ("MXFP8 linear layer training step: X[%d x %d] N(0,1), W[%d x %d] N(0,0.02), dY N(0,1); "
+                "row+col quantize of X, W, dY, fprop %dx%dx%d, dgrad %dx%dx%d on W's transposed copy, wgrad "
+                "%dx%dx%d on the transposed copies accumulated into a BF16 main gradient"
+                % (T, K, N, K, T, N, K, T, K, N, N, K, T))
     else:  # moe
         d = workloads.moe()
         G, N, K = d["W"].shape

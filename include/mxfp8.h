@@ -82,6 +82,16 @@ int mxfp8_last_hip_error(void);
  * (BF16/FP16/FP32/FP8/MXFP8)", commit notes on TN/NN/NT storage selection).
  * ------------------------------------------------------------------------ */
 
+/* Extra flags of mxfp8_quantize_ex (the with_amax option and the swizzled
+ * scale-output option of the quantization config in "[Common] Experimental
+ * CuTeDSL MXFP8 backends in C++ via TVM-FFI", review of the config key; the
+ * packed layout is the one mxfp8_pack_scales writes, so the GEMM can consume
+ * the quantizer's scales without a separate packing launch). */
+#define MXFP8_AMAX 8u            /* amax[0] = max |x| over the tensor (fp32)   */
+#define MXFP8_PACKED_SCALES 16u  /* s_row / s_colT in the packed word layout:
+                                    s_row  uint32 [cols/128][rows] (cols % 128 == 0),
+                                    s_colT uint32 [rows/128][cols] (rows % 128 == 0) */
+
 /* Bytes of workspace mxfp8_quantize needs for `flags` at this shape (0 when
  * DBIAS is not requested). */
 size_t mxfp8_quantize_workspace_bytes(int64_t rows, int64_t cols, uint32_t flags);
@@ -114,6 +124,33 @@ mxfp8_status mxfp8_quantize(const void *x, int64_t rows, int64_t cols, int64_t l
                             float *dbias,
                             void *workspace, size_t workspace_bytes,
                             void *stream);
+
+/*
+ * mxfp8_quantize with the fused extras.  Defining passage: the with_amax,
+ * swizzled and noop options of the quantization config and the device-side
+ * noop check, which must also cover the dbias reduction ("[Common]
+ * Experimental CuTeDSL MXFP8 backends in C++ via TVM-FFI", review of the
+ * config key, commit "Perform noop tensor check on device", Greptile summary
+ * on the noop + dbias interaction).
+ * flags   as mxfp8_quantize, plus MXFP8_AMAX and MXFP8_PACKED_SCALES.
+ * s_row, s_colT  byte scales as in mxfp8_quantize, or (PACKED_SCALES) uint32
+ *         words in the mxfp8_pack_scales layout, 4-byte aligned.
+ * amax    AMAX: fp32 [1], 4-byte aligned: the largest |x| of the tensor (a
+ *         BF16 value, exact; 0 for an empty tensor).  Else ignored.
+ * noop    optional DEVICE int32 flag, 4-byte aligned.  When non-NULL and
+ *         nonzero at the time the work executes, nothing is written (codes,
+ *         scales, dbias and amax keep their old contents).  NULL: always run.
+ * Errors: as mxfp8_quantize; SHAPE also for PACKED_SCALES with cols (rowwise)
+ *         or rows (columnwise) not a multiple of 128; NULL for AMAX without
+ *         amax.  mxfp8_quantize(...) rejects the extra flags (FLAGS).
+ */
+mxfp8_status mxfp8_quantize_ex(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                               uint32_t flags,
+                               uint8_t *q_row, void *s_row,
+                               uint8_t *q_colT, void *s_colT,
+                               float *dbias, float *amax, const int32_t *noop,
+                               void *workspace, size_t workspace_bytes,
+                               void *stream);
 
 /* ------------------------------------------------------------------------
  * Scale packing

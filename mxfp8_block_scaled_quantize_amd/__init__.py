@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libmxfp8.so")
 MXFP8_ROWWISE = 1
 MXFP8_COLWISE = 2
 MXFP8_DBIAS = 4
+MXFP8_AMAX = 8
+MXFP8_PACKED_SCALES = 16
 MXFP8_GEMM_ACCUMULATE = 1
 
 STATUS_NAMES = {0: "MXFP8_OK", 1: "MXFP8_ERR_NULL", 2: "MXFP8_ERR_SHAPE", 3: "MXFP8_ERR_MISALIGNED",
@@ -29,7 +31,7 @@ STATUS_NAMES = {0: "MXFP8_OK", 1: "MXFP8_ERR_NULL", 2: "MXFP8_ERR_SHAPE", 3: "MX
 
 EXPORTED = ("mxfp8_status_string", "mxfp8_last_hip_error", "mxfp8_quantize_workspace_bytes",
             "mxfp8_quantize", "mxfp8_packed_scale_bytes", "mxfp8_pack_scales", "mxfp8_gemm",
-            "mxfp8_grouped_gemm", "mxfp8_gemm_ex", "mxfp8_grouped_gemm_ex")
+            "mxfp8_grouped_gemm", "mxfp8_gemm_ex", "mxfp8_grouped_gemm_ex", "mxfp8_quantize_ex")
 
 
 class MXFP8Error(RuntimeError):
@@ -69,6 +71,8 @@ def lib() -> ctypes.CDLL:
     L.mxfp8_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
     L.mxfp8_grouped_gemm.restype = ctypes.c_int
     L.mxfp8_grouped_gemm.argtypes = [P, P, P, P, P, I32, P, I64, I64, I64, I64, P]
+    L.mxfp8_quantize_ex.restype = ctypes.c_int
+    L.mxfp8_quantize_ex.argtypes = [P, I64, I64, I64, U32, P, P, P, P, P, P, P, P, SZ, P]
     L.mxfp8_gemm_ex.restype = ctypes.c_int
     L.mxfp8_gemm_ex.argtypes = [P, P, P, P, P, I64, I64, I64, I64, U32, P]
     L.mxfp8_grouped_gemm_ex.restype = ctypes.c_int
@@ -122,6 +126,13 @@ def mxfp8_quantize(x, rows, cols, ld_x, flags, q_row=None, s_row=None, q_colT=No
            "mxfp8_quantize")
 
 
+def mxfp8_quantize_ex(x, rows, cols, ld_x, flags, q_row=None, s_row=None, q_colT=None, s_colT=None,
+                      dbias=None, amax=None, noop=None, workspace=None, workspace_bytes=0, stream=None):
+    _check(lib().mxfp8_quantize_ex(_p(x), rows, cols, ld_x, flags, _p(q_row), _p(s_row), _p(q_colT),
+                                   _p(s_colT), _p(dbias), _p(amax), _p(noop), _p(workspace), workspace_bytes,
+                                   _s(stream)), "mxfp8_quantize_ex")
+
+
 def mxfp8_packed_scale_bytes(dim: int, k: int) -> int:
     return lib().mxfp8_packed_scale_bytes(dim, k)
 
@@ -152,28 +163,47 @@ def mxfp8_grouped_gemm_ex(a, a_packed, b, b_packed, offsets, G, c, ldc, M_total,
 
 # ------------------------------------------------------ allocating helpers
 
-def quantize(x, rowwise=True, colwise=False, dbias=False, stream=None):
-    """Quantize a BF16 [rows, cols] CUDA tensor; returns a dict of outputs."""
+def quantize(x, rowwise=True, colwise=False, dbias=False, amax=False, packed=False, noop=None, stream=None):
+    """Quantize a BF16 [rows, cols] CUDA tensor; returns a dict of outputs.
+
+    packed=True returns the scales in the packed word layout ("p_row" int32
+    [cols/128, rows], "p_colT" int32 [rows/128, cols]) instead of bytes;
+    amax=True adds "amax" (fp32 [1]); noop is an optional device int32 flag."""
     import torch
     assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
     R, C = x.shape
     dev = x.device
     flags = (MXFP8_ROWWISE if rowwise else 0) | (MXFP8_COLWISE if colwise else 0) | (MXFP8_DBIAS if dbias else 0)
+    flags |= (MXFP8_AMAX if amax else 0) | (MXFP8_PACKED_SCALES if packed else 0)
     out = {}
     if rowwise:
         out["q_row"] = torch.empty((R, C), dtype=torch.uint8, device=dev)
-        out["s_row"] = torch.empty((R, C // 32), dtype=torch.uint8, device=dev)
+        if packed:
+            out["p_row"] = torch.empty((C // 128, R), dtype=torch.int32, device=dev)
+        else:
+            out["s_row"] = torch.empty((R, C // 32), dtype=torch.uint8, device=dev)
     if colwise:
         out["q_colT"] = torch.empty((C, R), dtype=torch.uint8, device=dev)
-        out["s_colT"] = torch.empty((C, R // 32), dtype=torch.uint8, device=dev)
+        if packed:
+            out["p_colT"] = torch.empty((R // 128, C), dtype=torch.int32, device=dev)
+        else:
+            out["s_colT"] = torch.empty((C, R // 32), dtype=torch.uint8, device=dev)
     ws = None
     nws = mxfp8_quantize_workspace_bytes(R, C, flags)
     if dbias:
         out["dbias"] = torch.empty((C,), dtype=torch.float32, device=dev)
+    if amax:
+        out["amax"] = torch.empty((1,), dtype=torch.float32, device=dev)
     if nws:
         ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
-    mxfp8_quantize(x, R, C, x.stride(0), flags, out.get("q_row"), out.get("s_row"), out.get("q_colT"),
-                   out.get("s_colT"), out.get("dbias"), ws, nws, stream)
+    s_row = out.get("p_row") if packed else out.get("s_row")
+    s_col = out.get("p_colT") if packed else out.get("s_colT")
+    if amax or packed or noop is not None:
+        mxfp8_quantize_ex(x, R, C, x.stride(0), flags, out.get("q_row"), s_row, out.get("q_colT"), s_col,
+                          out.get("dbias"), out.get("amax"), noop, ws, nws, stream)
+    else:
+        mxfp8_quantize(x, R, C, x.stride(0), flags, out.get("q_row"), s_row, out.get("q_colT"), s_col,
+                       out.get("dbias"), ws, nws, stream)
     return out
 
 

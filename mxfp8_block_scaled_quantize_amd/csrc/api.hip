@@ -23,10 +23,19 @@ mxfp8_status hip_status(hipError_t e) {
 }
 
 mxfp8_status check_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint32_t flags,
-                            const uint8_t* q_row, const uint8_t* s_row, const uint8_t* q_colT,
-                            const uint8_t* s_colT, const float* dbias, const void* ws, size_t ws_bytes) {
-  if (flags & ~(MXFP8_ROWWISE | MXFP8_COLWISE | MXFP8_DBIAS)) return MXFP8_ERR_FLAGS;
+                            const uint8_t* q_row, const void* s_row, const uint8_t* q_colT,
+                            const void* s_colT, const float* dbias, const float* amax, const int32_t* noop,
+                            const void* ws, size_t ws_bytes) {
+  if (flags & ~(MXFP8_ROWWISE | MXFP8_COLWISE | MXFP8_DBIAS | MXFP8_AMAX | MXFP8_PACKED_SCALES))
+    return MXFP8_ERR_FLAGS;
   if (!(flags & (MXFP8_ROWWISE | MXFP8_COLWISE))) return MXFP8_ERR_FLAGS;
+  if ((flags & MXFP8_AMAX) && !amax) return MXFP8_ERR_NULL;
+  if ((flags & MXFP8_AMAX) && !aligned(amax, 4)) return MXFP8_ERR_MISALIGNED;
+  if (noop && !aligned(noop, 4)) return MXFP8_ERR_MISALIGNED;
+  if (flags & MXFP8_PACKED_SCALES) {
+    if ((flags & MXFP8_ROWWISE) && cols % 128) return MXFP8_ERR_SHAPE;
+    if ((flags & MXFP8_COLWISE) && rows % 128) return MXFP8_ERR_SHAPE;
+  }
   if (rows < 0 || cols < 0 || ld_x < cols) return MXFP8_ERR_SHAPE;
   if (rows > kMaxDim || ld_x > kMaxDim || (rows > 0 && ld_x > kMaxDim / rows)) return MXFP8_ERR_LIMIT;
   if (cols % 32) return MXFP8_ERR_SHAPE;
@@ -40,6 +49,9 @@ mxfp8_status check_quantize(const void* x, int64_t rows, int64_t cols, int64_t l
     if (!aligned(x, 16) || ld_x % 8) return MXFP8_ERR_MISALIGNED;
     if ((flags & MXFP8_ROWWISE) && !aligned(q_row, 16)) return MXFP8_ERR_MISALIGNED;
     if ((flags & MXFP8_COLWISE) && !aligned(q_colT, 16)) return MXFP8_ERR_MISALIGNED;
+    if ((flags & MXFP8_PACKED_SCALES) && (flags & MXFP8_ROWWISE) && !aligned(s_row, 4)) return MXFP8_ERR_MISALIGNED;
+    if ((flags & MXFP8_PACKED_SCALES) && (flags & MXFP8_COLWISE) && !aligned(s_colT, 4))
+      return MXFP8_ERR_MISALIGNED;
   }
   if ((flags & MXFP8_DBIAS) && cols > 0 && !aligned(dbias, 4)) return MXFP8_ERR_MISALIGNED;
   if (mx::quantize_row_tiles(rows) * mx::quantize_col_tiles(cols) > kMaxGrid) return MXFP8_ERR_LIMIT;
@@ -91,17 +103,26 @@ size_t mxfp8_quantize_workspace_bytes(int64_t rows, int64_t cols, uint32_t flags
   return (size_t)mx::quantize_row_tiles(rows) * (size_t)cols * sizeof(float);
 }
 
+mxfp8_status mxfp8_quantize_ex(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint32_t flags,
+                               uint8_t* q_row, void* s_row, uint8_t* q_colT, void* s_colT, float* dbias,
+                               float* amax, const int32_t* noop, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  const mxfp8_status st = check_quantize(x, rows, cols, ld_x, flags, q_row, s_row, q_colT, s_colT, dbias, amax,
+                                         noop, workspace, workspace_bytes);
+  if (st != MXFP8_OK) return st;
+  const bool empty = rows == 0 || cols == 0;
+  if (empty && !(flags & MXFP8_AMAX) && !((flags & MXFP8_DBIAS) && cols > 0)) return MXFP8_OK;
+  return hip_status(mx::launch_quantize(static_cast<const uint16_t*>(x), rows, cols, ld_x, flags, q_row, s_row,
+                                        q_colT, s_colT, dbias, static_cast<float*>(workspace), amax, noop,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 mxfp8_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint32_t flags,
                             uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT, float* dbias,
                             void* workspace, size_t workspace_bytes, void* stream) {
-  const mxfp8_status st =
-      check_quantize(x, rows, cols, ld_x, flags, q_row, s_row, q_colT, s_colT, dbias, workspace, workspace_bytes);
-  if (st != MXFP8_OK) return st;
-  if (cols == 0) return MXFP8_OK;
-  if (rows == 0 && !(flags & MXFP8_DBIAS)) return MXFP8_OK;
-  return hip_status(mx::launch_quantize(static_cast<const uint16_t*>(x), rows, cols, ld_x, flags, q_row, s_row,
-                                        q_colT, s_colT, dbias, static_cast<float*>(workspace),
-                                        static_cast<hipStream_t>(stream)));
+  if (flags & ~(MXFP8_ROWWISE | MXFP8_COLWISE | MXFP8_DBIAS)) return MXFP8_ERR_FLAGS;
+  return mxfp8_quantize_ex(x, rows, cols, ld_x, flags, q_row, s_row, q_colT, s_colT, dbias, nullptr, nullptr,
+                           workspace, workspace_bytes, stream);
 }
 
 size_t mxfp8_packed_scale_bytes(int64_t dim, int64_t k) {

@@ -28,6 +28,31 @@
 
 namespace mx {
 
+// Options of one quantize call that only change where results go: all
+// uniform across the grid.
+struct QuantOpts {
+  uint32_t* amax;        // non-null: atomic max of |x| (fp32 bit patterns order like the values)
+  const int32_t* noop;   // non-null and *noop != 0: write nothing
+  int packed;            // scales in the packed word layout instead of bytes
+};
+
+__device__ __forceinline__ bool skip_call(const QuantOpts& o) { return o.noop != nullptr && *o.noop != 0; }
+
+// Fold a per-lane amax (15-bit BF16 magnitude pattern) into the tensor amax:
+// wave maximum, then one atomic per wave, skipped when the stored value is
+// already at least as large (max is order independent: the result is exact).
+__device__ __forceinline__ void fold_amax(const QuantOpts& o, uint32_t m) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const uint32_t t = (uint32_t)__shfl_xor((int)m, d, 64);
+    m = m > t ? m : t;
+  }
+  if ((threadIdx.x & 63) == 0) {
+    const uint32_t v = m << 16;   // |x| as fp32 bits
+    if (v > __hip_atomic_load(o.amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(o.amax, v);
+  }
+}
+
 constexpr int QT_C = 128;            // tile columns
 constexpr int QT_R_MIN = 128;        // rows of the smallest tile (4 waves)
 
@@ -36,7 +61,7 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
     const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
     uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
     uint8_t* __restrict__ q_colT, uint8_t* __restrict__ s_colT,
-    float* __restrict__ dbias_part, int64_t tiles_c) {
+    float* __restrict__ dbias_part, int64_t tiles_c, QuantOpts opt) {
   constexpr int TR = 32 * QW;   // tile rows
   constexpr int NT = 64 * QW;   // threads
   // Transposed FP8 tile [column][row]; 8-byte row units XOR-swizzled by the
@@ -51,6 +76,7 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
   const int w = tid >> 6;
   const int cg = lane & 15;
   const int rg = lane >> 4;
+  if (skip_call(opt)) return;   // uniform: the whole grid leaves
   const int64_t tr = (int64_t)blockIdx.x / tiles_c;
   const int64_t tc = (int64_t)blockIdx.x - tr * tiles_c;
   const int64_t r0 = tr * TR;
@@ -68,6 +94,7 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
       v[i] = make_uint4(0u, 0u, 0u, 0u);
   }
 
+  uint32_t lane_amax = 0;
   if (ROW) {
 #pragma unroll
     for (int i = 0; i < 8; i++) {
@@ -75,6 +102,7 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
                               pk_max_u16(abs_bits2(v[i].z), abs_bits2(v[i].w)));
       m = max(m & 0xFFFFu, m >> 16);
       m = quad_max(m);
+      lane_amax = max(lane_amax, m);
       const uint32_t byte = scale_byte_from_amax(m);
       const uint2 o = quantize8(v[i], byte);
       const int64_t r = rb + i;
@@ -104,6 +132,10 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
     for (int j = 0; j < 4; j++) {
       cm[j] = pk_max_u16(cm[j], (uint32_t)__shfl_xor((int)cm[j], 16, 64));
       cm[j] = pk_max_u16(cm[j], (uint32_t)__shfl_xor((int)cm[j], 32, 64));
+    }
+    if (!ROW) {
+#pragma unroll
+      for (int j = 0; j < 4; j++) lane_amax = max(lane_amax, max(cm[j] & 0xFFFFu, cm[j] >> 16));
     }
     // Dword j of every row holds columns 2j (low half) and 2j + 1 (high half):
     // clamp both halves with their own column's limit.
@@ -157,6 +189,8 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
     }
   }
 
+  if (opt.amax) fold_amax(opt, lane_amax);   // uniform branch
+
   __syncthreads();
 
   if (COL) {
@@ -176,8 +210,20 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
         else *reinterpret_cast<uint4*>(q_colT + col * R + row) = d;
       }
     }
-    // The QW scale bytes of a column: QW consecutive row blocks of s_colT.
-    if (tid < QT_C) {
+    // The QW scale bytes of a column: QW consecutive row blocks of s_colT
+    // (packed layout: QW / 4 words (t, col), t = 128-row slab, R % 128 == 0).
+    if (opt.packed && tid < QT_C) {
+      const int64_t col = c0 + tid;
+      if (col < C) {
+#pragma unroll
+        for (int k = 0; k < QW / 4; k++) {
+          const int64_t t = (r0 >> 7) + k;
+          if (t < (R >> 7))
+            reinterpret_cast<uint32_t*>(s_colT)[t * C + col] =
+                *reinterpret_cast<const uint32_t*>(lds_sc + tid * QW + 4 * k);
+        }
+      }
+    } else if (tid < QT_C) {
       const int64_t col = c0 + tid;
       const int64_t nrb = R >> 5;
       const int64_t b0 = r0 >> 5;
@@ -198,7 +244,10 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
     // The 4 scale bytes of a row of the tile (one per 32-column block).
     const int rl = tid - (NT - TR);
     const int64_t row = r0 + rl;
-    if (row < R) {
+    if (row < R && opt.packed) {
+      // packed layout: word (tc, row) of uint32 [C / 128][R] (C % 128 == 0)
+      reinterpret_cast<uint32_t*>(s_row)[tc * R + row] = *reinterpret_cast<const uint32_t*>(lds_sr + 4 * rl);
+    } else if (row < R) {
       const int64_t ncb = C >> 5;
       const uint32_t word = *reinterpret_cast<const uint32_t*>(lds_sr + 4 * rl);
       uint8_t* dst = s_row + row * ncb + 4 * tc;
@@ -240,8 +289,10 @@ constexpr int64_t FL_ELEMS = 512 * FL_LOADS;  // per wave
 __global__ __launch_bounds__(FL_THREADS) void quantize_rowwise_flat_kernel(const uint16_t* __restrict__ x,
                                                                           int64_t total,
                                                                           uint8_t* __restrict__ q,
-                                                                          uint8_t* __restrict__ s) {
+                                                                          uint8_t* __restrict__ s, QuantOpts opt) {
+  if (skip_call(opt)) return;
   const int lane = threadIdx.x & 63;
+  uint32_t lane_amax = 0;
   const int64_t base = ((int64_t)blockIdx.x * (FL_THREADS / 64) + (threadIdx.x >> 6)) * FL_ELEMS;
   uint4 v[FL_LOADS];
 #pragma unroll
@@ -256,6 +307,7 @@ __global__ __launch_bounds__(FL_THREADS) void quantize_rowwise_flat_kernel(const
                             pk_max_u16(abs_bits2(v[u].z), abs_bits2(v[u].w)));
     m = max(m & 0xFFFFu, m >> 16);
     m = quad_max(m);
+    lane_amax = max(lane_amax, m);
     const uint32_t byte = scale_byte_from_amax(m);
     const uint2 o = quantize8(v[u], byte);
     if (e < total) {  // total % 32 == 0: a quad is entirely in or out
@@ -263,6 +315,7 @@ __global__ __launch_bounds__(FL_THREADS) void quantize_rowwise_flat_kernel(const
       if ((lane & 3) == 0) s[e >> 5] = (uint8_t)byte;
     }
   }
+  if (opt.amax) fold_amax(opt, lane_amax);
 }
 
 // dbias[c] = sum over row tiles of the partial sums.  A workgroup owns 32
@@ -274,7 +327,9 @@ constexpr int DB_PARTS = 8;
 
 __global__ __launch_bounds__(DB_COLS * DB_PARTS) void dbias_reduce_kernel(const float* __restrict__ part,
                                                                           int64_t tiles, int64_t C,
-                                                                          float* __restrict__ out) {
+                                                                          float* __restrict__ out,
+                                                                          const int32_t* __restrict__ noop) {
+  if (noop != nullptr && *noop != 0) return;
   __shared__ float lds[DB_PARTS][DB_COLS];
   const int cl = threadIdx.x % DB_COLS;
   const int g = threadIdx.x / DB_COLS;
@@ -296,7 +351,9 @@ __global__ __launch_bounds__(DB_COLS * DB_PARTS) void dbias_reduce_kernel(const 
   }
 }
 
-__global__ __launch_bounds__(256) void fill_zero_f32_kernel(float* __restrict__ out, int64_t n) {
+__global__ __launch_bounds__(256) void fill_zero_f32_kernel(float* __restrict__ out, int64_t n,
+                                                            const int32_t* __restrict__ noop) {
+  if (noop != nullptr && *noop != 0) return;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) out[i] = 0.0f;
 }
@@ -311,7 +368,7 @@ int64_t quantize_col_tiles(int64_t C) { return (C + QT_C - 1) / QT_C; }
 template <bool ROW, bool COL, bool DBIAS>
 static hipError_t launch_tiles(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q_row,
                                uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT, float* dbias_part,
-                               int64_t* row_tiles, hipStream_t stream) {
+                               const QuantOpts& opt, int64_t* row_tiles, hipStream_t stream) {
   constexpr int QW = (ROW || !COL) ? 8 : 4;
   constexpr bool NT_QROW = true;
   constexpr bool NT_COLT = !ROW;
@@ -320,27 +377,36 @@ static hipError_t launch_tiles(const uint16_t* x, int64_t R, int64_t C, int64_t 
   *row_tiles = tr;
   if (tr * tc == 0) return hipSuccess;
   hipLaunchKernelGGL((quantize_tile_kernel<ROW, COL, DBIAS, QW, NT_QROW, NT_COLT>), dim3((unsigned)(tr * tc)),
-                     dim3(64 * QW), 0, stream, x, R, C, ldx, q_row, s_row, q_colT, s_colT, dbias_part, tc);
+                     dim3(64 * QW), 0, stream, x, R, C, ldx, q_row, s_row, q_colT, s_colT, dbias_part, tc, opt);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint32_t flags,
-                           uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT,
-                           float* dbias, float* dbias_part, hipStream_t stream) {
-  const bool row = flags & 1u, col = flags & 2u, db = flags & 4u;
-  if (row && !col && !db && ldx == C) {
+                           uint8_t* q_row, void* s_row, uint8_t* q_colT, void* s_colT,
+                           float* dbias, float* dbias_part, float* amax, const int32_t* noop,
+                           hipStream_t stream) {
+  const bool row = flags & 1u, col = flags & 2u, db = flags & 4u, want_amax = flags & 8u, packed = flags & 16u;
+  const QuantOpts opt{want_amax ? reinterpret_cast<uint32_t*>(amax) : nullptr, noop, packed ? 1 : 0};
+  if (want_amax) {   // max starts from 0 (also the amax of an empty tensor)
+    hipLaunchKernelGGL(fill_zero_f32_kernel, dim3(1), dim3(256), 0, stream, amax, (int64_t)1, noop);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  uint8_t* srow = static_cast<uint8_t*>(s_row);
+  uint8_t* scol = static_cast<uint8_t*>(s_colT);
+  if (row && !col && !db && !packed && ldx == C) {
     const int64_t total = R * C;
     const int64_t per_block = FL_ELEMS * (FL_THREADS / 64);
     const int64_t blocks = (total + per_block - 1) / per_block;
     if (blocks > 0)
       hipLaunchKernelGGL(quantize_rowwise_flat_kernel, dim3((unsigned)blocks), dim3(FL_THREADS), 0, stream, x, total,
-                         q_row, s_row);
+                         q_row, srow, opt);
     return hipGetLastError();
   }
   int64_t tiles_r = 0;
   hipError_t e;
 #define MX_Q_LAUNCH(RW, CL, DB) \
-  launch_tiles<RW, CL, DB>(x, R, C, ldx, q_row, s_row, q_colT, s_colT, dbias_part, &tiles_r, stream)
+  launch_tiles<RW, CL, DB>(x, R, C, ldx, q_row, srow, q_colT, scol, dbias_part, opt, &tiles_r, stream)
   if (row && col && db) e = MX_Q_LAUNCH(true, true, true);
   else if (row && col) e = MX_Q_LAUNCH(true, true, false);
   else if (row && db) e = MX_Q_LAUNCH(true, false, true);
@@ -353,9 +419,10 @@ hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
     const dim3 grid((unsigned)((C + DB_COLS - 1) / DB_COLS));
     if (tiles_r > 0)
       hipLaunchKernelGGL(dbias_reduce_kernel, grid, dim3(DB_COLS * DB_PARTS), 0, stream, dbias_part, tiles_r, C,
-                         dbias);
+                         dbias, noop);
     else
-      hipLaunchKernelGGL(fill_zero_f32_kernel, dim3((unsigned)((C + 255) / 256)), dim3(256), 0, stream, dbias, C);
+      hipLaunchKernelGGL(fill_zero_f32_kernel, dim3((unsigned)((C + 255) / 256)), dim3(256), 0, stream, dbias, C,
+                         noop);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -1,0 +1,88 @@
+"""MXFP8 linear layer (no bias) wired through the block-scaled GEMM.
+
+    fprop   y  = x W^T      TN GEMM: A = x rowwise [M][K],   B = W rowwise [N][K]
+    dgrad   dx = dy W       TN GEMM: A = dy rowwise [M][N],  B = W columnwise copy [K][N]
+    wgrad   dW = dy^T x     TN GEMM: A = dy columnwise copy [N][M], B = x columnwise copy [K][M]
+
+The columnwise copies are stored transposed, so every GEMM reduces over the
+contiguous dimension of both operands and runs on the same TN kernel; each
+quantization writes the rowwise and the transposed copy in one pass (the
+MXFP8 linear flow the FlyDSL backend page validates through te.Linear: forward,
+dgrad from W's columnwise copy, wgrad from the columnwise copies of dy and x).
+With fuse_wgrad_accumulation the weight gradient is added to ``weight.main_grad``
+(a BF16 buffer the caller owns) by the GEMM's accumulate epilogue instead of
+being returned.
+
+Shapes: x [M, K], W [N, K] BF16 with M, N and K multiples of 128 (each of the
+three GEMMs reduces over one of them).
+"""
+
+import torch
+
+from . import gemm, pack_scales, quantize
+
+
+def _quantize_both(t):
+    out = quantize(t, rowwise=True, colwise=True)
+    return (out["q_row"], pack_scales(out["s_row"]), out["q_colT"], pack_scales(out["s_colT"]))
+
+
+class MXFP8LinearFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, weight, fuse_wgrad_accumulation=False):
+        if x.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+            raise TypeError("MXFP8 linear takes BF16 input and weight")
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, x.shape[-1]).contiguous()
+        M, K = x2.shape
+        N = weight.shape[0]
+        if weight.shape[1] != K:
+            raise ValueError("weight is [%d, %d], input has %d features" % (weight.shape[0], weight.shape[1], K))
+        if M % 128 or N % 128 or K % 128:
+            raise ValueError("MXFP8 linear needs tokens, in- and out-features to be multiples of 128 "
+                             "(got M=%d, K=%d, N=%d)" % (M, K, N))
+        qx, px, qxT, pxT = _quantize_both(x2)
+        qw, pw, qwT, pwT = _quantize_both(weight.contiguous())
+        y = gemm(qx, px, qw, pw)
+        ctx.save_for_backward(qxT, pxT, qwT, pwT)
+        ctx.weight = weight
+        ctx.fuse = fuse_wgrad_accumulation
+        ctx.shape = (lead, M, K, N)
+        return y.view(*lead, N)
+
+    @staticmethod
+    def backward(ctx, dy):
+        qxT, pxT, qwT, pwT = ctx.saved_tensors
+        lead, M, K, N = ctx.shape
+        dy2 = dy.reshape(M, N).to(torch.bfloat16).contiguous()
+        qd, pd, qdT, pdT = _quantize_both(dy2)
+        dx = None
+        if ctx.needs_input_grad[0]:
+            dx = gemm(qd, pd, qwT, pwT).view(*lead, K)
+        dw = None
+        if ctx.needs_input_grad[1]:
+            if ctx.fuse:
+                main = getattr(ctx.weight, "main_grad", None)
+                if main is None or main.dtype != torch.bfloat16 or tuple(main.shape) != (N, K):
+                    raise ValueError("fuse_wgrad_accumulation needs weight.main_grad, a BF16 [N, K] tensor")
+                gemm(qdT, pdT, qxT, pxT, out=main, accumulate=True)
+            else:
+                dw = gemm(qdT, pdT, qxT, pxT)
+        return dx, dw, None
+
+
+class MXFP8Linear(torch.nn.Module):
+    """y = x W^T with MXFP8 block-scaled fprop, dgrad and wgrad (no bias)."""
+
+    def __init__(self, in_features, out_features, fuse_wgrad_accumulation=False, device=None):
+        super().__init__()
+        self.in_features, self.out_features = in_features, out_features
+        self.fuse_wgrad_accumulation = fuse_wgrad_accumulation
+        w = torch.empty((out_features, in_features), dtype=torch.bfloat16, device=device)
+        torch.nn.init.normal_(w, std=in_features ** -0.5)
+        self.weight = torch.nn.Parameter(w)
+        if fuse_wgrad_accumulation:
+            self.weight.main_grad = torch.zeros_like(w)
+
+    def forward(self, x):
+        return MXFP8LinearFunction.apply(x, self.weight, self.fuse_wgrad_accumulation)

@@ -178,6 +178,16 @@ def dbias(x_bits: np.ndarray) -> np.ndarray:
     return out
 
 
+def amax(x_bits: np.ndarray) -> float:
+    """Per-tensor amax: the largest |x| of the BF16 input (the with_amax output
+    of the quantization config, "[Common] Experimental CuTeDSL MXFP8 backends
+    in C++ via TVM-FFI", review of the config key); 0.0 for an empty tensor."""
+    x = np.asarray(x_bits, dtype=np.uint16)
+    if x.size == 0:
+        return 0.0
+    return float(np.abs(bf16_value(x)).max())
+
+
 def dequantize(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     """float64 values of codes q[R][C] under block scales s[R][C/32]."""
     q = np.ascontiguousarray(q, dtype=np.uint8)

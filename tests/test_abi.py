@@ -92,6 +92,30 @@ def test_quantize_validation(L):
     assert q(L, cols=0, ld=0, x=None, qr=None, sr=None) == OK
 
 
+def qx(L, x=A16, rows=128, cols=128, ld=128, flags=ROW, qr=A16, sr=A16, qc=A16, sc=A16, db=A16, am=A16,
+       noop=None, ws=A16, wsb=1 << 20):
+    return L.mxfp8_quantize_ex(x, rows, cols, ld, flags, qr, sr, qc, sc, db, am, noop, ws, wsb, None)
+
+
+def test_quantize_ex_validation(L):
+    AMAX, PACKED = mx.MXFP8_AMAX, mx.MXFP8_PACKED_SCALES
+    assert qx(L, flags=32 | ROW) == FLAGS
+    assert qx(L, flags=AMAX) == FLAGS                         # no copy requested
+    assert qx(L, flags=ROW | AMAX, am=None) == NULL
+    assert qx(L, flags=ROW | AMAX, am=A16 + 2) == MISALIGNED
+    assert qx(L, noop=A16 + 2) == MISALIGNED
+    assert qx(L, flags=ROW | PACKED, cols=96, ld=96) == SHAPE      # rowwise packed: cols % 128
+    assert qx(L, flags=COL | PACKED, rows=96) == SHAPE             # columnwise packed: rows % 128
+    # (the cases below stop at the last check, the workspace, so nothing is launched)
+    assert qx(L, flags=ROW | PACKED | DB, rows=96, ws=None) == WORKSPACE   # rows free for the rowwise copy
+    assert qx(L, flags=ROW | PACKED, sr=A16 + 2) == MISALIGNED
+    assert qx(L, flags=COL | PACKED, sc=A16 + 2) == MISALIGNED
+    assert qx(L, flags=ROW | DB, sr=A16 + 2, ws=None) == WORKSPACE   # byte scales need no alignment
+    # the plain entry point keeps rejecting the extra flags
+    assert q(L, flags=ROW | AMAX) == FLAGS
+    assert q(L, flags=ROW | PACKED) == FLAGS
+
+
 def test_quantize_grid_limit(L):
     assert q(L, rows=1 << 36, cols=1 << 20, ld=1 << 20) == LIMIT
     assert q(L, rows=1 << 41, cols=64, ld=64) == LIMIT

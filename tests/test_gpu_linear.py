@@ -1,0 +1,89 @@
+"""MXFP8 linear layer (fprop, dgrad, wgrad and fused wgrad accumulation) on
+the GPU path, against the oracle's GEMMs of its own quantizations of the same
+BF16 tensors (rowwise copies for fprop, the transposed columnwise copies for
+dgrad and wgrad), and loosely against plain fp32 PyTorch."""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import bf16_to_f64, gemm_tolerance_check, log, need_gpu, to_dev_bf16, to_host
+
+pytestmark = pytest.mark.gpu
+
+M, K, N = 256, 384, 512
+
+
+def _inputs(seed):
+    x = workloads.normal_bf16((M, K), seed)
+    w = workloads.normal_bf16((N, K), seed + 1, std=0.05)
+    dy = workloads.normal_bf16((M, N), seed + 2)
+    return x, w, dy
+
+
+def _refs(x, w, dy):
+    qx, sx = oracle.quantize_rowwise(x)
+    qw, sw = oracle.quantize_rowwise(w)
+    y = oracle.gemm_tn(qx, sx, qw, sw)
+    qd, sd = oracle.quantize_rowwise(dy)
+    qwT, swT = oracle.quantize_colwise(w)
+    dx = oracle.gemm_tn(qd, sd, qwT, swT)
+    qdT, sdT = oracle.quantize_colwise(dy)
+    qxT, sxT = oracle.quantize_colwise(x)
+    dw = oracle.gemm_tn(qdT, sdT, qxT, sxT)
+    return y, dx, dw
+
+
+def _run(x, w, dy, fuse=False, main_grad=None):
+    torch = need_gpu()
+    from mxfp8_block_scaled_quantize_amd.linear import MXFP8LinearFunction
+    xt = to_dev_bf16(x).requires_grad_(True)
+    wt = to_dev_bf16(w).requires_grad_(True)
+    if fuse:
+        wt.main_grad = main_grad
+    y = MXFP8LinearFunction.apply(xt, wt, fuse)
+    y.backward(to_dev_bf16(dy))
+    torch.cuda.synchronize()
+    return y.detach(), xt.grad, wt.grad
+
+
+def test_linear_fprop_dgrad_wgrad_match_oracle():
+    x, w, dy = _inputs(30)
+    log("linear M=%d K=%d N=%d" % (M, K, N))
+    y, dx, dw = _run(x, w, dy)
+    y_ref, dx_ref, dw_ref = _refs(x, w, dy)
+    gemm_tolerance_check(to_host(y), y_ref, K, label="fprop")
+    gemm_tolerance_check(to_host(dx), dx_ref, N, label="dgrad")
+    gemm_tolerance_check(to_host(dw), dw_ref, M, label="wgrad")
+
+
+def test_linear_close_to_fp32_pytorch():
+    torch = need_gpu()
+    x, w, dy = _inputs(31)
+    y, dx, dw = _run(x, w, dy)
+    xf = torch.from_numpy(bf16_to_f64(x))
+    wf = torch.from_numpy(bf16_to_f64(w))
+    dyf = torch.from_numpy(bf16_to_f64(dy))
+    for got, want, name in ((y, xf @ wf.T, "y"), (dx, dyf @ wf, "dx"), (dw, dyf.T @ xf, "dw")):
+        g = torch.from_numpy(bf16_to_f64(to_host(got)))
+        rel = (torch.linalg.norm(g - want) / torch.linalg.norm(want)).item()
+        log("%s relative error vs fp32: %.4f" % (name, rel))
+        assert rel < 0.08, (name, rel)   # MXFP8 (3 mantissa bits) on both operands
+
+
+def test_linear_fused_wgrad_accumulation():
+    torch = need_gpu()
+    x, w, dy = _inputs(32)
+    g0 = workloads.normal_bf16((N, K), 99, std=3.0)
+    main = to_dev_bf16(g0)
+    _, _, dw = _run(x, w, dy, fuse=True, main_grad=main)
+    assert dw is None
+    _, _, dw_ref = _refs(x, w, dy)
+    got1 = to_host(main).copy()
+    gemm_tolerance_check(got1, dw_ref + bf16_to_f64(g0), M, label="accumulate 1")
+    dy2 = workloads.normal_bf16((M, N), 77)
+    _run(x, w, dy2, fuse=True, main_grad=main)
+    _, _, dw2_ref = _refs(x, w, dy2)
+    # the second step adds to the BF16 result of the first
+    gemm_tolerance_check(to_host(main), dw2_ref + bf16_to_f64(got1), M, label="accumulate 2")

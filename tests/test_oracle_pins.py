@@ -459,3 +459,26 @@ def test_grouped_gemm_ragged_with_empty_groups():
     part = workloads.offsets_from_counts([32, 32, 0, 32])     # rows 96.. in no group
     out2 = oracle.grouped_gemm_tn(xq, xs, qw, sw, part)
     assert np.all(np.isnan(out2[96:])) and not np.any(np.isnan(out2[:96]))
+
+
+# ------------------------------------------------------------------ amax
+
+def test_amax_matches_torch_and_special_cases():
+    """Per-tensor amax against torch's own BF16 reduction (an independent
+    implementation), plus cases whose answer is known by construction."""
+    import torch
+    rng = np.random.default_rng(41)
+    for shape in ((64, 96), (3, 32), (257, 64)):
+        bits = workloads.wide_range_bf16(shape, int(rng.integers(1 << 30)), n_maxbf16=0, n_subnormal=16,
+                                         n_subnormal_blocks=1)
+        t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+        assert oracle.amax(bits) == float(t.abs().max().float())
+    z = np.zeros((32, 64), dtype=np.uint16)
+    assert oracle.amax(z) == 0.0
+    z[31, 63] = 0xC2F6                 # -123.0 in the last element: the sign is dropped
+    assert oracle.amax(z) == 123.0
+    z[0, 0] = workloads.BF16_MAX_BITS  # largest finite BF16
+    assert oracle.amax(z) == float(np.float32(3.3895313892515355e38))
+    assert oracle.amax(np.zeros((0, 32), dtype=np.uint16)) == 0.0
+    sub = np.full((32, 32), 0x8001, dtype=np.uint16)   # -2^-133 everywhere
+    assert oracle.amax(sub) == 2.0 ** -133
