@@ -342,15 +342,22 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
   if (ACC) {
     // Accumulate: stage the current C tile in the LDS tile (same layout and
     // thread mapping as the stores below; rows / columns outside C read as 0).
+    // All 32 loads of a thread are issued before the first LDS write, so the
+    // tile costs one memory latency.
     const int ch = elane & 31;
     const int64_t col = n0 + 8 * ch;
-#pragma unroll 8
+    u32x4 v[32];
+#pragma unroll
     for (int k = 0; k < 32; k++) {
       const int row = 2 * wave + (elane >> 5) + 8 * k;
       const int64_t grow = m_lo + row;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (col < N && grow < m_hi) v = *reinterpret_cast<const u32x4*>(Cm + grow * ldc + col);
-      *(__attribute__((address_space(3))) u32x4*)(smem + row * C_LDS_STRIDE + 16 * ch) = v;
+      v[k] = u32x4{0u, 0u, 0u, 0u};
+      if (col < N && grow < m_hi) v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Cm + grow * ldc + col));
+    }
+#pragma unroll
+    for (int k = 0; k < 32; k++) {
+      const int row = 2 * wave + (elane >> 5) + 8 * k;
+      *(__attribute__((address_space(3))) u32x4*)(smem + row * C_LDS_STRIDE + 16 * ch) = v[k];
     }
     wait_lgkm0();
     lds_barrier();
