@@ -29,7 +29,8 @@
 // 128-byte LDS row are XOR-swizzled by (row >> 1) & 7, which makes the
 // fragment reads conflict free.  Workgroup ids are remapped so the tiles
 // resident on one XCD (ids are dealt round-robin to the 8 XCDs) form groups of
-// 4 row tiles sharing A and B in that XCD's L2.
+// 4 tiles sharing A and B in that XCD's L2, with the XCDs splitting the larger
+// of M and N.
 #include "mx_device.h"
 #include "launch.h"
 
@@ -52,7 +53,7 @@ constexpr int SA_OFF = A_BYTES + B_BYTES;
 constexpr int SB_OFF = SA_OFF + BM * 4;
 constexpr int SLOT_BYTES = SB_OFF + BN * 4;          // 34 KB
 constexpr int LDS_BYTES = NSLOT * SLOT_BYTES;        // 136 KB
-constexpr int GROUP_M = 4;              // row tiles per L2 group
+constexpr int GROUP = 4;                // tiles per L2 group
 constexpr int C_LDS_STRIDE = 2 * BN + 16;            // BF16 output tile row in LDS, padded (528 B)
 static_assert(BM * C_LDS_STRIDE <= LDS_BYTES, "output tile must fit in the ring");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS");
@@ -92,18 +93,34 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA targets stay scalar
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- tile selection: XCD-aware remap, then groups of GROUP_M row tiles
+  // ---- tile selection: XCD-aware remap (each XCD gets a contiguous range of
+  // ids), then groups of GROUP tiles along one dimension walked across the
+  // other.  Each XCD streams its own share of one operand and all of the
+  // other, so the shares are taken along the larger dimension: N when
+  // tiles_n > tiles_m and for the grouped GEMM (every expert's B is read once
+  // instead of once per XCD), M otherwise.
   const int64_t nblk = tiles_m * tiles_n;
   const int64_t bid = blockIdx.x;
   const int64_t full = (nblk / 8) * 8;
   const int64_t lid = bid < full ? (bid & 7) * (full >> 3) + (bid >> 3) : bid;
-  const int64_t per_group = (int64_t)GROUP_M * tiles_n;
-  const int64_t grp = lid / per_group;
-  const int64_t first_m = grp * GROUP_M;
-  const int64_t gm = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
-  const int64_t rem = lid - grp * per_group;
-  int64_t tm = first_m + rem % gm;
-  const int64_t tn = rem / gm;
+  int64_t tm, tn;
+  if (!(GROUPED || tiles_n > tiles_m)) {
+    const int64_t per_group = (int64_t)GROUP * tiles_n;
+    const int64_t grp = lid / per_group;
+    const int64_t first_m = grp * GROUP;
+    const int64_t gm = (tiles_m - first_m) < GROUP ? (tiles_m - first_m) : GROUP;
+    const int64_t rem = lid - grp * per_group;
+    tm = first_m + rem % gm;
+    tn = rem / gm;
+  } else {
+    const int64_t per_group = (int64_t)GROUP * tiles_m;
+    const int64_t grp = lid / per_group;
+    const int64_t first_n = grp * GROUP;
+    const int64_t gn = (tiles_n - first_n) < GROUP ? (tiles_n - first_n) : GROUP;
+    const int64_t rem = lid - grp * per_group;
+    tn = first_n + rem % gn;
+    tm = rem / gn;
+  }
 
   int64_t m_lo, m_hi, b_row0 = 0;
   if (GROUPED) {
