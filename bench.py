@@ -2,9 +2,11 @@
 
 Default workload (the one whose JSON line is the benchmark): the dense linear
 layer.  One step = rowwise MXFP8 quantize of X BF16[8192x4096] ~ N(0,1),
-W BF16[14336x4096] ~ N(0,0.02) and the square A, B BF16[8192x8192], scale
-packing of all four, then the TN GEMMs 8192x14336x4096 and 8192x8192x8192
-with BF16 output.  Inputs are resident in HBM before timing starts.
+W BF16[14336x4096] ~ N(0,0.02) and the square A, B BF16[8192x8192], the
+quantizer writing the scales directly in the GEMM's packed word layout, then
+the TN GEMMs 8192x14336x4096 and 8192x8192x8192 with BF16 output.  Inputs are
+resident in HBM before timing starts.  (The backward, MoE and stress workloads
+keep byte scales plus the separate packing launch.)
 
 ``value`` is the end-to-end GEMM throughput of the step (GEMM FLOPs / wall
 time of the whole step, quantize and packing included).  ``roofline`` is the
@@ -103,7 +105,9 @@ def build_ops(workload, dev):
 
     ops, keep = [], []
 
-    def quantize_op(label, bits, flags):
+    def quantize_op(label, bits, flags, packed=False):
+        """Quantize launch (+ one packing launch per copy, unless the quantizer
+        writes the packed scale words itself)."""
         R, C = bits.shape
         b = {"x": upload(bits)}
         if flags & mx.MXFP8_ROWWISE:
@@ -120,9 +124,15 @@ def build_ops(workload, dev):
         b["ws"] = torch.empty((max(nws, 16),), dtype=torch.uint8, device=dev) if nws else None
         keep.append(b)
         copies = int(bool(flags & mx.MXFP8_ROWWISE)) + int(bool(flags & mx.MXFP8_COLWISE))
+        work = quant_bytes(R, C, copies, bool(flags & mx.MXFP8_DBIAS))
+        if packed:
+            ops.append(Op("quantize", label + " packed", lambda st: mx.mxfp8_quantize_ex(
+                b["x"], R, C, C, flags | mx.MXFP8_PACKED_SCALES, b.get("q"), b.get("p"), b.get("qT"), b.get("pT"),
+                b.get("db"), None, None, b["ws"], nws, stream=st), work))
+            return b
         ops.append(Op("quantize", label, lambda st: mx.mxfp8_quantize(
             b["x"], R, C, C, flags, b.get("q"), b.get("s"), b.get("qT"), b.get("sT"), b.get("db"),
-            b["ws"], nws, stream=st), quant_bytes(R, C, copies, bool(flags & mx.MXFP8_DBIAS))))
+            b["ws"], nws, stream=st), work))
         # packing reads the byte scales and writes the same bytes as words
         if flags & mx.MXFP8_ROWWISE:
             ops.append(Op("pack", label + " row", lambda st: mx.mxfp8_pack_scales(
@@ -146,14 +156,15 @@ def build_ops(workload, dev):
     if workload == "dense":
         lin, sq = workloads.dense_linear(), workloads.dense_square()
         host = {"X": lin["X"], "W": lin["W"], "A": sq["A"], "B": sq["B"]}
-        bx = quantize_op("X[8192x4096]", lin["X"], ROW)
-        bw = quantize_op("W[14336x4096]", lin["W"], ROW)
-        ba = quantize_op("A[8192x8192]", sq["A"], ROW)
-        bb = quantize_op("B[8192x8192]", sq["B"], ROW)
+        bx = quantize_op("X[8192x4096]", lin["X"], ROW, packed=True)
+        bw = quantize_op("W[14336x4096]", lin["W"], ROW, packed=True)
+        ba = quantize_op("A[8192x8192]", sq["A"], ROW, packed=True)
+        bb = quantize_op("B[8192x8192]", sq["B"], ROW, packed=True)
         dominant = gemm_op(bx["q"], bx["p"], bw["q"], bw["p"], 8192, 14336, 4096)
         gemm_op(ba["q"], ba["p"], bb["q"], bb["p"], 8192, 8192, 8192)
         desc = ("dense linear layer: rowwise MXFP8 quantize of X[8192x4096], W[14336x4096], A[8192x8192], "
-                "B[8192x8192] + scale packing + TN GEMMs 8192x14336x4096 and 8192x8192x8192, BF16 out")
+                "B[8192x8192] writing the packed scale words + TN GEMMs 8192x14336x4096 and 8192x8192x8192, "
+                "BF16 out")
     elif workload == "backward":
         d = workloads.backward()
         bd = quantize_op("dY[16384x4096] row+col+dbias", d["dY"], ROW | COL | DB)
@@ -173,10 +184,10 @@ def build_ops(workload, dev):
         T, K = lin["X"].shape
         N = lin["W"].shape[0]
         dy = workloads.normal_bf16((T, N), 4)
-        bx = quantize_op("X[%dx%d] row+col" % (T, K), lin["X"], ROW | COL)
-        bw = quantize_op("W[%dx%d] row+col" % (N, K), lin["W"], ROW | COL)
+        bx = quantize_op("X[%dx%d] row+col" % (T, K), lin["X"], ROW | COL, packed=True)
+        bw = quantize_op("W[%dx%d] row+col" % (N, K), lin["W"], ROW | COL, packed=True)
         dominant = gemm_op(bx["q"], bx["p"], bw["q"], bw["p"], T, N, K, name="fprop ")
-        bd = quantize_op("dY[%dx%d] row+col" % (T, N), dy, ROW | COL)
+        bd = quantize_op("dY[%dx%d] row+col" % (T, N), dy, ROW | COL, packed=True)
         gemm_op(bd["q"], bd["p"], bw["qT"], bw["pT"], T, K, N, name="dgrad ")
         gemm_op(bd["qT"], bd["pT"], bx["qT"], bx["pT"], N, K, T, accumulate=True, name="wgrad+= ")
         desc = ("MXFP8 linear layer training step: X[%d x %d] N(0,1), W[%d x %d] N(0,0.02), dY N(0,1); "

@@ -318,6 +318,68 @@ __global__ __launch_bounds__(FL_THREADS) void quantize_rowwise_flat_kernel(const
   if (opt.amax) fold_amax(opt, lane_amax);
 }
 
+// Rowwise copy with scales in the packed word layout (C % 128 == 0): a
+// workgroup owns a panel of 8 rows x 512 columns; wave w holds rows 2w, 2w+1
+// and lane l columns 8l + [0, 8) of each, so every load instruction still
+// reads 1 KB contiguous and each DPP quad holds one block.  The panel's 8 x 4
+// packed words (slab = 128 columns) are gathered in LDS and written as four
+// 32-byte runs; panels are ordered rows-fastest inside an XCD's id range, so
+// the four panels that fill one 128-byte line of a slab run back to back on
+// one XCD.
+constexpr int PN_ROWS = 8;
+constexpr int PN_COLS = 512;
+
+__global__ __launch_bounds__(256) void quantize_rowwise_packed_kernel(const uint16_t* __restrict__ x, int64_t R,
+                                                                      int64_t C, int64_t ldx,
+                                                                      uint8_t* __restrict__ q,
+                                                                      uint32_t* __restrict__ packed, QuantOpts opt) {
+  if (skip_call(opt)) return;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_s[PN_ROWS * 4 * 4];   // [row][slab][block]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int64_t n_rb = (R + PN_ROWS - 1) / PN_ROWS;
+  const int64_t nwg = gridDim.x;
+  const int64_t bid = blockIdx.x;
+  const int64_t full = (nwg / 8) * 8;
+  const int64_t lid = bid < full ? (bid & 7) * (full >> 3) + (bid >> 3) : bid;
+  const int64_t cbk = lid / n_rb;
+  const int64_t r0 = (lid - cbk * n_rb) * PN_ROWS;
+  const int64_t c0 = cbk * PN_COLS;
+  const int64_t col = c0 + 8 * lane;
+  const bool cval = col < C;            // C % 128 == 0: whole quads (and slabs) are valid
+  uint4 v[2];
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const int64_t r = r0 + 2 * w + u;
+    v[u] = (cval && r < R) ? *reinterpret_cast<const uint4*>(x + r * ldx + col) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  uint32_t lane_amax = 0;
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const int64_t r = r0 + 2 * w + u;
+    uint32_t m = pk_max_u16(pk_max_u16(abs_bits2(v[u].x), abs_bits2(v[u].y)),
+                            pk_max_u16(abs_bits2(v[u].z), abs_bits2(v[u].w)));
+    m = max(m & 0xFFFFu, m >> 16);
+    m = quad_max(m);
+    lane_amax = max(lane_amax, m);
+    const uint32_t byte = scale_byte_from_amax(m);
+    const uint2 o = quantize8(v[u], byte);
+    if (cval && r < R) store_nt8(q + r * C + col, o);
+    // lane 16k + 4b holds block b of slab k
+    if ((lane & 3) == 0) lds_s[((2 * w + u) * 4 + (lane >> 4)) * 4 + ((lane >> 2) & 3)] = (uint8_t)byte;
+  }
+  if (opt.amax) fold_amax(opt, lane_amax);
+  __syncthreads();
+  if (tid < PN_ROWS * 4) {
+    const int slab = tid >> 3, row = tid & 7;
+    const int64_t t = (c0 >> 7) + slab;
+    const int64_t r = r0 + row;
+    if (t < (C >> 7) && r < R)
+      packed[t * R + r] = *reinterpret_cast<const uint32_t*>(lds_s + (row * 4 + slab) * 4);
+  }
+}
+
 // dbias[c] = sum over row tiles of the partial sums.  A workgroup owns 32
 // columns; its 8 thread groups sum the row tiles g, g + 8, g + 16, ... of a
 // column and the 8 sums are combined pairwise (a fixed order: the result is
@@ -394,6 +456,13 @@ hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
   }
   uint8_t* srow = static_cast<uint8_t*>(s_row);
   uint8_t* scol = static_cast<uint8_t*>(s_colT);
+  if (row && !col && !db && packed) {
+    const int64_t blocks = ((R + PN_ROWS - 1) / PN_ROWS) * ((C + PN_COLS - 1) / PN_COLS);
+    if (blocks > 0)
+      hipLaunchKernelGGL(quantize_rowwise_packed_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, R, C, ldx,
+                         q_row, static_cast<uint32_t*>(s_row), opt);
+    return hipGetLastError();
+  }
   if (row && !col && !db && !packed && ldx == C) {
     const int64_t total = R * C;
     const int64_t per_block = FL_ELEMS * (FL_THREADS / 64);
