@@ -5,8 +5,8 @@ layer.  One step = rowwise MXFP8 quantize of X BF16[8192x4096] ~ N(0,1),
 W BF16[14336x4096] ~ N(0,0.02) and the square A, B BF16[8192x8192], the
 quantizer writing the scales directly in the GEMM's packed word layout, then
 the TN GEMMs 8192x14336x4096 and 8192x8192x8192 with BF16 output.  Inputs are
-resident in HBM before timing starts.  (The backward, MoE and stress workloads
-keep byte scales plus the separate packing launch.)
+resident in HBM before timing starts.  (The backward and MoE workloads keep byte
+scales plus the separate packing launch.)
 
 ``value`` is the end-to-end GEMM throughput of the step (GEMM FLOPs / wall
 time of the whole step, quantize and packing included).  ``roofline`` is the
@@ -174,8 +174,8 @@ def build_ops(workload, dev):
                 "fused dbias; X[16384x4096] columnwise; wgrad TN GEMM 4096x4096x16384 on the transposed copies")
     elif workload == "stress":
         d = workloads.stress()
-        ba = quantize_op("A[32768x8192] row+col", d["A"], ROW | COL)
-        bb = quantize_op("B[8192x8192]", d["B"], ROW)
+        ba = quantize_op("A[32768x8192] row+col", d["A"], ROW | COL, packed=True)
+        bb = quantize_op("B[8192x8192]", d["B"], ROW, packed=True)
         dominant = gemm_op(ba["q"], ba["p"], bb["q"], bb["p"], 32768, 8192, 8192)
         desc = ("wide-range stress: A[32768x8192] (2^u block scales, max BF16, subnormals) rowwise+columnwise, "
                 "B[8192x8192] rowwise, TN GEMM 32768x8192x8192")
@@ -235,17 +235,31 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        for op in ops:
+    # In the timed steps each GEMM launch is bracketed by HIP events on its
+    # stream, and each run of consecutive quantize / packing launches by one
+    # pair (per-launch markers between the short launches would add ~3 % of
+    # idle time to the step).  Per-launch times of those short kernels come
+    # from a separate pass after the timed region.
+    groups = []
+    for op in ops:
+        if op.kind == "gemm" or not groups or groups[-1][0].kind == "gemm":
+            groups.append([op])
+        else:
+            groups[-1].append(op)
+
+    def step(ev=None, per_launch=False):
+        for grp in (groups if not per_launch else [[op] for op in ops]):
             if ev is None:
-                op.fn(stream)
+                for op in grp:
+                    op.fn(stream)
                 continue
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            op.fn(stream)
+            for op in grp:
+                op.fn(stream)
             e1.record(stream)
-            ev.append((op, e0, e1))
+            ev.append((tuple(grp), e0, e1))
 
     for _ in range(args.warmup):
         step()
@@ -266,14 +280,34 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    dur = {}
-    for op, e0, e1 in events:
-        dur.setdefault(id(op), []).append(e0.elapsed_time(e1))
-    avg = {k: float(np.mean(v)) for k, v in dur.items()}
+    detail = []
+    for _ in range(min(args.steps, 10)):
+        step(detail, per_launch=True)
+    torch.cuda.synchronize()
+
+    def mean_ms(evs):
+        dur = {}
+        for grp, e0, e1 in evs:
+            dur.setdefault(tuple(id(op) for op in grp), []).append(e0.elapsed_time(e1))
+        return {k: float(np.mean(v)) for k, v in dur.items()}
+
+    timed = mean_ms(events)
+    avg = {k[0]: v for k, v in mean_ms(detail).items()}
+    for k, v in timed.items():       # GEMMs: the timed-region numbers
+        if len(k) == 1:
+            avg[k[0]] = v
+    short_block = [(k, v) for k, v in timed.items() if len(k) > 1 or
+                   [op for op in ops if id(op) == k[0]][0].kind != "gemm"]
 
     total_flops = sum(op.work for op in ops if op.kind == "gemm")
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
+    by_id = {id(op): op for op in ops}
+    block_report = []
+    for k, t in short_block:
+        work = sum(by_id[i].work for i in k)
+        block_report.append({"launches": [by_id[i].kind + " " + by_id[i].label for i in k], "ms": round(t, 4),
+                             "gbs": round(work / (t * 1e-3) / 1e9, 1)})
     gemm_report, quant_report, pack_report = {}, {}, {}
     for op in ops:
         t = avg[id(op)]
@@ -315,6 +349,9 @@ def main():
         "gemm": gemm_report,
         "quantize": quant_report,
         "pack": pack_report,
+        "short_launch_blocks": block_report,
+        "timing_note": "gemm: HIP events per launch in the timed steps; quantize / pack: per-launch events in a "
+                       "separate pass after them; short_launch_blocks: the same launches as timed in the steps",
     }
     if host is not None and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(host, args.cpu_seconds)
