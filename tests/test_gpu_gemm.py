@@ -343,3 +343,26 @@ def test_full_moe_sampled():
     ref = oracle.grouped_gemm_tn(oqx, osx, np.stack([q for q, _ in ws]), np.stack([s for _, s in ws]), off,
                                  rows=rows, cols=cols)
     gemm_tolerance_check(ch, ref, K, label="moe")
+
+
+@pytest.mark.slow
+def test_full_linear_wgrad_accumulate_sampled():
+    """The linear step's wgrad with accumulation at its full size
+    (14336 x 4096, K = 8192 tokens) on the transposed copies."""
+    torch = need_gpu()
+    lin = workloads.dense_linear()
+    x = lin["X"]                                        # [8192][4096]
+    dy = workloads.normal_bf16((8192, 14336), 4)        # [8192][14336]
+    qa, sa, pa = quantize_on_gpu(dy, colwise=True)      # [14336][8192]
+    qb, sb, pb = quantize_on_gpu(x, colwise=True)       # [4096][8192]
+    c_old = workloads.normal_bf16((14336, 4096), 13, std=8.0)
+    cd = to_dev_bf16(c_old)
+    log("wgrad accumulate 14336x4096x8192")
+    mx.gemm(qa, pa, qb, pb, out=cd, accumulate=True)
+    torch.cuda.synchronize()
+    rows = sample_indices(14336, 40, 11)
+    cols = sample_indices(4096, 40, 12)
+    oqa, osa = oracle.quantize_colwise(dy)
+    oqb, osb = oracle.quantize_colwise(x)
+    ref = oracle.gemm_tn(oqa, osa, oqb, osb, rows=rows, cols=cols) + bf16_to_f64(c_old[np.ix_(rows, cols)])
+    gemm_tolerance_check(to_host(cd)[np.ix_(rows, cols)], ref, 8192, label="wgrad accumulate")

@@ -132,3 +132,30 @@ def test_noop_flag_writes_nothing(flags):
     assert float(run["amax"][0]) == oracle.amax(bits)
     if flags & DB:
         assert np.allclose(run["dbias"], oracle.dbias(bits), rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["X", "W"])
+def test_full_dense_packed_rowwise(name):
+    """The default benchmark's quantize launches at full size: codes and packed
+    scale words bit-exact, amax exact."""
+    bits = workloads.dense_linear()[name]
+    log("packed full %s %s" % (name, bits.shape))
+    got = run_ex(bits, ROW | PACKED | AMAX)
+    q, s = oracle.quantize_rowwise(bits)
+    assert np.array_equal(got["q_row"], q)
+    assert np.array_equal(got["s_row"], oracle.pack_scales(s))
+    assert float(got["amax"][0]) == oracle.amax(bits)
+
+
+@pytest.mark.slow
+def test_full_stress_row_col_packed():
+    """The stress step's row+col launch with packed scales (32768 x 8192, wide range)."""
+    bits = workloads.stress()["A"]
+    got = run_ex(bits, ROW | COL | PACKED)
+    q, s = oracle.quantize_rowwise(bits)
+    assert np.array_equal(got["q_row"], q)
+    assert np.array_equal(got["s_row"], oracle.pack_scales(s))
+    qT, sT = oracle.quantize_colwise(bits)
+    assert np.array_equal(got["q_colT"], qT)
+    assert np.array_equal(got["s_colT"], oracle.pack_scales(sT))
