@@ -75,11 +75,14 @@ def _load():
     lib.oracle_scale_byte.argtypes = [ctypes.c_double]
     lib.oracle_bf16_to_double.restype = ctypes.c_double
     lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
-    for name in ("oracle_quantize_rows", "oracle_quantize_cols"):
+    for name in ("oracle_quantize_rows", "oracle_quantize_cols", "oracle_quantize_rows_f32",
+                 "oracle_quantize_cols_f32"):
         getattr(lib, name).restype = None
         getattr(lib, name).argtypes = [P, I64, I64, I64, P, P]
     lib.oracle_dbias.restype = None
     lib.oracle_dbias.argtypes = [P, I64, I64, I64, P]
+    lib.oracle_dbias_f32.restype = None
+    lib.oracle_dbias_f32.argtypes = [P, I64, I64, I64, P]
     lib.oracle_dequantize.restype = None
     lib.oracle_dequantize.argtypes = [P, P, I64, I64, P]
     lib.oracle_e4m3_encode_array.restype = None
@@ -175,6 +178,72 @@ def dbias(x_bits: np.ndarray) -> np.ndarray:
     R, C = x.shape
     out = np.empty(C, dtype=np.float32)
     _load().oracle_dbias(_ptr(x), R, C, C, _ptr(out))
+    return out
+
+
+# ------------------------------------------------ activation-fused quantize
+#
+# The quantization config of "[Common] Experimental CuTeDSL MXFP8 backends in
+# C++ via TVM-FFI" (review of the config key) has with_act / with_dact
+# options; the activation this library implements is the squared ReLU that
+# "gemm(cutedsl): add standalone Lightning W4A16 grouped GEMM" names as the
+# FC1 epilogue (relu(x)^2).  Its value and its derivative 2 relu(a) are
+# computed in fp32 exactly as a kernel does (numpy float32 arithmetic, round
+# to nearest even: both products of two BF16 values are exact unless they
+# leave the fp32 normal range), then quantized exactly.
+
+def act_sqrelu(x_bits: np.ndarray) -> np.ndarray:
+    """relu(x)^2 of BF16 x, in fp32."""
+    x = bf16_value(_check_bf16(x_bits)).astype(np.float32)
+    r = np.maximum(x, np.float32(0.0))
+    return (r * r).astype(np.float32)
+
+
+def dact_sqrelu(grad_bits: np.ndarray, act_bits: np.ndarray) -> np.ndarray:
+    """grad * d/da relu(a)^2 = grad * (2 relu(a)), in fp32."""
+    g = bf16_value(_check_bf16(grad_bits)).astype(np.float32)
+    a = bf16_value(_check_bf16(act_bits)).astype(np.float32)
+    two_r = np.float32(2.0) * np.maximum(a, np.float32(0.0))
+    return (g * two_r).astype(np.float32)
+
+
+def _check_f32(v: np.ndarray) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    if v.ndim != 2 or v.shape[1] % MX_BLOCK:
+        raise ValueError("expected [R][C] with C a multiple of 32")
+    if not np.all(np.isfinite(v)):
+        raise ValueError("values must be finite")
+    return v
+
+
+def quantize_rowwise_values(v: np.ndarray):
+    """Rowwise MXFP8 copy of fp32 values: (codes uint8[R][C], scales uint8[R][C/32])."""
+    v = _check_f32(v)
+    R, C = v.shape
+    q = np.empty((R, C), dtype=np.uint8)
+    s = np.empty((R, C // MX_BLOCK), dtype=np.uint8)
+    _load().oracle_quantize_rows_f32(_ptr(v), R, C, C, _ptr(q), _ptr(s))
+    return q, s
+
+
+def quantize_colwise_values(v: np.ndarray):
+    """Columnwise MXFP8 copy of fp32 values, stored transposed."""
+    v = _check_f32(v)
+    R, C = v.shape
+    if R % MX_BLOCK:
+        raise ValueError("rows must be a multiple of 32 for the columnwise copy")
+    qT = np.empty((C, R), dtype=np.uint8)
+    sT = np.empty((C, R // MX_BLOCK), dtype=np.uint8)
+    _load().oracle_quantize_cols_f32(_ptr(v), R, C, C, _ptr(qT), _ptr(sT))
+    return qT, sT
+
+
+def dbias_values(v: np.ndarray) -> np.ndarray:
+    """Column sums of fp32 values (double accumulation, rounded once)."""
+    v = _check_f32(v)
+    R, C = v.shape
+    out = np.empty(C, dtype=np.float32)
+    _load().oracle_dbias_f32(_ptr(v), R, C, C, _ptr(out))
     return out
 
 

@@ -174,6 +174,56 @@ void oracle_quantize_cols(const uint16_t *x, int64_t R, int64_t C, int64_t ld_x,
     }
 }
 
+/* The same two copies for fp32 values v[R][ld] (an activation's output,
+ * computed in fp32 by the caller). */
+void oracle_quantize_rows_f32(const float *x, int64_t R, int64_t C, int64_t ld,
+                              uint8_t *q, uint8_t *s)
+{
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < R; r++) {
+        double v[MX_BLOCK];
+        int64_t b;
+        int i;
+        for (b = 0; b < C / MX_BLOCK; b++) {
+            for (i = 0; i < MX_BLOCK; i++)
+                v[i] = (double)x[r * ld + b * MX_BLOCK + i];
+            quantize_block(v, MX_BLOCK, q + r * C + b * MX_BLOCK, s + r * (C / MX_BLOCK) + b);
+        }
+    }
+}
+
+void oracle_quantize_cols_f32(const float *x, int64_t R, int64_t C, int64_t ld,
+                              uint8_t *qT, uint8_t *sT)
+{
+    int64_t c;
+#pragma omp parallel for schedule(static)
+    for (c = 0; c < C; c++) {
+        double v[MX_BLOCK];
+        int64_t b;
+        int i;
+        for (b = 0; b < R / MX_BLOCK; b++) {
+            for (i = 0; i < MX_BLOCK; i++)
+                v[i] = (double)x[(b * MX_BLOCK + i) * ld + c];
+            quantize_block(v, MX_BLOCK, qT + c * R + b * MX_BLOCK, sT + c * (R / MX_BLOCK) + b);
+        }
+    }
+}
+
+/* Column sums of fp32 values, accumulated in double, rounded once. */
+void oracle_dbias_f32(const float *x, int64_t R, int64_t C, int64_t ld, float *dbias)
+{
+    int64_t c;
+#pragma omp parallel for schedule(static)
+    for (c = 0; c < C; c++) {
+        double acc = 0.0;
+        int64_t r;
+        for (r = 0; r < R; r++)
+            acc += (double)x[r * ld + c];
+        dbias[c] = (float)acc;
+    }
+}
+
 /* dbias[c] = sum over rows of x[r][c], accumulated in double, rounded once to
  * float. */
 void oracle_dbias(const uint16_t *x, int64_t R, int64_t C, int64_t ld_x, float *dbias)

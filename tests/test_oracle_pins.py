@@ -482,3 +482,54 @@ def test_amax_matches_torch_and_special_cases():
     assert oracle.amax(np.zeros((0, 32), dtype=np.uint16)) == 0.0
     sub = np.full((32, 32), 0x8001, dtype=np.uint16)   # -2^-133 everywhere
     assert oracle.amax(sub) == 2.0 ** -133
+
+
+# ------------------------------------------------ activation-fused quantize
+
+def test_sqrelu_and_its_derivative_match_torch_float32():
+    """The activation values against torch's own float32 arithmetic."""
+    import torch
+    x = workloads.wide_range_bf16((64, 96), 51, u_lo=-20, u_hi=20, n_maxbf16=0, n_subnormal=32,
+                                  n_subnormal_blocks=1)
+    g = workloads.normal_bf16((64, 96), 52)
+    tx = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).float()
+    tg = torch.from_numpy(g.view(np.int16)).view(torch.bfloat16).float()
+    assert np.array_equal(oracle.act_sqrelu(x), (torch.relu(tx) ** 2).numpy())
+    assert np.array_equal(oracle.dact_sqrelu(g, x), (tg * (2.0 * torch.relu(tx))).numpy())
+    assert oracle.act_sqrelu(np.array([[0xBF80] * 32], dtype=np.uint16)).max() == 0.0   # -1 -> 0
+
+
+def test_value_quantizer_by_brute_force():
+    """fp32 blocks (not BF16-representable: 24-bit mantissas, wide exponents)
+    against the exact-rational reference of the block rule."""
+    rng = np.random.default_rng(53)
+    v = (rng.standard_normal((200, 32)) * np.exp2(rng.integers(-30, 30, size=(200, 1)))).astype(np.float32)
+    v[5, :] = 0.0
+    v[6, 3] = np.float32(-0.0)
+    q, s = oracle.quantize_rowwise_values(v)
+    for i in range(v.shape[0]):
+        vals = [Fraction(float(t)) for t in v[i]]
+        amax = max(abs(t) for t in vals)
+        if amax == 0:
+            X = -127
+        else:
+            X = -200
+            while not (amax / Fraction(2) ** X < 512):
+                X += 1
+            X = max(X, -127)
+        assert s[i, 0] == (X + 127 if amax != 0 else 0)
+        for j, t in enumerate(vals):
+            assert q[i, j] == brute_force_encode(t / Fraction(2) ** X, bool(np.signbit(v[i, j]))), (i, j)
+    # BF16-representable values give exactly the BF16 path's result
+    bits = workloads.normal_bf16((64, 64), 54)
+    assert all(np.array_equal(a, b) for a, b in zip(oracle.quantize_rowwise_values(oracle.bf16_value(bits)),
+                                                    oracle.quantize_rowwise(bits)))
+    qT, sT = oracle.quantize_colwise_values(v[:192])
+    qr, sr = oracle.quantize_rowwise_values(np.ascontiguousarray(v[:192].T))
+    assert np.array_equal(qT, qr) and np.array_equal(sT, sr)
+
+
+def test_dbias_values_rounded_once():
+    v = np.full((4096, 32), np.float32(1.0) + np.float32(2.0 ** -23), dtype=np.float32)
+    want = np.float32(4096 * (1.0 + 2.0 ** -23))
+    assert np.all(oracle.dbias_values(v) == want)
