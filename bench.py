@@ -128,7 +128,7 @@ def build_ops(workload, dev):
         if packed:
             ops.append(Op("quantize", label + " packed", lambda st: mx.mxfp8_quantize_ex(
                 b["x"], R, C, C, flags | mx.MXFP8_PACKED_SCALES, b.get("q"), b.get("p"), b.get("qT"), b.get("pT"),
-                b.get("db"), None, None, b["ws"], nws, stream=st), work))
+                b.get("db"), workspace=b["ws"], workspace_bytes=nws, stream=st), work))
             return b
         ops.append(Op("quantize", label, lambda st: mx.mxfp8_quantize(
             b["x"], R, C, C, flags, b.get("q"), b.get("s"), b.get("qT"), b.get("sT"), b.get("db"),

@@ -91,6 +91,15 @@ int mxfp8_last_hip_error(void);
 #define MXFP8_PACKED_SCALES 16u  /* s_row / s_colT in the packed word layout:
                                     s_row  uint32 [cols/128][rows] (cols % 128 == 0),
                                     s_colT uint32 [rows/128][cols] (rows % 128 == 0) */
+/* Activation fused into mxfp8_quantize_ex (the with_act / with_dact /
+ * activation keys of the quantization config, "[Common] Experimental CuTeDSL
+ * MXFP8 backends in C++ via TVM-FFI", config key listing; squared ReLU is the
+ * FC1 activation of "gemm(cutedsl): add standalone Lightning W4A16 grouped
+ * GEMM - #811", section "API and compatibility impact").  The value that is
+ * quantized (and summed by DBIAS, and measured by AMAX) is then fp32:       */
+#define MXFP8_ACT_SQRELU 32u     /* relu(x)^2                                  */
+#define MXFP8_DACT_SQRELU 64u    /* x * 2 relu(act_in): backward of relu(a)^2,
+                                    x = incoming gradient, act_in = a           */
 
 /* Bytes of workspace mxfp8_quantize needs for `flags` at this shape (0 when
  * DBIAS is not requested). */
@@ -132,23 +141,35 @@ mxfp8_status mxfp8_quantize(const void *x, int64_t rows, int64_t cols, int64_t l
  * Experimental CuTeDSL MXFP8 backends in C++ via TVM-FFI", review of the
  * config key, commit "Perform noop tensor check on device", Greptile summary
  * on the noop + dbias interaction).
- * flags   as mxfp8_quantize, plus MXFP8_AMAX and MXFP8_PACKED_SCALES.
+ * flags   as mxfp8_quantize, plus MXFP8_AMAX, MXFP8_PACKED_SCALES and at most
+ *         one of MXFP8_ACT_SQRELU / MXFP8_DACT_SQRELU.  With an activation the
+ *         quantized value v is the fp32 result of the activation (each product
+ *         of two BF16 values is exact in fp32); its block scale follows the
+ *         same rule (exponent of the block amax - 8), codes are RNE of
+ *         v / 2^(scale - 127) saturated to +-448.
  * s_row, s_colT  byte scales as in mxfp8_quantize, or (PACKED_SCALES) uint32
  *         words in the mxfp8_pack_scales layout, 4-byte aligned.
- * amax    AMAX: fp32 [1], 4-byte aligned: the largest |x| of the tensor (a
- *         BF16 value, exact; 0 for an empty tensor).  Else ignored.
+ * amax    AMAX: fp32 [1], 4-byte aligned: the largest |v| of the tensor (v = x,
+ *         or the activation's output; exact; 0 for an empty tensor).  Else
+ *         ignored.
  * noop    optional DEVICE int32 flag, 4-byte aligned.  When non-NULL and
  *         nonzero at the time the work executes, nothing is written (codes,
  *         scales, dbias and amax keep their old contents).  NULL: always run.
+ * act_in  DACT_SQRELU: BF16 [rows][ld_x], the forward activation's input, same
+ *         layout as x, 16-byte aligned.  Else ignored.
  * Errors: as mxfp8_quantize; SHAPE also for PACKED_SCALES with cols (rowwise)
  *         or rows (columnwise) not a multiple of 128; NULL for AMAX without
- *         amax.  mxfp8_quantize(...) rejects the extra flags (FLAGS).
+ *         amax or DACT_SQRELU without act_in; FLAGS for both activations at
+ *         once.  Activation results that overflow fp32 or fall below its
+ *         normal range are outside the contract.  mxfp8_quantize(...) rejects
+ *         the extra flags (FLAGS).
  */
 mxfp8_status mxfp8_quantize_ex(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
                                uint32_t flags,
                                uint8_t *q_row, void *s_row,
                                uint8_t *q_colT, void *s_colT,
                                float *dbias, float *amax, const int32_t *noop,
+                               const void *act_in,
                                void *workspace, size_t workspace_bytes,
                                void *stream);
 

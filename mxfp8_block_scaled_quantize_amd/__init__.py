@@ -24,6 +24,8 @@ MXFP8_COLWISE = 2
 MXFP8_DBIAS = 4
 MXFP8_AMAX = 8
 MXFP8_PACKED_SCALES = 16
+MXFP8_ACT_SQRELU = 32
+MXFP8_DACT_SQRELU = 64
 MXFP8_GEMM_ACCUMULATE = 1
 
 STATUS_NAMES = {0: "MXFP8_OK", 1: "MXFP8_ERR_NULL", 2: "MXFP8_ERR_SHAPE", 3: "MXFP8_ERR_MISALIGNED",
@@ -72,7 +74,7 @@ def lib() -> ctypes.CDLL:
     L.mxfp8_grouped_gemm.restype = ctypes.c_int
     L.mxfp8_grouped_gemm.argtypes = [P, P, P, P, P, I32, P, I64, I64, I64, I64, P]
     L.mxfp8_quantize_ex.restype = ctypes.c_int
-    L.mxfp8_quantize_ex.argtypes = [P, I64, I64, I64, U32, P, P, P, P, P, P, P, P, SZ, P]
+    L.mxfp8_quantize_ex.argtypes = [P, I64, I64, I64, U32, P, P, P, P, P, P, P, P, P, SZ, P]
     L.mxfp8_gemm_ex.restype = ctypes.c_int
     L.mxfp8_gemm_ex.argtypes = [P, P, P, P, P, I64, I64, I64, I64, U32, P]
     L.mxfp8_grouped_gemm_ex.restype = ctypes.c_int
@@ -127,10 +129,11 @@ def mxfp8_quantize(x, rows, cols, ld_x, flags, q_row=None, s_row=None, q_colT=No
 
 
 def mxfp8_quantize_ex(x, rows, cols, ld_x, flags, q_row=None, s_row=None, q_colT=None, s_colT=None,
-                      dbias=None, amax=None, noop=None, workspace=None, workspace_bytes=0, stream=None):
+                      dbias=None, amax=None, noop=None, act_in=None, workspace=None, workspace_bytes=0,
+                      stream=None):
     _check(lib().mxfp8_quantize_ex(_p(x), rows, cols, ld_x, flags, _p(q_row), _p(s_row), _p(q_colT),
-                                   _p(s_colT), _p(dbias), _p(amax), _p(noop), _p(workspace), workspace_bytes,
-                                   _s(stream)), "mxfp8_quantize_ex")
+                                   _p(s_colT), _p(dbias), _p(amax), _p(noop), _p(act_in), _p(workspace),
+                                   workspace_bytes, _s(stream)), "mxfp8_quantize_ex")
 
 
 def mxfp8_packed_scale_bytes(dim: int, k: int) -> int:
@@ -163,18 +166,30 @@ def mxfp8_grouped_gemm_ex(a, a_packed, b, b_packed, offsets, G, c, ldc, M_total,
 
 # ------------------------------------------------------ allocating helpers
 
-def quantize(x, rowwise=True, colwise=False, dbias=False, amax=False, packed=False, noop=None, stream=None):
+def quantize(x, rowwise=True, colwise=False, dbias=False, amax=False, packed=False, noop=None, act=None,
+             act_in=None, stream=None):
     """Quantize a BF16 [rows, cols] CUDA tensor; returns a dict of outputs.
 
     packed=True returns the scales in the packed word layout ("p_row" int32
     [cols/128, rows], "p_colT" int32 [rows/128, cols]) instead of bytes;
-    amax=True adds "amax" (fp32 [1]); noop is an optional device int32 flag."""
+    amax=True adds "amax" (fp32 [1]); noop is an optional device int32 flag.
+    act="sqrelu" quantizes relu(x)^2; act="dsqrelu" quantizes
+    x * 2 relu(act_in) (x is the gradient, act_in the activation's input, a
+    BF16 tensor of x's shape and strides)."""
     import torch
     assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
     R, C = x.shape
     dev = x.device
     flags = (MXFP8_ROWWISE if rowwise else 0) | (MXFP8_COLWISE if colwise else 0) | (MXFP8_DBIAS if dbias else 0)
     flags |= (MXFP8_AMAX if amax else 0) | (MXFP8_PACKED_SCALES if packed else 0)
+    if act == "sqrelu":
+        flags |= MXFP8_ACT_SQRELU
+    elif act == "dsqrelu":
+        assert act_in is not None and act_in.dtype == torch.bfloat16 and act_in.shape == x.shape
+        assert act_in.stride() == x.stride() and act_in.device == x.device
+        flags |= MXFP8_DACT_SQRELU
+    elif act is not None:
+        raise ValueError("act must be None, 'sqrelu' or 'dsqrelu'")
     out = {}
     if rowwise:
         out["q_row"] = torch.empty((R, C), dtype=torch.uint8, device=dev)
@@ -198,9 +213,9 @@ def quantize(x, rowwise=True, colwise=False, dbias=False, amax=False, packed=Fal
         ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
     s_row = out.get("p_row") if packed else out.get("s_row")
     s_col = out.get("p_colT") if packed else out.get("s_colT")
-    if amax or packed or noop is not None:
+    if amax or packed or noop is not None or act is not None:
         mxfp8_quantize_ex(x, R, C, x.stride(0), flags, out.get("q_row"), s_row, out.get("q_colT"), s_col,
-                          out.get("dbias"), out.get("amax"), noop, ws, nws, stream)
+                          out.get("dbias"), out.get("amax"), noop, act_in, ws, nws, stream)
     else:
         mxfp8_quantize(x, R, C, x.stride(0), flags, out.get("q_row"), s_row, out.get("q_colT"), s_col,
                        out.get("dbias"), ws, nws, stream)

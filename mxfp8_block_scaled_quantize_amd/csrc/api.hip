@@ -25,10 +25,12 @@ mxfp8_status hip_status(hipError_t e) {
 mxfp8_status check_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint32_t flags,
                             const uint8_t* q_row, const void* s_row, const uint8_t* q_colT,
                             const void* s_colT, const float* dbias, const float* amax, const int32_t* noop,
-                            const void* ws, size_t ws_bytes) {
-  if (flags & ~(MXFP8_ROWWISE | MXFP8_COLWISE | MXFP8_DBIAS | MXFP8_AMAX | MXFP8_PACKED_SCALES))
+                            const void* act_in, const void* ws, size_t ws_bytes) {
+  if (flags & ~(MXFP8_ROWWISE | MXFP8_COLWISE | MXFP8_DBIAS | MXFP8_AMAX | MXFP8_PACKED_SCALES |
+                MXFP8_ACT_SQRELU | MXFP8_DACT_SQRELU))
     return MXFP8_ERR_FLAGS;
   if (!(flags & (MXFP8_ROWWISE | MXFP8_COLWISE))) return MXFP8_ERR_FLAGS;
+  if ((flags & MXFP8_ACT_SQRELU) && (flags & MXFP8_DACT_SQRELU)) return MXFP8_ERR_FLAGS;
   if ((flags & MXFP8_AMAX) && !amax) return MXFP8_ERR_NULL;
   if ((flags & MXFP8_AMAX) && !aligned(amax, 4)) return MXFP8_ERR_MISALIGNED;
   if (noop && !aligned(noop, 4)) return MXFP8_ERR_MISALIGNED;
@@ -44,9 +46,11 @@ mxfp8_status check_quantize(const void* x, int64_t rows, int64_t cols, int64_t l
   if (any && !x) return MXFP8_ERR_NULL;
   if (any && (flags & MXFP8_ROWWISE) && (!q_row || !s_row)) return MXFP8_ERR_NULL;
   if (any && (flags & MXFP8_COLWISE) && (!q_colT || !s_colT)) return MXFP8_ERR_NULL;
+  if (any && (flags & MXFP8_DACT_SQRELU) && !act_in) return MXFP8_ERR_NULL;
   if ((flags & MXFP8_DBIAS) && cols > 0 && !dbias) return MXFP8_ERR_NULL;
   if (any) {
     if (!aligned(x, 16) || ld_x % 8) return MXFP8_ERR_MISALIGNED;
+    if ((flags & MXFP8_DACT_SQRELU) && !aligned(act_in, 16)) return MXFP8_ERR_MISALIGNED;
     if ((flags & MXFP8_ROWWISE) && !aligned(q_row, 16)) return MXFP8_ERR_MISALIGNED;
     if ((flags & MXFP8_COLWISE) && !aligned(q_colT, 16)) return MXFP8_ERR_MISALIGNED;
     if ((flags & MXFP8_PACKED_SCALES) && (flags & MXFP8_ROWWISE) && !aligned(s_row, 4)) return MXFP8_ERR_MISALIGNED;
@@ -105,16 +109,16 @@ size_t mxfp8_quantize_workspace_bytes(int64_t rows, int64_t cols, uint32_t flags
 
 mxfp8_status mxfp8_quantize_ex(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint32_t flags,
                                uint8_t* q_row, void* s_row, uint8_t* q_colT, void* s_colT, float* dbias,
-                               float* amax, const int32_t* noop, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+                               float* amax, const int32_t* noop, const void* act_in, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   const mxfp8_status st = check_quantize(x, rows, cols, ld_x, flags, q_row, s_row, q_colT, s_colT, dbias, amax,
-                                         noop, workspace, workspace_bytes);
+                                         noop, act_in, workspace, workspace_bytes);
   if (st != MXFP8_OK) return st;
   const bool empty = rows == 0 || cols == 0;
   if (empty && !(flags & MXFP8_AMAX) && !((flags & MXFP8_DBIAS) && cols > 0)) return MXFP8_OK;
   return hip_status(mx::launch_quantize(static_cast<const uint16_t*>(x), rows, cols, ld_x, flags, q_row, s_row,
                                         q_colT, s_colT, dbias, static_cast<float*>(workspace), amax, noop,
-                                        static_cast<hipStream_t>(stream)));
+                                        static_cast<const uint16_t*>(act_in), static_cast<hipStream_t>(stream)));
 }
 
 mxfp8_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint32_t flags,
@@ -122,7 +126,7 @@ mxfp8_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, int64_t l
                             void* workspace, size_t workspace_bytes, void* stream) {
   if (flags & ~(MXFP8_ROWWISE | MXFP8_COLWISE | MXFP8_DBIAS)) return MXFP8_ERR_FLAGS;
   return mxfp8_quantize_ex(x, rows, cols, ld_x, flags, q_row, s_row, q_colT, s_colT, dbias, nullptr, nullptr,
-                           workspace, workspace_bytes, stream);
+                           nullptr, workspace, workspace_bytes, stream);
 }
 
 size_t mxfp8_packed_scale_bytes(int64_t dim, int64_t k) {

@@ -10,12 +10,13 @@ namespace mx {
 int64_t quantize_row_tiles(int64_t R);
 int64_t quantize_col_tiles(int64_t C);
 
-// flags: rowwise 1, colwise 2, dbias 4, amax 8, packed scales 16.  noop may be
-// null (always run).
+// flags: rowwise 1, colwise 2, dbias 4, amax 8, packed scales 16, squared-ReLU
+// activation 32, its backward 64 (act_in: the activation's input, same shape
+// and leading dimension as x).  noop may be null (always run).
 hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint32_t flags,
                            uint8_t* q_row, void* s_row, uint8_t* q_colT, void* s_colT,
                            float* dbias, float* dbias_part, float* amax, const int32_t* noop,
-                           hipStream_t stream);
+                           const uint16_t* act_in, hipStream_t stream);
 
 hipError_t launch_pack_scales(const uint8_t* s, int64_t dim, int64_t k, int64_t ld_s, uint32_t* packed,
                               hipStream_t stream);

@@ -38,9 +38,9 @@ struct QuantOpts {
 
 __device__ __forceinline__ bool skip_call(const QuantOpts& o) { return o.noop != nullptr && *o.noop != 0; }
 
-// Fold a per-lane amax (15-bit BF16 magnitude pattern) into the tensor amax:
-// wave maximum, then one atomic per wave, skipped when the stored value is
-// already at least as large (max is order independent: the result is exact).
+// Fold a per-lane amax (fp32 bit pattern of |x|) into the tensor amax: wave
+// maximum, then one atomic per wave, skipped when the stored value is already
+// at least as large (max is order independent: the result is exact).
 __device__ __forceinline__ void fold_amax(const QuantOpts& o, uint32_t m) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
@@ -48,20 +48,50 @@ __device__ __forceinline__ void fold_amax(const QuantOpts& o, uint32_t m) {
     m = m > t ? m : t;
   }
   if ((threadIdx.x & 63) == 0) {
-    const uint32_t v = m << 16;   // |x| as fp32 bits
-    if (v > __hip_atomic_load(o.amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(o.amax, v);
+    if (m > __hip_atomic_load(o.amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(o.amax, m);
   }
+}
+
+// Activation fused into the quantizer: none, squared ReLU relu(x)^2, or its
+// backward grad * 2 relu(a).  Values are fp32 (both products of two BF16
+// values are exact in fp32 inside its normal range) and are quantized with the
+// fp32 form of the scaled convert.
+enum { ACT_NONE = 0, ACT_SQRELU = 1, DACT_SQRELU = 2 };
+
+__device__ __forceinline__ float bf_half(uint4 v, int k) {
+  const uint32_t d = (k >> 1) == 0 ? v.x : (k >> 1) == 1 ? v.y : (k >> 1) == 2 ? v.z : v.w;
+  return (k & 1) ? bf_hi(d) : bf_lo(d);
+}
+
+// E8M0 byte of a block from the fp32 bit pattern of its amax (same rule as the
+// BF16 form: biased exponent - 8, clamped at 0).
+__device__ __forceinline__ uint32_t scale_byte_from_amax_f32(uint32_t amax_bits) {
+  const int e = (int)(amax_bits >> 23);
+  return (uint32_t)(e > 8 ? e - 8 : 0);
+}
+
+// Four fp32 values -> four E4M3 codes of v / 2^(byte - 127), magnitudes first
+// clamped to 448 * 2^(byte - 127) (fp32 pattern (byte + 8) << 23 | 0x600000).
+__device__ __forceinline__ uint32_t cvt4_scaled_f32(float a, float b, float c, float d, uint32_t byte) {
+  const float lim = __uint_as_float(((byte + 8u) << 23) | 0x600000u);
+  const float f = __uint_as_float(byte << 23);
+  i16x2 r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, __builtin_amdgcn_fmed3f(a, -lim, lim),
+                                               __builtin_amdgcn_fmed3f(b, -lim, lim), f, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, __builtin_amdgcn_fmed3f(c, -lim, lim),
+                                               __builtin_amdgcn_fmed3f(d, -lim, lim), f, true);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 constexpr int QT_C = 128;            // tile columns
 constexpr int QT_R_MIN = 128;        // rows of the smallest tile (4 waves)
 
-template <bool ROW, bool COL, bool DBIAS, int QW, bool NT_QROW, bool NT_COLT>
+template <bool ROW, bool COL, bool DBIAS, int QW, bool NT_QROW, bool NT_COLT, int ACT>
 __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
     const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
     uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
     uint8_t* __restrict__ q_colT, uint8_t* __restrict__ s_colT,
-    float* __restrict__ dbias_part, int64_t tiles_c, QuantOpts opt) {
+    float* __restrict__ dbias_part, int64_t tiles_c, QuantOpts opt, const uint16_t* __restrict__ act_in) {
   constexpr int TR = 32 * QW;   // tile rows
   constexpr int NT = 64 * QW;   // threads
   // Transposed FP8 tile [column][row]; 8-byte row units XOR-swizzled by the
@@ -95,6 +125,87 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
   }
 
   uint32_t lane_amax = 0;
+  if constexpr (ACT != ACT_NONE) {
+    // ---- activation path: fp32 values f[i][k] (row i, column k of the lane)
+    float f[8][8];
+    {
+      uint4 a[8];
+      if (ACT == DACT_SQRELU) {
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+          a[i] = (cval && rb + i < R) ? *reinterpret_cast<const uint4*>(act_in + (rb + i) * ldx + cb)
+                                      : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+          const float xv = bf_half(v[i], k);
+          if (ACT == ACT_SQRELU) {
+            const float r = fmaxf(xv, 0.0f);
+            f[i][k] = r * r;
+          } else {
+            f[i][k] = xv * (2.0f * fmaxf(bf_half(a[i], k), 0.0f));
+          }
+        }
+    }
+    if (ROW) {
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int k = 0; k < 8; k++) m = max(m, __float_as_uint(f[i][k]) & 0x7FFFFFFFu);
+        m = quad_max(m);
+        lane_amax = max(lane_amax, m);
+        const uint32_t byte = scale_byte_from_amax_f32(m);
+        uint2 o;
+        o.x = cvt4_scaled_f32(f[i][0], f[i][1], f[i][2], f[i][3], byte);
+        o.y = cvt4_scaled_f32(f[i][4], f[i][5], f[i][6], f[i][7], byte);
+        const int64_t r = rb + i;
+        if (cval && r < R) {
+          if (NT_QROW) store_nt8(q_row + r * C + cb, o);
+          else *reinterpret_cast<uint2*>(q_row + r * C + cb) = o;
+        }
+        if ((cg & 3) == 0) lds_sr[(32 * w + 8 * rg + i) * 4 + (cg >> 2)] = (uint8_t)byte;
+      }
+    }
+    if (COL) {
+      const int u = 4 * w + rg;
+      const int swz = 2 * (cg & 7);
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) m = max(m, __float_as_uint(f[i][k]) & 0x7FFFFFFFu);
+        m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
+        if (!ROW) lane_amax = max(lane_amax, m);
+        const uint32_t byte = scale_byte_from_amax_f32(m);
+        uint2 o;
+        o.x = cvt4_scaled_f32(f[0][k], f[1][k], f[2][k], f[3][k], byte);
+        o.y = cvt4_scaled_f32(f[4][k], f[5][k], f[6][k], f[7][k], byte);
+        const int cl = 8 * cg + k;
+        *reinterpret_cast<uint2*>(lds_t + cl * TR + 8 * (u ^ swz)) = o;
+        if (rg == 0) lds_sc[cl * QW + w] = (uint8_t)byte;
+      }
+    }
+    if (DBIAS) {
+      float cs[8];
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        float t = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) t += f[i][k];
+        t += __shfl_xor(t, 16, 64);
+        t += __shfl_xor(t, 32, 64);
+        cs[k] = t;
+      }
+      if (rg == 0) {
+#pragma unroll
+        for (int k = 0; k < 8; k++) lds_db[w * QT_C + 8 * cg + k] = cs[k];
+      }
+    }
+  } else {
   if (ROW) {
 #pragma unroll
     for (int i = 0; i < 8; i++) {
@@ -188,8 +299,9 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
       for (int k = 0; k < 8; k++) lds_db[w * QT_C + 8 * cg + k] = cs[k];
     }
   }
+  }   // activation / plain
 
-  if (opt.amax) fold_amax(opt, lane_amax);   // uniform branch
+  if (opt.amax) fold_amax(opt, ACT ? lane_amax : lane_amax << 16);   // uniform branch
 
   __syncthreads();
 
@@ -315,7 +427,7 @@ __global__ __launch_bounds__(FL_THREADS) void quantize_rowwise_flat_kernel(const
       if ((lane & 3) == 0) s[e >> 5] = (uint8_t)byte;
     }
   }
-  if (opt.amax) fold_amax(opt, lane_amax);
+  if (opt.amax) fold_amax(opt, lane_amax << 16);
 }
 
 // Rowwise copy with scales in the packed word layout (C % 128 == 0): a
@@ -369,7 +481,7 @@ __global__ __launch_bounds__(256) void quantize_rowwise_packed_kernel(const uint
     // lane 16k + 4b holds block b of slab k
     if ((lane & 3) == 0) lds_s[((2 * w + u) * 4 + (lane >> 4)) * 4 + ((lane >> 2) & 3)] = (uint8_t)byte;
   }
-  if (opt.amax) fold_amax(opt, lane_amax);
+  if (opt.amax) fold_amax(opt, lane_amax << 16);
   __syncthreads();
   if (tid < PN_ROWS * 4) {
     const int slab = tid >> 3, row = tid & 7;
@@ -427,10 +539,11 @@ int64_t quantize_col_tiles(int64_t C) { return (C + QT_C - 1) / QT_C; }
 // backward and columnwise-only shapes): 8 waves with non-temporal rowwise
 // codes and cached transposed codes when both copies are written; 4 waves with
 // non-temporal transposed codes for the columnwise copy alone.
-template <bool ROW, bool COL, bool DBIAS>
+template <bool ROW, bool COL, bool DBIAS, int ACT>
 static hipError_t launch_tiles(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q_row,
                                uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT, float* dbias_part,
-                               const QuantOpts& opt, int64_t* row_tiles, hipStream_t stream) {
+                               const QuantOpts& opt, const uint16_t* act_in, int64_t* row_tiles,
+                               hipStream_t stream) {
   constexpr int QW = (ROW || !COL) ? 8 : 4;
   constexpr bool NT_QROW = true;
   constexpr bool NT_COLT = !ROW;
@@ -438,16 +551,35 @@ static hipError_t launch_tiles(const uint16_t* x, int64_t R, int64_t C, int64_t 
   const int64_t tc = quantize_col_tiles(C);
   *row_tiles = tr;
   if (tr * tc == 0) return hipSuccess;
-  hipLaunchKernelGGL((quantize_tile_kernel<ROW, COL, DBIAS, QW, NT_QROW, NT_COLT>), dim3((unsigned)(tr * tc)),
-                     dim3(64 * QW), 0, stream, x, R, C, ldx, q_row, s_row, q_colT, s_colT, dbias_part, tc, opt);
+  hipLaunchKernelGGL((quantize_tile_kernel<ROW, COL, DBIAS, QW, NT_QROW, NT_COLT, ACT>), dim3((unsigned)(tr * tc)),
+                     dim3(64 * QW), 0, stream, x, R, C, ldx, q_row, s_row, q_colT, s_colT, dbias_part, tc, opt,
+                     act_in);
   return hipGetLastError();
+}
+
+// One tile launch for a copy set, with the activation ACT fused in.
+template <int ACT>
+static hipError_t launch_tiles_act(bool row, bool col, bool db, const uint16_t* x, int64_t R, int64_t C,
+                                   int64_t ldx, uint8_t* q_row, uint8_t* srow, uint8_t* q_colT, uint8_t* scol,
+                                   float* dbias_part, const QuantOpts& opt, const uint16_t* act_in,
+                                   int64_t* tiles_r, hipStream_t stream) {
+#define MX_Q_LAUNCH(RW, CL, DB) \
+  launch_tiles<RW, CL, DB, ACT>(x, R, C, ldx, q_row, srow, q_colT, scol, dbias_part, opt, act_in, tiles_r, stream)
+  if (row && col && db) return MX_Q_LAUNCH(true, true, true);
+  if (row && col) return MX_Q_LAUNCH(true, true, false);
+  if (row && db) return MX_Q_LAUNCH(true, false, true);
+  if (row) return MX_Q_LAUNCH(true, false, false);
+  if (col && db) return MX_Q_LAUNCH(false, true, true);
+  return MX_Q_LAUNCH(false, true, false);
+#undef MX_Q_LAUNCH
 }
 
 hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint32_t flags,
                            uint8_t* q_row, void* s_row, uint8_t* q_colT, void* s_colT,
                            float* dbias, float* dbias_part, float* amax, const int32_t* noop,
-                           hipStream_t stream) {
+                           const uint16_t* act_in, hipStream_t stream) {
   const bool row = flags & 1u, col = flags & 2u, db = flags & 4u, want_amax = flags & 8u, packed = flags & 16u;
+  const int act = (flags & 32u) ? ACT_SQRELU : (flags & 64u) ? DACT_SQRELU : ACT_NONE;
   const QuantOpts opt{want_amax ? reinterpret_cast<uint32_t*>(amax) : nullptr, noop, packed ? 1 : 0};
   if (want_amax) {   // max starts from 0 (also the amax of an empty tensor)
     hipLaunchKernelGGL(fill_zero_f32_kernel, dim3(1), dim3(256), 0, stream, amax, (int64_t)1, noop);
@@ -456,14 +588,14 @@ hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
   }
   uint8_t* srow = static_cast<uint8_t*>(s_row);
   uint8_t* scol = static_cast<uint8_t*>(s_colT);
-  if (row && !col && !db && packed) {
+  if (row && !col && !db && packed && act == ACT_NONE) {
     const int64_t blocks = ((R + PN_ROWS - 1) / PN_ROWS) * ((C + PN_COLS - 1) / PN_COLS);
     if (blocks > 0)
       hipLaunchKernelGGL(quantize_rowwise_packed_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, R, C, ldx,
                          q_row, static_cast<uint32_t*>(s_row), opt);
     return hipGetLastError();
   }
-  if (row && !col && !db && !packed && ldx == C) {
+  if (row && !col && !db && !packed && act == ACT_NONE && ldx == C) {
     const int64_t total = R * C;
     const int64_t per_block = FL_ELEMS * (FL_THREADS / 64);
     const int64_t blocks = (total + per_block - 1) / per_block;
@@ -474,15 +606,15 @@ hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
   }
   int64_t tiles_r = 0;
   hipError_t e;
-#define MX_Q_LAUNCH(RW, CL, DB) \
-  launch_tiles<RW, CL, DB>(x, R, C, ldx, q_row, srow, q_colT, scol, dbias_part, opt, &tiles_r, stream)
-  if (row && col && db) e = MX_Q_LAUNCH(true, true, true);
-  else if (row && col) e = MX_Q_LAUNCH(true, true, false);
-  else if (row && db) e = MX_Q_LAUNCH(true, false, true);
-  else if (row) e = MX_Q_LAUNCH(true, false, false);
-  else if (col && db) e = MX_Q_LAUNCH(false, true, true);
-  else e = MX_Q_LAUNCH(false, true, false);
-#undef MX_Q_LAUNCH
+  if (act == ACT_SQRELU)
+    e = launch_tiles_act<ACT_SQRELU>(row, col, db, x, R, C, ldx, q_row, srow, q_colT, scol, dbias_part, opt, act_in,
+                                     &tiles_r, stream);
+  else if (act == DACT_SQRELU)
+    e = launch_tiles_act<DACT_SQRELU>(row, col, db, x, R, C, ldx, q_row, srow, q_colT, scol, dbias_part, opt,
+                                      act_in, &tiles_r, stream);
+  else
+    e = launch_tiles_act<ACT_NONE>(row, col, db, x, R, C, ldx, q_row, srow, q_colT, scol, dbias_part, opt, act_in,
+                                   &tiles_r, stream);
   if (e != hipSuccess) return e;
   if (db && C > 0) {
     const dim3 grid((unsigned)((C + DB_COLS - 1) / DB_COLS));

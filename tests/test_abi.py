@@ -93,13 +93,20 @@ def test_quantize_validation(L):
 
 
 def qx(L, x=A16, rows=128, cols=128, ld=128, flags=ROW, qr=A16, sr=A16, qc=A16, sc=A16, db=A16, am=A16,
-       noop=None, ws=A16, wsb=1 << 20):
-    return L.mxfp8_quantize_ex(x, rows, cols, ld, flags, qr, sr, qc, sc, db, am, noop, ws, wsb, None)
+       noop=None, act=A16, ws=A16, wsb=1 << 20):
+    return L.mxfp8_quantize_ex(x, rows, cols, ld, flags, qr, sr, qc, sc, db, am, noop, act, ws, wsb, None)
 
 
 def test_quantize_ex_validation(L):
     AMAX, PACKED = mx.MXFP8_AMAX, mx.MXFP8_PACKED_SCALES
-    assert qx(L, flags=32 | ROW) == FLAGS
+    ACT, DACT = mx.MXFP8_ACT_SQRELU, mx.MXFP8_DACT_SQRELU
+    assert qx(L, flags=128 | ROW) == FLAGS
+    assert qx(L, flags=ROW | ACT | DACT) == FLAGS              # one activation at a time
+    assert qx(L, flags=ACT) == FLAGS
+    assert qx(L, flags=ROW | DACT, act=None) == NULL
+    assert qx(L, flags=COL | DACT, act=A16 + 2) == MISALIGNED
+    assert qx(L, flags=ROW | ACT, act=None, x=A16 + 2) == MISALIGNED   # act_in unused without DACT
+    assert qx(L, flags=ROW | DACT | DB, act=A16, ws=None) == WORKSPACE  # stops before launching
     assert qx(L, flags=AMAX) == FLAGS                         # no copy requested
     assert qx(L, flags=ROW | AMAX, am=None) == NULL
     assert qx(L, flags=ROW | AMAX, am=A16 + 2) == MISALIGNED
@@ -114,6 +121,7 @@ def test_quantize_ex_validation(L):
     # the plain entry point keeps rejecting the extra flags
     assert q(L, flags=ROW | AMAX) == FLAGS
     assert q(L, flags=ROW | PACKED) == FLAGS
+    assert q(L, flags=ROW | ACT) == FLAGS
 
 
 def test_quantize_grid_limit(L):

@@ -18,8 +18,9 @@ ROW, COL, DB = mx.MXFP8_ROWWISE, mx.MXFP8_COLWISE, mx.MXFP8_DBIAS
 AMAX, PACKED = mx.MXFP8_AMAX, mx.MXFP8_PACKED_SCALES
 
 
-def run_ex(bits, flags, noop_value=None, ld=None):
-    """mxfp8_quantize_ex into canary-filled buffers; returns host arrays."""
+def run_ex(bits, flags, noop_value=None, ld=None, act_bits=None):
+    """mxfp8_quantize_ex into canary-filled buffers; returns host arrays.
+    act_bits: the activation input for MXFP8_DACT_SQRELU (same shape)."""
     torch = need_gpu()
     R, C = bits.shape
     ld = C if ld is None else ld
@@ -40,10 +41,16 @@ def run_ex(bits, flags, noop_value=None, ld=None):
     if flags & AMAX:
         out["amax"] = torch.full((1,), -7.0, dtype=torch.float32, device="cuda")
     noop = None if noop_value is None else to_dev(np.array([noop_value], dtype=np.int32))
+    act_in = None
+    if act_bits is not None:
+        asrc = np.zeros((R, ld), dtype=np.uint16)
+        asrc[:, :C] = act_bits
+        act_in = to_dev_bf16(asrc)
     nws = mx.mxfp8_quantize_workspace_bytes(R, C, flags)
     ws = torch.empty((max(nws, 16),), dtype=torch.uint8, device="cuda")
     mx.mxfp8_quantize_ex(x, R, C, ld, flags, out.get("q_row"), out.get("s_row"), out.get("q_colT"),
-                         out.get("s_colT"), out.get("dbias"), out.get("amax"), noop, ws if nws else None, nws)
+                         out.get("s_colT"), out.get("dbias"), out.get("amax"), noop, act_in,
+                         ws if nws else None, nws)
     torch.cuda.synchronize()
     return {k: to_host(v) for k, v in out.items()}
 
@@ -159,3 +166,108 @@ def test_full_stress_row_col_packed():
     qT, sT = oracle.quantize_colwise(bits)
     assert np.array_equal(got["q_colT"], qT)
     assert np.array_equal(got["s_colT"], oracle.pack_scales(sT))
+
+
+# ------------------------------------------------ activation-fused quantize
+
+ACT, DACT = mx.MXFP8_ACT_SQRELU, mx.MXFP8_DACT_SQRELU
+
+
+def act_inputs(R, C, seed):
+    """Gradient-like x and activation input a whose products stay inside
+    fp32's normal range: block magnitudes 2^-30 .. 2^30, no BF16 subnormals."""
+    x = workloads.wide_range_bf16((R, C), seed, u_lo=-30, u_hi=30, n_maxbf16=0, n_subnormal=0, n_subnormal_blocks=0)
+    a = workloads.wide_range_bf16((R, C), seed + 1, u_lo=-30, u_hi=30, n_maxbf16=0, n_subnormal=0,
+                                  n_subnormal_blocks=0)
+    return x, a
+
+
+def check_act_result(got, v, flags, label):
+    if flags & ROW:
+        q, s = oracle.quantize_rowwise_values(v)
+        assert np.array_equal(got["q_row"], q), label + " q_row"
+        assert np.array_equal(got["s_row"], oracle.pack_scales(s) if flags & PACKED else s), label + " s_row"
+    if flags & COL:
+        qT, sT = oracle.quantize_colwise_values(v)
+        assert np.array_equal(got["q_colT"], qT), label + " q_colT"
+        assert np.array_equal(got["s_colT"], oracle.pack_scales(sT) if flags & PACKED else sT), label + " s_colT"
+    if flags & DB:
+        ref = oracle.dbias_values(v).astype(np.float64)
+        mag = np.abs(v.astype(np.float64)).sum(axis=0)
+        R = v.shape[0]
+        depth = 8 + 2 + 3 + ((R + 127) // 128 + 7) // 8 + 3     # the fp32 addition chain of the kernel
+        tol = 1.01 * depth * 2.0 ** -24 * mag + np.abs(ref) * 2.0 ** -24 + 2.0 ** -126
+        err = np.abs(got["dbias"].astype(np.float64) - ref)
+        assert np.all(err <= tol), "%s: dbias off by %g" % (label, err.max())
+    if flags & AMAX:
+        assert float(got["amax"][0]) == float(np.abs(v).max(initial=0.0)), label + " amax"
+
+
+ACT_FLAGS = [ROW, COL, ROW | COL, ROW | DB, COL | DB, ROW | COL | DB, ROW | COL | AMAX, ROW | PACKED,
+             ROW | COL | PACKED | DB]
+
+
+@pytest.mark.parametrize("R,C", [(128, 128), (256, 384), (640, 256)])
+@pytest.mark.parametrize("flags", ACT_FLAGS)
+def test_sqrelu_quantize_bit_exact(R, C, flags):
+    x, _ = act_inputs(R, C, 101 * R + C + flags)
+    label = "sqrelu R=%d C=%d flags=%d" % (R, C, flags)
+    log(label)
+    got = run_ex(x, flags | ACT)
+    check_act_result(got, oracle.act_sqrelu(x), flags, label)
+
+
+@pytest.mark.parametrize("R,C", [(128, 128), (256, 384), (640, 256)])
+@pytest.mark.parametrize("flags", ACT_FLAGS)
+def test_dsqrelu_quantize_bit_exact(R, C, flags):
+    g, a = act_inputs(R, C, 103 * R + C + flags)
+    label = "dsqrelu R=%d C=%d flags=%d" % (R, C, flags)
+    log(label)
+    got = run_ex(g, flags | DACT, act_bits=a)
+    check_act_result(got, oracle.dact_sqrelu(g, a), flags, label)
+
+
+def test_activation_ragged_rows_and_stride():
+    """Rowwise copies need no row multiple of 32; both inputs share ld_x."""
+    g, a = act_inputs(200, 512, 7)
+    got = run_ex(g, ROW | DB | AMAX | DACT, ld=520, act_bits=a)
+    check_act_result(got, oracle.dact_sqrelu(g, a), ROW | DB | AMAX, "dsqrelu ragged")
+    got = run_ex(g, ROW | AMAX | ACT, ld=520)
+    check_act_result(got, oracle.act_sqrelu(g), ROW | AMAX, "sqrelu ragged")
+
+
+def test_activation_special_values():
+    """All-negative blocks (relu gives exact zeros: scale byte 0, codes 0), a
+    zero activation input under a nonzero gradient, saturation at 448 * 2^X
+    (a block whose largest square rounds up past the E4M3 range) and the
+    amax of an all-zero result."""
+    R, C = 128, 256
+    x, a = act_inputs(R, C, 19)
+    x[:32, :32] |= 0x8000                 # one all-negative 32 x 32 square
+    a[32:64, :64] = 0                      # zero activation input
+    x[64, 0:32] = workloads.f32_to_bf16_bits(np.full(32, 1.0, dtype=np.float32))
+    x[64, 5] = 0x41F8                      # 31.0: 961 = 1.877 * 2^9, saturates to 448 * 2^1
+    for flags in (ROW | COL | DB | AMAX, ROW | COL | PACKED):
+        got = run_ex(x, flags | ACT)
+        check_act_result(got, oracle.act_sqrelu(x), flags, "sqrelu special")
+        got = run_ex(x, flags | DACT, act_bits=a)
+        check_act_result(got, oracle.dact_sqrelu(x, a), flags, "dsqrelu special")
+    neg = np.full((64, 64), 0xBF80, dtype=np.uint16)   # all -1.0
+    got = run_ex(neg, ROW | COL | AMAX | ACT)
+    assert float(got["amax"][0]) == 0.0
+    assert not got["q_row"].any() and not got["s_row"].any() and not got["q_colT"].any()
+
+
+@pytest.mark.parametrize("flags", [ROW | COL | DB | ACT, ROW | PACKED | DACT])
+def test_activation_noop(flags):
+    g, a = act_inputs(256, 256, 23)
+    got = run_ex(g, flags | AMAX, noop_value=1, act_bits=a if flags & DACT else None)
+    for k, v in got.items():
+        if v.dtype == np.uint8:
+            assert np.all(v == 0xA5), k
+        elif v.dtype == np.uint32:
+            assert np.all(v == 0xFFFFFFFF), k
+        elif k == "dbias":
+            assert np.all(v == -5.0), k
+        else:
+            assert np.all(v == -7.0), k
