@@ -15,11 +15,13 @@ with HIP events recorded on its launch stream; ``quantize`` reports each
 quantizer launch against the HBM peak; ``cpu_baseline`` is the CPU oracle on
 the same work.
 
-``--workload backward|moe|stress|linear`` measures the other workloads the
-same way: row+col+dbias quantize and the wgrad GEMM on the columnwise copies;
-the ragged grouped MoE GEMM; the wide-range 32768x8192x8192 GEMM; one MXFP8
-linear-layer training step (fprop, dgrad, wgrad accumulated into a BF16 main
-gradient).  They are reporting aids next to the default line.
+``--workload backward|moe|stress|linear|mlp`` measures the other workloads
+the same way: row+col+dbias quantize and the wgrad GEMM on the columnwise
+copies; the ragged grouped MoE GEMM; the wide-range 32768x8192x8192 GEMM; one
+MXFP8 linear-layer training step (fprop, dgrad, wgrad accumulated into a BF16
+main gradient); one squared-ReLU MLP training step (six GEMMs, the activation
+and its backward fused into the quantize launches).  They are reporting aids
+next to the default line.
 """
 
 import argparse
@@ -41,7 +43,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="dense", choices=["dense", "backward", "moe", "stress", "linear"])
+    p.add_argument("--workload", default="dense", choices=["dense", "backward", "moe", "stress", "linear", "mlp"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU-oracle time: whole oracle steps are repeated until reached")
@@ -77,10 +79,11 @@ def profiled_traffic(kernel_key):
     return None
 
 
-def quant_bytes(rows, cols, copies, dbias=False):
-    """Algorithmic bytes of a quantize: read 2 B per element, write 1 + 1/32 B
+def quant_bytes(rows, cols, copies, dbias=False, inputs=1):
+    """Algorithmic bytes of a quantize: read 2 B per element and input (x, and
+    the activation input of the fused backward activation), write 1 + 1/32 B
     per element and copy, plus 4 B per column for dbias."""
-    return rows * cols * (2 + copies * (1 + 1.0 / 32)) + (4 * cols if dbias else 0)
+    return rows * cols * (2 * inputs + copies * (1 + 1.0 / 32)) + (4 * cols if dbias else 0)
 
 
 class Op:
@@ -105,11 +108,12 @@ def build_ops(workload, dev):
 
     ops, keep = [], []
 
-    def quantize_op(label, bits, flags, packed=False):
+    def quantize_op(label, bits, flags, packed=False, act_in=None):
         """Quantize launch (+ one packing launch per copy, unless the quantizer
-        writes the packed scale words itself)."""
+        writes the packed scale words itself).  bits: host BF16 bit patterns,
+        or a device BF16 tensor written by an earlier launch of the step."""
         R, C = bits.shape
-        b = {"x": upload(bits)}
+        b = {"x": bits if isinstance(bits, torch.Tensor) else upload(bits), "act_in": act_in}
         if flags & mx.MXFP8_ROWWISE:
             b["q"] = torch.empty((R, C), dtype=torch.uint8, device=dev)
             b["s"] = torch.empty((R, C // 32), dtype=torch.uint8, device=dev)
@@ -124,11 +128,11 @@ def build_ops(workload, dev):
         b["ws"] = torch.empty((max(nws, 16),), dtype=torch.uint8, device=dev) if nws else None
         keep.append(b)
         copies = int(bool(flags & mx.MXFP8_ROWWISE)) + int(bool(flags & mx.MXFP8_COLWISE))
-        work = quant_bytes(R, C, copies, bool(flags & mx.MXFP8_DBIAS))
+        work = quant_bytes(R, C, copies, bool(flags & mx.MXFP8_DBIAS), 2 if act_in is not None else 1)
         if packed:
             ops.append(Op("quantize", label + " packed", lambda st: mx.mxfp8_quantize_ex(
                 b["x"], R, C, C, flags | mx.MXFP8_PACKED_SCALES, b.get("q"), b.get("p"), b.get("qT"), b.get("pT"),
-                b.get("db"), workspace=b["ws"], workspace_bytes=nws, stream=st), work))
+                b.get("db"), act_in=b["act_in"], workspace=b["ws"], workspace_bytes=nws, stream=st), work))
             return b
         ops.append(Op("quantize", label, lambda st: mx.mxfp8_quantize(
             b["x"], R, C, C, flags, b.get("q"), b.get("s"), b.get("qT"), b.get("sT"), b.get("db"),
@@ -142,13 +146,15 @@ def build_ops(workload, dev):
                 b["sT"], C, R, R // 32, b["pT"], stream=st), 2.0 * R * C / 32))
         return b
 
-    def gemm_op(a, pa, b, pb, M, N, K, accumulate=False, name=""):
+    def gemm_op(a, pa, b, pb, M, N, K, accumulate=False, name="", out=None):
         c = torch.zeros((M, N), dtype=torch.bfloat16, device=dev)
         keep.append(c)
         label = name + "%dx%dx%d" % (M, N, K)
         flags = mx.MXFP8_GEMM_ACCUMULATE if accumulate else 0
         ops.append(Op("gemm", label, lambda st: mx.mxfp8_gemm_ex(a, pa, b, pb, c, N, M, N, K, flags, stream=st),
                       2.0 * M * N * K))
+        if out is not None:
+            out.append(c)
         return label
 
     ROW, COL, DB = mx.MXFP8_ROWWISE, mx.MXFP8_COLWISE, mx.MXFP8_DBIAS
@@ -194,6 +200,31 @@ def build_ops(workload, dev):
                 "row+col quantize of X, W, dY, fprop %dx%dx%d, dgrad %dx%dx%d on W's transposed copy, wgrad "
                 "%dx%dx%d on the transposed copies accumulated into a BF16 main gradient"
                 % (T, K, N, K, T, N, K, T, K, N, N, K, T))
+    elif workload == "mlp":
+        lin = workloads.dense_linear()
+        T, D = lin["X"].shape
+        F = lin["W"].shape[0]
+        w2 = workloads.normal_bf16((D, F), 5, std=0.02)
+        dy = workloads.normal_bf16((T, D), 6)
+        ACT, DACT = mx.MXFP8_ACT_SQRELU, mx.MXFP8_DACT_SQRELU
+        h, da = [], []
+        bx = quantize_op("X[%dx%d] row+col" % (T, D), lin["X"], ROW | COL, packed=True)
+        bw1 = quantize_op("W1[%dx%d] row+col" % (F, D), lin["W"], ROW | COL, packed=True)
+        dominant = gemm_op(bx["q"], bx["p"], bw1["q"], bw1["p"], T, F, D, name="fc1 ", out=h)
+        ba = quantize_op("relu^2(H)[%dx%d] row+col" % (T, F), h[0], ROW | COL | ACT, packed=True)
+        bw2 = quantize_op("W2[%dx%d] row+col" % (D, F), w2, ROW | COL, packed=True)
+        gemm_op(ba["q"], ba["p"], bw2["q"], bw2["p"], T, D, F, name="fc2 ")
+        bdy = quantize_op("dY[%dx%d] row+col" % (T, D), dy, ROW | COL, packed=True)
+        gemm_op(bdy["q"], bdy["p"], bw2["qT"], bw2["pT"], T, F, D, name="fc2 dgrad ", out=da)
+        gemm_op(bdy["qT"], bdy["pT"], ba["qT"], ba["pT"], D, F, T, name="fc2 wgrad ")
+        bdh = quantize_op("dH=dA*2relu(H)[%dx%d] row+col+dbias" % (T, F), da[0], ROW | COL | DB | DACT, packed=True,
+                          act_in=h[0])
+        gemm_op(bdh["q"], bdh["p"], bw1["qT"], bw1["pT"], T, D, F, name="fc1 dgrad ")
+        gemm_op(bdh["qT"], bdh["pT"], bx["qT"], bx["pT"], F, D, T, name="fc1 wgrad ")
+        desc = ("squared-ReLU MLP training step, tokens %d, d_model %d, d_ff %d: X N(0,1), W1 N(0,0.02), "
+                "W2 N(0,0.02), dY N(0,1); row+col quantize of X, W1, W2, dY; FC1 GEMM; relu^2 fused into the "
+                "quantize of its BF16 output; FC2 GEMM; FC2 dgrad and wgrad; the activation's backward fused "
+                "into the row+col+dbias quantize of FC2's dgrad output; FC1 dgrad and wgrad" % (T, D, F))
     else:  # moe
         d = workloads.moe()
         G, N, K = d["W"].shape
