@@ -75,9 +75,11 @@ __device__ __forceinline__ uint32_t scale_byte_from_amax_f32(uint32_t amax_bits)
 __device__ __forceinline__ uint32_t cvt4_scaled_f32(float a, float b, float c, float d, uint32_t byte) {
   const float lim = __uint_as_float(((byte + 8u) << 23) | 0x600000u);
   const float f = __uint_as_float(byte << 23);
-  i16x2 r = {0, 0};
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, __builtin_amdgcn_fmed3f(a, -lim, lim),
-                                               __builtin_amdgcn_fmed3f(b, -lim, lim), f, false);
+  const float ca = __builtin_amdgcn_fmed3f(a, -lim, lim);
+  // both halves of the result are written below: any register serves as the
+  // initial contents (a dead one saves a move)
+  i16x2 r = __builtin_bit_cast(i16x2, ca);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, ca, __builtin_amdgcn_fmed3f(b, -lim, lim), f, false);
   r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, __builtin_amdgcn_fmed3f(c, -lim, lim),
                                                __builtin_amdgcn_fmed3f(d, -lim, lim), f, true);
   return __builtin_bit_cast(uint32_t, r);
@@ -115,52 +117,76 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
   const int64_t cb = c0 + 8 * cg;           // first column of this lane
   const bool cval = cb < C;                 // C % 32 == 0: whole quads are valid
 
-  uint4 v[8];
+  // Tiles entirely inside the tensor (uniform test) load without per-row
+  // guards; edge tiles read zeros outside it.
+  const bool full_tile = r0 + TR <= R && c0 + QT_C <= C;
+  auto load_rows = [&](const uint16_t* __restrict__ src, uint4 (&d)[8]) {
+    if (full_tile) {
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    if (cval && rb + i < R)
-      v[i] = *reinterpret_cast<const uint4*>(x + (rb + i) * ldx + cb);
-    else
-      v[i] = make_uint4(0u, 0u, 0u, 0u);
-  }
+      for (int i = 0; i < 8; i++) d[i] = *reinterpret_cast<const uint4*>(src + (rb + i) * ldx + cb);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+        d[i] = (cval && rb + i < R) ? *reinterpret_cast<const uint4*>(src + (rb + i) * ldx + cb)
+                                    : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  uint4 v[8];
+  load_rows(x, v);
 
   uint32_t lane_amax = 0;
   if constexpr (ACT != ACT_NONE) {
-    // ---- activation path: fp32 values f[i][k] (row i, column k of the lane)
-    float f[8][8];
-    {
-      uint4 a[8];
-      if (ACT == DACT_SQRELU) {
-#pragma unroll
-        for (int i = 0; i < 8; i++)
-          a[i] = (cval && rb + i < R) ? *reinterpret_cast<const uint4*>(act_in + (rb + i) * ldx + cb)
-                                      : make_uint4(0u, 0u, 0u, 0u);
-      }
+    // ---- activation path.  relu is applied to the BF16 bits in place.  The
+    // fp32 value of row i, column k of the lane is recomputed where it is
+    // needed (keeping 64 fp32 values live would halve the waves per SIMD).
+    // Squared ReLU: max r^2 = (max r)^2, so block amaxes come from integer
+    // maxima of the relu'd BF16 bits, as in the plain path.
+    uint4 a[8];
+    if (ACT == DACT_SQRELU) {
+      load_rows(act_in, a);
 #pragma unroll
       for (int i = 0; i < 8; i++)
+        a[i] = make_uint4(twice_bf16x2(relu_bf16x2(a[i].x)), twice_bf16x2(relu_bf16x2(a[i].y)),
+                          twice_bf16x2(relu_bf16x2(a[i].z)), twice_bf16x2(relu_bf16x2(a[i].w)));
+    } else {
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
-          const float xv = bf_half(v[i], k);
-          if (ACT == ACT_SQRELU) {
-            const float r = fmaxf(xv, 0.0f);
-            f[i][k] = r * r;
-          } else {
-            f[i][k] = xv * (2.0f * fmaxf(bf_half(a[i], k), 0.0f));
-          }
-        }
+      for (int i = 0; i < 8; i++)
+        v[i] = make_uint4(relu_bf16x2(v[i].x), relu_bf16x2(v[i].y), relu_bf16x2(v[i].z), relu_bf16x2(v[i].w));
     }
+    auto val = [&](int i, int k) -> float {
+      const float xv = bf_half(v[i], k);
+      if (ACT == ACT_SQRELU) return xv * xv;
+      return xv * bf_half(a[i], k);   // a holds 2 relu(a)
+    };
+    // |value| bits -> block amax bits (squared ReLU: from the max relu'd input)
+    auto sq_bits = [](uint32_t r15) -> uint32_t {
+      const float r = __uint_as_float(r15 << 16);
+      return __float_as_uint(r * r);
+    };
     if (ROW) {
 #pragma unroll
       for (int i = 0; i < 8; i++) {
+        float f[8];
         uint32_t m = 0;
+        if (ACT == ACT_SQRELU) {
+          uint32_t h = pk_max_u16(pk_max_u16(v[i].x, v[i].y), pk_max_u16(v[i].z, v[i].w));
+          m = sq_bits(quad_max(max(h & 0xFFFFu, h >> 16)));
 #pragma unroll
-        for (int k = 0; k < 8; k++) m = max(m, __float_as_uint(f[i][k]) & 0x7FFFFFFFu);
-        m = quad_max(m);
+          for (int k = 0; k < 8; k++) f[k] = val(i, k);
+        } else {
+          float fm = 0.0f;
+#pragma unroll
+          for (int k = 0; k < 8; k++) {
+            f[k] = val(i, k);
+            fm = fmaxf(fm, fabsf(f[k]));
+          }
+          m = quad_max(__float_as_uint(fm));
+        }
         lane_amax = max(lane_amax, m);
         const uint32_t byte = scale_byte_from_amax_f32(m);
         uint2 o;
-        o.x = cvt4_scaled_f32(f[i][0], f[i][1], f[i][2], f[i][3], byte);
-        o.y = cvt4_scaled_f32(f[i][4], f[i][5], f[i][6], f[i][7], byte);
+        o.x = cvt4_scaled_f32(f[0], f[1], f[2], f[3], byte);
+        o.y = cvt4_scaled_f32(f[4], f[5], f[6], f[7], byte);
         const int64_t r = rb + i;
         if (cval && r < R) {
           if (NT_QROW) store_nt8(q_row + r * C + cb, o);
@@ -169,38 +195,69 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
         if ((cg & 3) == 0) lds_sr[(32 * w + 8 * rg + i) * 4 + (cg >> 2)] = (uint8_t)byte;
       }
     }
-    if (COL) {
-      const int u = 4 * w + rg;
-      const int swz = 2 * (cg & 7);
+    if (ROW && (COL || DBIAS)) {
+      // Opaque to the optimiser: the column pass recomputes its values
+      // instead of keeping the row pass's 64 fp32 results alive.
 #pragma unroll
-      for (int k = 0; k < 8; k++) {
-        uint32_t m = 0;
-#pragma unroll
-        for (int i = 0; i < 8; i++) m = max(m, __float_as_uint(f[i][k]) & 0x7FFFFFFFu);
-        m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));
-        m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
-        if (!ROW) lane_amax = max(lane_amax, m);
-        const uint32_t byte = scale_byte_from_amax_f32(m);
-        uint2 o;
-        o.x = cvt4_scaled_f32(f[0][k], f[1][k], f[2][k], f[3][k], byte);
-        o.y = cvt4_scaled_f32(f[4][k], f[5][k], f[6][k], f[7][k], byte);
-        const int cl = 8 * cg + k;
-        *reinterpret_cast<uint2*>(lds_t + cl * TR + 8 * (u ^ swz)) = o;
-        if (rg == 0) lds_sc[cl * QW + w] = (uint8_t)byte;
+      for (int i = 0; i < 8; i++) {
+        asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
+        if (ACT == DACT_SQRELU) asm volatile("" : "+v"(a[i].x), "+v"(a[i].y), "+v"(a[i].z), "+v"(a[i].w));
       }
     }
-    if (DBIAS) {
+    if (COL || DBIAS) {
+      const int u = 4 * w + rg;
+      const int swz = 2 * (cg & 7);
+      uint32_t cm[4] = {0u, 0u, 0u, 0u};
+      if (ACT == ACT_SQRELU && COL) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          cm[0] = pk_max_u16(cm[0], v[i].x);
+          cm[1] = pk_max_u16(cm[1], v[i].y);
+          cm[2] = pk_max_u16(cm[2], v[i].z);
+          cm[3] = pk_max_u16(cm[3], v[i].w);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          cm[j] = pk_max_u16(cm[j], (uint32_t)__shfl_xor((int)cm[j], 16, 64));
+          cm[j] = pk_max_u16(cm[j], (uint32_t)__shfl_xor((int)cm[j], 32, 64));
+        }
+      }
       float cs[8];
 #pragma unroll
       for (int k = 0; k < 8; k++) {
+        float f[8];
+        float fm = 0.0f;
         float t = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; i++) t += f[i][k];
-        t += __shfl_xor(t, 16, 64);
-        t += __shfl_xor(t, 32, 64);
-        cs[k] = t;
+        for (int i = 0; i < 8; i++) {
+          f[i] = val(i, k);
+          if (ACT == DACT_SQRELU) fm = fmaxf(fm, fabsf(f[i]));
+          if (DBIAS) t += f[i];
+        }
+        uint32_t m = __float_as_uint(fm);
+        if (DBIAS) {
+          t += __shfl_xor(t, 16, 64);
+          t += __shfl_xor(t, 32, 64);
+          cs[k] = t;
+        }
+        if (COL) {
+          if (ACT == ACT_SQRELU) {
+            m = sq_bits((k & 1) ? (cm[k >> 1] >> 16) : (cm[k >> 1] & 0xFFFFu));
+          } else {
+            m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));
+            m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
+          }
+          if (!ROW) lane_amax = max(lane_amax, m);
+          const uint32_t byte = scale_byte_from_amax_f32(m);
+          uint2 o;
+          o.x = cvt4_scaled_f32(f[0], f[1], f[2], f[3], byte);
+          o.y = cvt4_scaled_f32(f[4], f[5], f[6], f[7], byte);
+          const int cl = 8 * cg + k;
+          *reinterpret_cast<uint2*>(lds_t + cl * TR + 8 * (u ^ swz)) = o;
+          if (rg == 0) lds_sc[cl * QW + w] = (uint8_t)byte;
+        }
       }
-      if (rg == 0) {
+      if (DBIAS && rg == 0) {
 #pragma unroll
         for (int k = 0; k < 8; k++) lds_db[w * QT_C + 8 * cg + k] = cs[k];
       }
