@@ -201,15 +201,14 @@ def build_ops(workload, dev):
                 "%dx%dx%d on the transposed copies accumulated into a BF16 main gradient"
                 % (T, K, N, K, T, N, K, T, K, N, N, K, T))
     elif workload == "mlp":
-        lin = workloads.dense_linear()
+        lin = workloads.mlp()
         T, D = lin["X"].shape
-        F = lin["W"].shape[0]
-        w2 = workloads.normal_bf16((D, F), 5, std=0.02)
-        dy = workloads.normal_bf16((T, D), 6)
+        F = lin["W1"].shape[0]
+        w2, dy = lin["W2"], lin["dY"]
         ACT, DACT = mx.MXFP8_ACT_SQRELU, mx.MXFP8_DACT_SQRELU
         h, da = [], []
         bx = quantize_op("X[%dx%d] row+col" % (T, D), lin["X"], ROW | COL, packed=True)
-        bw1 = quantize_op("W1[%dx%d] row+col" % (F, D), lin["W"], ROW | COL, packed=True)
+        bw1 = quantize_op("W1[%dx%d] row+col" % (F, D), lin["W1"], ROW | COL, packed=True)
         dominant = gemm_op(bx["q"], bx["p"], bw1["q"], bw1["p"], T, F, D, name="fc1 ", out=h)
         ba = quantize_op("relu^2(H)[%dx%d] row+col" % (T, F), h[0], ROW | COL | ACT, packed=True)
         bw2 = quantize_op("W2[%dx%d] row+col" % (D, F), w2, ROW | COL, packed=True)

@@ -58,6 +58,25 @@ __device__ __forceinline__ void fold_amax(const QuantOpts& o, uint32_t m) {
 // fp32 form of the scaled convert.
 enum { ACT_NONE = 0, ACT_SQRELU = 1, DACT_SQRELU = 2 };
 
+// relu of two BF16 values on their bits: every negative value (-0 included)
+// is a negative signed halfword, so a signed max with 0 (v_pk_max_i16) gives
+// +0 for it and leaves non-negative values unchanged.
+__device__ __forceinline__ uint32_t relu_bf16x2(uint32_t w) {
+  const i16x2 z = {0, 0};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(i16x2, w), z));
+}
+
+// Exact doubling of two non-negative BF16 values on their bits: a normal
+// value gains one in the exponent field (+0x80); a zero or subnormal one
+// (bits < 0x80) doubles its bit pattern, carrying into the exponent field
+// when it becomes normal.  Both cases are bits + min(bits, 0x80).  Values of
+// 2^127 and above overflow to the infinity / NaN patterns, as 2a does in fp32.
+__device__ __forceinline__ uint32_t twice_bf16x2(uint32_t w) {
+  const u16x2 h = __builtin_bit_cast(u16x2, w);
+  const u16x2 c = {0x80, 0x80};
+  return __builtin_bit_cast(uint32_t, h + __builtin_elementwise_min(h, c));
+}
+
 __device__ __forceinline__ float bf_half(uint4 v, int k) {
   const uint32_t d = (k >> 1) == 0 ? v.x : (k >> 1) == 1 ? v.y : (k >> 1) == 2 ? v.z : v.w;
   return (k & 1) ? bf_hi(d) : bf_lo(d);

@@ -271,3 +271,37 @@ def test_activation_noop(flags):
             assert np.all(v == -5.0), k
         else:
             assert np.all(v == -7.0), k
+
+
+def test_dsqrelu_with_subnormal_activation_input():
+    """Subnormal BF16 a under a large gradient gives normal products: 2 relu(a)
+    must be exact for subnormal a too (a doubling that carries into the
+    exponent field included)."""
+    R, C = 128, 128
+    rng = np.random.default_rng(29)
+    a = rng.integers(1, 128, size=(R, C)).astype(np.uint16)          # positive subnormals
+    a[:, ::3] |= 0x8000                                                # some negative ones (relu -> 0)
+    a[::5, :] = 0x007F                                                 # largest subnormal: 2a is normal
+    g = workloads.wide_range_bf16((R, C), 31, u_lo=100, u_hi=120, n_maxbf16=0, n_subnormal=0,
+                                  n_subnormal_blocks=0)
+    v = oracle.dact_sqrelu(g, a)
+    assert np.all(np.abs(v[v != 0]) >= 2.0 ** -126)                   # inside the contract
+    for flags in (ROW | COL | AMAX, ROW | COL | PACKED | DB):
+        got = run_ex(g, flags | DACT, act_bits=a)
+        check_act_result(got, v, flags, "dsqrelu subnormal a")
+
+
+@pytest.mark.slow
+def test_full_mlp_activation_quantize():
+    """The MLP step's two activation launches at full size (8192 x 14336, row +
+    col, packed scales): relu^2 of H, and the backward of dA through H with
+    dbias.  Codes and scale words bit-exact, dbias within its bound, amax exact."""
+    d = workloads.mlp_hidden()
+    h, da = d["H"], d["dA"]
+    log("full mlp relu^2 %s" % (h.shape,))
+    got = run_ex(h, ROW | COL | PACKED | AMAX | ACT)
+    check_act_result(got, oracle.act_sqrelu(h), ROW | COL | PACKED | AMAX, "full relu^2")
+    del got
+    log("full mlp dsqrelu %s" % (h.shape,))
+    got = run_ex(da, ROW | COL | PACKED | DB | DACT, act_bits=h)
+    check_act_result(got, oracle.dact_sqrelu(da, h), ROW | COL | PACKED | DB, "full dsqrelu")

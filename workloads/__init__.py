@@ -152,6 +152,23 @@ def dense_square():
             "B": normal_bf16((8192, 8192), 3, std=0.02)}
 
 
+def mlp():
+    """Squared-ReLU MLP step: tokens 8192, d_model 4096, d_ff 14336.  X and W1
+    are the dense linear layer's tensors; W2 [4096 x 14336] ~ N(0, 0.02);
+    dY [8192 x 4096] ~ N(0, 1)."""
+    d = dense_linear()
+    return {"X": d["X"], "W1": d["W"], "W2": normal_bf16((4096, 14336), 5, std=0.02),
+            "dY": normal_bf16((8192, 4096), 6)}
+
+
+def mlp_hidden():
+    """Stand-ins for the MLP step's BF16 GEMM outputs at full size: H = X W1^T
+    and dA = dY W2 are sums of 4096 (14336) products of N(0,1) and
+    N(0,0.02) values, i.e. N(0, 1.28^2) and N(0, 2.39^2)."""
+    return {"H": normal_bf16((8192, 14336), 7, std=1.28),
+            "dA": normal_bf16((8192, 14336), 8, std=2.39)}
+
+
 def backward():
     return {"dY": student_t_bf16((16384, 4096), 0),
             "X": normal_bf16((16384, 4096), 1)}
