@@ -1,11 +1,11 @@
 """Benchmark of the MXFP8 hot path on one MI355X.
 
 Default workload (the one whose JSON line is the benchmark): the dense linear
-layer.  One step = rowwise MXFP8 quantize of X BF16[8192x4096] ~ N(0,1),
-W BF16[14336x4096] ~ N(0,0.02) and the square A, B BF16[8192x8192], the
-quantizer writing the scales directly in the GEMM's packed word layout, then
-the TN GEMMs 8192x14336x4096 and 8192x8192x8192 with BF16 output.  Inputs are
-resident in HBM before timing starts.  (The backward and MoE workloads keep byte
+layer.  One step = rowwise MXFP8 quantize of X BF16[8192x4096] ~ N(0,1) and
+W BF16[14336x4096] ~ N(0,0.02), the quantizer writing the scales directly in
+the GEMM's packed word layout, the TN GEMM 8192x14336x4096 with BF16 output,
+then the same for the square A, B BF16[8192x8192] and the GEMM
+8192x8192x8192.  Inputs are resident in HBM before timing starts.  (The backward and MoE workloads keep byte
 scales plus the separate packing launch.)
 
 ``value`` is the end-to-end GEMM throughput of the step (GEMM FLOPs / wall
@@ -162,15 +162,16 @@ def build_ops(workload, dev):
     if workload == "dense":
         lin, sq = workloads.dense_linear(), workloads.dense_square()
         host = {"X": lin["X"], "W": lin["W"], "A": sq["A"], "B": sq["B"]}
+        # each GEMM right after the quantize launches that produce its operands
         bx = quantize_op("X[8192x4096]", lin["X"], ROW, packed=True)
         bw = quantize_op("W[14336x4096]", lin["W"], ROW, packed=True)
+        dominant = gemm_op(bx["q"], bx["p"], bw["q"], bw["p"], 8192, 14336, 4096)
         ba = quantize_op("A[8192x8192]", sq["A"], ROW, packed=True)
         bb = quantize_op("B[8192x8192]", sq["B"], ROW, packed=True)
-        dominant = gemm_op(bx["q"], bx["p"], bw["q"], bw["p"], 8192, 14336, 4096)
         gemm_op(ba["q"], ba["p"], bb["q"], bb["p"], 8192, 8192, 8192)
-        desc = ("dense linear layer: rowwise MXFP8 quantize of X[8192x4096], W[14336x4096], A[8192x8192], "
-                "B[8192x8192] writing the packed scale words + TN GEMMs 8192x14336x4096 and 8192x8192x8192, "
-                "BF16 out")
+        desc = ("dense linear layer: rowwise MXFP8 quantize of X[8192x4096] and W[14336x4096] writing the packed "
+                "scale words, TN GEMM 8192x14336x4096; the same for A[8192x8192], B[8192x8192] and the TN GEMM "
+                "8192x8192x8192; BF16 out")
     elif workload == "backward":
         d = workloads.backward()
         bd = quantize_op("dY[16384x4096] row+col+dbias", d["dY"], ROW | COL | DB)

@@ -467,7 +467,7 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
 // the scales [rows][cols/32] are the flat block index.  Each wave quantizes
 // FL_ELEMS contiguous elements: load u of lane l covers elements
 // 512u + 8l + [0, 8), i.e. every load instruction reads 1 KB contiguous, each
-// DPP quad holds one block, codes go out (non-temporally) as 512-byte runs and
+// DPP quad holds one block, codes go out as 512-byte runs and
 // the wave's 32 scale bytes are contiguous.  Two loads per lane measured best
 // (more waves in flight than with four or eight).
 constexpr int FL_THREADS = 256;
@@ -499,7 +499,7 @@ __global__ __launch_bounds__(FL_THREADS) void quantize_rowwise_flat_kernel(const
     const uint32_t byte = scale_byte_from_amax(m);
     const uint2 o = quantize8(v[u], byte);
     if (e < total) {  // total % 32 == 0: a quad is entirely in or out
-      store_nt8(q + e, o);
+      *reinterpret_cast<uint2*>(q + e) = o;
       if ((lane & 3) == 0) s[e >> 5] = (uint8_t)byte;
     }
   }
@@ -553,7 +553,7 @@ __global__ __launch_bounds__(256) void quantize_rowwise_packed_kernel(const uint
     lane_amax = max(lane_amax, m);
     const uint32_t byte = scale_byte_from_amax(m);
     const uint2 o = quantize8(v[u], byte);
-    if (cval && r < R) store_nt8(q + r * C + col, o);
+    if (cval && r < R) *reinterpret_cast<uint2*>(q + r * C + col) = o;
     // lane 16k + 4b holds block b of slab k
     if ((lane & 3) == 0) lds_s[((2 * w + u) * 4 + (lane >> 4)) * 4 + ((lane >> 2) & 3)] = (uint8_t)byte;
   }
@@ -612,17 +612,18 @@ int64_t quantize_row_tiles(int64_t R) { return (R + QT_R_MIN - 1) / QT_R_MIN; }
 int64_t quantize_col_tiles(int64_t C) { return (C + QT_C - 1) / QT_C; }
 
 // Tile configuration per copy set (measured on MI355X with the stress,
-// backward and columnwise-only shapes): 8 waves with non-temporal rowwise
-// codes and cached transposed codes when both copies are written; 4 waves with
-// non-temporal transposed codes for the columnwise copy alone.
+// backward and columnwise-only shapes): 8 waves when the rowwise copy is
+// written, 4 for the columnwise copy alone.  Codes are written with cached
+// stores: non-temporal ones made the quantize launch alone slightly faster,
+// but cached codes make the GEMM that reads them next faster by more.
 template <bool ROW, bool COL, bool DBIAS, int ACT>
 static hipError_t launch_tiles(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q_row,
                                uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT, float* dbias_part,
                                const QuantOpts& opt, const uint16_t* act_in, int64_t* row_tiles,
                                hipStream_t stream) {
   constexpr int QW = (ROW || !COL) ? 8 : 4;
-  constexpr bool NT_QROW = true;
-  constexpr bool NT_COLT = !ROW;
+  constexpr bool NT_QROW = false;
+  constexpr bool NT_COLT = false;
   const int64_t tr = (R + 32 * QW - 1) / (32 * QW);
   const int64_t tc = quantize_col_tiles(C);
   *row_tiles = tr;
