@@ -533,3 +533,23 @@ def test_dbias_values_rounded_once():
     v = np.full((4096, 32), np.float32(1.0) + np.float32(2.0 ** -23), dtype=np.float32)
     want = np.float32(4096 * (1.0 + 2.0 ** -23))
     assert np.all(oracle.dbias_values(v) == want)
+
+
+def test_golden_e8m0_readback():
+    """tests/golden/e8m0_readback.txt: the page's byte << 23 readback for a
+    few bytes, and its rule that an all-zero block gets scale byte 0."""
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "e8m0_readback.txt")
+    rows = [l.split() for l in open(path) if l.strip() and not l.startswith("#")]
+    checked = 0
+    for r in rows:
+        if r[0] == "zero_block_byte":
+            q, s = oracle.quantize_rowwise(np.zeros((2, 64), dtype=np.uint16))
+            assert np.all(s == int(r[1])) and not q.any()
+            checked += 1
+            continue
+        b, bits = int(r[0]), int(r[1], 16)
+        assert bits == b << 23
+        assert oracle.e8m0_decode(b) == float(np.array([bits], dtype=np.uint32).view(np.float32)[0])
+        checked += 1
+    assert checked == 8
