@@ -11,14 +11,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 
-// Streaming (non-temporal) global stores for data written once.
+// Streaming (non-temporal) global store for data nothing reads soon (the
+// GEMM's output tile).
 __device__ __forceinline__ void store_nt16(void* p, uint4 d) {
   const u32x4 v = {d.x, d.y, d.z, d.w};
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-}
-__device__ __forceinline__ void store_nt8(void* p, uint2 d) {
-  __builtin_nontemporal_store(d.x, reinterpret_cast<uint32_t*>(p));
-  __builtin_nontemporal_store(d.y, reinterpret_cast<uint32_t*>(p) + 1);
 }
 
 // Packed per-halfword unsigned max / min (v_pk_max_u16 / v_pk_min_u16).

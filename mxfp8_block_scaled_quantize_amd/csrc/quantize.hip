@@ -107,7 +107,7 @@ __device__ __forceinline__ uint32_t cvt4_scaled_f32(float a, float b, float c, f
 constexpr int QT_C = 128;            // tile columns
 constexpr int QT_R_MIN = 128;        // rows of the smallest tile (4 waves)
 
-template <bool ROW, bool COL, bool DBIAS, int QW, bool NT_QROW, bool NT_COLT, int ACT>
+template <bool ROW, bool COL, bool DBIAS, int QW, int ACT>
 __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
     const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
     uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
@@ -207,10 +207,7 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
         o.x = cvt4_scaled_f32(f[0], f[1], f[2], f[3], byte);
         o.y = cvt4_scaled_f32(f[4], f[5], f[6], f[7], byte);
         const int64_t r = rb + i;
-        if (cval && r < R) {
-          if (NT_QROW) store_nt8(q_row + r * C + cb, o);
-          else *reinterpret_cast<uint2*>(q_row + r * C + cb) = o;
-        }
+        if (cval && r < R) *reinterpret_cast<uint2*>(q_row + r * C + cb) = o;
         if ((cg & 3) == 0) lds_sr[(32 * w + 8 * rg + i) * 4 + (cg >> 2)] = (uint8_t)byte;
       }
     }
@@ -293,10 +290,7 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
       const uint32_t byte = scale_byte_from_amax(m);
       const uint2 o = quantize8(v[i], byte);
       const int64_t r = rb + i;
-      if (cval && r < R) {
-        if (NT_QROW) store_nt8(q_row + r * C + cb, o);
-        else *reinterpret_cast<uint2*>(q_row + r * C + cb) = o;
-      }
+      if (cval && r < R) *reinterpret_cast<uint2*>(q_row + r * C + cb) = o;
       if ((cg & 3) == 0) lds_sr[(32 * w + 8 * rg + i) * 4 + (cg >> 2)] = (uint8_t)byte;
     }
   }
@@ -393,10 +387,7 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
       const uint4 d = *reinterpret_cast<const uint4*>(lds_t + cl * TR + 8 * ((2 * ch) ^ swz));
       const int64_t col = c0 + cl;
       const int64_t row = r0 + 16 * ch;
-      if (col < C && row < R) {
-        if (NT_COLT) store_nt16(q_colT + col * R + row, d);
-        else *reinterpret_cast<uint4*>(q_colT + col * R + row) = d;
-      }
+      if (col < C && row < R) *reinterpret_cast<uint4*>(q_colT + col * R + row) = d;
     }
     // The QW scale bytes of a column: QW consecutive row blocks of s_colT
     // (packed layout: QW / 4 words (t, col), t = 128-row slab, R % 128 == 0).
@@ -622,13 +613,11 @@ static hipError_t launch_tiles(const uint16_t* x, int64_t R, int64_t C, int64_t 
                                const QuantOpts& opt, const uint16_t* act_in, int64_t* row_tiles,
                                hipStream_t stream) {
   constexpr int QW = (ROW || !COL) ? 8 : 4;
-  constexpr bool NT_QROW = false;
-  constexpr bool NT_COLT = false;
   const int64_t tr = (R + 32 * QW - 1) / (32 * QW);
   const int64_t tc = quantize_col_tiles(C);
   *row_tiles = tr;
   if (tr * tc == 0) return hipSuccess;
-  hipLaunchKernelGGL((quantize_tile_kernel<ROW, COL, DBIAS, QW, NT_QROW, NT_COLT, ACT>), dim3((unsigned)(tr * tc)),
+  hipLaunchKernelGGL((quantize_tile_kernel<ROW, COL, DBIAS, QW, ACT>), dim3((unsigned)(tr * tc)),
                      dim3(64 * QW), 0, stream, x, R, C, ldx, q_row, s_row, q_colT, s_colT, dbias_part, tc, opt,
                      act_in);
   return hipGetLastError();
