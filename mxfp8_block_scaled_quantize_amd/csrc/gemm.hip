@@ -384,8 +384,10 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
     const bool odd = lane & 1;
     const int rb = wm * 128 + 4 * lg;
     const int cb = wn * 128 + lr - (odd ? 1 : 0);
-    const uint32_t send_shift = odd ? 0u : 16u;                   // odd sends row R, even sends row R+1
-    const uint32_t sel = odd ? 0x03020504u : 0x05040100u;         // (partner, own) halves -> word
+    // Each lane sends its whole packed pair; the even lane keeps the low
+    // halves (row R) of its and its partner's word, the odd lane the high
+    // halves (row R+1): one byte permute, no rotation.
+    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
 #pragma unroll
@@ -401,18 +403,17 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
             // columns c, c+1; the partner holds the other row.  Trade halves
             // the same way as below so each lane gets rows R, R+1 of its column.
             const uint32_t w_old = *slot_word;
-            const uint32_t y_old =
-                (uint32_t)__builtin_amdgcn_mov_dpp((int)__builtin_amdgcn_alignbit(w_old, w_old, send_shift), 0xB1,
-                                                   0xF, 0xF, true);
-            const uint32_t c_r = odd ? y_old : w_old;                 // row R of this column in the low half
+            const uint32_t y_old = (uint32_t)__builtin_amdgcn_mov_dpp((int)w_old, 0xB1, 0xF, 0xF, true);
+            // even lane: own word is row R, partner's row R+1 (its column in the low halves);
+            // odd lane: partner's word is row R, own row R+1 (its column in the high halves)
+            const uint32_t c_r = odd ? (y_old >> 16) : w_old;          // row R of this column in the low half
             const uint32_t c_r1 = odd ? (w_old >> 16) : y_old;         // row R+1 of this column in the low half
             v0 += __uint_as_float(c_r << 16);
             v1 += __uint_as_float(c_r1 << 16);
           }
           const bf16x2 h = {(__bf16)v0, (__bf16)v1};
           const uint32_t pk = __builtin_bit_cast(uint32_t, h);   // row R low, row R+1 high
-          const uint32_t send = __builtin_amdgcn_alignbit(pk, pk, send_shift);
-          const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, true);  // lane ^ 1
+          const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)pk, 0xB1, 0xF, 0xF, true);  // lane ^ 1
           *slot_word = __builtin_amdgcn_perm(y, pk, sel);
         }
       __builtin_amdgcn_sched_barrier(0);   // bounds the registers the batched AGPR reads take
