@@ -177,7 +177,10 @@ def quantize(x, rowwise=True, colwise=False, dbias=False, amax=False, packed=Fal
     x * 2 relu(act_in) (x is the gradient, act_in the activation's input, a
     BF16 tensor of x's shape and strides)."""
     import torch
-    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a BF16 [rows, cols] tensor with unit column stride")
+    if x.device.type != "cuda":
+        raise ValueError("x must be a CUDA (HIP) tensor, got %s" % x.device)
     R, C = x.shape
     dev = x.device
     flags = (MXFP8_ROWWISE if rowwise else 0) | (MXFP8_COLWISE if colwise else 0) | (MXFP8_DBIAS if dbias else 0)
@@ -185,8 +188,9 @@ def quantize(x, rowwise=True, colwise=False, dbias=False, amax=False, packed=Fal
     if act == "sqrelu":
         flags |= MXFP8_ACT_SQRELU
     elif act == "dsqrelu":
-        assert act_in is not None and act_in.dtype == torch.bfloat16 and act_in.shape == x.shape
-        assert act_in.stride() == x.stride() and act_in.device == x.device
+        if (act_in is None or act_in.dtype != torch.bfloat16 or act_in.shape != x.shape
+                or act_in.stride() != x.stride() or act_in.device != x.device):
+            raise ValueError("act='dsqrelu' needs act_in: a BF16 tensor with x's shape, strides and device")
         flags |= MXFP8_DACT_SQRELU
     elif act is not None:
         raise ValueError("act must be None, 'sqrelu' or 'dsqrelu'")
@@ -213,22 +217,44 @@ def quantize(x, rowwise=True, colwise=False, dbias=False, amax=False, packed=Fal
         ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
     s_row = out.get("p_row") if packed else out.get("s_row")
     s_col = out.get("p_colT") if packed else out.get("s_colT")
-    if amax or packed or noop is not None or act is not None:
-        mxfp8_quantize_ex(x, R, C, x.stride(0), flags, out.get("q_row"), s_row, out.get("q_colT"), s_col,
-                          out.get("dbias"), out.get("amax"), noop, act_in, ws, nws, stream)
-    else:
-        mxfp8_quantize(x, R, C, x.stride(0), flags, out.get("q_row"), s_row, out.get("q_colT"), s_col,
-                       out.get("dbias"), ws, nws, stream)
+    with torch.cuda.device(dev):
+        if amax or packed or noop is not None or act is not None:
+            mxfp8_quantize_ex(x, R, C, x.stride(0), flags, out.get("q_row"), s_row, out.get("q_colT"), s_col,
+                              out.get("dbias"), out.get("amax"), noop, act_in, ws, nws, stream)
+        else:
+            mxfp8_quantize(x, R, C, x.stride(0), flags, out.get("q_row"), s_row, out.get("q_colT"), s_col,
+                           out.get("dbias"), ws, nws, stream)
     return out
+
+
+def _require(t, name, dtype, shape=None, device=None):
+    """Host-side checks of a tensor handed to the C ABI as a dense array."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a CUDA (HIP) tensor, got %s" % (name, t.device))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
 
 
 def pack_scales(s, stream=None):
     """E8M0 scales uint8 [dim, K/32] -> packed int32 words [K/128, dim]."""
     import torch
-    assert s.dtype == torch.uint8 and s.dim() == 2 and s.stride(1) == 1
+    if not isinstance(s, torch.Tensor) or s.dtype != torch.uint8 or s.dim() != 2 or s.stride(1) != 1:
+        raise ValueError("s must be a uint8 [dim, K/32] tensor with unit column stride")
+    if s.device.type != "cuda":
+        raise ValueError("s must be a CUDA (HIP) tensor, got %s" % s.device)
     dim, kb = s.shape
     out = torch.empty((kb // 4, dim), dtype=torch.int32, device=s.device)
-    mxfp8_pack_scales(s, dim, kb * 32, s.stride(0), out, stream)
+    with torch.cuda.device(s.device):
+        mxfp8_pack_scales(s, dim, kb * 32, s.stride(0), out, stream)
     return out
 
 
@@ -236,25 +262,45 @@ def gemm(a, a_packed, b, b_packed, out=None, accumulate=False, stream=None):
     """C = dq(A) dq(B)^T in BF16 for E4M3 codes a [M, K], b [N, K]; with
     accumulate=True the product is added to `out` (beta = 1)."""
     import torch
+    if not isinstance(a, torch.Tensor) or a.dim() != 2 or not isinstance(b, torch.Tensor) or b.dim() != 2:
+        raise ValueError("a and b must be 2-D tensors of E4M3 codes")
     M, K = a.shape
     N = b.shape[0]
+    dev = a.device
+    _require(a, "a", torch.uint8)
+    _require(b, "b", torch.uint8, (N, K), dev)
+    _require(a_packed, "a_packed", torch.int32, (K // 128, M), dev)
+    _require(b_packed, "b_packed", torch.int32, (K // 128, N), dev)
     if accumulate and out is None:
         raise ValueError("accumulate=True needs out")
-    c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
-    assert c.dtype == torch.bfloat16 and c.shape == (M, N) and c.stride(1) == 1
-    mxfp8_gemm_ex(a, a_packed, b, b_packed, c, c.stride(0), M, N, K, MXFP8_GEMM_ACCUMULATE if accumulate else 0,
-                  stream)
+    c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if c.dtype != torch.bfloat16 or tuple(c.shape) != (M, N) or c.stride(1) != 1 or c.device != dev:
+        raise ValueError("out must be a BF16 [M, N] tensor with unit column stride on the operands' device")
+    with torch.cuda.device(dev):
+        mxfp8_gemm_ex(a, a_packed, b, b_packed, c, c.stride(0), M, N, K,
+                      MXFP8_GEMM_ACCUMULATE if accumulate else 0, stream)
     return c
 
 
 def grouped_gemm(a, a_packed, b, b_packed, offsets, out=None, accumulate=False, stream=None):
     """Ragged grouped GEMM; b is [G, N, K]; rows outside every group keep `out`'s values."""
     import torch
+    if not isinstance(a, torch.Tensor) or a.dim() != 2 or not isinstance(b, torch.Tensor) or b.dim() != 3:
+        raise ValueError("a must be 2-D [M, K] and b 3-D [G, N, K] tensors of E4M3 codes")
     M, K = a.shape
     G, N, _ = b.shape
+    dev = a.device
+    _require(a, "a", torch.uint8)
+    _require(b, "b", torch.uint8, (G, N, K), dev)
+    _require(a_packed, "a_packed", torch.int32, (K // 128, M), dev)
+    _require(b_packed, "b_packed", torch.int32, (K // 128, G * N), dev)
+    _require(offsets, "offsets", torch.int32, (G + 1,), dev)
     if accumulate and out is None:
         raise ValueError("accumulate=True needs out")
-    c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
-    mxfp8_grouped_gemm_ex(a, a_packed, b, b_packed, offsets, G, c, c.stride(0), M, N, K,
-                          MXFP8_GEMM_ACCUMULATE if accumulate else 0, stream)
+    c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if c.dtype != torch.bfloat16 or tuple(c.shape) != (M, N) or c.stride(1) != 1 or c.device != dev:
+        raise ValueError("out must be a BF16 [M, N] tensor with unit column stride on the operands' device")
+    with torch.cuda.device(dev):
+        mxfp8_grouped_gemm_ex(a, a_packed, b, b_packed, offsets, G, c, c.stride(0), M, N, K,
+                              MXFP8_GEMM_ACCUMULATE if accumulate else 0, stream)
     return c

@@ -31,6 +31,8 @@
 // resident on one XCD (ids are dealt round-robin to the 8 XCDs) form groups of
 // 4 tiles sharing A and B in that XCD's L2, with the XCDs splitting the larger
 // of M and N.
+#include <atomic>
+
 #include "mx_device.h"
 #include "launch.h"
 
@@ -448,12 +450,19 @@ template <bool GROUPED, bool ACC>
 static hipError_t launch_gemm_t(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
                                 uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, const int32_t* offsets,
                                 int32_t G, int64_t tiles_m, int64_t tiles_n, hipStream_t stream) {
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<GROUPED, ACC>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  // The dynamic-LDS opt-in is set once per device (bit d of the mask, for
+  // device ids below 64; others set it on every launch), race-free across
+  // host threads.
+  static std::atomic<uint64_t> attr_done{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<GROUPED, ACC>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (e != hipSuccess) return e;
-    attr_done = true;
+    attr_done.fetch_or(bit, std::memory_order_release);
   }
   hipLaunchKernelGGL((gemm_kernel<GROUPED, ACC>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), LDS_BYTES, stream,
                      a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n);

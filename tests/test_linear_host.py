@@ -21,3 +21,29 @@ def test_rejects_non_bf16_and_mismatched_weight():
     with pytest.raises(ValueError):
         MXFP8LinearFunction.apply(torch.zeros((128, 128), dtype=torch.bfloat16),
                                   torch.zeros((128, 256), dtype=torch.bfloat16), False)
+
+
+def test_helpers_reject_bad_tensors_before_any_launch():
+    """The allocating helpers check dtype, shape, contiguity and device on the
+    host (CPU tensors are refused before the library is called)."""
+    import pytest
+    import torch
+
+    import mxfp8_block_scaled_quantize_amd as mx
+    x = torch.zeros((64, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="CUDA"):
+        mx.quantize(x)
+    with pytest.raises(ValueError, match="BF16"):
+        mx.quantize(x.float())
+    with pytest.raises(ValueError, match="unit column stride"):
+        mx.quantize(torch.zeros((64, 128), dtype=torch.bfloat16)[:, ::2])
+    a = torch.zeros((64, 128), dtype=torch.uint8)
+    p = torch.zeros((1, 64), dtype=torch.int32)
+    with pytest.raises(ValueError, match="CUDA"):
+        mx.gemm(a, p, a, p)
+    with pytest.raises(ValueError, match="2-D"):
+        mx.gemm(a[0], p, a, p)
+    with pytest.raises(ValueError, match="CUDA"):
+        mx.grouped_gemm(a, p, a.reshape(1, 64, 128), p, torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="uint8"):
+        mx.pack_scales(torch.zeros((64, 4), dtype=torch.int32))
