@@ -366,3 +366,29 @@ def test_full_linear_wgrad_accumulate_sampled():
     oqb, osb = oracle.quantize_colwise(x)
     ref = oracle.gemm_tn(oqa, osa, oqb, osb, rows=rows, cols=cols) + bf16_to_f64(c_old[np.ix_(rows, cols)])
     gemm_tolerance_check(to_host(cd)[np.ix_(rows, cols)], ref, 8192, label="wgrad accumulate")
+
+
+def test_side_stream_pipeline_matches_default_stream():
+    """The whole path (quantize into packed scales, GEMM) enqueued on a
+    non-default stream, ordered after the input upload by an event, gives the
+    same bytes as on the default stream: every launch goes to the stream it is
+    given."""
+    torch = need_gpu()
+    a = workloads.normal_bf16((512, 640), 41)
+    b = workloads.normal_bf16((384, 640), 42, std=0.05)
+    xa, xb = to_dev_bf16(a), to_dev_bf16(b)
+    ref_qa = mx.quantize(xa, packed=True)
+    ref_qb = mx.quantize(xb, packed=True)
+    ref = mx.gemm(ref_qa["q_row"], ref_qa["p_row"], ref_qb["q_row"], ref_qb["p_row"])
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    ready = torch.cuda.Event()
+    ready.record(torch.cuda.current_stream())
+    side.wait_event(ready)
+    with torch.cuda.stream(side):
+        qa = mx.quantize(xa, packed=True, stream=side)
+        qb = mx.quantize(xb, packed=True, stream=side)
+        c = mx.gemm(qa["q_row"], qa["p_row"], qb["q_row"], qb["p_row"], stream=side)
+    side.synchronize()
+    assert torch.equal(qa["q_row"], ref_qa["q_row"]) and torch.equal(qa["p_row"], ref_qa["p_row"])
+    assert torch.equal(c.view(torch.int16), ref.view(torch.int16))
