@@ -15,9 +15,10 @@ with HIP events recorded on its launch stream; ``quantize`` reports each
 quantizer launch against the HBM peak; ``cpu_baseline`` is the CPU oracle on
 the same work.
 
-``--workload backward|moe|stress|linear|mlp`` measures the other workloads
-the same way: row+col+dbias quantize and the wgrad GEMM on the columnwise
-copies; the ragged grouped MoE GEMM; the wide-range 32768x8192x8192 GEMM; one
+``--workload backward|moe|moe_sqrelu|stress|linear|mlp`` measures the other
+workloads the same way: row+col+dbias quantize and the wgrad GEMM on the
+columnwise copies; the ragged grouped MoE GEMM (also with the squared-ReLU
+epilogue of an MoE first projection); the wide-range 32768x8192x8192 GEMM; one
 MXFP8 linear-layer training step (fprop, dgrad, wgrad accumulated into a BF16
 main gradient); one squared-ReLU MLP training step (six GEMMs, the activation
 and its backward fused into the quantize launches).  They are reporting aids
@@ -43,7 +44,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="dense", choices=["dense", "backward", "moe", "stress", "linear", "mlp"])
+    p.add_argument("--workload", default="dense", choices=["dense", "backward", "moe", "moe_sqrelu", "stress", "linear", "mlp"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU-oracle time: whole oracle steps are repeated until reached")
@@ -225,6 +226,23 @@ def build_ops(workload, dev):
                 "W2 N(0,0.02), dY N(0,1); row+col quantize of X, W1, W2, dY; FC1 GEMM; relu^2 fused into the "
                 "quantize of its BF16 output; FC2 GEMM; FC2 dgrad and wgrad; the activation's backward fused "
                 "into the row+col+dbias quantize of FC2's dgrad output; FC1 dgrad and wgrad" % (T, D, F))
+    elif workload == "moe_sqrelu":
+        d = workloads.moe()
+        G, N, K = d["W"].shape
+        Mt = d["X"].shape[0]
+        bx = quantize_op("X[%dx%d]" % (Mt, K), d["X"], ROW, packed=True)
+        bw = quantize_op("W[%dx%dx%d]" % (G, N, K), d["W"].reshape(G * N, K), ROW, packed=True)
+        off = torch.from_numpy(d["offsets"]).to(dev)
+        c = torch.empty((Mt, N), dtype=torch.bfloat16, device=dev)
+        keep.extend([c, off])
+        tokens = int(d["offsets"][-1] - d["offsets"][0])
+        dominant = "grouped relu^2 %dx%dx%d G=%d" % (Mt, N, K, G)
+        ops.append(Op("gemm", dominant, lambda st: mx.mxfp8_grouped_gemm_ex(
+            bx["q"], bx["p"], bw["q"], bw["p"], off, G, c, N, Mt, N, K, mx.MXFP8_GEMM_SQRELU, stream=st),
+            2.0 * tokens * N * K))
+        desc = ("MoE first projection with the squared-ReLU epilogue: X[%dx%d] and W[%d][%dx%d] rowwise into "
+                "packed scales, ragged grouped GEMM over %d experts (token counts %s) writing relu(XW^T)^2"
+                % (Mt, K, G, N, K, G, np.diff(d["offsets"]).tolist()))
     else:  # moe
         d = workloads.moe()
         G, N, K = d["W"].shape

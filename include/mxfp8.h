@@ -229,18 +229,26 @@ mxfp8_status mxfp8_gemm(const uint8_t *a, const uint32_t *a_packed,
                         void *c, int64_t ldc,
                         int64_t M, int64_t N, int64_t K, void *stream);
 
-/* Flags of mxfp8_gemm_ex / mxfp8_grouped_gemm_ex. */
+/* Flags of mxfp8_gemm_ex / mxfp8_grouped_gemm_ex (at most one of them). */
 #define MXFP8_GEMM_ACCUMULATE 1u /* C = bf16_rne( float(C) + sum_k dq(A) dq(B) ): beta = 1 */
+#define MXFP8_GEMM_SQRELU 2u     /* C = bf16_rne( relu(acc)^2 ), acc = the fp32 sum and
+                                    relu(acc)^2 formed in fp32: the squared-ReLU
+                                    epilogue of an MLP's first projection */
 
 /*
  * mxfp8_gemm with options.  Defining passage: the accumulate option that the
  * FlyDSL backend still rejects (wgrad accumulation into an existing gradient,
  * "Experimental FlyDSL GEMM backend for TE PyTorch (BF16/FP16/FP32/FP8/MXFP8)",
  * review of the epilogue validation and of the fallback exceptions).
- * flags   0 or MXFP8_GEMM_ACCUMULATE.  With ACCUMULATE, C is read and the sum
- *         is rounded once (fp32 accumulator + the old BF16 value, then BF16
- *         round-to-nearest-even); K == 0 leaves C unchanged.
- * Other arguments and errors as mxfp8_gemm; unknown flag bits -> FLAGS.
+ * flags   0, MXFP8_GEMM_ACCUMULATE or MXFP8_GEMM_SQRELU.  With ACCUMULATE, C
+ *         is read and the sum is rounded once (fp32 accumulator + the old BF16
+ *         value, then BF16 round-to-nearest-even); K == 0 leaves C unchanged.
+ *         With SQRELU the fp32 accumulator goes through relu(v)^2 before the
+ *         BF16 rounding (the FC1 "squared_relu" epilogue of "gemm(cutedsl):
+ *         add standalone Lightning W4A16 grouped GEMM - #811", section "API
+ *         and compatibility impact"); K == 0 writes zeros.
+ * Other arguments and errors as mxfp8_gemm; unknown flag bits or both flags
+ * -> FLAGS.
  * mxfp8_gemm(...) is mxfp8_gemm_ex(..., 0, stream).
  */
 mxfp8_status mxfp8_gemm_ex(const uint8_t *a, const uint32_t *a_packed,

@@ -27,6 +27,7 @@ MXFP8_PACKED_SCALES = 16
 MXFP8_ACT_SQRELU = 32
 MXFP8_DACT_SQRELU = 64
 MXFP8_GEMM_ACCUMULATE = 1
+MXFP8_GEMM_SQRELU = 2
 
 STATUS_NAMES = {0: "MXFP8_OK", 1: "MXFP8_ERR_NULL", 2: "MXFP8_ERR_SHAPE", 3: "MXFP8_ERR_MISALIGNED",
                 4: "MXFP8_ERR_FLAGS", 5: "MXFP8_ERR_WORKSPACE", 6: "MXFP8_ERR_HIP", 7: "MXFP8_ERR_LIMIT"}
@@ -258,9 +259,10 @@ def pack_scales(s, stream=None):
     return out
 
 
-def gemm(a, a_packed, b, b_packed, out=None, accumulate=False, stream=None):
+def gemm(a, a_packed, b, b_packed, out=None, accumulate=False, sqrelu=False, stream=None):
     """C = dq(A) dq(B)^T in BF16 for E4M3 codes a [M, K], b [N, K]; with
-    accumulate=True the product is added to `out` (beta = 1)."""
+    accumulate=True the product is added to `out` (beta = 1); with
+    sqrelu=True C = relu(product)^2 (formed in fp32, rounded once)."""
     import torch
     if not isinstance(a, torch.Tensor) or a.dim() != 2 or not isinstance(b, torch.Tensor) or b.dim() != 2:
         raise ValueError("a and b must be 2-D tensors of E4M3 codes")
@@ -276,14 +278,15 @@ def gemm(a, a_packed, b, b_packed, out=None, accumulate=False, stream=None):
     c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     if c.dtype != torch.bfloat16 or tuple(c.shape) != (M, N) or c.stride(1) != 1 or c.device != dev:
         raise ValueError("out must be a BF16 [M, N] tensor with unit column stride on the operands' device")
+    flags = (MXFP8_GEMM_ACCUMULATE if accumulate else 0) | (MXFP8_GEMM_SQRELU if sqrelu else 0)
     with torch.cuda.device(dev):
-        mxfp8_gemm_ex(a, a_packed, b, b_packed, c, c.stride(0), M, N, K,
-                      MXFP8_GEMM_ACCUMULATE if accumulate else 0, stream)
+        mxfp8_gemm_ex(a, a_packed, b, b_packed, c, c.stride(0), M, N, K, flags, stream)
     return c
 
 
-def grouped_gemm(a, a_packed, b, b_packed, offsets, out=None, accumulate=False, stream=None):
-    """Ragged grouped GEMM; b is [G, N, K]; rows outside every group keep `out`'s values."""
+def grouped_gemm(a, a_packed, b, b_packed, offsets, out=None, accumulate=False, sqrelu=False, stream=None):
+    """Ragged grouped GEMM; b is [G, N, K]; rows outside every group keep `out`'s values;
+    sqrelu=True writes relu(product)^2 (an MoE block's first projection)."""
     import torch
     if not isinstance(a, torch.Tensor) or a.dim() != 2 or not isinstance(b, torch.Tensor) or b.dim() != 3:
         raise ValueError("a must be 2-D [M, K] and b 3-D [G, N, K] tensors of E4M3 codes")
@@ -300,7 +303,7 @@ def grouped_gemm(a, a_packed, b, b_packed, offsets, out=None, accumulate=False, 
     c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     if c.dtype != torch.bfloat16 or tuple(c.shape) != (M, N) or c.stride(1) != 1 or c.device != dev:
         raise ValueError("out must be a BF16 [M, N] tensor with unit column stride on the operands' device")
+    flags = (MXFP8_GEMM_ACCUMULATE if accumulate else 0) | (MXFP8_GEMM_SQRELU if sqrelu else 0)
     with torch.cuda.device(dev):
-        mxfp8_grouped_gemm_ex(a, a_packed, b, b_packed, offsets, G, c, c.stride(0), M, N, K,
-                              MXFP8_GEMM_ACCUMULATE if accumulate else 0, stream)
+        mxfp8_grouped_gemm_ex(a, a_packed, b, b_packed, offsets, G, c, c.stride(0), M, N, K, flags, stream)
     return c

@@ -147,13 +147,15 @@ mxfp8_status mxfp8_pack_scales(const uint8_t* s, int64_t dim, int64_t k, int64_t
 
 mxfp8_status mxfp8_gemm_ex(const uint8_t* a, const uint32_t* a_packed, const uint8_t* b, const uint32_t* b_packed,
                            void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, uint32_t flags, void* stream) {
-  if (flags & ~MXFP8_GEMM_ACCUMULATE) return MXFP8_ERR_FLAGS;
+  if (flags & ~(MXFP8_GEMM_ACCUMULATE | MXFP8_GEMM_SQRELU)) return MXFP8_ERR_FLAGS;
+  if ((flags & MXFP8_GEMM_ACCUMULATE) && (flags & MXFP8_GEMM_SQRELU)) return MXFP8_ERR_FLAGS;
   const mxfp8_status st = check_gemm_common(a, a_packed, b, b_packed, c, ldc, M, N, K);
   if (st != MXFP8_OK) return st;
   if (M == 0 || N == 0) return MXFP8_OK;
   if (mx::gemm_blocks(M, N, 0, false) > kMaxGrid) return MXFP8_ERR_LIMIT;
   return hip_status(mx::launch_gemm(a, a_packed, b, b_packed, static_cast<uint16_t*>(c), ldc, M, N, K, nullptr, 0,
-                                    (flags & MXFP8_GEMM_ACCUMULATE) != 0, static_cast<hipStream_t>(stream)));
+                                    (flags & MXFP8_GEMM_ACCUMULATE) != 0, (flags & MXFP8_GEMM_SQRELU) != 0,
+                                    static_cast<hipStream_t>(stream)));
 }
 
 mxfp8_status mxfp8_gemm(const uint8_t* a, const uint32_t* a_packed, const uint8_t* b, const uint32_t* b_packed,
@@ -164,7 +166,8 @@ mxfp8_status mxfp8_gemm(const uint8_t* a, const uint32_t* a_packed, const uint8_
 mxfp8_status mxfp8_grouped_gemm_ex(const uint8_t* a, const uint32_t* a_packed, const uint8_t* b,
                                    const uint32_t* b_packed, const int32_t* offsets, int32_t G, void* c, int64_t ldc,
                                    int64_t M_total, int64_t N, int64_t K, uint32_t flags, void* stream) {
-  if (flags & ~MXFP8_GEMM_ACCUMULATE) return MXFP8_ERR_FLAGS;
+  if (flags & ~(MXFP8_GEMM_ACCUMULATE | MXFP8_GEMM_SQRELU)) return MXFP8_ERR_FLAGS;
+  if ((flags & MXFP8_GEMM_ACCUMULATE) && (flags & MXFP8_GEMM_SQRELU)) return MXFP8_ERR_FLAGS;
   if (G < 1 || G > 65536) return MXFP8_ERR_SHAPE;
   const mxfp8_status st = check_gemm_common(a, a_packed, b, b_packed, c, ldc, M_total, N, K);
   if (st != MXFP8_OK) return st;
@@ -174,7 +177,7 @@ mxfp8_status mxfp8_grouped_gemm_ex(const uint8_t* a, const uint32_t* a_packed, c
   if (mx::gemm_blocks(M_total, N, G, true) > kMaxGrid) return MXFP8_ERR_LIMIT;
   return hip_status(mx::launch_gemm(a, a_packed, b, b_packed, static_cast<uint16_t*>(c), ldc, M_total, N, K,
                                     offsets, G, (flags & MXFP8_GEMM_ACCUMULATE) != 0,
-                                    static_cast<hipStream_t>(stream)));
+                                    (flags & MXFP8_GEMM_SQRELU) != 0, static_cast<hipStream_t>(stream)));
 }
 
 mxfp8_status mxfp8_grouped_gemm(const uint8_t* a, const uint32_t* a_packed, const uint8_t* b,

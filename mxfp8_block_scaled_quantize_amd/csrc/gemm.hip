@@ -81,7 +81,7 @@ struct ic {
   static constexpr int value = V;
 };
 
-template <bool GROUPED, bool ACC>
+template <bool GROUPED, bool ACC, bool SQRELU>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
                  const uint8_t* __restrict__ B, const uint32_t* __restrict__ Bp,
@@ -413,6 +413,12 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
             v0 += __uint_as_float(c_r << 16);
             v1 += __uint_as_float(c_r1 << 16);
           }
+          if (SQRELU) {   // relu(acc)^2 in fp32, then the one BF16 rounding
+            v0 = fmaxf(v0, 0.0f);
+            v1 = fmaxf(v1, 0.0f);
+            v0 *= v0;
+            v1 *= v1;
+          }
           const bf16x2 h = {(__bf16)v0, (__bf16)v1};
           const uint32_t pk = __builtin_bit_cast(uint32_t, h);   // row R low, row R+1 high
           const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)pk, 0xB1, 0xF, 0xF, true);  // lane ^ 1
@@ -446,7 +452,7 @@ int64_t gemm_blocks(int64_t M, int64_t N, int32_t G, bool grouped) {
   return tm * tn;
 }
 
-template <bool GROUPED, bool ACC>
+template <bool GROUPED, bool ACC, bool SQRELU>
 static hipError_t launch_gemm_t(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
                                 uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, const int32_t* offsets,
                                 int32_t G, int64_t tiles_m, int64_t tiles_n, hipStream_t stream) {
@@ -459,28 +465,32 @@ static hipError_t launch_gemm_t(const uint8_t* a, const uint32_t* ap, const uint
   if (e != hipSuccess) return e;
   const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
   if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<GROUPED, ACC>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<GROUPED, ACC, SQRELU>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_done.fetch_or(bit, std::memory_order_release);
   }
-  hipLaunchKernelGGL((gemm_kernel<GROUPED, ACC>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), LDS_BYTES, stream,
+  hipLaunchKernelGGL((gemm_kernel<GROUPED, ACC, SQRELU>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), LDS_BYTES, stream,
                      a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
                        uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                       const int32_t* offsets, int32_t G, bool accumulate, hipStream_t stream) {
+                       const int32_t* offsets, int32_t G, bool accumulate, bool sqrelu, hipStream_t stream) {
   const bool grouped = offsets != nullptr;
   const int64_t tiles_n = (N + BN - 1) / BN;
   const int64_t tiles_m = (M + BM - 1) / BM + (grouped ? (int64_t)G : 0);
   if (tiles_m * tiles_n == 0) return hipSuccess;
+#define MX_G_LAUNCH(GR, AC, SQ) \
+  launch_gemm_t<GR, AC, SQ>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, stream)
+  // accumulate and the relu^2 epilogue are exclusive (the API rejects both)
   if (grouped)
-    return accumulate ? launch_gemm_t<true, true>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, stream)
-                      : launch_gemm_t<true, false>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, stream);
-  return accumulate ? launch_gemm_t<false, true>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, stream)
-                    : launch_gemm_t<false, false>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, stream);
+    return accumulate ? MX_G_LAUNCH(true, true, false)
+                      : (sqrelu ? MX_G_LAUNCH(true, false, true) : MX_G_LAUNCH(true, false, false));
+  return accumulate ? MX_G_LAUNCH(false, true, false)
+                    : (sqrelu ? MX_G_LAUNCH(false, false, true) : MX_G_LAUNCH(false, false, false));
+#undef MX_G_LAUNCH
 }
 
 }  // namespace mx

@@ -22,11 +22,11 @@ hipError_t launch_pack_scales(const uint8_t* s, int64_t dim, int64_t k, int64_t 
                               hipStream_t stream);
 int64_t pack_scales_blocks(int64_t dim, int64_t k);
 
-// Dense (offsets == nullptr) or grouped GEMM; accumulate adds the product to C.  b_rows_total is the number of
-// rows of the packed B scale matrix (N dense, G*N grouped).
+// Dense (offsets == nullptr) or grouped GEMM; accumulate adds the product to C; sqrelu writes relu(product)^2
+// (not together with accumulate).
 hipError_t launch_gemm(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
                        uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                       const int32_t* offsets, int32_t G, bool accumulate, hipStream_t stream);
+                       const int32_t* offsets, int32_t G, bool accumulate, bool sqrelu, hipStream_t stream);
 int64_t gemm_blocks(int64_t M, int64_t N, int32_t G, bool grouped);
 
 }  // namespace mx

@@ -207,6 +207,16 @@ def dact_sqrelu(grad_bits: np.ndarray, act_bits: np.ndarray) -> np.ndarray:
     return (g * two_r).astype(np.float32)
 
 
+def sqrelu_epilogue(r: np.ndarray) -> np.ndarray:
+    """relu(r)^2 of a GEMM result, in fp64: the FC1 "squared_relu" epilogue of
+    "gemm(cutedsl): add standalone Lightning W4A16 grouped GEMM - #811"
+    (section "API and compatibility impact"), applied to the product before
+    its output rounding."""
+    r = np.asarray(r, dtype=np.float64)
+    z = np.maximum(r, 0.0)
+    return z * z
+
+
 def _check_f32(v: np.ndarray) -> np.ndarray:
     v = np.ascontiguousarray(v, dtype=np.float32)
     if v.ndim != 2 or v.shape[1] % MX_BLOCK:

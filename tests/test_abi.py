@@ -169,11 +169,15 @@ def test_grouped_gemm_validation(L):
 
 def test_gemm_ex_flags(L):
     G = L.mxfp8_gemm_ex
-    assert G(A16, A16, A16, A16, A16, 64, 64, 64, 128, 2, None) == FLAGS
+    assert G(A16, A16, A16, A16, A16, 64, 64, 64, 128, 4, None) == FLAGS
+    assert G(A16, A16, A16, A16, A16, 64, 64, 64, 128, 3, None) == FLAGS   # accumulate and relu^2 together
+    assert G(A16, A16, A16, A16, A16, 64, 64, 64, 100, 2, None) == SHAPE
     assert G(A16, A16, A16, A16, A16, 64, 64, 64, 100, 1, None) == SHAPE   # the dense checks still apply
     assert G(None, None, None, None, None, 64, 0, 64, 128, 1, None) == OK
     GG = L.mxfp8_grouped_gemm_ex
     assert GG(A16, A16, A16, A16, A16, 4, A16, 64, 64, 64, 128, 4, None) == FLAGS
+    assert GG(A16, A16, A16, A16, A16, 4, A16, 64, 64, 64, 128, 3, None) == FLAGS
+    assert GG(A16, A16, A16, A16, None, 4, None, 64, 0, 64, 128, 2, None) == OK
     assert GG(A16, A16, A16, A16, A16, 0, A16, 64, 64, 64, 128, 1, None) == SHAPE
     assert GG(A16, A16, A16, A16, None, 4, None, 64, 0, 64, 128, 1, None) == OK
 

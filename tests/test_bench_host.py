@@ -29,7 +29,8 @@ def test_quant_bytes():
 def test_profiles_match_the_gemm_sources():
     """Each workload's dominant GEMM has a traffic line taken on the current GEMM sources."""
     for key in ("gemm:8192x14336x4096", "gemm:4096x4096x16384", "gemm:grouped:16384x14336x4096:G=8",
-                "gemm:32768x8192x8192", "gemm:fprop:8192x14336x4096", "gemm:fc1:8192x14336x4096"):
+                "gemm:32768x8192x8192", "gemm:fprop:8192x14336x4096", "gemm:fc1:8192x14336x4096",
+                "gemm:grouped:relu^2:16384x14336x4096:G=8"):
         got = bench.profiled_traffic(key)
         assert got is not None, key
         nbytes, fname = got

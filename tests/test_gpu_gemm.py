@@ -25,7 +25,7 @@ def quantize_on_gpu(bits, colwise=False):
     return q, s, mx.pack_scales(s)
 
 
-def gemm_gpu(qa, pa, qb, pb, ldc=None, canary=False):
+def gemm_gpu(qa, pa, qb, pb, ldc=None, canary=False, flags=0):
     torch = need_gpu()
     M, K = qa.shape
     N = qb.shape[0]
@@ -33,7 +33,7 @@ def gemm_gpu(qa, pa, qb, pb, ldc=None, canary=False):
     G = 1024 if canary else 0
     full = torch.full((M * ldc + 2 * G,), -12345, dtype=torch.int16, device="cuda")
     c = full[G:G + M * ldc].view(torch.bfloat16)
-    mx.mxfp8_gemm(qa, pa, qb, pb, c, ldc, M, N, K)
+    mx.mxfp8_gemm_ex(qa, pa, qb, pb, c, ldc, M, N, K, flags)
     torch.cuda.synchronize()
     h = to_host(full.view(torch.bfloat16))
     if canary:
@@ -216,7 +216,7 @@ def test_gemm_accumulate_k_zero_keeps_c():
 
 # --------------------------------------------------------- grouped GEMM
 
-def grouped_case(M, N, K, counts, seed, canary_rows=True, accumulate=False):
+def grouped_case(M, N, K, counts, seed, canary_rows=True, accumulate=False, sqrelu=False):
     torch = need_gpu()
     G = len(counts)
     x = workloads.normal_bf16((M, K), seed)
@@ -232,7 +232,7 @@ def grouped_case(M, N, K, counts, seed, canary_rows=True, accumulate=False):
     else:
         out = torch.full((M, N), -7.0, dtype=torch.bfloat16, device="cuda")
     log("grouped M=%d N=%d K=%d counts=%s accumulate=%d" % (M, N, K, list(counts), accumulate))
-    mx.grouped_gemm(qx, px, qw, pw, to_dev(off), out=out, accumulate=accumulate)
+    mx.grouped_gemm(qx, px, qw, pw, to_dev(off), out=out, accumulate=accumulate, sqrelu=sqrelu)
     torch.cuda.synchronize()
     c = to_host(out)
     oqx, osx = oracle.quantize_rowwise(x)
@@ -245,11 +245,65 @@ def grouped_case(M, N, K, counts, seed, canary_rows=True, accumulate=False):
     ref = oracle.grouped_gemm_tn(oqx, osx, qwo, swo, off, rows=rows)
     if accumulate:
         ref = ref + bf16_to_f64(c_old[rows])
-    gemm_tolerance_check(c[rows], ref, K, label="grouped")
+    if sqrelu:
+        sqrelu_tolerance_check(c[rows], ref, K, label="grouped sqrelu")
+    else:
+        gemm_tolerance_check(c[rows], ref, K, label="grouped")
     if canary_rows and accumulate:
         assert np.array_equal(c[~covered], c_old[~covered]), "rows outside the groups were written"
     elif canary_rows:
         assert np.all(bf16_to_f64(c[~covered]) == -7.0), "rows outside the groups were written"
+
+
+def sqrelu_tolerance_check(gpu_bits, r, K, label=""):
+    """relu(R)^2 epilogue: the GPU forms relu(acc)^2 from its fp32 sum acc,
+    |acc - R| <= t = 8e-3 |R| + 1e-3 sqrt(K) rms(R) (the GEMM bound), so
+    |relu(acc)^2 - relu(R)^2| <= t (2|R| + t), plus the one BF16 rounding,
+    2^-9 (|R| + t)^2 (doubled for margin)."""
+    gpu = bf16_to_f64(gpu_bits)
+    r = np.asarray(r, dtype=np.float64)
+    t = 8e-3 * np.abs(r) + 1e-3 * np.sqrt(K) * np.sqrt(np.mean(r ** 2))
+    tol = t * (2 * np.abs(r) + t) + 2.0 ** -8 * (np.abs(r) + t) ** 2
+    err = np.abs(gpu - oracle.sqrelu_epilogue(r))
+    bad = ~(err <= tol)
+    assert not bad.any(), "%s: %d entries out of tolerance, worst %g vs %g" % (
+        label, bad.sum(), err[bad].max(), tol[bad][np.argmax(err[bad])])
+    assert np.all(gpu >= 0.0), label
+
+
+@pytest.mark.parametrize("M,N,K", [(32, 32, 128), (160, 96, 1024), (1000, 320, 256), (288, 288, 1152)])
+def test_gemm_sqrelu_epilogue(M, N, K):
+    a = workloads.normal_bf16((M, K), 3 * M + K)
+    b = workloads.normal_bf16((N, K), 5 * N + K, std=0.5)
+    qa, sa, pa = quantize_on_gpu(a)
+    qb, sb, pb = quantize_on_gpu(b)
+    log("sqrelu epilogue M=%d N=%d K=%d" % (M, N, K))
+    c = gemm_gpu(qa, pa, qb, pb, ldc=N + 24, canary=True, flags=mx.MXFP8_GEMM_SQRELU)
+    oqa, osa = oracle.quantize_rowwise(a)
+    oqb, osb = oracle.quantize_rowwise(b)
+    sqrelu_tolerance_check(c, oracle.gemm_tn(oqa, osa, oqb, osb), K, "sqrelu")
+
+
+def test_gemm_sqrelu_epilogue_exact_on_integers():
+    """Integer operands: the fp32 sum is exact, its square is exact in fp32
+    (< 2^24), so the output is the BF16 rounding of relu(R)^2 exactly."""
+    rng = np.random.default_rng(12)
+    A = rng.integers(-3, 4, size=(160, 256))
+    B = rng.integers(-3, 4, size=(96, 256))
+    ab = (A.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    bb = (B.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    qa, sa, pa = quantize_on_gpu(ab)
+    qb, sb, pb = quantize_on_gpu(bb)
+    log("sqrelu integers")
+    c = gemm_gpu(qa, pa, qb, pb, flags=mx.MXFP8_GEMM_SQRELU)
+    v = oracle.sqrelu_epilogue((A @ B.T).astype(np.float64))
+    assert v.max() < 2.0 ** 24
+    want = bf16_to_f64(workloads.f32_to_bf16_bits(v.astype(np.float32)))
+    assert np.array_equal(bf16_to_f64(c), want)
+
+
+def test_grouped_sqrelu_epilogue():
+    grouped_case(1200, 96, 256, [5, 0, 131, 257, 600], 9, sqrelu=True)
 
 
 def test_grouped_uniform_counts():
@@ -343,6 +397,30 @@ def test_full_moe_sampled():
     ref = oracle.grouped_gemm_tn(oqx, osx, np.stack([q for q, _ in ws]), np.stack([s for _, s in ws]), off,
                                  rows=rows, cols=cols)
     gemm_tolerance_check(ch, ref, K, label="moe")
+
+
+@pytest.mark.slow
+def test_full_moe_sqrelu_sampled():
+    """The MoE first projection with the relu^2 epilogue as the benchmark runs
+    it (operands quantized into packed scales), sampled against the oracle."""
+    torch = need_gpu()
+    d = workloads.moe()
+    x, w, off = d["X"], d["W"], d["offsets"]
+    G, N, K = w.shape
+    px_ = mx.quantize(to_dev_bf16(x), packed=True)
+    pw_ = mx.quantize(to_dev_bf16(w.reshape(G * N, K)), packed=True)
+    log("moe relu^2 grouped 16384x14336x4096")
+    c = mx.grouped_gemm(px_["q_row"], px_["p_row"], pw_["q_row"].view(G, N, K), pw_["p_row"], to_dev(off),
+                        sqrelu=True)
+    torch.cuda.synchronize()
+    rows = sample_indices(16384, 48, 11)
+    cols = sample_indices(N, 32, 12)
+    ch = to_host(c)[np.ix_(rows, cols)]
+    oqx, osx = oracle.quantize_rowwise(x)
+    ws = [oracle.quantize_rowwise(w[g]) for g in range(G)]
+    ref = oracle.grouped_gemm_tn(oqx, osx, np.stack([q for q, _ in ws]), np.stack([s for _, s in ws]), off,
+                                 rows=rows, cols=cols)
+    sqrelu_tolerance_check(ch, ref, K, label="moe relu^2")
 
 
 @pytest.mark.slow

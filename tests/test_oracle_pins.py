@@ -553,3 +553,18 @@ def test_golden_e8m0_readback():
         assert oracle.e8m0_decode(b) == float(np.array([bits], dtype=np.uint32).view(np.float32)[0])
         checked += 1
     assert checked == 8
+
+
+def test_sqrelu_epilogue_matches_the_activation_and_torch():
+    """The GEMM epilogue's relu(r)^2 (fp64) against torch's float64 relu and
+    power, and against the activation quantizer's fp32 relu(x)^2 on BF16
+    values (where both are exact)."""
+    import torch
+    rng = np.random.default_rng(57)
+    r = rng.standard_normal(5000) * np.exp2(rng.integers(-20, 20, size=5000))
+    r[:5] = [0.0, -0.0, -1.0, 3.0, -1e300]
+    want = (torch.relu(torch.from_numpy(r)) ** 2).numpy()
+    assert np.array_equal(oracle.sqrelu_epilogue(r), want)
+    bits = workloads.wide_range_bf16((8, 64), 58, u_lo=-20, u_hi=20, n_maxbf16=0, n_subnormal=0, n_subnormal_blocks=0)
+    assert np.array_equal(oracle.sqrelu_epilogue(oracle.bf16_value(bits)),
+                          oracle.act_sqrelu(bits).astype(np.float64))
