@@ -247,3 +247,16 @@ def test_full_stress_row_col():
     log("stress B row")
     res = gpu_quantize(data["B"], ROW)
     check_against_oracle(data["B"], ROW, res, "stress B")
+
+
+@pytest.mark.slow
+def test_full_moe_rowwise():
+    """The MoE workload's operands at full size (X [16384 x 4096], the eight
+    experts' W as one [114688 x 4096] tensor), byte scales, bit-exact."""
+    data = workloads.moe()
+    G, N, K = data["W"].shape
+    for name, bits in (("X", data["X"]), ("W", data["W"].reshape(G * N, K))):
+        log("moe %s rowwise %s" % (name, bits.shape))
+        res = gpu_quantize(bits, ROW)
+        check_against_oracle(bits, ROW, res, "moe " + name)
+        del res

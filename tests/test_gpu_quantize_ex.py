@@ -305,3 +305,36 @@ def test_full_mlp_activation_quantize():
     log("full mlp dsqrelu %s" % (h.shape,))
     got = run_ex(da, ROW | COL | PACKED | DB | DACT, act_bits=h)
     check_act_result(got, oracle.dact_sqrelu(da, h), ROW | COL | PACKED | DB, "full dsqrelu")
+
+
+@pytest.mark.slow
+def test_full_square_and_linear_packed():
+    """The dense step's square operands (rowwise, packed) and the linear
+    step's dY [8192 x 14336] (row + col, packed) at full size, bit-exact."""
+    sq = workloads.dense_square()
+    for name in ("A", "B"):
+        log("packed full square %s" % name)
+        got = run_ex(sq[name], ROW | PACKED)
+        q, s = oracle.quantize_rowwise(sq[name])
+        assert np.array_equal(got["q_row"], q) and np.array_equal(got["s_row"], oracle.pack_scales(s)), name
+        del got
+    dy = workloads.normal_bf16((8192, 14336), 4)
+    log("packed full linear dY row+col")
+    got = run_ex(dy, ROW | COL | PACKED)
+    q, s = oracle.quantize_rowwise(dy)
+    assert np.array_equal(got["q_row"], q) and np.array_equal(got["s_row"], oracle.pack_scales(s))
+    qT, sT = oracle.quantize_colwise(dy)
+    assert np.array_equal(got["q_colT"], qT) and np.array_equal(got["s_colT"], oracle.pack_scales(sT))
+
+
+@pytest.mark.slow
+def test_full_moe_packed_rowwise():
+    """The relu^2 MoE workload's operands, quantized into packed scales at full size."""
+    data = workloads.moe()
+    G, N, K = data["W"].shape
+    for name, bits in (("X", data["X"]), ("W", data["W"].reshape(G * N, K))):
+        log("packed full moe %s %s" % (name, bits.shape))
+        got = run_ex(bits, ROW | PACKED)
+        q, s = oracle.quantize_rowwise(bits)
+        assert np.array_equal(got["q_row"], q) and np.array_equal(got["s_row"], oracle.pack_scales(s)), name
+        del got
