@@ -126,23 +126,42 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
 
   int64_t m_lo, m_hi, b_row0 = 0;
   if (GROUPED) {
-    int64_t found = -1;
+    // Row tile tm counts the groups' tiles in order.  Each wave looks at 64
+    // groups at a time: lane g loads its group's bounds (clamped into
+    // [0, M], empty when reversed), a wave prefix sum of the tile counts
+    // finds the group holding tile tm, and the result is broadcast from that
+    // lane.  Every wave of the workgroup computes the same answer.
+    int found = -1;
     m_lo = m_hi = 0;
-    for (int g = 0; g < G; g++) {
-      int64_t lo = offsets[g], hi = offsets[g + 1];
-      lo = lo < 0 ? 0 : (lo > M ? M : lo);
-      hi = hi < lo ? lo : (hi > M ? M : hi);
-      const int64_t nt = (hi - lo + BM - 1) / BM;
-      if (tm < nt) {
-        found = g;
-        m_lo = lo + tm * BM;
-        m_hi = hi;
+    for (int g0 = 0; g0 < G; g0 += 64) {
+      const int g = g0 + lane;
+      int64_t lo = 0, hi = 0;
+      if (g < G) {
+        lo = offsets[g];
+        hi = offsets[g + 1];
+        lo = lo < 0 ? 0 : (lo > M ? M : lo);
+        hi = hi < lo ? lo : (hi > M ? M : hi);
+      }
+      const int nt = (int)((hi - lo + BM - 1) / BM);
+      int incl = nt;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += t;
+      }
+      const int total = __builtin_amdgcn_readlane(incl, 63);
+      if (tm < total) {
+        const int fl = __builtin_ctzll(__ballot(incl > tm));
+        const int before = __builtin_amdgcn_readlane(incl - nt, fl);
+        found = g0 + fl;
+        m_lo = (int64_t)__builtin_amdgcn_readlane((int)lo, fl) + (tm - before) * BM;
+        m_hi = (int64_t)__builtin_amdgcn_readlane((int)hi, fl);
         break;
       }
-      tm -= nt;
+      tm -= total;
     }
     if (found < 0) return;  // whole workgroup leaves together
-    b_row0 = found * N;
+    b_row0 = (int64_t)found * N;
   } else {
     m_lo = tm * BM;
     m_hi = M;

@@ -322,6 +322,20 @@ def test_grouped_accumulate():
     grouped_case(1200, 96, 256, [5, 0, 131, 257, 600], 8, accumulate=True)
 
 
+def test_grouped_many_experts():
+    """More experts than a wave's 64 lanes (the device-side group search walks
+    the offsets 64 groups at a time): 200 ragged groups, empty ones among them
+    (around the 64-group chunk boundaries too), unaligned counts, and rows
+    past the last group left untouched."""
+    rng = np.random.default_rng(17)
+    counts = rng.integers(0, 90, size=200)
+    counts[[0, 63, 64, 65, 127, 128, 199]] = 0
+    counts[rng.choice(200, size=30, replace=False)] = 0
+    counts[10] = 300                                   # a group spanning two row tiles
+    M = int(counts.sum()) + 40
+    grouped_case(M, 96, 256, list(counts), 19)
+
+
 def test_grouped_single_group_matches_dense():
     grouped_case(512, 128, 256, [512], 7)
 
