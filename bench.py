@@ -399,6 +399,7 @@ def main():
         "quantize": quant_report,
         "pack": pack_report,
         "short_launch_blocks": block_report,
+        "launch_order": [op.kind + " " + op.label for op in ops],
         "timing_note": "gemm: HIP events per launch in the timed steps; quantize / pack: per-launch events in a "
                        "separate pass after them; short_launch_blocks: the same launches as timed in the steps",
     }
