@@ -175,11 +175,12 @@ def build_ops(workload, dev):
                 "8192x8192x8192; BF16 out")
     elif workload == "backward":
         d = workloads.backward()
-        bd = quantize_op("dY[16384x4096] row+col+dbias", d["dY"], ROW | COL | DB)
-        bx = quantize_op("X[16384x4096] col", d["X"], COL)
+        bd = quantize_op("dY[16384x4096] row+col+dbias", d["dY"], ROW | COL | DB, packed=True)
+        bx = quantize_op("X[16384x4096] col", d["X"], COL, packed=True)
         dominant = gemm_op(bd["qT"], bd["pT"], bx["qT"], bx["pT"], 4096, 4096, 16384)
         desc = ("backward: dY[16384x4096] = 0.1*t(3) with 1% zero 32x32 tiles, rowwise+columnwise quantize with "
-                "fused dbias; X[16384x4096] columnwise; wgrad TN GEMM 4096x4096x16384 on the transposed copies")
+                "fused dbias; X[16384x4096] columnwise; both writing the packed scale words; wgrad TN GEMM "
+                "4096x4096x16384 on the transposed copies")
     elif workload == "stress":
         d = workloads.stress()
         ba = quantize_op("A[32768x8192] row+col", d["A"], ROW | COL, packed=True)

@@ -168,6 +168,30 @@ def test_full_stress_row_col_packed():
     assert np.array_equal(got["s_colT"], oracle.pack_scales(sT))
 
 
+@pytest.mark.slow
+def test_full_backward_packed():
+    """The backward step's launches as timed: dY [16384 x 4096] (heavy tails,
+    1 % zero blocks) row+col+dbias and X [16384 x 4096] columnwise, both
+    writing packed scale words; codes and words bit-exact, dbias within the
+    fp32 summation bound."""
+    from test_gpu_quantize import check_dbias
+    d = workloads.backward()
+    log("backward dY row+col+dbias packed")
+    got = run_ex(d["dY"], ROW | COL | DB | PACKED)
+    q, s = oracle.quantize_rowwise(d["dY"])
+    assert np.array_equal(got["q_row"], q)
+    assert np.array_equal(got["s_row"], oracle.pack_scales(s))
+    qT, sT = oracle.quantize_colwise(d["dY"])
+    assert np.array_equal(got["q_colT"], qT)
+    assert np.array_equal(got["s_colT"], oracle.pack_scales(sT))
+    check_dbias(d["dY"], got["dbias"], "backward dY packed")
+    log("backward X col packed")
+    got = run_ex(d["X"], COL | PACKED)
+    qT, sT = oracle.quantize_colwise(d["X"])
+    assert np.array_equal(got["q_colT"], qT)
+    assert np.array_equal(got["s_colT"], oracle.pack_scales(sT))
+
+
 # ------------------------------------------------ activation-fused quantize
 
 ACT, DACT = mx.MXFP8_ACT_SQRELU, mx.MXFP8_DACT_SQRELU
