@@ -258,22 +258,6 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
 #pragma unroll
     for (int j = 0; j < 4; j++) acc[i][j] = v16f{};
 
-  auto read_frags = [&](auto SLOT, auto H, auto SET) {
-    constexpr int h = decltype(H)::value;
-    constexpr int set = decltype(SET)::value;
-    const lds_u8* base = smem + decltype(SLOT)::value * SLOT_BYTES;
-    const int p0 = 16 * ((4 * h + lg) ^ swz);       // K = 64h + 16lg + [0,16)  (scale block 2h)
-    const int p1 = 16 * ((4 * h + 2 + lg) ^ swz);   // K = 64h + 32 + 16lg + [0,16) (block 2h+1)
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const u32x4 lo = *(lds_u32x4*)(base + a_row_off + i * 32 * BK + p0);
-      const u32x4 hi = *(lds_u32x4*)(base + a_row_off + i * 32 * BK + p1);
-      fa[set][i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      const u32x4 blo = *(lds_u32x4*)(base + b_row_off + i * 32 * BK + p0);
-      const u32x4 bhi = *(lds_u32x4*)(base + b_row_off + i * 32 * BK + p1);
-      fb[set][i] = v8i{(int)blo.x, (int)blo.y, (int)blo.z, (int)blo.w, (int)bhi.x, (int)bhi.y, (int)bhi.z, (int)bhi.w};
-    }
-  };
   // One 16-byte piece q of the fragments: frag q/2 (A blocks 0..3, then B
   // blocks 0..3), low (K block 2h) or high (block 2h+1) half.
   auto read_piece = [&](auto SLOT, auto H, auto SET, int qq) {
@@ -350,8 +334,18 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
     issue_step(1, ic<1>{});
     wait_vmcnt<18>();
     lds_barrier();
-    read_frags(ic<0>{}, ic<0>{}, ic<0>{});
+    // Scale words first, then the fragments in the loop's own read order:
+    // on loop entry the outstanding LDS reads are then in the same order as
+    // on the back edge, so the wait in front of the first MFMA only covers
+    // the reads it needs (otherwise every iteration starts with a full
+    // drain of the LDS read queue).
     read_scales(ic<0>{}, sa, sb);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 16; q++) {
+      read_piece(ic<0>{}, ic<0>{}, ic<0>{}, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       sa[i] >>= sh;
