@@ -148,6 +148,34 @@ def test_one_scale_byte_doubles_exactly_its_block():
     _ = torch
 
 
+@pytest.mark.slow
+def test_largest_k():
+    """K = 2^22, the largest K the library accepts (a 256-row operand tile is
+    then 2^30 bytes of buffer range), with a ragged second row tile
+    (M = 288): random E4M3 codes (NaN patterns excluded) and scale bytes
+    120..127 made on the device, the sampled entries checked against the
+    oracle on the same codes."""
+    torch = need_gpu()
+    M, N, K = 288, 256, 1 << 22
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+
+    def codes(rows):
+        c = torch.randint(0, 254, (rows, K), dtype=torch.uint8, device="cuda", generator=gen)
+        return torch.where(c >= 0x7F, c + 1, c)
+
+    qa, qb = codes(M), codes(N)
+    sa = torch.randint(120, 128, (M, K // 32), dtype=torch.uint8, device="cuda", generator=gen)
+    sb = torch.randint(120, 128, (N, K // 32), dtype=torch.uint8, device="cuda", generator=gen)
+    log("largest K: M=%d N=%d K=%d" % (M, N, K))
+    c = gemm_gpu(qa, mx.pack_scales(sa), qb, mx.pack_scales(sb))
+    rows = np.array([0, 1, 100, 255, 256, 270, 287])
+    cols = np.array([0, 31, 128, 200, 255])
+    ref = oracle.gemm_tn(qa[rows].cpu().numpy(), sa[rows].cpu().numpy(), qb[cols].cpu().numpy(),
+                         sb[cols].cpu().numpy())
+    gemm_tolerance_check(c[np.ix_(rows, cols)], ref, K, label="K=2^22")
+
+
 def test_k_zero_writes_zeros():
     torch = need_gpu()
     c = torch.full((64, 96), 3.0, dtype=torch.bfloat16, device="cuda")
