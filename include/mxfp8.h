@@ -53,7 +53,11 @@ typedef enum mxfp8_status {
     MXFP8_ERR_FLAGS = 4,       /* unknown flag bits or no copy requested            */
     MXFP8_ERR_WORKSPACE = 5,   /* DBIAS workspace missing or too small              */
     MXFP8_ERR_HIP = 6,         /* the HIP runtime reported an error at launch       */
-    MXFP8_ERR_LIMIT = 7        /* a size exceeds what one launch grid can cover     */
+    MXFP8_ERR_LIMIT = 7        /* a size exceeds what one launch grid can cover:
+                                * a kernel of the call would need more than
+                                * 2^32 - 1 work-items (the 32-bit grid field of
+                                * an AQL dispatch packet), a dimension or
+                                * rows * ld exceeds 2^40, or GEMM K exceeds 2^22 */
 } mxfp8_status;
 
 /* Flags of mxfp8_quantize (the rowwise / colwise / with_dbias options of the

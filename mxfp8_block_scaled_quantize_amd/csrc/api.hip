@@ -10,7 +10,6 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int64_t kMaxGrid = 0x7FFFFFFF;  // one-dimensional grid limit
 constexpr int64_t kMaxDim = int64_t(1) << 40; // keeps every element offset well inside int64
 constexpr int64_t kMaxGemmK = int64_t(1) << 22; // a 256-row operand tile stays below 2^31 bytes
 
@@ -58,7 +57,7 @@ mxfp8_status check_quantize(const void* x, int64_t rows, int64_t cols, int64_t l
       return MXFP8_ERR_MISALIGNED;
   }
   if ((flags & MXFP8_DBIAS) && cols > 0 && !aligned(dbias, 4)) return MXFP8_ERR_MISALIGNED;
-  if (mx::quantize_row_tiles(rows) * mx::quantize_col_tiles(cols) > kMaxGrid) return MXFP8_ERR_LIMIT;
+  if (!mx::quantize_grids_fit(rows, cols, ld_x, flags)) return MXFP8_ERR_LIMIT;
   const size_t need = mxfp8_quantize_workspace_bytes(rows, cols, flags);
   if (need > 0) {
     if (!ws || ws_bytes < need) return MXFP8_ERR_WORKSPACE;
@@ -141,7 +140,7 @@ mxfp8_status mxfp8_pack_scales(const uint8_t* s, int64_t dim, int64_t k, int64_t
   if (dim == 0 || k == 0) return MXFP8_OK;
   if (!s || !packed) return MXFP8_ERR_NULL;
   if (!aligned(s, 4) || ld_s % 4 || !aligned(packed, 4)) return MXFP8_ERR_MISALIGNED;
-  if (mx::pack_scales_blocks(dim, k) > kMaxGrid) return MXFP8_ERR_LIMIT;
+  if (!mx::pack_scales_grid_fits(dim, k)) return MXFP8_ERR_LIMIT;
   return hip_status(mx::launch_pack_scales(s, dim, k, ld_s, packed, static_cast<hipStream_t>(stream)));
 }
 
@@ -152,7 +151,7 @@ mxfp8_status mxfp8_gemm_ex(const uint8_t* a, const uint32_t* a_packed, const uin
   const mxfp8_status st = check_gemm_common(a, a_packed, b, b_packed, c, ldc, M, N, K);
   if (st != MXFP8_OK) return st;
   if (M == 0 || N == 0) return MXFP8_OK;
-  if (mx::gemm_blocks(M, N, 0, false) > kMaxGrid) return MXFP8_ERR_LIMIT;
+  if (!mx::gemm_grid_fits(M, N, 0, false)) return MXFP8_ERR_LIMIT;
   return hip_status(mx::launch_gemm(a, a_packed, b, b_packed, static_cast<uint16_t*>(c), ldc, M, N, K, nullptr, 0,
                                     (flags & MXFP8_GEMM_ACCUMULATE) != 0, (flags & MXFP8_GEMM_SQRELU) != 0,
                                     static_cast<hipStream_t>(stream)));
@@ -174,7 +173,7 @@ mxfp8_status mxfp8_grouped_gemm_ex(const uint8_t* a, const uint32_t* a_packed, c
   if (M_total == 0 || N == 0) return MXFP8_OK;
   if (!offsets) return MXFP8_ERR_NULL;
   if (!aligned(offsets, 4)) return MXFP8_ERR_MISALIGNED;
-  if (mx::gemm_blocks(M_total, N, G, true) > kMaxGrid) return MXFP8_ERR_LIMIT;
+  if (!mx::gemm_grid_fits(M_total, N, G, true)) return MXFP8_ERR_LIMIT;
   return hip_status(mx::launch_gemm(a, a_packed, b, b_packed, static_cast<uint16_t*>(c), ldc, M_total, N, K,
                                     offsets, G, (flags & MXFP8_GEMM_ACCUMULATE) != 0,
                                     (flags & MXFP8_GEMM_SQRELU) != 0, static_cast<hipStream_t>(stream)));

@@ -459,10 +459,10 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
   }
 }
 
-int64_t gemm_blocks(int64_t M, int64_t N, int32_t G, bool grouped) {
+bool gemm_grid_fits(int64_t M, int64_t N, int32_t G, bool grouped) {
   const int64_t tn = (N + BN - 1) / BN;
   const int64_t tm = (M + BM - 1) / BM + (grouped ? (int64_t)G : 0);
-  return tm * tn;
+  return grid_fits(tm, tn, 256);
 }
 
 template <bool GROUPED, bool ACC, bool SQRELU>

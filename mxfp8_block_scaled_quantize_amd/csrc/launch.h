@@ -10,6 +10,19 @@ namespace mx {
 int64_t quantize_row_tiles(int64_t R);
 int64_t quantize_col_tiles(int64_t C);
 
+// An AQL dispatch packet holds the grid size in work-items as a 32-bit
+// field: a launch of `a * b` workgroups of `threads` work-items fits when the
+// product is at most 2^32 - 1 (checked without overflow; a or b == 0 fits).
+constexpr int64_t kMaxWorkItems = 0xFFFFFFFFll;
+inline bool grid_fits(int64_t a, int64_t b, int64_t threads) {
+  if (a <= 0 || b <= 0) return true;
+  return a <= kMaxWorkItems / threads / b;
+}
+
+// Whether every launch of mxfp8_quantize_ex with these sizes and flags fits
+// in one grid (R, C >= 0, R * C <= 2^40).
+bool quantize_grids_fit(int64_t R, int64_t C, int64_t ldx, uint32_t flags);
+
 // flags: rowwise 1, colwise 2, dbias 4, amax 8, packed scales 16, squared-ReLU
 // activation 32, its backward 64 (act_in: the activation's input, same shape
 // and leading dimension as x).  noop may be null (always run).
@@ -20,13 +33,13 @@ hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
 
 hipError_t launch_pack_scales(const uint8_t* s, int64_t dim, int64_t k, int64_t ld_s, uint32_t* packed,
                               hipStream_t stream);
-int64_t pack_scales_blocks(int64_t dim, int64_t k);
+bool pack_scales_grid_fits(int64_t dim, int64_t k);
 
 // Dense (offsets == nullptr) or grouped GEMM; accumulate adds the product to C; sqrelu writes relu(product)^2
 // (not together with accumulate).
 hipError_t launch_gemm(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
                        uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
                        const int32_t* offsets, int32_t G, bool accumulate, bool sqrelu, hipStream_t stream);
-int64_t gemm_blocks(int64_t M, int64_t N, int32_t G, bool grouped);
+bool gemm_grid_fits(int64_t M, int64_t N, int32_t G, bool grouped);
 
 }  // namespace mx

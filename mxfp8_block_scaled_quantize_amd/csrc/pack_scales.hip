@@ -40,16 +40,16 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restr
   }
 }
 
-int64_t pack_scales_blocks(int64_t dim, int64_t k) {
+bool pack_scales_grid_fits(int64_t dim, int64_t k) {
   const int64_t kw = k / 128;
-  return ((dim + PK_T - 1) / PK_T) * ((kw + PK_T - 1) / PK_T);
+  return grid_fits((dim + PK_T - 1) / PK_T, (kw + PK_T - 1) / PK_T, 256);
 }
 
 hipError_t launch_pack_scales(const uint8_t* s, int64_t dim, int64_t k, int64_t ld_s, uint32_t* packed,
                               hipStream_t stream) {
   const int64_t kw = k / 128;
   const int64_t tiles_k = (kw + PK_T - 1) / PK_T;
-  const int64_t blocks = pack_scales_blocks(dim, k);
+  const int64_t blocks = ((dim + PK_T - 1) / PK_T) * tiles_k;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(pack_scales_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, s, dim, kw, ld_s,
                      packed, tiles_k);

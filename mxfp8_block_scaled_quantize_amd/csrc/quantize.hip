@@ -602,6 +602,43 @@ __global__ __launch_bounds__(256) void fill_zero_f32_kernel(float* __restrict__ 
 int64_t quantize_row_tiles(int64_t R) { return (R + QT_R_MIN - 1) / QT_R_MIN; }
 int64_t quantize_col_tiles(int64_t C) { return (C + QT_C - 1) / QT_C; }
 
+// Which kernel a call runs: the packed-scale rowwise panel kernel, the flat
+// rowwise kernel (contiguous rows, byte scales) or the tile kernel (every
+// other copy set, dbias, activations).
+enum QuantPath { QP_PACKED_ROW, QP_FLAT, QP_TILES };
+static QuantPath quantize_path(int64_t C, int64_t ldx, uint32_t flags) {
+  const bool row = flags & 1u, col = flags & 2u, db = flags & 4u, packed = flags & 16u;
+  const bool act = flags & (32u | 64u);
+  if (row && !col && !db && packed && !act) return QP_PACKED_ROW;
+  if (row && !col && !db && !packed && !act && ldx == C) return QP_FLAT;
+  return QP_TILES;
+}
+// Waves of the tile kernel: 8 when the rowwise copy is written or for the
+// rowwise copy alone, 4 for the columnwise copy alone.
+constexpr int tile_waves(bool row, bool col) { return (row || !col) ? 8 : 4; }
+
+bool quantize_grids_fit(int64_t R, int64_t C, int64_t ldx, uint32_t flags) {
+  bool ok;
+  switch (quantize_path(C, ldx, flags)) {
+    case QP_PACKED_ROW:
+      ok = grid_fits((R + PN_ROWS - 1) / PN_ROWS, (C + PN_COLS - 1) / PN_COLS, 256);
+      break;
+    case QP_FLAT: {
+      const int64_t per_block = FL_ELEMS * (FL_THREADS / 64);
+      ok = grid_fits((R * C + per_block - 1) / per_block, 1, FL_THREADS);
+      break;
+    }
+    default: {
+      const int qw = tile_waves(flags & 1u, flags & 2u);
+      ok = grid_fits((R + 32 * qw - 1) / (32 * qw), quantize_col_tiles(C), 64 * qw);
+    }
+  }
+  // the dbias reduce (one 32-column group per workgroup; the zero fill of an
+  // empty dbias needs fewer work-items)
+  if (flags & 4u) ok = ok && grid_fits((C + DB_COLS - 1) / DB_COLS, 1, DB_COLS * DB_PARTS);
+  return ok;
+}
+
 // Tile configuration per copy set (measured on MI355X with the stress,
 // backward and columnwise-only shapes): 8 waves when the rowwise copy is
 // written, 4 for the columnwise copy alone.  Codes are written with cached
@@ -612,7 +649,7 @@ static hipError_t launch_tiles(const uint16_t* x, int64_t R, int64_t C, int64_t 
                                uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT, float* dbias_part,
                                const QuantOpts& opt, const uint16_t* act_in, int64_t* row_tiles,
                                hipStream_t stream) {
-  constexpr int QW = (ROW || !COL) ? 8 : 4;
+  constexpr int QW = tile_waves(ROW, COL);
   const int64_t tr = (R + 32 * QW - 1) / (32 * QW);
   const int64_t tc = quantize_col_tiles(C);
   *row_tiles = tr;
@@ -654,14 +691,15 @@ hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
   }
   uint8_t* srow = static_cast<uint8_t*>(s_row);
   uint8_t* scol = static_cast<uint8_t*>(s_colT);
-  if (row && !col && !db && packed && act == ACT_NONE) {
+  const QuantPath path = quantize_path(C, ldx, flags);
+  if (path == QP_PACKED_ROW) {
     const int64_t blocks = ((R + PN_ROWS - 1) / PN_ROWS) * ((C + PN_COLS - 1) / PN_COLS);
     if (blocks > 0)
       hipLaunchKernelGGL(quantize_rowwise_packed_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, R, C, ldx,
                          q_row, static_cast<uint32_t*>(s_row), opt);
     return hipGetLastError();
   }
-  if (row && !col && !db && !packed && act == ACT_NONE && ldx == C) {
+  if (path == QP_FLAT) {
     const int64_t total = R * C;
     const int64_t per_block = FL_ELEMS * (FL_THREADS / 64);
     const int64_t blocks = (total + per_block - 1) / per_block;

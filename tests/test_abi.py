@@ -127,6 +127,30 @@ def test_quantize_ex_validation(L):
 def test_quantize_grid_limit(L):
     assert q(L, rows=1 << 36, cols=1 << 20, ld=1 << 20) == LIMIT
     assert q(L, rows=1 << 41, cols=64, ld=64) == LIMIT
+    # Grids are counted in work-items (a 32-bit field of the dispatch packet).
+    # Flat rowwise kernel, 4096 elements per 256-work-item workgroup: 2^36
+    # elements need exactly 2^32 work-items, one too many.
+    assert q(L, rows=1 << 22, cols=1 << 14, ld=1 << 14) == LIMIT
+    # columnwise tiles (128 x 128, 256 work-items): 2^25 tiles need 2^33
+    assert q(L, rows=1 << 20, cols=1 << 19, ld=1 << 19, flags=COL) == LIMIT
+    # row+col tiles (256 x 128, 512 work-items): 2^23 tiles need 2^32, one
+    # tile fewer fits (the missing workspace is then the first error found)
+    assert q(L, rows=256 * (1 << 23), cols=128, ld=128, flags=ROW | COL | DB, ws=None) == LIMIT
+    assert q(L, rows=256 * ((1 << 23) - 1), cols=128, ld=128, flags=ROW | COL | DB, ws=None) == WORKSPACE
+    # the dbias reduce (256 work-items per 32 columns) is the larger grid here
+    assert q(L, rows=32, cols=1 << 29, ld=1 << 29, flags=ROW | COL | DB, ws=None) == LIMIT
+    assert q(L, rows=32, cols=(1 << 29) - 32, ld=(1 << 29) - 32, flags=ROW | COL | DB, ws=None) == WORKSPACE
+
+
+def test_gemm_and_pack_grid_limits(L):
+    # 256 x 256 tiles of 256 work-items: 2^24 tiles need 2^32 work-items
+    assert L.mxfp8_gemm(A16, A16, A16, A16, A16, 1 << 20, 1 << 20, 1 << 20, 128, None) == LIMIT
+    # tile counts whose product would overflow int64 if formed naively
+    assert L.mxfp8_gemm(A16, A16, A16, A16, A16, 1 << 40, 1 << 40, 1 << 40, 128, None) == LIMIT
+    # grouped: the row tiles include one spare per group
+    assert L.mxfp8_grouped_gemm(A16, A16, A16, A16, A16, 1, A16, 1 << 20, 1 << 20, 1 << 20, 128, None) == LIMIT
+    # packing: 64 x 64 word tiles of 256 work-items
+    assert L.mxfp8_pack_scales(A16, 1 << 30, 1 << 20, 1 << 15, A16, None) == LIMIT
 
 
 def test_pack_validation(L):
