@@ -19,12 +19,14 @@ three GEMMs reduces over one of them).
 
 import torch
 
-from . import gemm, pack_scales, quantize
+from . import gemm, quantize
 
 
 def _quantize_both(t):
-    out = quantize(t, rowwise=True, colwise=True)
-    return (out["q_row"], pack_scales(out["s_row"]), out["q_colT"], pack_scales(out["s_colT"]))
+    # one pass writes both copies with their scales already in the GEMM's
+    # packed word layout (rows and columns are multiples of 128 here)
+    out = quantize(t, rowwise=True, colwise=True, packed=True)
+    return out["q_row"], out["p_row"], out["q_colT"], out["p_colT"]
 
 
 class MXFP8LinearFunction(torch.autograd.Function):
