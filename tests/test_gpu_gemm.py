@@ -488,6 +488,26 @@ def test_full_linear_wgrad_accumulate_sampled():
     gemm_tolerance_check(to_host(cd)[np.ix_(rows, cols)], ref, 8192, label="wgrad accumulate")
 
 
+@pytest.mark.slow
+def test_full_linear_dgrad_sampled():
+    """The linear step's dgrad at its full size (8192 x 4096, K = 14336, the
+    reduction of the MLP's second projection too): dY rowwise times W's
+    transposed copy."""
+    need_gpu()
+    w = workloads.dense_linear()["W"]                   # [14336][4096]
+    dy = workloads.normal_bf16((8192, 14336), 4)        # [8192][14336]
+    qa, sa, pa = quantize_on_gpu(dy)                    # [8192][14336]
+    qb, sb, pb = quantize_on_gpu(w, colwise=True)       # [4096][14336]
+    log("dgrad 8192x4096x14336")
+    c = gemm_gpu(qa, pa, qb, pb)
+    rows = sample_indices(8192, 40, 14)
+    cols = sample_indices(4096, 40, 15)
+    oqa, osa = oracle.quantize_rowwise(dy)
+    oqb, osb = oracle.quantize_colwise(w)
+    ref = oracle.gemm_tn(oqa, osa, oqb, osb, rows=rows, cols=cols)
+    gemm_tolerance_check(c[np.ix_(rows, cols)], ref, 14336, label="dgrad")
+
+
 def test_side_stream_pipeline_matches_default_stream():
     """The whole path (quantize into packed scales, GEMM) enqueued on a
     non-default stream, ordered after the input upload by an event, gives the
