@@ -53,20 +53,29 @@ def parse():
     return p.parse_args()
 
 
-def gemm_source_hash():
-    """Hash of the sources that define the GEMM kernel (profile traffic is tied to it)."""
+GEMM_SOURCES = ("mxfp8_block_scaled_quantize_amd/csrc/gemm.hip", "mxfp8_block_scaled_quantize_amd/csrc/mx_device.h")
+QUANTIZE_SOURCES = ("mxfp8_block_scaled_quantize_amd/csrc/quantize.hip",
+                    "mxfp8_block_scaled_quantize_amd/csrc/mx_device.h")
+
+
+def source_hash(files=GEMM_SOURCES):
+    """Hash of the sources that define a kernel (profile traffic is tied to it)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("mxfp8_block_scaled_quantize_amd/csrc/gemm.hip", "mxfp8_block_scaled_quantize_amd/csrc/mx_device.h"):
+    for f in files:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def profiled_traffic(kernel_key):
+def gemm_source_hash():
+    return source_hash(GEMM_SOURCES)
+
+
+def profiled_traffic(kernel_key, files=GEMM_SOURCES):
     """HBM-side bytes per launch from the rocprofv3 summaries in profiles/, or None
-    when no summary was taken for the current GEMM sources."""
-    src = gemm_source_hash()
+    when no summary was taken for the current sources of that kernel."""
+    src = source_hash(files)
     pdir = os.path.join(ROOT, "profiles")
     if not os.path.isdir(pdir):
         return None
@@ -381,6 +390,25 @@ def main():
         roofline["traffic_unit"] = "bytes per launch (HBM side, calibrated FETCH_SIZE + WRITE_SIZE)"
         roofline["traffic_source"] = "profiles/" + prof[1]
 
+    # the quantizer's roofline: its largest launch of the step (per-launch HIP
+    # events), and all quantize / packing launches as timed inside the steps
+    qops = [op for op in ops if op.kind == "quantize"]
+    qroof = None
+    if qops:
+        qdom = max(qops, key=lambda op: op.work)
+        qt = avg[id(qdom)]
+        qgbs = qdom.work / (qt * 1e-3) / 1e9
+        qprof = profiled_traffic("quantize:" + qdom.label.replace(" ", ":"), QUANTIZE_SOURCES)
+        in_steps = sum(sum(by_id[i].work for i in k) for k, _ in short_block)
+        in_steps_ms = sum(t for _, t in short_block)
+        qroof = {"bound": "hbm", "achieved": round(qgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(qgbs / HBM_PEAK_GBS, 4), "traffic": qprof[0] if qprof else None,
+                 "kernel": "mxfp8 quantize " + qdom.label, "ms": round(qt, 4),
+                 "bytes_per_launch": qdom.work,
+                 "all_short_launches_in_steps_gbs": round(in_steps / (in_steps_ms * 1e-3) / 1e9, 1)}
+        if qprof:
+            qroof["traffic_source"] = "profiles/" + qprof[1]
+
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -396,6 +424,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc, "gemm_flops_per_step": total_flops},
         "roofline": roofline,
+        "quantize_roofline": qroof,
         "gemm": gemm_report,
         "quantize": quant_report,
         "pack": pack_report,

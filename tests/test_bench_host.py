@@ -37,6 +37,18 @@ def test_profiles_match_the_gemm_sources():
         assert nbytes > 0 and os.path.exists(os.path.join(ROOT, "profiles", fname))
 
 
+def test_profiles_match_the_quantize_sources():
+    """The largest quantize launch of each workload has a traffic line taken
+    on the current quantizer sources (reported as quantize_roofline.traffic)."""
+    for key in ("quantize:A[8192x8192]:packed", "quantize:dY[16384x4096]:row+col+dbias:packed",
+                "quantize:W[8x14336x4096]", "quantize:W[8x14336x4096]:packed",
+                "quantize:A[32768x8192]:row+col:packed", "quantize:dY[8192x14336]:row+col:packed",
+                "quantize:dH=dA*2relu(H)[8192x14336]:row+col+dbias:packed"):
+        got = bench.profiled_traffic(key, bench.QUANTIZE_SOURCES)
+        assert got is not None, key
+        assert got[0] > 0
+
+
 def test_profiles_are_short_text():
     for name in os.listdir(os.path.join(ROOT, "profiles")):
         assert name.endswith((".md", ".txt")), name
