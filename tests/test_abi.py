@@ -38,6 +38,21 @@ def test_header_declares_the_four_entry_points():
         assert n in names
 
 
+def test_header_constants_match_the_binding():
+    """Every flag and status value the header defines has the same value in
+    the Python binding (and the binding defines no flag the header lacks)."""
+    import re
+    text = open(HEADER).read()
+    flags = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (MXFP8_[A-Z_]+) (\d+)u", text)}
+    assert len(flags) == 9, flags
+    for name, value in flags.items():
+        assert getattr(mx, name) == value, name
+    binding = {n for n in dir(mx) if re.fullmatch(r"MXFP8_[A-Z_]+", n) and isinstance(getattr(mx, n), int)}
+    assert binding == set(flags), binding ^ set(flags)
+    status = {m.group(1): int(m.group(2)) for m in re.finditer(r"(MXFP8_(?:OK|ERR_[A-Z]+)) = (\d+)", text)}
+    assert {v: k for k, v in status.items()} == mx.STATUS_NAMES
+
+
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert names and set(names) == set(mx.EXPORTED)
