@@ -421,6 +421,47 @@ def test_gemm_scale_byte_doubles_one_row_block():
     _ = rng
 
 
+
+def test_gemm_abs_equals_gemm_on_nonnegative_operands():
+    """With every code's sign bit clear the terms are non-negative, so the
+    size of the terms is the product itself (same dequantized operands)."""
+    rng = np.random.default_rng(14)
+    qa = rng.integers(0, 0x7F, size=(48, 256)).astype(np.uint8)      # 0x00..0x7E: non-negative, finite
+    qb = rng.integers(0, 0x7F, size=(40, 256)).astype(np.uint8)
+    sa = rng.integers(100, 150, size=(48, 8)).astype(np.uint8)
+    sb = rng.integers(100, 150, size=(40, 8)).astype(np.uint8)
+    assert np.array_equal(oracle.gemm_tn_abs(qa, sa, qb, sb), oracle.gemm_tn(qa, sa, qb, sb))
+    rows, cols = np.array([3, 0, 47]), np.array([39, 5])
+    sub = oracle.gemm_tn_abs(qa, sa, qb, sb, rows=rows, cols=cols)
+    full = oracle.gemm_tn(qa, sa, qb, sb)[np.ix_(rows, cols)]
+    # the sub-grid is summed by BLAS in another order: equal within fp64 summation error
+    assert np.all(np.abs(sub - full) <= full * 256 * 2.0 ** -52)
+
+
+def test_gemm_abs_tiny_mixed_signs_rationals():
+    """sum_k |dq(a) dq(b)| on mixed-sign codes against exact rationals built
+    from torch's E4M3 decode and the scale bytes (2^(byte - 127)), with a
+    row / column selection.  A dropped abs on either operand, a scale applied
+    twice or a transposed selection fails here."""
+    rng = np.random.default_rng(15)
+    M, N, K = 5, 4, 128
+    qa = rng.integers(0, 256, size=(M, K)).astype(np.uint8)
+    qb = rng.integers(0, 256, size=(N, K)).astype(np.uint8)
+    qa[(qa & 0x7F) == 0x7F] = 0xB3
+    qb[(qb & 0x7F) == 0x7F] = 0x35
+    sa = rng.integers(90, 160, size=(M, K // 32)).astype(np.uint8)
+    sb = rng.integers(90, 160, size=(N, K // 32)).astype(np.uint8)
+    vals = {c: Fraction(float(v)) for c, v in enumerate(torch_e4m3_values()) if not math.isnan(v)}
+    rows, cols = np.array([4, 1, 2]), np.array([3, 0])
+    got = oracle.gemm_tn_abs(qa, sa, qb, sb, rows=rows, cols=cols)
+    assert got.shape == (3, 2)
+    for i, m in enumerate(rows):
+        for j, n in enumerate(cols):
+            exact = sum(abs(vals[int(qa[m, k])]) * Fraction(2) ** (int(sa[m, k // 32]) - 127) *
+                        abs(vals[int(qb[n, k])]) * Fraction(2) ** (int(sb[n, k // 32]) - 127)
+                        for k in range(K))
+            assert abs(Fraction(got[i, j]) - exact) <= exact * Fraction(K, 2 ** 52), (m, n)
+
 # ------------------------------------------------------------ scale packing
 
 def test_pack_scales_hand_example():
@@ -533,6 +574,22 @@ def test_dbias_values_rounded_once():
     v = np.full((4096, 32), np.float32(1.0) + np.float32(2.0 ** -23), dtype=np.float32)
     want = np.float32(4096 * (1.0 + 2.0 ** -23))
     assert np.all(oracle.dbias_values(v) == want)
+
+
+def test_dbias_values_match_correctly_rounded_column_sums():
+    """fp32 column sums of distinct values (full 24-bit significands, exponents
+    over 2^-40 .. 2^40, both signs, a non-square shape) against the correctly
+    rounded sum of each column (math.fsum).  A transposed index, a wrong
+    leading dimension or an fp32 running sum fails here."""
+    rng = np.random.default_rng(56)
+    R, C = 300, 96
+    v = (rng.standard_normal((R, C)) * np.exp2(rng.integers(-40, 41, size=(R, C)))).astype(np.float32)
+    v[7, :] = np.float32(2.0 ** 30)          # large terms that an fp32 running sum would absorb small ones into
+    v[8, :] = np.float32(-(2.0 ** 30))
+    got = oracle.dbias_values(v)
+    assert got.dtype == np.float32 and got.shape == (C,)
+    for c in range(C):
+        assert got[c] == np.float32(math.fsum(float(t) for t in v[:, c])), c
 
 
 def test_golden_e8m0_readback():
