@@ -1,28 +1,30 @@
 """Benchmark of the MXFP8 hot path on one MI355X.
 
-Default workload (the one whose JSON line is the benchmark): the dense linear
-layer.  One step = rowwise MXFP8 quantize of X BF16[8192x4096] ~ N(0,1) and
-W BF16[14336x4096] ~ N(0,0.02), the quantizer writing the scales directly in
-the GEMM's packed word layout, the TN GEMM 8192x14336x4096 with BF16 output,
-then the same for the square A, B BF16[8192x8192] and the GEMM
-8192x8192x8192.  Inputs are resident in HBM before timing starts.  (The backward and MoE workloads keep byte
-scales plus the separate packing launch.)
+Default workload (the one whose JSON line is the benchmark): the wide-range
+stress configuration, the largest dense shape.  One step = rowwise +
+columnwise MXFP8 quantize of A BF16[32768x8192] (32-element blocks scaled by
+2^u, u uniform in [-40, 40], with max-BF16 and subnormal values injected) and
+rowwise quantize of B BF16[8192x8192] (same recipe without max-BF16), each
+writing its scales directly in the GEMM's packed word layout, then the TN
+GEMM C[32768x8192] = A B^T (K = 8192) with BF16 output.  Inputs are resident
+in HBM before timing starts.
 
 ``value`` is the end-to-end GEMM throughput of the step (GEMM FLOPs / wall
-time of the whole step, quantize and packing included).  ``roofline`` is the
-dominant kernel (the GEMM at 8192x14336x4096) against the FP8 MFMA peak, timed
-with HIP events recorded on its launch stream; ``quantize`` reports each
-quantizer launch against the HBM peak; ``cpu_baseline`` is the CPU oracle on
-the same work.
+time of the whole step, quantize included).  ``roofline`` is the dominant
+kernel (the GEMM) against the FP8 MFMA peak, timed with HIP events recorded on
+its launch stream; ``quantize_roofline`` is the largest quantize launch (A
+row+col, 1.09 GB) against the HBM peak; ``cpu_baseline`` is the CPU oracle
+running whole steps of the same workload on the host.  Per-launch times are
+reported as mean, median, min and max over the timed steps.
 
-``--workload backward|moe|moe_sqrelu|stress|linear|mlp`` measures the other
-workloads the same way: row+col+dbias quantize and the wgrad GEMM on the
-columnwise copies; the ragged grouped MoE GEMM (also with the squared-ReLU
-epilogue of an MoE first projection); the wide-range 32768x8192x8192 GEMM; one
-MXFP8 linear-layer training step (fprop, dgrad, wgrad accumulated into a BF16
-main gradient); one squared-ReLU MLP training step (six GEMMs, the activation
-and its backward fused into the quantize launches).  They are reporting aids
-next to the default line.
+``--workload dense|backward|moe|moe_sqrelu|linear|mlp`` measures the other
+workloads the same way: rowwise quantize and the TN GEMMs 8192x14336x4096 and
+8192^3; row+col+dbias quantize and the wgrad GEMM on the columnwise copies;
+the ragged grouped MoE GEMM (also with the squared-ReLU epilogue of an MoE
+first projection); one MXFP8 linear-layer training step (fprop, dgrad, wgrad
+accumulated into a BF16 main gradient); one squared-ReLU MLP training step
+(six GEMMs, the activation and its backward fused into the quantize
+launches).  They are reporting aids next to the default line.
 """
 
 import argparse
@@ -44,10 +46,12 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="dense", choices=["dense", "backward", "moe", "moe_sqrelu", "stress", "linear", "mlp"])
+    p.add_argument("--workload", default="stress",
+                   choices=["stress", "dense", "backward", "moe", "moe_sqrelu", "linear", "mlp"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
-                   help="minimum CPU-oracle time: whole oracle steps are repeated until reached")
+                   help="minimum CPU-oracle time: whole oracle steps are repeated until reached "
+                        "(at least one whole step runs)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain 256 MiB device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -168,7 +172,7 @@ def build_ops(workload, dev):
         return label
 
     ROW, COL, DB = mx.MXFP8_ROWWISE, mx.MXFP8_COLWISE, mx.MXFP8_DBIAS
-    host = None
+    host = {}
     if workload == "dense":
         lin, sq = workloads.dense_linear(), workloads.dense_square()
         host = {"X": lin["X"], "W": lin["W"], "A": sq["A"], "B": sq["B"]}
@@ -184,6 +188,7 @@ def build_ops(workload, dev):
                 "8192x8192x8192; BF16 out")
     elif workload == "backward":
         d = workloads.backward()
+        host = d
         bd = quantize_op("dY[16384x4096] row+col+dbias", d["dY"], ROW | COL | DB, packed=True)
         bx = quantize_op("X[16384x4096] col", d["X"], COL, packed=True)
         dominant = gemm_op(bd["qT"], bd["pT"], bx["qT"], bx["pT"], 4096, 4096, 16384)
@@ -192,6 +197,7 @@ def build_ops(workload, dev):
                 "4096x4096x16384 on the transposed copies")
     elif workload == "stress":
         d = workloads.stress()
+        host = d
         ba = quantize_op("A[32768x8192] row+col", d["A"], ROW | COL, packed=True)
         bb = quantize_op("B[8192x8192]", d["B"], ROW, packed=True)
         dominant = gemm_op(ba["q"], ba["p"], bb["q"], bb["p"], 32768, 8192, 8192)
@@ -202,6 +208,7 @@ def build_ops(workload, dev):
         T, K = lin["X"].shape
         N = lin["W"].shape[0]
         dy = workloads.normal_bf16((T, N), 4)
+        host = {"X": lin["X"], "W": lin["W"], "dY": dy}
         bx = quantize_op("X[%dx%d] row+col" % (T, K), lin["X"], ROW | COL, packed=True)
         bw = quantize_op("W[%dx%d] row+col" % (N, K), lin["W"], ROW | COL, packed=True)
         dominant = gemm_op(bx["q"], bx["p"], bw["q"], bw["p"], T, N, K, name="fprop ")
@@ -214,6 +221,7 @@ def build_ops(workload, dev):
                 % (T, K, N, K, T, N, K, T, K, N, N, K, T))
     elif workload == "mlp":
         lin = workloads.mlp()
+        host = dict(lin, **workloads.mlp_hidden())
         T, D = lin["X"].shape
         F = lin["W1"].shape[0]
         w2, dy = lin["W2"], lin["dY"]
@@ -238,6 +246,7 @@ def build_ops(workload, dev):
                 "into the row+col+dbias quantize of FC2's dgrad output; FC1 dgrad and wgrad" % (T, D, F))
     elif workload == "moe_sqrelu":
         d = workloads.moe()
+        host = d
         G, N, K = d["W"].shape
         Mt = d["X"].shape[0]
         bx = quantize_op("X[%dx%d]" % (Mt, K), d["X"], ROW, packed=True)
@@ -255,6 +264,7 @@ def build_ops(workload, dev):
                 % (Mt, K, G, N, K, G, np.diff(d["offsets"]).tolist()))
     else:  # moe
         d = workloads.moe()
+        host = d
         G, N, K = d["W"].shape
         Mt = d["X"].shape[0]
         bx = quantize_op("X[%dx%d]" % (Mt, K), d["X"], ROW)
@@ -344,19 +354,28 @@ def main():
         step(detail, per_launch=True)
     torch.cuda.synchronize()
 
-    def mean_ms(evs):
+    def durations(evs):
         dur = {}
         for grp, e0, e1 in evs:
             dur.setdefault(tuple(id(op) for op in grp), []).append(e0.elapsed_time(e1))
-        return {k: float(np.mean(v)) for k, v in dur.items()}
+        return dur
 
-    timed = mean_ms(events)
-    avg = {k[0]: v for k, v in mean_ms(detail).items()}
-    for k, v in timed.items():       # GEMMs: the timed-region numbers
+    def stats(v):
+        return {"ms": float(np.mean(v)), "ms_median": float(np.median(v)), "ms_min": float(np.min(v)),
+                "ms_max": float(np.max(v)), "n": len(v)}
+
+    timed_d = durations(events)
+    timed = {k: float(np.mean(v)) for k, v in timed_d.items()}
+    per = {k[0]: stats(v) for k, v in durations(detail).items()}
+    for k, v in timed_d.items():     # GEMMs: the timed-region numbers
         if len(k) == 1:
-            avg[k[0]] = v
+            per[k[0]] = stats(v)
+    avg = {k: v["ms"] for k, v in per.items()}
     short_block = [(k, v) for k, v in timed.items() if len(k) > 1 or
                    [op for op in ops if id(op) == k[0]][0].kind != "gemm"]
+
+    def rounded(st):
+        return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in st.items()}
 
     total_flops = sum(op.work for op in ops if op.kind == "gemm")
     value = total_flops / (ms_per_step * 1e-3) / 1e12
@@ -372,12 +391,14 @@ def main():
         t = avg[id(op)]
         if op.kind == "gemm":
             tf = op.work / (t * 1e-3) / 1e12
-            gemm_report[op.label] = {"ms": round(t, 4), "tflops": round(tf, 1),
-                                     "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
+            gemm_report[op.label] = dict(rounded(per[id(op)]), tflops=round(tf, 1),
+                                         frac_fp8_peak=round(tf / FP8_PEAK_TFLOPS, 4),
+                                         tflops_at_median=round(op.work / (per[id(op)]["ms_median"] * 1e-3) / 1e12, 1))
         else:
             gbs = op.work / (t * 1e-3) / 1e9
             rep = quant_report if op.kind == "quantize" else pack_report
-            rep[op.label] = {"ms": round(t, 4), "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+            rep[op.label] = dict(rounded(per[id(op)]), gbs=round(gbs, 1), frac_hbm_peak=round(gbs / HBM_PEAK_GBS, 4),
+                                 gbs_at_median=round(op.work / (per[id(op)]["ms_median"] * 1e-3) / 1e9, 1))
 
     dom = [op for op in ops if op.kind == "gemm" and op.label == dominant][0]
     dom_t = avg[id(dom)]
@@ -385,7 +406,8 @@ def main():
     prof = profiled_traffic("gemm:" + dominant.replace(" ", ":"))
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": prof[0] if prof else None,
-                "kernel": "mxfp8 gemm " + dominant, "ms": round(dom_t, 4)}
+                "kernel": "mxfp8 gemm " + dominant, "flops_per_launch": dom.work}
+    roofline.update(rounded(per[id(dom)]))
     if prof:
         roofline["traffic_unit"] = "bytes per launch (HBM side, calibrated FETCH_SIZE + WRITE_SIZE)"
         roofline["traffic_source"] = "profiles/" + prof[1]
@@ -403,9 +425,9 @@ def main():
         in_steps_ms = sum(t for _, t in short_block)
         qroof = {"bound": "hbm", "achieved": round(qgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                  "frac": round(qgbs / HBM_PEAK_GBS, 4), "traffic": qprof[0] if qprof else None,
-                 "kernel": "mxfp8 quantize " + qdom.label, "ms": round(qt, 4),
-                 "bytes_per_launch": qdom.work,
+                 "kernel": "mxfp8 quantize " + qdom.label, "bytes_per_launch": qdom.work,
                  "all_short_launches_in_steps_gbs": round(in_steps / (in_steps_ms * 1e-3) / 1e9, 1)}
+        qroof.update(rounded(per[id(qdom)]))
         if qprof:
             qroof["traffic_source"] = "profiles/" + qprof[1]
 
@@ -431,42 +453,131 @@ def main():
         "short_launch_blocks": block_report,
         "launch_order": [op.kind + " " + op.label for op in ops],
         "timing_note": "gemm: HIP events per launch in the timed steps; quantize / pack: per-launch events in a "
-                       "separate pass after them; short_launch_blocks: the same launches as timed in the steps",
+                       "separate pass after them (%d steps); ms = mean, with median, min and max; "
+                       "short_launch_blocks: the same launches as timed in the steps" % min(args.steps, 10),
     }
-    if host is not None and not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(host, args.cpu_seconds)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.workload, host, total_flops, args.cpu_seconds)
 
     print(json.dumps(result))
 
 
-def cpu_baseline(host, min_seconds):
-    """The CPU oracle on the same step: rowwise quantize of X, W, A, B, scale
-    packing, and the two GEMMs in fp64; whole steps are repeated until
-    min_seconds have passed.  Reported as GEMM TFLOP/s, like ``value``."""
+def oracle_step(workload, h):
+    """One step of the workload run by the CPU oracle on the same inputs: the
+    same quantizations (scale packing where the GPU step writes packed words),
+    dbias and activations where the GPU fuses them, and every GEMM in fp64 in
+    1024-row panels.  Returns the step callable and a description."""
+    import numpy as np
+
+    import oracle
+    P = 1024
+
+    def both(x):
+        q, s = oracle.quantize_rowwise(x)
+        qT, sT = oracle.quantize_colwise(x)
+        oracle.pack_scales(s)
+        oracle.pack_scales(sT)
+        return q, s, qT, sT
+
+    def rowp(x):
+        q, s = oracle.quantize_rowwise(x)
+        oracle.pack_scales(s)
+        return q, s
+
+    if workload == "stress":
+        def step():
+            qa, sa, _, _ = both(h["A"])
+            qb, sb = rowp(h["B"])
+            oracle.gemm_tn(qa, sa, qb, sb, panel=P)
+        return step, ("rowwise + columnwise quantize of A[32768x8192], rowwise B[8192x8192], scale packing, "
+                      "fp64 GEMM 32768x8192x8192")
+    if workload == "dense":
+        def step():
+            for a, b in (("X", "W"), ("A", "B")):
+                oracle.gemm_tn(*rowp(h[a]), *rowp(h[b]), panel=P)
+        return step, ("rowwise quantize of X, W, A, B, scale packing, fp64 GEMMs 8192x14336x4096 and "
+                      "8192x8192x8192")
+    if workload == "backward":
+        def step():
+            _, _, qdT, sdT = both(h["dY"])
+            oracle.dbias(h["dY"])
+            qxT, sxT = oracle.quantize_colwise(h["X"])
+            oracle.pack_scales(sxT)
+            oracle.gemm_tn(qdT, sdT, qxT, sxT, panel=P)
+        return step, ("rowwise + columnwise quantize and dbias of dY[16384x4096], columnwise X, scale packing, "
+                      "fp64 wgrad 4096x4096x16384")
+    if workload in ("moe", "moe_sqrelu"):
+        def step():
+            qx, sx = rowp(h["X"])
+            ws = [rowp(w) for w in h["W"]]
+            c = oracle.grouped_gemm_tn(qx, sx, np.stack([q for q, _ in ws]), np.stack([s for _, s in ws]),
+                                       h["offsets"], panel=P)
+            if workload == "moe_sqrelu":
+                oracle.sqrelu_epilogue(c)
+        return step, ("rowwise quantize of X[16384x4096] and W[8][14336x4096], scale packing, fp64 grouped "
+                      "GEMM" + (" with the relu^2 epilogue" if workload == "moe_sqrelu" else ""))
+    if workload == "linear":
+        def step():
+            qx, sx, qxT, sxT = both(h["X"])
+            qw, sw, qwT, swT = both(h["W"])
+            qd, sd, qdT, sdT = both(h["dY"])
+            oracle.gemm_tn(qx, sx, qw, sw, panel=P)
+            oracle.gemm_tn(qd, sd, qwT, swT, panel=P)
+            oracle.gemm_tn(qdT, sdT, qxT, sxT, panel=P)
+        return step, "row+col quantize of X, W, dY, scale packing, fp64 fprop, dgrad and wgrad"
+    if workload == "mlp":
+        def step():
+            qx, sx, qxT, sxT = both(h["X"])
+            q1, s1, q1T, s1T = both(h["W1"])
+            q2, s2, q2T, s2T = both(h["W2"])
+            qy, sy, qyT, syT = both(h["dY"])
+            oracle.gemm_tn(qx, sx, q1, s1, panel=P)                 # fc1
+            a = oracle.act_sqrelu(h["H"])
+            qa, sa = oracle.quantize_rowwise_values(a)
+            qaT, saT = oracle.quantize_colwise_values(a)
+            oracle.gemm_tn(qa, sa, q2, s2, panel=P)                 # fc2
+            oracle.gemm_tn(qy, sy, q2T, s2T, panel=P)               # fc2 dgrad
+            oracle.gemm_tn(qyT, syT, qaT, saT, panel=P)             # fc2 wgrad
+            g = oracle.dact_sqrelu(h["dA"], h["H"])
+            qg, sg = oracle.quantize_rowwise_values(g)
+            qgT, sgT = oracle.quantize_colwise_values(g)
+            oracle.dbias_values(g)
+            oracle.gemm_tn(qg, sg, q1T, s1T, panel=P)               # fc1 dgrad
+            oracle.gemm_tn(qgT, sgT, qxT, sxT, panel=P)             # fc1 wgrad
+        return step, ("row+col quantize of X, W1, W2, dY, the relu^2 activation and its backward (on the "
+                      "full-size stand-ins for the GEMM outputs H and dA) quantized row+col (+dbias), six fp64 "
+                      "GEMMs")
+    raise ValueError(workload)
+
+
+def cpu_baseline(workload, host, flops_per_step, min_seconds):
+    """The CPU oracle running whole steps of the same workload on the host
+    cores until min_seconds have passed (at least one step).  Reported as GEMM
+    TFLOP/s of the step, like ``value``."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas_threads = 1
-    flops = 2.0 * (8192 * 14336 * 4096 + 8192 * 8192 * 8192)
-    steps = 0
+    step, what = oracle_step(workload, host)
+    steps, times = 0, []
     t0 = time.perf_counter()
     while True:
-        q = {name: oracle.quantize_rowwise(bits) for name, bits in host.items()}
-        _ = [oracle.pack_scales(s) for _, s in q.values()]
-        for a, b in (("X", "W"), ("A", "B")):
-            c = oracle.gemm_tn(*q[a], *q[b])
-            del c
+        ts = time.perf_counter()
+        step()
+        times.append(time.perf_counter() - ts)
         steps += 1
         t1 = time.perf_counter()
         if t1 - t0 >= min_seconds:
             break
-    return {"value": round(steps * flops / (t1 - t0) / 1e12, 5), "unit": "TFLOP/s",
+    import numpy as np
+    return {"value": round(steps * flops_per_step / (t1 - t0) / 1e12, 5), "unit": "TFLOP/s",
             "cores": int(max(oracle.num_threads(), blas_threads)), "kind": "oracle",
-            "seconds": round(t1 - t0, 2), "steps": steps,
-            "sample": "%d whole step(s) of the same workload on the host: oracle rowwise quantize of X, W, A, B, "
-                      "scale packing, fp64 GEMMs 8192x14336x4096 and 8192x8192x8192" % steps}
+            "omp_threads": int(oracle.num_threads()), "blas_threads": int(blas_threads),
+            "host_cpu_count": os.cpu_count(),
+            "seconds": round(t1 - t0, 2), "steps": steps, "step_s_median": round(float(np.median(times)), 3),
+            "sample": "%d whole step(s) of the same workload on the host: %s" % (steps, what)}
 
 
 if __name__ == "__main__":

@@ -284,9 +284,13 @@ mxfp8_status mxfp8_gemm_ex(const uint8_t *a, const uint32_t *a_packed,
  *            row g*N + n).
  * offsets    DEVICE int32 [G+1]: offsets[0] = 0, non-decreasing,
  *            offsets[G] <= M_total.  Rows of C outside every group are not
- *            written.  Values are read on the device only; out-of-range or
- *            decreasing offsets are clamped (such groups become empty) so no
- *            access leaves the buffers.
+ *            written.  Values are read on the device only.  Invalid offsets
+ *            cannot make an access leave the buffers: each bound is clamped
+ *            into [0, M_total] and then raised to the largest bound before
+ *            it, i.e. group g covers rows [e_g, e_{g+1}) with
+ *            e_i = max_{j <= i} clamp(offsets[j], 0, M_total).  Groups
+ *            therefore never overlap, and a group whose offsets decrease is
+ *            empty (for valid offsets e_i = offsets[i]).
  * G          1 <= G <= 65536.
  * c          BF16 [M_total][ldc]; ldc >= N, ldc % 8 == 0.
  * M_total >= 0; N >= 0 and N % 32 == 0; K >= 0, K % 128 == 0 and K <= 2^22.

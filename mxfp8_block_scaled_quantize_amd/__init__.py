@@ -173,7 +173,8 @@ def quantize(x, rowwise=True, colwise=False, dbias=False, amax=False, packed=Fal
 
     packed=True returns the scales in the packed word layout ("p_row" int32
     [cols/128, rows], "p_colT" int32 [rows/128, cols]) instead of bytes;
-    amax=True adds "amax" (fp32 [1]); noop is an optional device int32 flag.
+    amax=True adds "amax" (fp32 [1]); noop is an optional int32 tensor on x's
+    device whose first element is the flag (nonzero: nothing is written).
     act="sqrelu" quantizes relu(x)^2; act="dsqrelu" quantizes
     x * 2 relu(act_in) (x is the gradient, act_in the activation's input, a
     BF16 tensor of x's shape and strides)."""
@@ -184,6 +185,9 @@ def quantize(x, rowwise=True, colwise=False, dbias=False, amax=False, packed=Fal
         raise ValueError("x must be a CUDA (HIP) tensor, got %s" % x.device)
     R, C = x.shape
     dev = x.device
+    if noop is not None and (not isinstance(noop, torch.Tensor) or noop.dtype != torch.int32
+                             or noop.device != dev or noop.numel() < 1):
+        raise ValueError("noop must be an int32 tensor with at least one element on x's device (%s)" % dev)
     flags = (MXFP8_ROWWISE if rowwise else 0) | (MXFP8_COLWISE if colwise else 0) | (MXFP8_DBIAS if dbias else 0)
     flags |= (MXFP8_AMAX if amax else 0) | (MXFP8_PACKED_SCALES if packed else 0)
     if act == "sqrelu":

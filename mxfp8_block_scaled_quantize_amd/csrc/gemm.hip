@@ -49,14 +49,16 @@ constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 128;                 // K bytes per pipeline step
 constexpr int NSLOT = 2;
-constexpr int A_BYTES = BM * BK;        // 16 KB
-constexpr int B_BYTES = BN * BK;        // 16 KB
+constexpr int A_BYTES = BM * BK;        // 32 KB
+constexpr int B_BYTES = BN * BK;        // 32 KB
 constexpr int SA_OFF = A_BYTES + B_BYTES;
 constexpr int SB_OFF = SA_OFF + BM * 4;
-constexpr int SLOT_BYTES = SB_OFF + BN * 4;          // 34 KB
-constexpr int LDS_BYTES = NSLOT * SLOT_BYTES;        // 136 KB
+constexpr int SLOT_BYTES = SB_OFF + BN * 4;          // 66 KB (67584 B)
+constexpr int LDS_BYTES = NSLOT * SLOT_BYTES;        // 132 KB (135168 B)
 constexpr int GROUP = 4;                // tiles per L2 group
 constexpr int C_LDS_STRIDE = 2 * BN + 16;            // BF16 output tile row in LDS, padded (528 B)
+// The staged output tile (256 x 528 B = 135168 B) fills the ring exactly: a
+// wider row stride needs a larger ring.
 static_assert(BM * C_LDS_STRIDE <= LDS_BYTES, "output tile must fit in the ring");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 constexpr uint32_t RSRC_FLAGS = 0x00020000u;         // raw buffer, 32-bit data format
@@ -127,22 +129,33 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
   int64_t m_lo, m_hi, b_row0 = 0;
   if (GROUPED) {
     // Row tile tm counts the groups' tiles in order.  Each wave looks at 64
-    // groups at a time: lane g loads its group's bounds (clamped into
-    // [0, M], empty when reversed), a wave prefix sum of the tile counts
-    // finds the group holding tile tm, and the result is broadcast from that
-    // lane.  Every wave of the workgroup computes the same answer.
+    // groups at a time: lane g loads its group's bounds, a wave prefix sum of
+    // the tile counts finds the group holding tile tm, and the result is
+    // broadcast from that lane.  Every wave of the workgroup computes the
+    // same answer.  Bounds are clamped into [0, M] and then replaced by the
+    // running maximum of all bounds so far (carried across 64-group chunks),
+    // so groups never overlap even for decreasing offsets (such a group is
+    // empty) and the tile count stays within ceil(M / 256) + G.
     int found = -1;
     m_lo = m_hi = 0;
+    int carry = 0;   // running maximum of the clamped bounds of earlier chunks
     for (int g0 = 0; g0 < G; g0 += 64) {
       const int g = g0 + lane;
-      int64_t lo = 0, hi = 0;
+      int lo = 0, hi = 0;
       if (g < G) {
-        lo = offsets[g];
-        hi = offsets[g + 1];
-        lo = lo < 0 ? 0 : (lo > M ? M : lo);
-        hi = hi < lo ? lo : (hi > M ? M : hi);
+        const int64_t l = offsets[g], h = offsets[g + 1];
+        lo = (int)(l < 0 ? 0 : (l > M ? M : l));
+        hi = (int)(h < 0 ? 0 : (h > M ? M : h));
       }
-      const int nt = (int)((hi - lo + BM - 1) / BM);
+      lo = lo > carry ? lo : carry;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {   // inclusive prefix max of the lower bounds
+        const int t = __shfl_up(lo, d, 64);
+        if (lane >= d) lo = lo > t ? lo : t;
+      }
+      hi = hi > lo ? hi : lo;
+      carry = __builtin_amdgcn_readlane(hi, 63);
+      const int nt = (hi - lo + BM - 1) / BM;
       int incl = nt;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
@@ -154,8 +167,8 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
         const int fl = __builtin_ctzll(__ballot(incl > tm));
         const int before = __builtin_amdgcn_readlane(incl - nt, fl);
         found = g0 + fl;
-        m_lo = (int64_t)__builtin_amdgcn_readlane((int)lo, fl) + (tm - before) * BM;
-        m_hi = (int64_t)__builtin_amdgcn_readlane((int)hi, fl);
+        m_lo = (int64_t)__builtin_amdgcn_readlane(lo, fl) + (tm - before) * BM;
+        m_hi = (int64_t)__builtin_amdgcn_readlane(hi, fl);
         break;
       }
       tm -= total;
@@ -173,9 +186,6 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
 
   // ---- DMA addressing (same for A and B).  Data goes through raw buffers
   // over the tile's rows, so rows past the end of the operand read as zero.
-  // DMA instruction i of wave w covers LDS rows 8(8w+i) + lane/8, chunk slot
-  // lane%8; the swizzle (row>>1)&7 = (4(i&1) + lane/16) & 7 only depends on
-  // the parity of i.
   // DMA instruction i of wave w covers LDS rows 8(8w + i) + lane/8, chunk
   // slot lane%8; the swizzle (row >> 1) & 7 is (4i + lane/16) & 7.  The step's
   // K offset goes into the scalar offset field.

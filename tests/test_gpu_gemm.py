@@ -9,8 +9,8 @@ import pytest
 import mxfp8_block_scaled_quantize_amd as mx
 import oracle
 import workloads
-from gpu_util import (bf16_to_f64, gemm_tolerance_check, log, need_gpu, sample_indices, to_dev,
-                      to_dev_bf16, to_host)
+from gpu_util import (bf16_to_f64, gemm_full_check, gemm_tolerance_check, log, need_gpu,
+                      overflow_candidate_rows, to_dev, to_dev_bf16, to_host, whole_output_rms)
 
 pytestmark = pytest.mark.gpu
 
@@ -86,7 +86,11 @@ def test_tiny_config():
 
 
 @pytest.mark.parametrize("M,N,K", [(32, 32, 128), (96, 224, 384), (160, 96, 1024), (1000, 320, 256),
-                                   (7, 64, 128), (256, 4096, 128), (130, 160, 2048), (288, 288, 1152)])
+                                   (7, 64, 128), (256, 4096, 128), (130, 160, 2048), (288, 288, 1152),
+                                   # 10 x 3 and 3 x 11 tiles of 256: the L2 groups of 4 tiles along the
+                                   # larger dimension end in a partial group, and the tile count is not
+                                   # a multiple of the 8 XCDs (both branches of the tile remap)
+                                   (2520, 736, 256), (700, 2800, 256)])
 def test_ragged_gemm_shapes(M, N, K):
     a = workloads.normal_bf16((M, K), M + K)
     b = workloads.normal_bf16((N, K), N + 3 * K, std=0.5)
@@ -283,14 +287,16 @@ def grouped_case(M, N, K, counts, seed, canary_rows=True, accumulate=False, sqre
         assert np.all(bf16_to_f64(c[~covered]) == -7.0), "rows outside the groups were written"
 
 
-def sqrelu_tolerance_check(gpu_bits, r, K, label=""):
+def sqrelu_tolerance_check(gpu_bits, r, K, label="", rms=None):
     """relu(R)^2 epilogue: the GPU forms relu(acc)^2 from its fp32 sum acc,
     |acc - R| <= t = 8e-3 |R| + 1e-3 sqrt(K) rms(R) (the GEMM bound), so
     |relu(acc)^2 - relu(R)^2| <= t (2|R| + t), plus the one BF16 rounding,
     2^-9 (|R| + t)^2 (doubled for margin)."""
     gpu = bf16_to_f64(gpu_bits)
     r = np.asarray(r, dtype=np.float64)
-    t = 8e-3 * np.abs(r) + 1e-3 * np.sqrt(K) * np.sqrt(np.mean(r ** 2))
+    if rms is None:
+        rms = np.sqrt(np.mean(r ** 2))
+    t = 8e-3 * np.abs(r) + 1e-3 * np.sqrt(K) * rms
     tol = t * (2 * np.abs(r) + t) + 2.0 ** -8 * (np.abs(r) + t) ** 2
     err = np.abs(gpu - oracle.sqrelu_epilogue(r))
     bad = ~(err <= tol)
@@ -350,6 +356,33 @@ def test_grouped_accumulate():
     grouped_case(1200, 96, 256, [5, 0, 131, 257, 600], 8, accumulate=True)
 
 
+def test_grouped_decreasing_offsets_never_overlap():
+    """Offsets that decrease or leave [0, M]: each bound is clamped into
+    [0, M] and raised to the largest bound before it, so groups never
+    overlap (a decreasing group is empty).  The result equals the oracle's
+    grouped GEMM on those effective bounds, and rows outside them are not
+    written."""
+    torch = need_gpu()
+    M, N, K = 256, 96, 256
+    raw = np.array([-5, 100, 50, 200, 170, 300, 260], dtype=np.int32)
+    G = len(raw) - 1
+    eff = np.maximum.accumulate(np.clip(raw.astype(np.int64), 0, M))
+    assert eff.tolist() == [0, 100, 100, 200, 200, 256, 256]
+    x = workloads.normal_bf16((M, K), 71)
+    w = workloads.normal_bf16((G, N, K), 72, std=0.02)
+    qx, sx, px = quantize_on_gpu(x)
+    wq = quantize_on_gpu(w.reshape(G * N, K))
+    out = torch.full((M, N), -7.0, dtype=torch.bfloat16, device="cuda")
+    log("grouped decreasing offsets %s" % raw.tolist())
+    mx.grouped_gemm(qx, px, wq[0].view(G, N, K), wq[2], to_dev(raw), out=out)
+    torch.cuda.synchronize()
+    c = to_host(out)
+    oqx, osx = oracle.quantize_rowwise(x)
+    oq = [oracle.quantize_rowwise(w[g]) for g in range(G)]
+    ref = oracle.grouped_gemm_tn(oqx, osx, np.stack([q for q, _ in oq]), np.stack([s for _, s in oq]), eff)
+    gemm_tolerance_check(c, ref, K, label="grouped decreasing offsets")
+
+
 def test_grouped_many_experts():
     """More experts than a wave's 64 lanes (the device-side group search walks
     the offsets 64 groups at a time): 200 ragged groups, empty ones among them
@@ -376,99 +409,138 @@ def test_grouped_empty_total():
 
 
 # ------------------------------------------------------ full workload sizes
+#
+# Every entry of every full-size output is compared with the oracle (fp64 in
+# row panels), with rms over the whole output: a misplaced or skipped tile of
+# the XCD / L2-group tile remap cannot hide between samples.
 
-@pytest.mark.slow
-def test_full_dense_linear_sampled():
-    d = workloads.dense_linear()
-    rows = sample_indices(8192, 48, 1)
-    cols = sample_indices(14336, 48, 2)
-    check_dense(d["X"], d["W"], "dense 8192x14336x4096", rows=rows, cols=cols)
-
-
-@pytest.mark.slow
-def test_full_dense_square_sampled():
-    d = workloads.dense_square()
-    rows = sample_indices(8192, 40, 3)
-    cols = sample_indices(8192, 40, 4)
-    check_dense(d["A"], d["B"], "dense 8192^3", rows=rows, cols=cols)
+PANEL = 2048
 
 
-@pytest.mark.slow
-def test_full_backward_wgrad_sampled():
-    d = workloads.backward()
-    qa, sa, pa = quantize_on_gpu(d["dY"], colwise=True)    # [4096][16384]
-    qb, sb, pb = quantize_on_gpu(d["X"], colwise=True)     # [4096][16384]
-    log("wgrad 4096x4096x16384")
+def full_dense(qa, pa, qb, pb, oq_a, oq_b, K, label, excl=None):
+    """GPU GEMM of device operands against the oracle's GEMM of its own
+    quantizations (oq_a, oq_b = (codes, scales)) on every entry."""
+    log("%s M=%d N=%d K=%d (every entry)" % (label, qa.shape[0], qb.shape[0], K))
     c = gemm_gpu(qa, pa, qb, pb)
-    rows = sample_indices(4096, 40, 5)
-    cols = sample_indices(4096, 40, 6)
-    oqa, osa = oracle.quantize_colwise(d["dY"])
-    oqb, osb = oracle.quantize_colwise(d["X"])
-    ref = oracle.gemm_tn(oqa, osa, oqb, osb, rows=rows, cols=cols)
-    gemm_tolerance_check(c[np.ix_(rows, cols)], ref, 16384, label="wgrad")
+    ref = oracle.gemm_tn(*oq_a, *oq_b, panel=PANEL)
+    return gemm_full_check(c, ref, K, excl=excl, label=label, panel=PANEL)
 
 
 @pytest.mark.slow
-def test_full_stress_sampled():
+def test_full_dense_linear():
+    d = workloads.dense_linear()
+    qa, _, pa = quantize_on_gpu(d["X"])
+    qb, _, pb = quantize_on_gpu(d["W"])
+    full_dense(qa, pa, qb, pb, oracle.quantize_rowwise(d["X"]), oracle.quantize_rowwise(d["W"]), 4096,
+               "dense 8192x14336x4096")
+
+
+@pytest.mark.slow
+def test_full_dense_square():
+    d = workloads.dense_square()
+    qa, _, pa = quantize_on_gpu(d["A"])
+    qb, _, pb = quantize_on_gpu(d["B"])
+    full_dense(qa, pa, qb, pb, oracle.quantize_rowwise(d["A"]), oracle.quantize_rowwise(d["B"]), 8192,
+               "dense 8192^3")
+
+
+@pytest.mark.slow
+def test_full_backward_wgrad():
+    d = workloads.backward()
+    qa, _, pa = quantize_on_gpu(d["dY"], colwise=True)    # [4096][16384]
+    qb, _, pb = quantize_on_gpu(d["X"], colwise=True)     # [4096][16384]
+    full_dense(qa, pa, qb, pb, oracle.quantize_colwise(d["dY"]), oracle.quantize_colwise(d["X"]), 16384,
+               "wgrad 4096x4096x16384")
+
+
+@pytest.mark.slow
+def test_full_stress():
+    """Stress GEMM 32768x8192x8192 on every entry.  Entries whose term
+    magnitudes reach 2^127 are excluded from the tolerance and from rms; the
+    rows that can hold them are found from the scale bytes (a rigorous bound)
+    and their magnitudes come from the oracle.  The excluded count is checked
+    against a count made from the input alone: a row's max-BF16 inputs
+    quantize to 448 * 2^119 = 1.75 * 2^127 (the rest of their block flushes to
+    zero), so an entry is excluded when 1.75 * 2^127 * sum |dq(b)| over those
+    positions, plus at most the row's other terms, reaches 2^127."""
     d = workloads.stress()
-    a = d["A"]
-    # include the rows that carry max-BF16 values (overflow exclusion applies)
-    hot = np.unique(np.nonzero((a & 0x7FFF) == workloads.BF16_MAX_BITS)[0])[:8]
-    rows = np.unique(np.concatenate([sample_indices(32768, 32, 7), hot]))
-    cols = sample_indices(8192, 32, 8)
-    n_ex, _, _ = check_dense(a, d["B"], "stress 32768x8192x8192", rows=rows, cols=cols)
-    log("stress: %d entries excluded for overflow" % n_ex)
+    a, b = d["A"], d["B"]
+    K = a.shape[1]
+    oqa, osa = oracle.quantize_rowwise(a)
+    oqb, osb = oracle.quantize_rowwise(b)
+    hot = overflow_candidate_rows(osa, osb, K)
+    max_rows = np.unique(np.nonzero((a & 0x7FFF) == workloads.BF16_MAX_BITS)[0])
+    assert set(max_rows.tolist()) <= set(hot.tolist()) and len(max_rows) > 0
+    excl = np.zeros((a.shape[0], b.shape[0]), dtype=bool)
+    mag = oracle.gemm_tn_abs(oqa, osa, oqb, osb, rows=hot)
+    excl[hot] = mag >= 2.0 ** 127
+    qa, _, pa = quantize_on_gpu(a)
+    qb, _, pb = quantize_on_gpu(b)
+    n_ex = full_dense(qa, pa, qb, pb, (oqa, osa), (oqb, osb), K, "stress 32768x8192x8192", excl=excl)
+    # independent count from the max-BF16 positions of the input
+    db_abs = np.abs(oracle.dequantize(oqb, osb))
+    other = (osa.astype(np.float64), osb.astype(np.float64))
+    lo = hi = 0
+    for m in max_rows:
+        pos = np.nonzero((a[m] & 0x7FFF) == workloads.BF16_MAX_BITS)[0]
+        big = 1.75 * 2.0 ** 127 * db_abs[:, pos].sum(axis=1)
+        blocks_with_max = set((pos // 32).tolist())
+        rest_bytes = [other[0][m, j] for j in range(K // 32) if j not in blocks_with_max]
+        rest = K * 448.0 * 448.0 * 2.0 ** ((max(rest_bytes) if rest_bytes else 0) + other[1].max() - 254.0)
+        lo += int(np.sum(big >= 2.0 ** 127))
+        hi += int(np.sum(big + rest >= 2.0 ** 127))
+    log("stress: %d entries excluded for overflow (independent count %d..%d)" % (n_ex, lo, hi))
+    assert lo <= n_ex <= hi and n_ex > 0
+
+
+def _moe_refs(x, w, off):
+    G = w.shape[0]
+    oqx, osx = oracle.quantize_rowwise(x)
+    ws = [oracle.quantize_rowwise(w[g]) for g in range(G)]
+    return oracle.grouped_gemm_tn(oqx, osx, np.stack([q for q, _ in ws]), np.stack([s for _, s in ws]), off,
+                                  panel=PANEL)
 
 
 @pytest.mark.slow
-def test_full_moe_sampled():
+def test_full_moe():
     torch = need_gpu()
     d = workloads.moe()
     x, w, off = d["X"], d["W"], d["offsets"]
     G, N, K = w.shape
     qx, sx, px = quantize_on_gpu(x)
     wq = quantize_on_gpu(w.reshape(G * N, K))
-    log("moe grouped 16384x14336x4096 counts=%s" % np.diff(off).tolist())
-    c = mx.grouped_gemm(qx, px, wq[0].view(G, N, K), wq[2], to_dev(off))
+    log("moe grouped 16384x14336x4096 counts=%s (every entry)" % np.diff(off).tolist())
+    c = to_host(mx.grouped_gemm(qx, px, wq[0].view(G, N, K), wq[2], to_dev(off)))
     torch.cuda.synchronize()
-    rows = sample_indices(16384, 48, 9)
-    cols = sample_indices(N, 32, 10)
-    ch = to_host(c)[np.ix_(rows, cols)]
-    oqx, osx = oracle.quantize_rowwise(x)
-    ws = [oracle.quantize_rowwise(w[g]) for g in range(G)]
-    ref = oracle.grouped_gemm_tn(oqx, osx, np.stack([q for q, _ in ws]), np.stack([s for _, s in ws]), off,
-                                 rows=rows, cols=cols)
-    gemm_tolerance_check(ch, ref, K, label="moe")
+    ref = _moe_refs(x, w, off)
+    assert off[0] == 0 and off[-1] == x.shape[0] and not np.isnan(ref).any()
+    gemm_full_check(c, ref, K, label="moe", panel=PANEL)
 
 
 @pytest.mark.slow
-def test_full_moe_sqrelu_sampled():
+def test_full_moe_sqrelu():
     """The MoE first projection with the relu^2 epilogue as the benchmark runs
-    it (operands quantized into packed scales), sampled against the oracle."""
+    it (operands quantized into packed scales), every entry."""
     torch = need_gpu()
     d = workloads.moe()
     x, w, off = d["X"], d["W"], d["offsets"]
     G, N, K = w.shape
     px_ = mx.quantize(to_dev_bf16(x), packed=True)
     pw_ = mx.quantize(to_dev_bf16(w.reshape(G * N, K)), packed=True)
-    log("moe relu^2 grouped 16384x14336x4096")
-    c = mx.grouped_gemm(px_["q_row"], px_["p_row"], pw_["q_row"].view(G, N, K), pw_["p_row"], to_dev(off),
-                        sqrelu=True)
+    log("moe relu^2 grouped 16384x14336x4096 (every entry)")
+    c = to_host(mx.grouped_gemm(px_["q_row"], px_["p_row"], pw_["q_row"].view(G, N, K), pw_["p_row"],
+                                to_dev(off), sqrelu=True))
     torch.cuda.synchronize()
-    rows = sample_indices(16384, 48, 11)
-    cols = sample_indices(N, 32, 12)
-    ch = to_host(c)[np.ix_(rows, cols)]
-    oqx, osx = oracle.quantize_rowwise(x)
-    ws = [oracle.quantize_rowwise(w[g]) for g in range(G)]
-    ref = oracle.grouped_gemm_tn(oqx, osx, np.stack([q for q, _ in ws]), np.stack([s for _, s in ws]), off,
-                                 rows=rows, cols=cols)
-    sqrelu_tolerance_check(ch, ref, K, label="moe relu^2")
+    ref = _moe_refs(x, w, off)
+    rms = whole_output_rms(ref, panel=PANEL)
+    for r0 in range(0, ref.shape[0], PANEL):
+        sqrelu_tolerance_check(c[r0:r0 + PANEL], ref[r0:r0 + PANEL], K, label="moe relu^2", rms=rms)
 
 
 @pytest.mark.slow
-def test_full_linear_wgrad_accumulate_sampled():
+def test_full_linear_wgrad_accumulate():
     """The linear step's wgrad with accumulation at its full size
-    (14336 x 4096, K = 8192 tokens) on the transposed copies."""
+    (14336 x 4096, K = 8192 tokens) on the transposed copies, every entry."""
     torch = need_gpu()
     lin = workloads.dense_linear()
     x = lin["X"]                                        # [8192][4096]
@@ -477,35 +549,26 @@ def test_full_linear_wgrad_accumulate_sampled():
     qb, sb, pb = quantize_on_gpu(x, colwise=True)       # [4096][8192]
     c_old = workloads.normal_bf16((14336, 4096), 13, std=8.0)
     cd = to_dev_bf16(c_old)
-    log("wgrad accumulate 14336x4096x8192")
+    log("wgrad accumulate 14336x4096x8192 (every entry)")
     mx.gemm(qa, pa, qb, pb, out=cd, accumulate=True)
     torch.cuda.synchronize()
-    rows = sample_indices(14336, 40, 11)
-    cols = sample_indices(4096, 40, 12)
-    oqa, osa = oracle.quantize_colwise(dy)
-    oqb, osb = oracle.quantize_colwise(x)
-    ref = oracle.gemm_tn(oqa, osa, oqb, osb, rows=rows, cols=cols) + bf16_to_f64(c_old[np.ix_(rows, cols)])
-    gemm_tolerance_check(to_host(cd)[np.ix_(rows, cols)], ref, 8192, label="wgrad accumulate")
+    ref = oracle.gemm_tn(*oracle.quantize_colwise(dy), *oracle.quantize_colwise(x), panel=PANEL)
+    ref += bf16_to_f64(c_old)
+    gemm_full_check(to_host(cd), ref, 8192, label="wgrad accumulate", panel=PANEL)
 
 
 @pytest.mark.slow
-def test_full_linear_dgrad_sampled():
+def test_full_linear_dgrad():
     """The linear step's dgrad at its full size (8192 x 4096, K = 14336, the
     reduction of the MLP's second projection too): dY rowwise times W's
-    transposed copy."""
+    transposed copy, every entry."""
     need_gpu()
     w = workloads.dense_linear()["W"]                   # [14336][4096]
     dy = workloads.normal_bf16((8192, 14336), 4)        # [8192][14336]
-    qa, sa, pa = quantize_on_gpu(dy)                    # [8192][14336]
-    qb, sb, pb = quantize_on_gpu(w, colwise=True)       # [4096][14336]
-    log("dgrad 8192x4096x14336")
-    c = gemm_gpu(qa, pa, qb, pb)
-    rows = sample_indices(8192, 40, 14)
-    cols = sample_indices(4096, 40, 15)
-    oqa, osa = oracle.quantize_rowwise(dy)
-    oqb, osb = oracle.quantize_colwise(w)
-    ref = oracle.gemm_tn(oqa, osa, oqb, osb, rows=rows, cols=cols)
-    gemm_tolerance_check(c[np.ix_(rows, cols)], ref, 14336, label="dgrad")
+    qa, _, pa = quantize_on_gpu(dy)                     # [8192][14336]
+    qb, _, pb = quantize_on_gpu(w, colwise=True)        # [4096][14336]
+    full_dense(qa, pa, qb, pb, oracle.quantize_rowwise(dy), oracle.quantize_colwise(w), 14336,
+               "dgrad 8192x4096x14336")
 
 
 def test_side_stream_pipeline_matches_default_stream():

@@ -87,3 +87,43 @@ def test_linear_fused_wgrad_accumulation():
     _, _, dw2_ref = _refs(x, w, dy2)
     # the second step adds to the BF16 result of the first
     gemm_tolerance_check(to_host(main), dw2_ref + bf16_to_f64(got1), M, label="accumulate 2")
+
+
+def test_linear_module_reuses_weight_quantization_until_the_weight_changes(monkeypatch):
+    """MXFP8Linear quantizes W once per weight value: a second forward with an
+    unchanged weight launches only the input's quantize; an in-place update
+    (as an optimizer step does) makes the next forward quantize W again.
+    Outputs match the oracle on the current weight each time."""
+    torch = need_gpu()
+    import mxfp8_block_scaled_quantize_amd.linear as lin
+    calls = []
+    real = lin.quantize
+
+    def counting(t, **kw):
+        calls.append(tuple(t.shape))
+        return real(t, **kw)
+
+    monkeypatch.setattr(lin, "quantize", counting)
+    x1, w, _ = _inputs(33)
+    x2 = workloads.normal_bf16((M, K), 34)
+    layer = lin.MXFP8Linear(K, N, device="cuda")
+    with torch.no_grad():
+        layer.weight.copy_(to_dev_bf16(w))
+    log("linear module weight cache")
+    for i, x in enumerate((x1, x2)):
+        y = layer(to_dev_bf16(x))
+        torch.cuda.synchronize()
+        qx, sx = oracle.quantize_rowwise(x)
+        qw, sw = oracle.quantize_rowwise(w)
+        gemm_tolerance_check(to_host(y), oracle.gemm_tn(qx, sx, qw, sw), K, label="forward %d" % i)
+    assert calls == [(M, K), (N, K), (M, K)], calls      # W quantized once, x twice
+    w2 = workloads.normal_bf16((N, K), 35, std=0.05)
+    with torch.no_grad():
+        layer.weight.copy_(to_dev_bf16(w2))              # in-place: bumps the version counter
+    del calls[:]
+    y = layer(to_dev_bf16(x1))
+    torch.cuda.synchronize()
+    assert calls == [(M, K), (N, K)], calls
+    qx, sx = oracle.quantize_rowwise(x1)
+    qw, sw = oracle.quantize_rowwise(w2)
+    gemm_tolerance_check(to_host(y), oracle.gemm_tn(qx, sx, qw, sw), K, label="forward after update")

@@ -47,3 +47,27 @@ def test_helpers_reject_bad_tensors_before_any_launch():
         mx.grouped_gemm(a, p, a.reshape(1, 64, 128), p, torch.zeros(2, dtype=torch.int32))
     with pytest.raises(ValueError, match="uint8"):
         mx.pack_scales(torch.zeros((64, 4), dtype=torch.int32))
+
+
+def test_module_weight_cache_key(monkeypatch):
+    """MXFP8Linear.quantized_weight quantizes again exactly when the weight's
+    version counter, storage or shape changes (host logic only: the quantizer
+    is replaced by a stub that records its calls)."""
+    import mxfp8_block_scaled_quantize_amd.linear as lin
+    calls = []
+
+    def stub(t, **kw):
+        calls.append(t.data_ptr())
+        return {"q_row": t, "p_row": t, "q_colT": t, "p_colT": t}
+
+    monkeypatch.setattr(lin, "quantize", stub)
+    layer = lin.MXFP8Linear(128, 256)
+    first = layer.quantized_weight()
+    assert layer.quantized_weight() is first and len(calls) == 1
+    with torch.no_grad():
+        layer.weight.add_(1.0)                  # in-place update: version counter moves
+    assert layer.quantized_weight() is not first and len(calls) == 2
+    again = layer.quantized_weight()
+    assert len(calls) == 2
+    layer.weight.data = torch.zeros((256, 128), dtype=torch.bfloat16)   # new storage
+    assert layer.quantized_weight() is not again and len(calls) == 3

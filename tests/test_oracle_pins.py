@@ -408,6 +408,25 @@ def test_gemm_tiny_brute_force_rationals():
             assert abs(Fraction(c[m, n]) - exact) <= mag * Fraction(K, 2 ** 52)
 
 
+def test_gemm_row_panels_equal_the_whole_product():
+    """Panel-wise evaluation gives the same entries (within the fp64 summation
+    error bound), including a partial last panel, and exactly on integers."""
+    qa, sa = oracle.quantize_rowwise(workloads.normal_bf16((200, 384), 16))
+    qb, sb = oracle.quantize_rowwise(workloads.normal_bf16((72, 384), 17))
+    whole = oracle.gemm_tn(qa, sa, qb, sb)
+    mag = oracle.gemm_tn_abs(qa, sa, qb, sb)
+    for panel in (64, 199, 1000):
+        got = oracle.gemm_tn(qa, sa, qb, sb, panel=panel)
+        assert got.shape == whole.shape
+        assert np.all(np.abs(got - whole) <= mag * 2 * 384 * 2.0 ** -53)
+    rng = np.random.default_rng(18)
+    A = rng.integers(-14, 15, size=(130, 256))
+    B = rng.integers(-14, 15, size=(40, 256))
+    qa, sa = oracle.quantize_rowwise(bf16_bits(A.astype(np.float64)))
+    qb, sb = oracle.quantize_rowwise(bf16_bits(B.astype(np.float64)))
+    assert np.array_equal(oracle.gemm_tn(qa, sa, qb, sb, panel=32), (A @ B.T).astype(np.float64))
+
+
 def test_gemm_scale_byte_doubles_one_row_block():
     rng = np.random.default_rng(12)
     qa = oracle.quantize_rowwise(workloads.normal_bf16((64, 256), 3))
