@@ -116,14 +116,14 @@ def test_linear_module_reuses_weight_quantization_until_the_weight_changes(monke
         qx, sx = oracle.quantize_rowwise(x)
         qw, sw = oracle.quantize_rowwise(w)
         gemm_tolerance_check(to_host(y), oracle.gemm_tn(qx, sx, qw, sw), K, label="forward %d" % i)
-    assert calls == [(M, K), (N, K), (M, K)], calls      # W quantized once, x twice
+    assert calls == [(N, K), (M, K), (M, K)], calls      # W quantized once (first), x twice
     w2 = workloads.normal_bf16((N, K), 35, std=0.05)
     with torch.no_grad():
         layer.weight.copy_(to_dev_bf16(w2))              # in-place: bumps the version counter
     del calls[:]
     y = layer(to_dev_bf16(x1))
     torch.cuda.synchronize()
-    assert calls == [(M, K), (N, K)], calls
+    assert calls == [(N, K), (M, K)], calls
     qx, sx = oracle.quantize_rowwise(x1)
     qw, sw = oracle.quantize_rowwise(w2)
     gemm_tolerance_check(to_host(y), oracle.gemm_tn(qx, sx, qw, sw), K, label="forward after update")
