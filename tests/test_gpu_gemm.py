@@ -90,7 +90,7 @@ def test_tiny_config():
                                    # 10 x 3 and 3 x 11 tiles of 256: the L2 groups of 4 tiles along the
                                    # larger dimension end in a partial group, and the tile count is not
                                    # a multiple of the 8 XCDs (both branches of the tile remap)
-                                   (2520, 736, 256), (700, 2800, 256)])
+                                   (2520, 736, 256), (700, 2784, 256)])
 def test_ragged_gemm_shapes(M, N, K):
     a = workloads.normal_bf16((M, K), M + K)
     b = workloads.normal_bf16((N, K), N + 3 * K, std=0.5)
