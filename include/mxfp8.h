@@ -177,6 +177,34 @@ mxfp8_status mxfp8_quantize_ex(const void *x, int64_t rows, int64_t cols, int64_
                                void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/*
+ * mxfp8_quantize_ex without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  The dbias partial sums go to a static device
+ * buffer of MXFP8_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on until the process ends; nothing is allocated or freed by the call.
+ * Arguments, results and errors are those of mxfp8_quantize_ex without
+ * workspace / workspace_bytes, plus:
+ *  - MXFP8_ERR_WORKSPACE when DBIAS needs more partial-sum space than the
+ *    buffer holds, i.e. mxfp8_quantize_workspace_bytes(rows, cols, flags) >
+ *    MXFP8_NOALLOC_SCRATCH_BYTES (e.g. 8 MiB covers 16384 rows x 16384
+ *    columns); nothing is launched then;
+ *  - MXFP8_ERR_HIP when the buffer's device address cannot be obtained (it is
+ *    looked up once per device, on the first call that needs it there).
+ * Every call on one GPU shares that GPU's buffer and leaves its contents
+ * behind: calls that can overlap on one GPU (e.g. on two streams) race and
+ * must be ordered by the caller.  Every partial sum is written before it is
+ * read, so nothing needs clearing between calls.
+ */
+#define MXFP8_NOALLOC_SCRATCH_BYTES 8388608u
+mxfp8_status mxfp8_quantize_ex_noalloc(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                                       uint32_t flags,
+                                       uint8_t *q_row, void *s_row,
+                                       uint8_t *q_colT, void *s_colT,
+                                       float *dbias, float *amax, const int32_t *noop,
+                                       const void *act_in,
+                                       void *stream);
+
 /* ------------------------------------------------------------------------
  * Scale packing
  *

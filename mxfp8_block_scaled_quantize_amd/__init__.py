@@ -28,13 +28,15 @@ MXFP8_ACT_SQRELU = 32
 MXFP8_DACT_SQRELU = 64
 MXFP8_GEMM_ACCUMULATE = 1
 MXFP8_GEMM_SQRELU = 2
+MXFP8_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 STATUS_NAMES = {0: "MXFP8_OK", 1: "MXFP8_ERR_NULL", 2: "MXFP8_ERR_SHAPE", 3: "MXFP8_ERR_MISALIGNED",
                 4: "MXFP8_ERR_FLAGS", 5: "MXFP8_ERR_WORKSPACE", 6: "MXFP8_ERR_HIP", 7: "MXFP8_ERR_LIMIT"}
 
 EXPORTED = ("mxfp8_status_string", "mxfp8_last_hip_error", "mxfp8_quantize_workspace_bytes",
             "mxfp8_quantize", "mxfp8_packed_scale_bytes", "mxfp8_pack_scales", "mxfp8_gemm",
-            "mxfp8_grouped_gemm", "mxfp8_gemm_ex", "mxfp8_grouped_gemm_ex", "mxfp8_quantize_ex")
+            "mxfp8_grouped_gemm", "mxfp8_gemm_ex", "mxfp8_grouped_gemm_ex", "mxfp8_quantize_ex",
+            "mxfp8_quantize_ex_noalloc")
 
 
 class MXFP8Error(RuntimeError):
@@ -76,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.mxfp8_grouped_gemm.argtypes = [P, P, P, P, P, I32, P, I64, I64, I64, I64, P]
     L.mxfp8_quantize_ex.restype = ctypes.c_int
     L.mxfp8_quantize_ex.argtypes = [P, I64, I64, I64, U32, P, P, P, P, P, P, P, P, P, SZ, P]
+    L.mxfp8_quantize_ex_noalloc.restype = ctypes.c_int
+    L.mxfp8_quantize_ex_noalloc.argtypes = [P, I64, I64, I64, U32, P, P, P, P, P, P, P, P, P]
     L.mxfp8_gemm_ex.restype = ctypes.c_int
     L.mxfp8_gemm_ex.argtypes = [P, P, P, P, P, I64, I64, I64, I64, U32, P]
     L.mxfp8_grouped_gemm_ex.restype = ctypes.c_int
@@ -135,6 +139,13 @@ def mxfp8_quantize_ex(x, rows, cols, ld_x, flags, q_row=None, s_row=None, q_colT
     _check(lib().mxfp8_quantize_ex(_p(x), rows, cols, ld_x, flags, _p(q_row), _p(s_row), _p(q_colT),
                                    _p(s_colT), _p(dbias), _p(amax), _p(noop), _p(act_in), _p(workspace),
                                    workspace_bytes, _s(stream)), "mxfp8_quantize_ex")
+
+
+def mxfp8_quantize_ex_noalloc(x, rows, cols, ld_x, flags, q_row=None, s_row=None, q_colT=None, s_colT=None,
+                              dbias=None, amax=None, noop=None, act_in=None, stream=None):
+    _check(lib().mxfp8_quantize_ex_noalloc(_p(x), rows, cols, ld_x, flags, _p(q_row), _p(s_row), _p(q_colT),
+                                           _p(s_colT), _p(dbias), _p(amax), _p(noop), _p(act_in), _s(stream)),
+           "mxfp8_quantize_ex_noalloc")
 
 
 def mxfp8_packed_scale_bytes(dim: int, k: int) -> int:

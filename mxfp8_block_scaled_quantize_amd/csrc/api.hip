@@ -120,6 +120,30 @@ mxfp8_status mxfp8_quantize_ex(const void* x, int64_t rows, int64_t cols, int64_
                                         static_cast<const uint16_t*>(act_in), static_cast<hipStream_t>(stream)));
 }
 
+mxfp8_status mxfp8_quantize_ex_noalloc(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint32_t flags,
+                                       uint8_t* q_row, void* s_row, uint8_t* q_colT, void* s_colT, float* dbias,
+                                       float* amax, const int32_t* noop, const void* act_in, void* stream) {
+  static_assert(MXFP8_NOALLOC_SCRATCH_BYTES == mx::kNoallocScratchBytes, "scratch size");
+  const size_t need = mxfp8_quantize_workspace_bytes(rows, cols, flags);
+  // every other rule as mxfp8_quantize_ex (a stand-in workspace of the right
+  // size passes its workspace checks), then the scratch limit
+  void* const stand_in = need ? reinterpret_cast<void*>(uintptr_t(256)) : nullptr;
+  const mxfp8_status st = check_quantize(x, rows, cols, ld_x, flags, q_row, s_row, q_colT, s_colT, dbias, amax,
+                                         noop, act_in, stand_in, need);
+  if (st != MXFP8_OK) return st;
+  if (need > MXFP8_NOALLOC_SCRATCH_BYTES) return MXFP8_ERR_WORKSPACE;
+  const bool empty = rows == 0 || cols == 0;
+  if (empty && !(flags & MXFP8_AMAX) && !((flags & MXFP8_DBIAS) && cols > 0)) return MXFP8_OK;
+  float* ws = nullptr;
+  if (need) {
+    const hipError_t e = mx::noalloc_scratch(static_cast<hipStream_t>(stream), &ws);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return hip_status(mx::launch_quantize(static_cast<const uint16_t*>(x), rows, cols, ld_x, flags, q_row, s_row,
+                                        q_colT, s_colT, dbias, ws, amax, noop,
+                                        static_cast<const uint16_t*>(act_in), static_cast<hipStream_t>(stream)));
+}
+
 mxfp8_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint32_t flags,
                             uint8_t* q_row, uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT, float* dbias,
                             void* workspace, size_t workspace_bytes, void* stream) {

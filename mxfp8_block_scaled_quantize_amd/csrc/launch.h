@@ -31,6 +31,13 @@ hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
                            float* dbias, float* dbias_part, float* amax, const int32_t* noop,
                            const uint16_t* act_in, hipStream_t stream);
 
+// Bytes of the static device scratch behind the allocation-free quantize
+// entry point (equal to MXFP8_NOALLOC_SCRATCH_BYTES of the C ABI).
+constexpr size_t kNoallocScratchBytes = size_t(8) << 20;
+// Device address of that scratch on the device of `stream` (looked up once per
+// device with hipGetSymbolAddress, that device current).
+hipError_t noalloc_scratch(hipStream_t stream, float** out);
+
 hipError_t launch_pack_scales(const uint8_t* s, int64_t dim, int64_t k, int64_t ld_s, uint32_t* packed,
                               hipStream_t stream);
 bool pack_scales_grid_fits(int64_t dim, int64_t k);

@@ -23,10 +23,48 @@
 //
 // Flat kernel: the rowwise copy of a contiguous input is one stream of
 // 32-element blocks (see quantize_rowwise_flat_kernel).
+#include <mutex>
+
 #include "mx_device.h"
 #include "launch.h"
 
 namespace mx {
+
+// Device scratch of the allocation-free quantize entry point: the dbias
+// partial sums (one fp32 per row tile and column) live here instead of in a
+// caller workspace.  Each GPU holds its own copy for the life of the process;
+// host code reaches it only through the address hipGetSymbolAddress returns
+// for that device (the array's name is not a device address on the host).
+static __device__ __align__(256) float scratch[kNoallocScratchBytes / sizeof(float)];
+
+hipError_t noalloc_scratch(hipStream_t stream, float** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    // once per device, with that device current
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 // Options of one quantize call that only change where results go: all
 // uniform across the grid.

@@ -39,12 +39,13 @@ def test_header_declares_the_four_entry_points():
 
 
 def test_header_constants_match_the_binding():
-    """Every flag and status value the header defines has the same value in
-    the Python binding (and the binding defines no flag the header lacks)."""
+    """Every flag, size constant and status value the header defines has the
+    same value in the Python binding (and the binding defines no such constant
+    the header lacks)."""
     import re
     text = open(HEADER).read()
     flags = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (MXFP8_[A-Z_]+) (\d+)u", text)}
-    assert len(flags) == 9, flags
+    assert len(flags) == 10, flags
     for name, value in flags.items():
         assert getattr(mx, name) == value, name
     binding = {n for n in dir(mx) if re.fullmatch(r"MXFP8_[A-Z_]+", n) and isinstance(getattr(mx, n), int)}
@@ -225,3 +226,22 @@ def test_binding_raises_on_error(L):
     with pytest.raises(mx.MXFP8Error) as ei:
         mx.mxfp8_quantize(A16, 64, 48, 64, ROW, A16, A16, stream=0)
     assert ei.value.status == SHAPE and "SHAPE" in str(ei.value)
+
+
+def test_noalloc_quantize_validation(L):
+    """The allocation-free quantize applies mxfp8_quantize_ex's rules, then
+    rejects dbias requests whose partial sums exceed the static scratch
+    (MXFP8_ERR_WORKSPACE), all on the host before anything is launched."""
+    def qn(x=A16, rows=128, cols=128, ld=128, flags=ROW, db=A16):
+        return L.mxfp8_quantize_ex_noalloc(x, rows, cols, ld, flags, A16, A16, A16, A16, db, A16, None, A16, None)
+    assert qn(flags=0) == FLAGS
+    assert qn(cols=48, ld=48) == SHAPE
+    assert qn(x=None) == NULL
+    assert qn(flags=ROW | DB, db=None) == NULL
+    assert qn(x=A16 + 2) == MISALIGNED
+    limit = mx.MXFP8_NOALLOC_SCRATCH_BYTES
+    # partial sums of 1024 row tiles x 2048 columns = 8 MiB fit; one more tile does not
+    assert L.mxfp8_quantize_workspace_bytes(1024 * 128, 2048, ROW | DB) == limit
+    assert L.mxfp8_quantize_workspace_bytes(1025 * 128, 2048, ROW | DB) > limit
+    assert qn(rows=1025 * 128, cols=2048, ld=2048, flags=ROW | DB) == WORKSPACE
+    assert qn(rows=1025 * 128, cols=2048, ld=2048, flags=ROW | COL | DB) == WORKSPACE
