@@ -9,7 +9,10 @@
 // lane are scaled by the scale operand of lane (l % 32) and bytes 16..31 by
 // that of lane 32 + (l % 32) (byte chosen by op_sel): lane l supplies the
 // scale of K-block l / 32.  Result register i of lane l is row
-// 8*(i/4) + 4*(l/32) + (i%4), column l % 32.
+// 8*(i/4) + 4*(l/32) + (i%4), column l % 32 of the product of the first
+// operand's rows with the second's.  The kernel passes B first, so it holds
+// C^T: lane l has C[l % 32][8*(i/4) + 4*(l/32) + (i%4)], four consecutive
+// columns of one row of C in registers 4g .. 4g + 3.
 //
 // Tiling: one workgroup of 4 waves computes a 256 x 256 tile; wave (wm, wn)
 // owns 128 x 128 = 4 x 4 MFMA blocks (256 fp32 accumulators per lane, in
@@ -41,6 +44,7 @@ namespace mx {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
@@ -302,8 +306,9 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
     constexpr int set = decltype(SET)::value;
     constexpr int op = decltype(OPSEL)::value;
     const int i = q >> 2, j = q & 3;
-    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[set][i], fb[set][j], acc[i][j], 0, 0, op,
-                                                                (int)sa[i], op, (int)sb[j]);
+    // B first: the block of C^T, so a lane's registers are consecutive columns of C
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[set][j], fa[set][i], acc[i][j], 0, 0, op,
+                                                                (int)sb[j], op, (int)sa[i]);
   };
   // One K step: first half from register set 0 while the second half's
   // fragments load; then make step t+1 resident, refill this step's slot with
@@ -373,97 +378,86 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
   // ---- epilogue: fp32 -> BF16 (RNE, v_cvt_pk_bf16_f32) into a padded
   // row-major LDS tile (the ring is free once every wave is past its last
   // step), then 16-byte stores that cover whole 512-byte row segments of C.
-  // Registers r, r+1 of a lane are rows R, R+1 of one column; lane pairs
-  // (columns c, c+1) trade halves so each LDS write is one 32-bit word of two
-  // adjacent columns: the even lane writes row R, the odd lane row R+1.
+  // Registers 4g .. 4g + 3 of block (i, j) are four consecutive columns of one
+  // row: one 8-byte LDS write each.  With ACCUMULATE the current C tile is
+  // staged first and each lane adds the old values at its own positions.
   wait_lgkm0();
   lds_barrier();
   // Lane-derived values are re-derived from the lane id here so that none of
   // them stays live (or spills) across the main loop.
   const int elane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int ech = elane & 31;                    // 16-byte chunk of a tile row
+  const int erow0 = 2 * wave + (elane >> 5);     // rows erow0 + 8 k
+  const int64_t ecol = n0 + 8 * ech;
+  const bool full_rows = m_lo + BM <= m_hi;
   if (ACC) {
-    // Accumulate: stage the current C tile in the LDS tile (same layout and
-    // thread mapping as the stores below; rows / columns outside C read as 0).
-    // All 32 loads of a thread are issued before the first LDS write, so the
-    // tile costs one memory latency.
-    const int ch = elane & 31;
-    const int64_t col = n0 + 8 * ch;
+    // all 32 loads of a thread are issued before the first LDS write, so the
+    // tile costs one memory latency (rows / columns outside C read as 0)
     u32x4 v[32];
 #pragma unroll
     for (int k = 0; k < 32; k++) {
-      const int row = 2 * wave + (elane >> 5) + 8 * k;
-      const int64_t grow = m_lo + row;
+      const int64_t grow = m_lo + erow0 + 8 * k;
       v[k] = u32x4{0u, 0u, 0u, 0u};
-      if (col < N && grow < m_hi) v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Cm + grow * ldc + col));
+      if (ecol < N && grow < m_hi)
+        v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Cm + grow * ldc + ecol));
     }
 #pragma unroll
-    for (int k = 0; k < 32; k++) {
-      const int row = 2 * wave + (elane >> 5) + 8 * k;
-      *(__attribute__((address_space(3))) u32x4*)(smem + row * C_LDS_STRIDE + 16 * ch) = v[k];
-    }
+    for (int k = 0; k < 32; k++)
+      *(__attribute__((address_space(3))) u32x4*)(smem + (erow0 + 8 * k) * C_LDS_STRIDE + 16 * ech) = v[k];
     wait_lgkm0();
     lds_barrier();
   }
   {
-    const int lane = elane, lr = elane & 31, lg = elane >> 5;
-    const bool odd = lane & 1;
-    const int rb = wm * 128 + 4 * lg;
-    const int cb = wn * 128 + lr - (odd ? 1 : 0);
-    // Each lane sends its whole packed pair; the even lane keeps the low
-    // halves (row R) of its and its partner's word, the odd lane the high
-    // halves (row R+1): one byte permute, no rotation.
-    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+    const int lr = elane & 31, lg = elane >> 5;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
+      const int row = wm * 128 + 32 * i + lr;
 #pragma unroll
       for (int j = 0; j < 4; j++)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const int row = rb + 32 * i + 8 * (r >> 2) + (r & 3) + (odd ? 1 : 0);
-          __attribute__((address_space(3))) uint32_t* slot_word =
-              (__attribute__((address_space(3))) uint32_t*)(smem + row * C_LDS_STRIDE + 2 * (cb + 32 * j));
-          float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
+        for (int g = 0; g < 4; g++) {
+          const int col = wn * 128 + 32 * j + 8 * g + 4 * lg;
+          __attribute__((address_space(3))) u32x2* p =
+              (__attribute__((address_space(3))) u32x2*)(smem + row * C_LDS_STRIDE + 2 * col);
+          float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
+          float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
           if (ACC) {
-            // The word at this lane's address holds the old C of its row for
-            // columns c, c+1; the partner holds the other row.  Trade halves
-            // the same way as below so each lane gets rows R, R+1 of its column.
-            const uint32_t w_old = *slot_word;
-            const uint32_t y_old = (uint32_t)__builtin_amdgcn_mov_dpp((int)w_old, 0xB1, 0xF, 0xF, true);
-            // even lane: own word is row R, partner's row R+1 (its column in the low halves);
-            // odd lane: partner's word is row R, own row R+1 (its column in the high halves)
-            const uint32_t c_r = odd ? (y_old >> 16) : w_old;          // row R of this column in the low half
-            const uint32_t c_r1 = odd ? (w_old >> 16) : y_old;         // row R+1 of this column in the low half
-            v0 += __uint_as_float(c_r << 16);
-            v1 += __uint_as_float(c_r1 << 16);
+            const u32x2 o = *p;
+            v0 += __uint_as_float(o.x << 16);
+            v1 += __uint_as_float(o.x & 0xFFFF0000u);
+            v2 += __uint_as_float(o.y << 16);
+            v3 += __uint_as_float(o.y & 0xFFFF0000u);
           }
           if (SQRELU) {   // relu(acc)^2 in fp32, then the one BF16 rounding
             v0 = fmaxf(v0, 0.0f);
             v1 = fmaxf(v1, 0.0f);
+            v2 = fmaxf(v2, 0.0f);
+            v3 = fmaxf(v3, 0.0f);
             v0 *= v0;
             v1 *= v1;
+            v2 *= v2;
+            v3 *= v3;
           }
-          const bf16x2 h = {(__bf16)v0, (__bf16)v1};
-          const uint32_t pk = __builtin_bit_cast(uint32_t, h);   // row R low, row R+1 high
-          const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)pk, 0xB1, 0xF, 0xF, true);  // lane ^ 1
-          *slot_word = __builtin_amdgcn_perm(y, pk, sel);
+          const bf16x2 h0 = {(__bf16)v0, (__bf16)v1};
+          const bf16x2 h1 = {(__bf16)v2, (__bf16)v3};
+          *p = u32x2{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1)};
         }
       __builtin_amdgcn_sched_barrier(0);   // bounds the registers the batched AGPR reads take
     }
   }
   wait_lgkm0();
   lds_barrier();
-  {
-    // 16-byte chunk of a 512-byte tile row (tid & 31, re-derived from the lane
-    // id so the value is not kept live through the conversion above)
-    const int ch = (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & 31);
-    const int64_t col = n0 + 8 * ch;
-    if (col < N) {
-#pragma unroll 8
-      for (int k = 0; k < 32; k++) {
-        const int row = 2 * wave + (elane >> 5) + 8 * k;   // tid / 32 + 8k
-        const int64_t grow = m_lo + row;
-        const u32x4 v = *(lds_u32x4*)(smem + row * C_LDS_STRIDE + 16 * ch);
-        if (grow < m_hi) store_nt16(Cm + grow * ldc + col, make_uint4(v.x, v.y, v.z, v.w));
+  if (ecol < N) {
+    // all LDS reads of a batch before its stores (one LDS latency per batch)
+#pragma unroll
+    for (int kb = 0; kb < 32; kb += 16) {
+      u32x4 v[16];
+#pragma unroll
+      for (int k = 0; k < 16; k++) v[k] = *(lds_u32x4*)(smem + (erow0 + 8 * (kb + k)) * C_LDS_STRIDE + 16 * ech);
+#pragma unroll
+      for (int k = 0; k < 16; k++) {
+        const int64_t grow = m_lo + erow0 + 8 * (kb + k);
+        if (full_rows || grow < m_hi) store_nt16(Cm + grow * ldc + ecol, make_uint4(v[k].x, v[k].y, v[k].z, v[k].w));
       }
     }
   }
