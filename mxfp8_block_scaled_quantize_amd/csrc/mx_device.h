@@ -11,11 +11,21 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 
-// Streaming (non-temporal) global store for data nothing reads soon (the
-// GEMM's output tile).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Streaming (non-temporal) global stores and loads: data written or read once
+// in a pass (the GEMM's output tile; the tile quantizer's inputs and row codes).
 __device__ __forceinline__ void store_nt16(void* p, uint4 d) {
   const u32x4 v = {d.x, d.y, d.z, d.w};
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void store_nt8(void* p, uint2 d) {
+  const u32x2 v = {d.x, d.y};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // Packed per-halfword unsigned max / min (v_pk_max_u16 / v_pk_min_u16).

@@ -153,6 +153,7 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
     float* __restrict__ dbias_part, int64_t tiles_c, QuantOpts opt, const uint16_t* __restrict__ act_in) {
   constexpr int TR = 32 * QW;   // tile rows
   constexpr int NT = 64 * QW;   // threads
+  constexpr int TGR = QW == 8 ? 8 : 1;   // row tiles per group of the tile order (1: plain row-major)
   // Transposed FP8 tile [column][row]; 8-byte row units XOR-swizzled by the
   // column group to spread the transposing writes over the banks.
   __shared__ __attribute__((aligned(16))) uint8_t lds_t[COL ? QT_C * TR : 16];
@@ -166,8 +167,19 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
   const int cg = lane & 15;
   const int rg = lane >> 4;
   if (skip_call(opt)) return;   // uniform: the whole grid leaves
-  const int64_t tr = (int64_t)blockIdx.x / tiles_c;
-  const int64_t tc = (int64_t)blockIdx.x - tr * tiles_c;
+  // Tile order: groups of TGR row tiles walked row tile fastest, so the 8
+  // XCDs (workgroup ids are dealt to them round-robin) each take one row band
+  // of a group across all its column tiles: contiguous input rows and
+  // row-code rows per XCD, and the transposed codes of a column band written
+  // as 8 adjacent row runs at once.
+  const int64_t tiles_r = (R + TR - 1) / TR;
+  const int64_t per_g = (int64_t)TGR * tiles_c;
+  const int64_t gq = (int64_t)blockIdx.x / per_g;
+  const int64_t first_r = gq * TGR;
+  const int64_t gr = (tiles_r - first_r) < TGR ? (tiles_r - first_r) : TGR;
+  const int64_t remq = (int64_t)blockIdx.x - gq * per_g;
+  const int64_t tr = first_r + remq % gr;
+  const int64_t tc = remq / gr;
   const int64_t r0 = tr * TR;
   const int64_t c0 = tc * QT_C;
   const int64_t rb = r0 + 32 * w + 8 * rg;  // first row of this lane
@@ -177,15 +189,15 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
   // Tiles entirely inside the tensor (uniform test) load without per-row
   // guards; edge tiles read zeros outside it.
   const bool full_tile = r0 + TR <= R && c0 + QT_C <= C;
+  // Inputs are read once: non-temporal loads.
   auto load_rows = [&](const uint16_t* __restrict__ src, uint4 (&d)[8]) {
     if (full_tile) {
 #pragma unroll
-      for (int i = 0; i < 8; i++) d[i] = *reinterpret_cast<const uint4*>(src + (rb + i) * ldx + cb);
+      for (int i = 0; i < 8; i++) d[i] = load_nt16(src + (rb + i) * ldx + cb);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; i++)
-        d[i] = (cval && rb + i < R) ? *reinterpret_cast<const uint4*>(src + (rb + i) * ldx + cb)
-                                    : make_uint4(0u, 0u, 0u, 0u);
+        d[i] = (cval && rb + i < R) ? load_nt16(src + (rb + i) * ldx + cb) : make_uint4(0u, 0u, 0u, 0u);
     }
   };
   uint4 v[8];
@@ -245,7 +257,7 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
         o.x = cvt4_scaled_f32(f[0], f[1], f[2], f[3], byte);
         o.y = cvt4_scaled_f32(f[4], f[5], f[6], f[7], byte);
         const int64_t r = rb + i;
-        if (cval && r < R) *reinterpret_cast<uint2*>(q_row + r * C + cb) = o;
+        if (cval && r < R) store_nt8(q_row + r * C + cb, o);
         if ((cg & 3) == 0) lds_sr[(32 * w + 8 * rg + i) * 4 + (cg >> 2)] = (uint8_t)byte;
       }
     }
@@ -328,7 +340,7 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
       const uint32_t byte = scale_byte_from_amax(m);
       const uint2 o = quantize8(v[i], byte);
       const int64_t r = rb + i;
-      if (cval && r < R) *reinterpret_cast<uint2*>(q_row + r * C + cb) = o;
+      if (cval && r < R) store_nt8(q_row + r * C + cb, o);
       if ((cg & 3) == 0) lds_sr[(32 * w + 8 * rg + i) * 4 + (cg >> 2)] = (uint8_t)byte;
     }
   }
