@@ -89,6 +89,8 @@ def _load():
     lib.oracle_e4m3_encode_array.argtypes = [P, I64, P]
     lib.oracle_pack_scales.restype = None
     lib.oracle_pack_scales.argtypes = [P, I64, I64, I64, P]
+    lib.oracle_scale_byte_array.restype = None
+    lib.oracle_scale_byte_array.argtypes = [P, I64, P]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -129,6 +131,14 @@ def e4m3_encode(values) -> np.ndarray:
 
 def scale_byte(amax: float) -> int:
     return int(_load().oracle_scale_byte(float(amax)))
+
+
+def scale_bytes(amax) -> np.ndarray:
+    """E8M0 scale bytes of an array of block amax values (same rule as scale_byte)."""
+    a = np.ascontiguousarray(amax, dtype=np.float64)
+    out = np.empty(a.shape, dtype=np.uint8)
+    _load().oracle_scale_byte_array(_ptr(a), a.size, _ptr(out))
+    return out
 
 
 def bf16_value(bits) -> np.ndarray:
@@ -215,6 +225,52 @@ def sqrelu_epilogue(r: np.ndarray) -> np.ndarray:
     r = np.asarray(r, dtype=np.float64)
     z = np.maximum(r, 0.0)
     return z * z
+
+
+# GELU (the with_act / with_dact activation the quantization config of
+# "[Common] Experimental CuTeDSL MXFP8 backends in C++ via TVM-FFI" names, and
+# the fused GELU epilogue that "Experimental FlyDSL GEMM backend for TE PyTorch
+# (BF16/FP16/FP32/FP8/MXFP8)" says its MXFP8 path drops).  The pages give no
+# formula; the reading is the exact (erf) form GELU(x) = x Phi(x) with Phi the
+# standard normal CDF, written as 0.5 x erfc(-x / sqrt(2)) so that the negative
+# tail keeps its relative accuracy, and its derivative Phi(a) + a phi(a).
+# Values are exact up to fp64 rounding (scipy's erfc and exp).
+
+_SQRT1_2 = 0.7071067811865476
+_INV_SQRT_2PI = 0.3989422804014327
+
+
+def _erfc(z):
+    from scipy.special import erfc
+    return erfc(z)
+
+
+def gelu_f64(x) -> np.ndarray:
+    """GELU(x) = 0.5 x erfc(-x / sqrt(2)) in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * _erfc(-x * _SQRT1_2)
+
+
+def dgelu_terms(a):
+    """The two terms of GELU'(a) = Phi(a) + a phi(a), in float64."""
+    a = np.asarray(a, dtype=np.float64)
+    return 0.5 * _erfc(-a * _SQRT1_2), a * np.exp(-0.5 * a * a) * _INV_SQRT_2PI
+
+
+def act_gelu(x_bits: np.ndarray) -> np.ndarray:
+    """GELU of BF16 inputs, float64."""
+    return gelu_f64(bf16_value(_check_bf16(x_bits)))
+
+
+def dact_gelu(grad_bits: np.ndarray, act_bits: np.ndarray) -> np.ndarray:
+    """grad * GELU'(a) of BF16 inputs, float64."""
+    t1, t2 = dgelu_terms(bf16_value(_check_bf16(act_bits)))
+    return bf16_value(_check_bf16(grad_bits)) * (t1 + t2)
+
+
+def gelu_epilogue(r: np.ndarray) -> np.ndarray:
+    """GELU of a GEMM result (the epilogue applied before the output rounding)."""
+    return gelu_f64(r)
 
 
 def _check_f32(v: np.ndarray) -> np.ndarray:

@@ -277,6 +277,14 @@ void oracle_pack_scales(const uint8_t *s, int64_t dim, int64_t kblocks, int64_t 
                 packed[(t * dim + r) * 4 + j] = s[r * ld_s + 4 * t + j];
 }
 
+/* Scale bytes of an array of block amax values (the oracle_scale_byte rule). */
+void oracle_scale_byte_array(const double *amax, int64_t n, uint8_t *out)
+{
+    int64_t i;
+    for (i = 0; i < n; i++)
+        out[i] = oracle_scale_byte(amax[i]);
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

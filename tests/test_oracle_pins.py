@@ -644,3 +644,57 @@ def test_sqrelu_epilogue_matches_the_activation_and_torch():
     bits = workloads.wide_range_bf16((8, 64), 58, u_lo=-20, u_hi=20, n_maxbf16=0, n_subnormal=0, n_subnormal_blocks=0)
     assert np.array_equal(oracle.sqrelu_epilogue(oracle.bf16_value(bits)),
                           oracle.act_sqrelu(bits).astype(np.float64))
+
+
+# ------------------------------------------------------------------ GELU
+
+def test_gelu_matches_torch_and_closed_forms():
+    """GELU(x) = x Phi(x) against torch's float64 gelu (erf form) where that is
+    accurate (|x| <= 5: torch adds 1 + erf(x / sqrt 2), which cancels in the
+    negative tail), against tabulated normal-CDF values in the tail, and the
+    exact identity GELU(x) - GELU(-x) = x (Phi(x) + Phi(-x) = 1)."""
+    import torch
+    rng = np.random.default_rng(60)
+    x = np.concatenate([rng.standard_normal(4000) * 2.0, np.linspace(-5, 5, 1001)])
+    got = oracle.gelu_f64(x)
+    want = torch.nn.functional.gelu(torch.from_numpy(x)).numpy()
+    assert np.all(np.abs(got - want) <= 1e-8 * np.abs(want) + 1e-15)
+    # Phi(-3) = 0.00134989803163009, Phi(-8) = 6.22096057427178e-16 (normal CDF tables)
+    assert abs(oracle.gelu_f64(-3.0) - (-3.0 * 0.00134989803163009)) <= 1e-15
+    assert abs(oracle.gelu_f64(-8.0) / (-8.0 * 6.22096057427178e-16) - 1.0) <= 1e-12
+    assert oracle.gelu_f64(0.0) == 0.0 and oracle.gelu_f64(40.0) == 40.0
+    y = rng.standard_normal(2000) * 8.0
+    assert np.all(np.abs(oracle.gelu_f64(y) - oracle.gelu_f64(-y) - y) <= 4 * np.spacing(np.abs(y)))
+
+
+def test_gelu_derivative_terms():
+    """GELU'(a) = Phi(a) + a phi(a): the sum against torch's float64 autograd of
+    gelu (|a| <= 5) and central differences of the oracle's GELU; Phi(0) = 1/2,
+    and the sign change of GELU' at GELU's minimum near a = -0.7518."""
+    import torch
+    a = np.linspace(-5, 5, 2001)
+    t1, t2 = oracle.dgelu_terms(a)
+    ta = torch.from_numpy(a).requires_grad_(True)
+    torch.nn.functional.gelu(ta).sum().backward()
+    assert np.all(np.abs((t1 + t2) - ta.grad.numpy()) <= 1e-9)
+    h = 1e-5
+    fd = (oracle.gelu_f64(a + h) - oracle.gelu_f64(a - h)) / (2 * h)
+    assert np.all(np.abs((t1 + t2) - fd) <= 1e-8)
+    p0, q0 = oracle.dgelu_terms(0.0)
+    assert p0 == 0.5 and q0 == 0.0
+    # GELU has its minimum (about -0.16997) at x = -0.75179...: GELU' changes sign there
+    lo, hi = oracle.dgelu_terms(-0.75180), oracle.dgelu_terms(-0.75178)
+    assert sum(lo) < 0.0 < sum(hi)
+    assert abs(oracle.gelu_f64(-0.75179) - (-0.16997)) < 1e-5
+    g = workloads.normal_bf16((4, 64), 61)
+    ab = workloads.normal_bf16((4, 64), 62)
+    want = oracle.bf16_value(g) * np.add(*oracle.dgelu_terms(oracle.bf16_value(ab)))
+    assert np.array_equal(oracle.dact_gelu(g, ab), want)
+    assert np.array_equal(oracle.act_gelu(ab), oracle.gelu_f64(oracle.bf16_value(ab)))
+
+
+def test_scale_bytes_array_matches_the_scalar_rule():
+    rng = np.random.default_rng(63)
+    a = np.abs(rng.standard_normal(3000)) * np.exp2(rng.integers(-140, 130, size=3000))
+    a[:4] = [0.0, 2.0 ** -130, 448.0 * 2.0 ** 119, 1.0]
+    assert np.array_equal(oracle.scale_bytes(a), np.array([oracle.scale_byte(v) for v in a], dtype=np.uint8))
