@@ -104,6 +104,15 @@ int mxfp8_last_hip_error(void);
 #define MXFP8_ACT_SQRELU 32u     /* relu(x)^2                                  */
 #define MXFP8_DACT_SQRELU 64u    /* x * 2 relu(act_in): backward of relu(a)^2,
                                     x = incoming gradient, act_in = a           */
+/* GELU, the activation that the config key's activation field names besides
+ * the ReLU family and that the GEMM review finds silently dropped from the
+ * FlyDSL path ("Experimental FlyDSL GEMM backend for TE PyTorch
+ * (BF16/FP16/FP32/FP8/MXFP8)", review of the gelu / grad epilogue
+ * arguments).  The pages fix no formula; this library uses the exact form
+ * GELU(a) = a * Phi(a) = 0.5 a erfc(-a / sqrt 2), evaluated in fp32:       */
+#define MXFP8_ACT_GELU 128u      /* GELU(x)                                    */
+#define MXFP8_DACT_GELU 256u     /* x * GELU'(act_in), GELU'(a) = Phi(a) +
+                                    a phi(a) (phi the standard normal density) */
 
 /* Bytes of workspace mxfp8_quantize needs for `flags` at this shape (0 when
  * DBIAS is not requested). */
@@ -146,10 +155,13 @@ mxfp8_status mxfp8_quantize(const void *x, int64_t rows, int64_t cols, int64_t l
  * config key, commit "Perform noop tensor check on device", Greptile summary
  * on the noop + dbias interaction).
  * flags   as mxfp8_quantize, plus MXFP8_AMAX, MXFP8_PACKED_SCALES and at most
- *         one of MXFP8_ACT_SQRELU / MXFP8_DACT_SQRELU.  With an activation the
- *         quantized value v is the fp32 result of the activation (each product
- *         of two BF16 values is exact in fp32); its block scale follows the
- *         same rule (exponent of the block amax - 8), codes are RNE of
+ *         one of MXFP8_ACT_SQRELU / MXFP8_DACT_SQRELU / MXFP8_ACT_GELU /
+ *         MXFP8_DACT_GELU.  With an activation the quantized value v is the
+ *         fp32 result of the activation (for squared ReLU each product of two
+ *         BF16 values is exact in fp32; GELU uses the device erfcf / expf,
+ *         within (8 + 3 a^2) fp32 ulp of GELU(a) and 8 ulp of |Phi(a)| +
+ *         |a phi(a)| for its derivative); its block scale follows the same
+ *         rule (exponent of the block amax - 8), codes are RNE of
  *         v / 2^(scale - 127) saturated to +-448.
  * s_row, s_colT  byte scales as in mxfp8_quantize, or (PACKED_SCALES) uint32
  *         words in the mxfp8_pack_scales layout, 4-byte aligned.
@@ -159,11 +171,12 @@ mxfp8_status mxfp8_quantize(const void *x, int64_t rows, int64_t cols, int64_t l
  * noop    optional DEVICE int32 flag, 4-byte aligned.  When non-NULL and
  *         nonzero at the time the work executes, nothing is written (codes,
  *         scales, dbias and amax keep their old contents).  NULL: always run.
- * act_in  DACT_SQRELU: BF16 [rows][ld_x], the forward activation's input, same
- *         layout as x, 16-byte aligned.  Else ignored.
+ * act_in  DACT_SQRELU / DACT_GELU: BF16 [rows][ld_x], the forward
+ *         activation's input, same layout as x, 16-byte aligned.  Else
+ *         ignored.
  * Errors: as mxfp8_quantize; SHAPE also for PACKED_SCALES with cols (rowwise)
  *         or rows (columnwise) not a multiple of 128; NULL for AMAX without
- *         amax or DACT_SQRELU without act_in; FLAGS for both activations at
+ *         amax or a DACT flag without act_in; FLAGS for two activations at
  *         once.  Activation results that overflow fp32 or fall below its
  *         normal range are outside the contract.  mxfp8_quantize(...) rejects
  *         the extra flags (FLAGS).
@@ -266,20 +279,27 @@ mxfp8_status mxfp8_gemm(const uint8_t *a, const uint32_t *a_packed,
 #define MXFP8_GEMM_SQRELU 2u     /* C = bf16_rne( relu(acc)^2 ), acc = the fp32 sum and
                                     relu(acc)^2 formed in fp32: the squared-ReLU
                                     epilogue of an MLP's first projection */
+#define MXFP8_GEMM_GELU 4u       /* C = bf16_rne( GELU(acc) ), GELU in fp32 as for
+                                    MXFP8_ACT_GELU: the fused GELU epilogue that the
+                                    FlyDSL review asks for ("Experimental FlyDSL GEMM
+                                    backend for TE PyTorch (BF16/FP16/FP32/FP8/MXFP8)",
+                                    review of the gelu / grad arguments) */
 
 /*
  * mxfp8_gemm with options.  Defining passage: the accumulate option that the
  * FlyDSL backend still rejects (wgrad accumulation into an existing gradient,
  * "Experimental FlyDSL GEMM backend for TE PyTorch (BF16/FP16/FP32/FP8/MXFP8)",
  * review of the epilogue validation and of the fallback exceptions).
- * flags   0, MXFP8_GEMM_ACCUMULATE or MXFP8_GEMM_SQRELU.  With ACCUMULATE, C
+ * flags   0, MXFP8_GEMM_ACCUMULATE, MXFP8_GEMM_SQRELU or MXFP8_GEMM_GELU.
+ *         With ACCUMULATE, C
  *         is read and the sum is rounded once (fp32 accumulator + the old BF16
  *         value, then BF16 round-to-nearest-even); K == 0 leaves C unchanged.
  *         With SQRELU the fp32 accumulator goes through relu(v)^2 before the
  *         BF16 rounding (the FC1 "squared_relu" epilogue of "gemm(cutedsl):
  *         add standalone Lightning W4A16 grouped GEMM - #811", section "API
- *         and compatibility impact"); K == 0 writes zeros.
- * Other arguments and errors as mxfp8_gemm; unknown flag bits or both flags
+ *         and compatibility impact"); K == 0 writes zeros.  GELU likewise
+ *         (GELU(0) = 0).
+ * Other arguments and errors as mxfp8_gemm; unknown flag bits or two flags
  * -> FLAGS.
  * mxfp8_gemm(...) is mxfp8_gemm_ex(..., 0, stream).
  */

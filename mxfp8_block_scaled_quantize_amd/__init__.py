@@ -26,8 +26,11 @@ MXFP8_AMAX = 8
 MXFP8_PACKED_SCALES = 16
 MXFP8_ACT_SQRELU = 32
 MXFP8_DACT_SQRELU = 64
+MXFP8_ACT_GELU = 128
+MXFP8_DACT_GELU = 256
 MXFP8_GEMM_ACCUMULATE = 1
 MXFP8_GEMM_SQRELU = 2
+MXFP8_GEMM_GELU = 4
 MXFP8_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 STATUS_NAMES = {0: "MXFP8_OK", 1: "MXFP8_ERR_NULL", 2: "MXFP8_ERR_SHAPE", 3: "MXFP8_ERR_MISALIGNED",
@@ -188,7 +191,8 @@ def quantize(x, rowwise=True, colwise=False, dbias=False, amax=False, packed=Fal
     device whose first element is the flag (nonzero: nothing is written).
     act="sqrelu" quantizes relu(x)^2; act="dsqrelu" quantizes
     x * 2 relu(act_in) (x is the gradient, act_in the activation's input, a
-    BF16 tensor of x's shape and strides)."""
+    BF16 tensor of x's shape and strides); act="gelu" quantizes GELU(x) and
+    act="dgelu" x * GELU'(act_in) (exact erfc form, fp32)."""
     import torch
     if not isinstance(x, torch.Tensor) or x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a BF16 [rows, cols] tensor with unit column stride")
@@ -201,15 +205,16 @@ def quantize(x, rowwise=True, colwise=False, dbias=False, amax=False, packed=Fal
         raise ValueError("noop must be an int32 tensor with at least one element on x's device (%s)" % dev)
     flags = (MXFP8_ROWWISE if rowwise else 0) | (MXFP8_COLWISE if colwise else 0) | (MXFP8_DBIAS if dbias else 0)
     flags |= (MXFP8_AMAX if amax else 0) | (MXFP8_PACKED_SCALES if packed else 0)
-    if act == "sqrelu":
-        flags |= MXFP8_ACT_SQRELU
-    elif act == "dsqrelu":
+    acts = {"sqrelu": MXFP8_ACT_SQRELU, "dsqrelu": MXFP8_DACT_SQRELU, "gelu": MXFP8_ACT_GELU,
+            "dgelu": MXFP8_DACT_GELU}
+    if act is not None and act not in acts:
+        raise ValueError("act must be None or one of %s" % ", ".join(repr(k) for k in acts))
+    if act in ("dsqrelu", "dgelu"):
         if (act_in is None or act_in.dtype != torch.bfloat16 or act_in.shape != x.shape
                 or act_in.stride() != x.stride() or act_in.device != x.device):
-            raise ValueError("act='dsqrelu' needs act_in: a BF16 tensor with x's shape, strides and device")
-        flags |= MXFP8_DACT_SQRELU
-    elif act is not None:
-        raise ValueError("act must be None, 'sqrelu' or 'dsqrelu'")
+            raise ValueError("act=%r needs act_in: a BF16 tensor with x's shape, strides and device" % act)
+    if act is not None:
+        flags |= acts[act]
     out = {}
     if rowwise:
         out["q_row"] = torch.empty((R, C), dtype=torch.uint8, device=dev)
@@ -274,10 +279,18 @@ def pack_scales(s, stream=None):
     return out
 
 
-def gemm(a, a_packed, b, b_packed, out=None, accumulate=False, sqrelu=False, stream=None):
+def _gemm_flags(accumulate, sqrelu, gelu):
+    if accumulate + sqrelu + gelu > 1:
+        raise ValueError("accumulate, sqrelu and gelu exclude each other")
+    return ((MXFP8_GEMM_ACCUMULATE if accumulate else 0) | (MXFP8_GEMM_SQRELU if sqrelu else 0)
+            | (MXFP8_GEMM_GELU if gelu else 0))
+
+
+def gemm(a, a_packed, b, b_packed, out=None, accumulate=False, sqrelu=False, gelu=False, stream=None):
     """C = dq(A) dq(B)^T in BF16 for E4M3 codes a [M, K], b [N, K]; with
     accumulate=True the product is added to `out` (beta = 1); with
-    sqrelu=True C = relu(product)^2 (formed in fp32, rounded once)."""
+    sqrelu=True C = relu(product)^2, with gelu=True C = GELU(product)
+    (formed in fp32, rounded once)."""
     import torch
     if not isinstance(a, torch.Tensor) or a.dim() != 2 or not isinstance(b, torch.Tensor) or b.dim() != 2:
         raise ValueError("a and b must be 2-D tensors of E4M3 codes")
@@ -293,15 +306,16 @@ def gemm(a, a_packed, b, b_packed, out=None, accumulate=False, sqrelu=False, str
     c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     if c.dtype != torch.bfloat16 or tuple(c.shape) != (M, N) or c.stride(1) != 1 or c.device != dev:
         raise ValueError("out must be a BF16 [M, N] tensor with unit column stride on the operands' device")
-    flags = (MXFP8_GEMM_ACCUMULATE if accumulate else 0) | (MXFP8_GEMM_SQRELU if sqrelu else 0)
+    flags = _gemm_flags(accumulate, sqrelu, gelu)
     with torch.cuda.device(dev):
         mxfp8_gemm_ex(a, a_packed, b, b_packed, c, c.stride(0), M, N, K, flags, stream)
     return c
 
 
-def grouped_gemm(a, a_packed, b, b_packed, offsets, out=None, accumulate=False, sqrelu=False, stream=None):
+def grouped_gemm(a, a_packed, b, b_packed, offsets, out=None, accumulate=False, sqrelu=False, gelu=False,
+                 stream=None):
     """Ragged grouped GEMM; b is [G, N, K]; rows outside every group keep `out`'s values;
-    sqrelu=True writes relu(product)^2 (an MoE block's first projection)."""
+    sqrelu=True writes relu(product)^2 (an MoE block's first projection), gelu=True GELU(product)."""
     import torch
     if not isinstance(a, torch.Tensor) or a.dim() != 2 or not isinstance(b, torch.Tensor) or b.dim() != 3:
         raise ValueError("a must be 2-D [M, K] and b 3-D [G, N, K] tensors of E4M3 codes")
@@ -318,7 +332,7 @@ def grouped_gemm(a, a_packed, b, b_packed, offsets, out=None, accumulate=False, 
     c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     if c.dtype != torch.bfloat16 or tuple(c.shape) != (M, N) or c.stride(1) != 1 or c.device != dev:
         raise ValueError("out must be a BF16 [M, N] tensor with unit column stride on the operands' device")
-    flags = (MXFP8_GEMM_ACCUMULATE if accumulate else 0) | (MXFP8_GEMM_SQRELU if sqrelu else 0)
+    flags = _gemm_flags(accumulate, sqrelu, gelu)
     with torch.cuda.device(dev):
         mxfp8_grouped_gemm_ex(a, a_packed, b, b_packed, offsets, G, c, c.stride(0), M, N, K, flags, stream)
     return c

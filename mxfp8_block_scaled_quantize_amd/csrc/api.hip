@@ -25,11 +25,12 @@ mxfp8_status check_quantize(const void* x, int64_t rows, int64_t cols, int64_t l
                             const uint8_t* q_row, const void* s_row, const uint8_t* q_colT,
                             const void* s_colT, const float* dbias, const float* amax, const int32_t* noop,
                             const void* act_in, const void* ws, size_t ws_bytes) {
-  if (flags & ~(MXFP8_ROWWISE | MXFP8_COLWISE | MXFP8_DBIAS | MXFP8_AMAX | MXFP8_PACKED_SCALES |
-                MXFP8_ACT_SQRELU | MXFP8_DACT_SQRELU))
+  constexpr uint32_t kActs = MXFP8_ACT_SQRELU | MXFP8_DACT_SQRELU | MXFP8_ACT_GELU | MXFP8_DACT_GELU;
+  constexpr uint32_t kDacts = MXFP8_DACT_SQRELU | MXFP8_DACT_GELU;
+  if (flags & ~(MXFP8_ROWWISE | MXFP8_COLWISE | MXFP8_DBIAS | MXFP8_AMAX | MXFP8_PACKED_SCALES | kActs))
     return MXFP8_ERR_FLAGS;
   if (!(flags & (MXFP8_ROWWISE | MXFP8_COLWISE))) return MXFP8_ERR_FLAGS;
-  if ((flags & MXFP8_ACT_SQRELU) && (flags & MXFP8_DACT_SQRELU)) return MXFP8_ERR_FLAGS;
+  if (__builtin_popcount(flags & kActs) > 1) return MXFP8_ERR_FLAGS;   // at most one activation
   if ((flags & MXFP8_AMAX) && !amax) return MXFP8_ERR_NULL;
   if ((flags & MXFP8_AMAX) && !aligned(amax, 4)) return MXFP8_ERR_MISALIGNED;
   if (noop && !aligned(noop, 4)) return MXFP8_ERR_MISALIGNED;
@@ -45,11 +46,11 @@ mxfp8_status check_quantize(const void* x, int64_t rows, int64_t cols, int64_t l
   if (any && !x) return MXFP8_ERR_NULL;
   if (any && (flags & MXFP8_ROWWISE) && (!q_row || !s_row)) return MXFP8_ERR_NULL;
   if (any && (flags & MXFP8_COLWISE) && (!q_colT || !s_colT)) return MXFP8_ERR_NULL;
-  if (any && (flags & MXFP8_DACT_SQRELU) && !act_in) return MXFP8_ERR_NULL;
+  if (any && (flags & kDacts) && !act_in) return MXFP8_ERR_NULL;
   if ((flags & MXFP8_DBIAS) && cols > 0 && !dbias) return MXFP8_ERR_NULL;
   if (any) {
     if (!aligned(x, 16) || ld_x % 8) return MXFP8_ERR_MISALIGNED;
-    if ((flags & MXFP8_DACT_SQRELU) && !aligned(act_in, 16)) return MXFP8_ERR_MISALIGNED;
+    if ((flags & kDacts) && !aligned(act_in, 16)) return MXFP8_ERR_MISALIGNED;
     if ((flags & MXFP8_ROWWISE) && !aligned(q_row, 16)) return MXFP8_ERR_MISALIGNED;
     if ((flags & MXFP8_COLWISE) && !aligned(q_colT, 16)) return MXFP8_ERR_MISALIGNED;
     if ((flags & MXFP8_PACKED_SCALES) && (flags & MXFP8_ROWWISE) && !aligned(s_row, 4)) return MXFP8_ERR_MISALIGNED;
@@ -79,6 +80,15 @@ mxfp8_status check_gemm_common(const uint8_t* a, const uint32_t* ap, const uint8
   if (K > 0 && (!aligned(a, 16) || !aligned(b, 16) || !aligned(ap, 4) || !aligned(bp, 4)))
     return MXFP8_ERR_MISALIGNED;
   return MXFP8_OK;
+}
+
+// GEMM options: known bits only, at most one of accumulate / relu^2 / GELU.
+bool gemm_flags_ok(uint32_t flags) {
+  constexpr uint32_t kAll = MXFP8_GEMM_ACCUMULATE | MXFP8_GEMM_SQRELU | MXFP8_GEMM_GELU;
+  return !(flags & ~kAll) && __builtin_popcount(flags) <= 1;
+}
+int gemm_epilogue(uint32_t flags) {
+  return (flags & MXFP8_GEMM_SQRELU) ? 1 : (flags & MXFP8_GEMM_GELU) ? 2 : 0;
 }
 
 }  // namespace
@@ -170,14 +180,13 @@ mxfp8_status mxfp8_pack_scales(const uint8_t* s, int64_t dim, int64_t k, int64_t
 
 mxfp8_status mxfp8_gemm_ex(const uint8_t* a, const uint32_t* a_packed, const uint8_t* b, const uint32_t* b_packed,
                            void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, uint32_t flags, void* stream) {
-  if (flags & ~(MXFP8_GEMM_ACCUMULATE | MXFP8_GEMM_SQRELU)) return MXFP8_ERR_FLAGS;
-  if ((flags & MXFP8_GEMM_ACCUMULATE) && (flags & MXFP8_GEMM_SQRELU)) return MXFP8_ERR_FLAGS;
+  if (!gemm_flags_ok(flags)) return MXFP8_ERR_FLAGS;
   const mxfp8_status st = check_gemm_common(a, a_packed, b, b_packed, c, ldc, M, N, K);
   if (st != MXFP8_OK) return st;
   if (M == 0 || N == 0) return MXFP8_OK;
   if (!mx::gemm_grid_fits(M, N, 0, false)) return MXFP8_ERR_LIMIT;
   return hip_status(mx::launch_gemm(a, a_packed, b, b_packed, static_cast<uint16_t*>(c), ldc, M, N, K, nullptr, 0,
-                                    (flags & MXFP8_GEMM_ACCUMULATE) != 0, (flags & MXFP8_GEMM_SQRELU) != 0,
+                                    (flags & MXFP8_GEMM_ACCUMULATE) != 0, gemm_epilogue(flags),
                                     static_cast<hipStream_t>(stream)));
 }
 
@@ -189,8 +198,7 @@ mxfp8_status mxfp8_gemm(const uint8_t* a, const uint32_t* a_packed, const uint8_
 mxfp8_status mxfp8_grouped_gemm_ex(const uint8_t* a, const uint32_t* a_packed, const uint8_t* b,
                                    const uint32_t* b_packed, const int32_t* offsets, int32_t G, void* c, int64_t ldc,
                                    int64_t M_total, int64_t N, int64_t K, uint32_t flags, void* stream) {
-  if (flags & ~(MXFP8_GEMM_ACCUMULATE | MXFP8_GEMM_SQRELU)) return MXFP8_ERR_FLAGS;
-  if ((flags & MXFP8_GEMM_ACCUMULATE) && (flags & MXFP8_GEMM_SQRELU)) return MXFP8_ERR_FLAGS;
+  if (!gemm_flags_ok(flags)) return MXFP8_ERR_FLAGS;
   if (G < 1 || G > 65536) return MXFP8_ERR_SHAPE;
   const mxfp8_status st = check_gemm_common(a, a_packed, b, b_packed, c, ldc, M_total, N, K);
   if (st != MXFP8_OK) return st;
@@ -199,8 +207,8 @@ mxfp8_status mxfp8_grouped_gemm_ex(const uint8_t* a, const uint32_t* a_packed, c
   if (!aligned(offsets, 4)) return MXFP8_ERR_MISALIGNED;
   if (!mx::gemm_grid_fits(M_total, N, G, true)) return MXFP8_ERR_LIMIT;
   return hip_status(mx::launch_gemm(a, a_packed, b, b_packed, static_cast<uint16_t*>(c), ldc, M_total, N, K,
-                                    offsets, G, (flags & MXFP8_GEMM_ACCUMULATE) != 0,
-                                    (flags & MXFP8_GEMM_SQRELU) != 0, static_cast<hipStream_t>(stream)));
+                                    offsets, G, (flags & MXFP8_GEMM_ACCUMULATE) != 0, gemm_epilogue(flags),
+                                    static_cast<hipStream_t>(stream)));
 }
 
 mxfp8_status mxfp8_grouped_gemm(const uint8_t* a, const uint32_t* a_packed, const uint8_t* b,

@@ -86,7 +86,7 @@ struct ic {
   static constexpr int value = V;
 };
 
-template <bool GROUPED, bool ACC, bool SQRELU>
+template <bool GROUPED, bool ACC, int EPI>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
                  const uint8_t* __restrict__ B, const uint32_t* __restrict__ Bp,
@@ -427,7 +427,7 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
             v2 += __uint_as_float(o.y << 16);
             v3 += __uint_as_float(o.y & 0xFFFF0000u);
           }
-          if (SQRELU) {   // relu(acc)^2 in fp32, then the one BF16 rounding
+          if (EPI == 1) {   // relu(acc)^2 in fp32, then the one BF16 rounding
             v0 = fmaxf(v0, 0.0f);
             v1 = fmaxf(v1, 0.0f);
             v2 = fmaxf(v2, 0.0f);
@@ -436,6 +436,12 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
             v1 *= v1;
             v2 *= v2;
             v3 *= v3;
+          }
+          if (EPI == 2) {   // GELU(acc) in fp32, then the one BF16 rounding
+            v0 = gelu_f32(v0);
+            v1 = gelu_f32(v1);
+            v2 = gelu_f32(v2);
+            v3 = gelu_f32(v3);
           }
           const bf16x2 h0 = {(__bf16)v0, (__bf16)v1};
           const bf16x2 h1 = {(__bf16)v2, (__bf16)v3};
@@ -468,7 +474,7 @@ bool gemm_grid_fits(int64_t M, int64_t N, int32_t G, bool grouped) {
   return grid_fits(tm, tn, 256);
 }
 
-template <bool GROUPED, bool ACC, bool SQRELU>
+template <bool GROUPED, bool ACC, int EPI>
 static hipError_t launch_gemm_t(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
                                 uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, const int32_t* offsets,
                                 int32_t G, int64_t tiles_m, int64_t tiles_n, hipStream_t stream) {
@@ -481,31 +487,35 @@ static hipError_t launch_gemm_t(const uint8_t* a, const uint32_t* ap, const uint
   if (e != hipSuccess) return e;
   const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
   if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<GROUPED, ACC, SQRELU>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<GROUPED, ACC, EPI>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_done.fetch_or(bit, std::memory_order_release);
   }
-  hipLaunchKernelGGL((gemm_kernel<GROUPED, ACC, SQRELU>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), LDS_BYTES, stream,
+  hipLaunchKernelGGL((gemm_kernel<GROUPED, ACC, EPI>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), LDS_BYTES, stream,
                      a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
                        uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                       const int32_t* offsets, int32_t G, bool accumulate, bool sqrelu, hipStream_t stream) {
+                       const int32_t* offsets, int32_t G, bool accumulate, int epilogue, hipStream_t stream) {
   const bool grouped = offsets != nullptr;
   const int64_t tiles_n = (N + BN - 1) / BN;
   const int64_t tiles_m = (M + BM - 1) / BM + (grouped ? (int64_t)G : 0);
   if (tiles_m * tiles_n == 0) return hipSuccess;
-#define MX_G_LAUNCH(GR, AC, SQ) \
-  launch_gemm_t<GR, AC, SQ>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, stream)
-  // accumulate and the relu^2 epilogue are exclusive (the API rejects both)
+#define MX_G_LAUNCH(GR, AC, EP) \
+  launch_gemm_t<GR, AC, EP>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, stream)
+  // accumulate and the epilogues are exclusive (the API rejects combinations)
   if (grouped)
-    return accumulate ? MX_G_LAUNCH(true, true, false)
-                      : (sqrelu ? MX_G_LAUNCH(true, false, true) : MX_G_LAUNCH(true, false, false));
-  return accumulate ? MX_G_LAUNCH(false, true, false)
-                    : (sqrelu ? MX_G_LAUNCH(false, false, true) : MX_G_LAUNCH(false, false, false));
+    return accumulate ? MX_G_LAUNCH(true, true, 0)
+                      : epilogue == 1 ? MX_G_LAUNCH(true, false, 1)
+                      : epilogue == 2 ? MX_G_LAUNCH(true, false, 2)
+                                      : MX_G_LAUNCH(true, false, 0);
+  return accumulate ? MX_G_LAUNCH(false, true, 0)
+                    : epilogue == 1 ? MX_G_LAUNCH(false, false, 1)
+                    : epilogue == 2 ? MX_G_LAUNCH(false, false, 2)
+                                    : MX_G_LAUNCH(false, false, 0);
 #undef MX_G_LAUNCH
 }
 

@@ -24,8 +24,9 @@ inline bool grid_fits(int64_t a, int64_t b, int64_t threads) {
 bool quantize_grids_fit(int64_t R, int64_t C, int64_t ldx, uint32_t flags);
 
 // flags: rowwise 1, colwise 2, dbias 4, amax 8, packed scales 16, squared-ReLU
-// activation 32, its backward 64 (act_in: the activation's input, same shape
-// and leading dimension as x).  noop may be null (always run).
+// activation 32, its backward 64, GELU 128, its backward 256 (act_in: the
+// activation's input, same shape and leading dimension as x).  noop may be
+// null (always run).
 hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint32_t flags,
                            uint8_t* q_row, void* s_row, uint8_t* q_colT, void* s_colT,
                            float* dbias, float* dbias_part, float* amax, const int32_t* noop,
@@ -42,11 +43,11 @@ hipError_t launch_pack_scales(const uint8_t* s, int64_t dim, int64_t k, int64_t 
                               hipStream_t stream);
 bool pack_scales_grid_fits(int64_t dim, int64_t k);
 
-// Dense (offsets == nullptr) or grouped GEMM; accumulate adds the product to C; sqrelu writes relu(product)^2
-// (not together with accumulate).
+// Dense (offsets == nullptr) or grouped GEMM; accumulate adds the product to C; epilogue 1 writes
+// relu(product)^2, 2 writes GELU(product) (neither together with accumulate).
 hipError_t launch_gemm(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
                        uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                       const int32_t* offsets, int32_t G, bool accumulate, bool sqrelu, hipStream_t stream);
+                       const int32_t* offsets, int32_t G, bool accumulate, int epilogue, hipStream_t stream);
 bool gemm_grid_fits(int64_t M, int64_t N, int32_t G, bool grouped);
 
 }  // namespace mx

@@ -91,6 +91,17 @@ __device__ __forceinline__ uint2 quantize8(uint4 v, uint32_t byte) {
   return o;
 }
 
+// GELU(x) = x Phi(x) = 0.5 x erfc(-x / sqrt 2): the erfc form keeps its
+// relative accuracy in the negative tail, where 1 + erf(x / sqrt 2) cancels.
+// GELU'(a) = Phi(a) + a phi(a), phi the standard normal density.  Measured on
+// every BF16 input against an fp64 evaluation: GELU within (4 + 1.5 x^2) ulp
+// (the argument's rounding grows through erfc's tail), GELU' within 3.6 ulp of
+// |Phi(a)| + |a phi(a)| (it cancels near its root at a = -0.7518).
+__device__ __forceinline__ float gelu_f32(float x) { return 0.5f * x * erfcf(-x * 0.70710678118654752f); }
+__device__ __forceinline__ float dgelu_f32(float a) {
+  return 0.5f * erfcf(-a * 0.70710678118654752f) + a * expf(-0.5f * a * a) * 0.39894228040143268f;
+}
+
 // Cross-lane max inside a quad of lanes via DPP quad permutes.
 __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
   uint32_t t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // lane ^ 1

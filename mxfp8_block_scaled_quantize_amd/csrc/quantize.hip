@@ -90,11 +90,13 @@ __device__ __forceinline__ void fold_amax(const QuantOpts& o, uint32_t m) {
   }
 }
 
-// Activation fused into the quantizer: none, squared ReLU relu(x)^2, or its
-// backward grad * 2 relu(a).  Values are fp32 (both products of two BF16
-// values are exact in fp32 inside its normal range) and are quantized with the
-// fp32 form of the scaled convert.
-enum { ACT_NONE = 0, ACT_SQRELU = 1, DACT_SQRELU = 2 };
+// Activation fused into the quantizer: none, squared ReLU relu(x)^2 or its
+// backward grad * 2 relu(a), GELU x Phi(x) or its backward grad * GELU'(a).
+// Values are fp32 and are quantized with the fp32 form of the scaled convert.
+// The squared-ReLU values are exact in fp32 (products of two BF16 values
+// inside its normal range); the GELU values come from the device library's
+// erfcf / expf (gelu_f32 in mx_device.h).
+enum { ACT_NONE = 0, ACT_SQRELU = 1, DACT_SQRELU = 2, ACT_GELU = 3, DACT_GELU = 4 };
 
 // relu of two BF16 values on their bits: every negative value (-0 included)
 // is a negative signed halfword, so a signed max with 0 (v_pk_max_i16) gives
@@ -210,6 +212,7 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
     // needed (keeping 64 fp32 values live would halve the waves per SIMD).
     // Squared ReLU: max r^2 = (max r)^2, so block amaxes come from integer
     // maxima of the relu'd BF16 bits, as in the plain path.
+    constexpr bool DACT = ACT == DACT_SQRELU || ACT == DACT_GELU;
     uint4 a[8];
     if (ACT == DACT_SQRELU) {
       load_rows(act_in, a);
@@ -217,7 +220,9 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
       for (int i = 0; i < 8; i++)
         a[i] = make_uint4(twice_bf16x2(relu_bf16x2(a[i].x)), twice_bf16x2(relu_bf16x2(a[i].y)),
                           twice_bf16x2(relu_bf16x2(a[i].z)), twice_bf16x2(relu_bf16x2(a[i].w)));
-    } else {
+    } else if (ACT == DACT_GELU) {
+      load_rows(act_in, a);
+    } else if (ACT == ACT_SQRELU) {
 #pragma unroll
       for (int i = 0; i < 8; i++)
         v[i] = make_uint4(relu_bf16x2(v[i].x), relu_bf16x2(v[i].y), relu_bf16x2(v[i].z), relu_bf16x2(v[i].w));
@@ -225,6 +230,8 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
     auto val = [&](int i, int k) -> float {
       const float xv = bf_half(v[i], k);
       if (ACT == ACT_SQRELU) return xv * xv;
+      if (ACT == ACT_GELU) return gelu_f32(xv);
+      if (ACT == DACT_GELU) return xv * dgelu_f32(bf_half(a[i], k));
       return xv * bf_half(a[i], k);   // a holds 2 relu(a)
     };
     // |value| bits -> block amax bits (squared ReLU: from the max relu'd input)
@@ -267,7 +274,7 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
 #pragma unroll
       for (int i = 0; i < 8; i++) {
         asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
-        if (ACT == DACT_SQRELU) asm volatile("" : "+v"(a[i].x), "+v"(a[i].y), "+v"(a[i].z), "+v"(a[i].w));
+        if (DACT) asm volatile("" : "+v"(a[i].x), "+v"(a[i].y), "+v"(a[i].z), "+v"(a[i].w));
       }
     }
     if (COL || DBIAS) {
@@ -297,7 +304,7 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
 #pragma unroll
         for (int i = 0; i < 8; i++) {
           f[i] = val(i, k);
-          if (ACT == DACT_SQRELU) fm = fmaxf(fm, fabsf(f[i]));
+          if (ACT != ACT_SQRELU) fm = fmaxf(fm, fabsf(f[i]));
           if (DBIAS) t += f[i];
         }
         uint32_t m = __float_as_uint(fm);
@@ -658,7 +665,7 @@ int64_t quantize_col_tiles(int64_t C) { return (C + QT_C - 1) / QT_C; }
 enum QuantPath { QP_PACKED_ROW, QP_FLAT, QP_TILES };
 static QuantPath quantize_path(int64_t C, int64_t ldx, uint32_t flags) {
   const bool row = flags & 1u, col = flags & 2u, db = flags & 4u, packed = flags & 16u;
-  const bool act = flags & (32u | 64u);
+  const bool act = flags & (32u | 64u | 128u | 256u);
   if (row && !col && !db && packed && !act) return QP_PACKED_ROW;
   if (row && !col && !db && !packed && !act && ldx == C) return QP_FLAT;
   return QP_TILES;
@@ -732,7 +739,11 @@ hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
                            float* dbias, float* dbias_part, float* amax, const int32_t* noop,
                            const uint16_t* act_in, hipStream_t stream) {
   const bool row = flags & 1u, col = flags & 2u, db = flags & 4u, want_amax = flags & 8u, packed = flags & 16u;
-  const int act = (flags & 32u) ? ACT_SQRELU : (flags & 64u) ? DACT_SQRELU : ACT_NONE;
+  const int act = (flags & 32u)    ? ACT_SQRELU
+                  : (flags & 64u)  ? DACT_SQRELU
+                  : (flags & 128u) ? ACT_GELU
+                  : (flags & 256u) ? DACT_GELU
+                                   : ACT_NONE;
   const QuantOpts opt{want_amax ? reinterpret_cast<uint32_t*>(amax) : nullptr, noop, packed ? 1 : 0};
   if (want_amax) {   // max starts from 0 (also the amax of an empty tensor)
     hipLaunchKernelGGL(fill_zero_f32_kernel, dim3(1), dim3(256), 0, stream, amax, (int64_t)1, noop);
@@ -766,6 +777,12 @@ hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
   else if (act == DACT_SQRELU)
     e = launch_tiles_act<DACT_SQRELU>(row, col, db, x, R, C, ldx, q_row, srow, q_colT, scol, dbias_part, opt,
                                       act_in, &tiles_r, stream);
+  else if (act == ACT_GELU)
+    e = launch_tiles_act<ACT_GELU>(row, col, db, x, R, C, ldx, q_row, srow, q_colT, scol, dbias_part, opt, act_in,
+                                   &tiles_r, stream);
+  else if (act == DACT_GELU)
+    e = launch_tiles_act<DACT_GELU>(row, col, db, x, R, C, ldx, q_row, srow, q_colT, scol, dbias_part, opt,
+                                    act_in, &tiles_r, stream);
   else
     e = launch_tiles_act<ACT_NONE>(row, col, db, x, R, C, ldx, q_row, srow, q_colT, scol, dbias_part, opt, act_in,
                                    &tiles_r, stream);

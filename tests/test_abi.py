@@ -45,7 +45,7 @@ def test_header_constants_match_the_binding():
     import re
     text = open(HEADER).read()
     flags = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (MXFP8_[A-Z_]+) (\d+)u", text)}
-    assert len(flags) == 10, flags
+    assert len(flags) == 13, flags
     for name, value in flags.items():
         assert getattr(mx, name) == value, name
     binding = {n for n in dir(mx) if re.fullmatch(r"MXFP8_[A-Z_]+", n) and isinstance(getattr(mx, n), int)}
@@ -116,8 +116,16 @@ def qx(L, x=A16, rows=128, cols=128, ld=128, flags=ROW, qr=A16, sr=A16, qc=A16, 
 def test_quantize_ex_validation(L):
     AMAX, PACKED = mx.MXFP8_AMAX, mx.MXFP8_PACKED_SCALES
     ACT, DACT = mx.MXFP8_ACT_SQRELU, mx.MXFP8_DACT_SQRELU
-    assert qx(L, flags=128 | ROW) == FLAGS
+    GELU, DGELU = mx.MXFP8_ACT_GELU, mx.MXFP8_DACT_GELU
+    assert qx(L, flags=512 | ROW) == FLAGS
     assert qx(L, flags=ROW | ACT | DACT) == FLAGS              # one activation at a time
+    for a, b in ((ACT, GELU), (DACT, GELU), (ACT, DGELU), (GELU, DGELU), (DACT, DGELU)):
+        assert qx(L, flags=ROW | a | b, act=A16) == FLAGS
+    assert qx(L, flags=ROW | DGELU, act=None) == NULL
+    assert qx(L, flags=COL | DGELU, act=A16 + 2) == MISALIGNED
+    assert qx(L, flags=ROW | GELU, act=None, x=A16 + 2) == MISALIGNED   # act_in unused for the forward
+    assert qx(L, flags=ROW | GELU | DB, act=None, ws=None) == WORKSPACE
+    assert qx(L, flags=ROW | DGELU | DB, act=A16, ws=None) == WORKSPACE
     assert qx(L, flags=ACT) == FLAGS
     assert qx(L, flags=ROW | DACT, act=None) == NULL
     assert qx(L, flags=COL | DACT, act=A16 + 2) == MISALIGNED
@@ -209,14 +217,20 @@ def test_grouped_gemm_validation(L):
 
 def test_gemm_ex_flags(L):
     G = L.mxfp8_gemm_ex
-    assert G(A16, A16, A16, A16, A16, 64, 64, 64, 128, 4, None) == FLAGS
+    assert G(A16, A16, A16, A16, A16, 64, 64, 64, 128, 8, None) == FLAGS
     assert G(A16, A16, A16, A16, A16, 64, 64, 64, 128, 3, None) == FLAGS   # accumulate and relu^2 together
+    assert G(A16, A16, A16, A16, A16, 64, 64, 64, 128, 5, None) == FLAGS   # accumulate and GELU
+    assert G(A16, A16, A16, A16, A16, 64, 64, 64, 128, 6, None) == FLAGS   # two epilogues
+    assert G(A16, A16, A16, A16, A16, 64, 64, 64, 100, 4, None) == SHAPE   # GELU alone passes the flag check
+    assert G(None, None, None, None, None, 64, 0, 64, 128, 4, None) == OK
     assert G(A16, A16, A16, A16, A16, 64, 64, 64, 100, 2, None) == SHAPE
     assert G(A16, A16, A16, A16, A16, 64, 64, 64, 100, 1, None) == SHAPE   # the dense checks still apply
     assert G(None, None, None, None, None, 64, 0, 64, 128, 1, None) == OK
     GG = L.mxfp8_grouped_gemm_ex
-    assert GG(A16, A16, A16, A16, A16, 4, A16, 64, 64, 64, 128, 4, None) == FLAGS
+    assert GG(A16, A16, A16, A16, A16, 4, A16, 64, 64, 64, 128, 8, None) == FLAGS
     assert GG(A16, A16, A16, A16, A16, 4, A16, 64, 64, 64, 128, 3, None) == FLAGS
+    assert GG(A16, A16, A16, A16, A16, 4, A16, 64, 64, 64, 128, 6, None) == FLAGS
+    assert GG(A16, A16, A16, A16, None, 4, None, 64, 0, 64, 128, 4, None) == OK
     assert GG(A16, A16, A16, A16, None, 4, None, 64, 0, 64, 128, 2, None) == OK
     assert GG(A16, A16, A16, A16, A16, 0, A16, 64, 64, 64, 128, 1, None) == SHAPE
     assert GG(A16, A16, A16, A16, None, 4, None, 64, 0, 64, 128, 1, None) == OK

@@ -248,7 +248,7 @@ def test_gemm_accumulate_k_zero_keeps_c():
 
 # --------------------------------------------------------- grouped GEMM
 
-def grouped_case(M, N, K, counts, seed, canary_rows=True, accumulate=False, sqrelu=False):
+def grouped_case(M, N, K, counts, seed, canary_rows=True, accumulate=False, sqrelu=False, gelu=False):
     torch = need_gpu()
     G = len(counts)
     x = workloads.normal_bf16((M, K), seed)
@@ -264,7 +264,7 @@ def grouped_case(M, N, K, counts, seed, canary_rows=True, accumulate=False, sqre
     else:
         out = torch.full((M, N), -7.0, dtype=torch.bfloat16, device="cuda")
     log("grouped M=%d N=%d K=%d counts=%s accumulate=%d" % (M, N, K, list(counts), accumulate))
-    mx.grouped_gemm(qx, px, qw, pw, to_dev(off), out=out, accumulate=accumulate, sqrelu=sqrelu)
+    mx.grouped_gemm(qx, px, qw, pw, to_dev(off), out=out, accumulate=accumulate, sqrelu=sqrelu, gelu=gelu)
     torch.cuda.synchronize()
     c = to_host(out)
     oqx, osx = oracle.quantize_rowwise(x)
@@ -279,6 +279,8 @@ def grouped_case(M, N, K, counts, seed, canary_rows=True, accumulate=False, sqre
         ref = ref + bf16_to_f64(c_old[rows])
     if sqrelu:
         sqrelu_tolerance_check(c[rows], ref, K, label="grouped sqrelu")
+    elif gelu:
+        gelu_tolerance_check(c[rows], ref, K, label="grouped gelu")
     else:
         gemm_tolerance_check(c[rows], ref, K, label="grouped")
     if canary_rows and accumulate:
@@ -338,6 +340,73 @@ def test_gemm_sqrelu_epilogue_exact_on_integers():
 
 def test_grouped_sqrelu_epilogue():
     grouped_case(1200, 96, 256, [5, 0, 131, 257, 600], 9, sqrelu=True)
+
+
+GELU_MIN = -0.16997   # min GELU, at x = -0.7518 (GELU(-0.75179) = -0.169971)
+
+
+def gelu_tolerance_check(gpu_bits, r, K, label="", rms=None):
+    """GELU(R) epilogue: the GPU applies GELU to its fp32 sum acc with
+    |acc - R| <= t (the GEMM bound); |GELU'| <= 1.13 everywhere, so the exact
+    GELU moves by at most 1.13 t; the fp32 GELU adds (8 + 3 acc^2) 2^-24 of
+    its value, and the BF16 rounding 2^-9 (doubled for margin)."""
+    gpu = bf16_to_f64(gpu_bits)
+    r = np.asarray(r, dtype=np.float64)
+    if rms is None:
+        rms = np.sqrt(np.mean(r ** 2))
+    t = 8e-3 * np.abs(r) + 1e-3 * np.sqrt(K) * rms
+    g = oracle.gelu_epilogue(r)
+    mag = np.abs(g) + 1.13 * t
+    tol = 1.13 * t + 2.0 ** -8 * mag + (8.0 + 3.0 * (np.abs(r) + t) ** 2) * 2.0 ** -24 * mag
+    err = np.abs(gpu - g)
+    bad = ~(err <= tol)
+    assert not bad.any(), "%s: %d entries out of tolerance, worst %g vs %g" % (
+        label, bad.sum(), err[bad].max(), tol[bad][np.argmax(err[bad])])
+    assert np.all(gpu >= GELU_MIN * (1 + 2.0 ** -7)), label
+
+
+@pytest.mark.parametrize("M,N,K", [(32, 32, 128), (160, 96, 1024), (1000, 320, 256), (288, 288, 1152)])
+def test_gemm_gelu_epilogue(M, N, K):
+    a = workloads.normal_bf16((M, K), 7 * M + K)
+    b = workloads.normal_bf16((N, K), 11 * N + K, std=0.5)
+    qa, sa, pa = quantize_on_gpu(a)
+    qb, sb, pb = quantize_on_gpu(b)
+    log("gelu epilogue M=%d N=%d K=%d" % (M, N, K))
+    c = gemm_gpu(qa, pa, qb, pb, ldc=N + 24, canary=True, flags=mx.MXFP8_GEMM_GELU)
+    oqa, osa = oracle.quantize_rowwise(a)
+    oqb, osb = oracle.quantize_rowwise(b)
+    gelu_tolerance_check(c, oracle.gemm_tn(oqa, osa, oqb, osb), K, "gelu")
+
+
+def test_gemm_gelu_epilogue_on_integers():
+    """Integer operands: the fp32 sum R is exact, so the output is the BF16
+    rounding of the fp32 GELU(R): between the BF16 roundings of GELU(R) -+ its
+    fp32 error bound, i.e. the correctly rounded value unless GELU(R) is within
+    that bound of a rounding boundary.  Far negative sums (R < -12) give
+    values below 1e-30."""
+    rng = np.random.default_rng(14)
+    A = rng.integers(-1, 2, size=(160, 128))
+    B = rng.integers(-1, 2, size=(96, 128))
+    ab = (A.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    bb = (B.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    qa, sa, pa = quantize_on_gpu(ab)
+    qb, sb, pb = quantize_on_gpu(bb)
+    log("gelu integers")
+    c = bf16_to_f64(gemm_gpu(qa, pa, qb, pb, flags=mx.MXFP8_GEMM_GELU))
+    R = (A @ B.T).astype(np.float64)
+    g = oracle.gelu_epilogue(R)
+    e = (8.0 + 3.0 * R * R) * 2.0 ** -24 * np.abs(g)
+    near = R >= -12
+    lo = bf16_to_f64(workloads.f32_to_bf16_bits((g - e).astype(np.float32)))
+    hi = bf16_to_f64(workloads.f32_to_bf16_bits((g + e).astype(np.float32)))
+    ok = (c >= lo) & (c <= hi)
+    assert ok[near].all(), "%d of %d outside the rounding bracket" % ((~ok[near]).sum(), near.sum())
+    assert np.all(np.abs(c[~near]) <= 1e-30)
+    assert near.mean() > 0.9 and (lo == hi)[near].mean() > 0.99   # nearly every entry decided exactly
+
+
+def test_grouped_gelu_epilogue():
+    grouped_case(1200, 96, 256, [5, 0, 131, 257, 600], 10, gelu=True)
 
 
 def test_grouped_uniform_counts():

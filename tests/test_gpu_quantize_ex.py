@@ -362,3 +362,215 @@ def test_full_moe_packed_rowwise():
         q, s = oracle.quantize_rowwise(bits)
         assert np.array_equal(got["q_row"], q) and np.array_equal(got["s_row"], oracle.pack_scales(s)), name
         del got
+
+
+# ------------------------------------------------ GELU-fused quantize
+#
+# The kernel evaluates GELU and its derivative in fp32 with the device
+# library's erfcf / expf, so its value w of an element is known only within
+# a bound e of the exact value v (the oracle's float64 GELU).  The check below
+# accepts exactly the outputs that some w in [v - e, v + e] (per element)
+# would give: the block's scale byte between the bytes of the smallest and the
+# largest possible block amax, each code between the codes of v - e and v + e
+# under that byte.  Elements whose bound straddles a rounding boundary are
+# counted; everywhere else the comparison is exact.
+
+GELU, DGELU = mx.MXFP8_ACT_GELU, mx.MXFP8_DACT_GELU
+ULP32 = 2.0 ** -24
+
+
+def gelu_bound(x_bits):
+    """|w - GELU(x)| <= (8 + 3 x^2) 2^-24 |GELU(x)|: twice the largest error
+    measured over every BF16 input for the erfc form in fp32."""
+    x = oracle.bf16_value(x_bits)
+    return (8.0 + 3.0 * x * x) * ULP32 * np.abs(oracle.gelu_f64(x))
+
+
+def dgelu_bound(g_bits, a_bits):
+    """|w - g GELU'(a)| <= |g| 8 2^-24 (|Phi(a)| + |a phi(a)|) + 2^-23 |v|:
+    the derivative's sum within 8 ulp of its terms' magnitudes (measured: 3.6),
+    then the product's rounding."""
+    g = oracle.bf16_value(g_bits)
+    t1, t2 = oracle.dgelu_terms(oracle.bf16_value(a_bits))
+    return np.abs(g) * 8.0 * ULP32 * (np.abs(t1) + np.abs(t2)) + 2.0 * ULP32 * np.abs(g * (t1 + t2))
+
+
+def unpack_words(p, dim):
+    """Packed scale words uint32 [k/128][dim] -> bytes [dim][k/32], checked
+    to be the oracle's packing of the bytes returned."""
+    w = np.ascontiguousarray(p).view(np.uint32)
+    T = w.shape[0]
+    s = np.ascontiguousarray(w.view(np.uint8).reshape(T, dim, 4).transpose(1, 0, 2).reshape(dim, 4 * T))
+    assert np.array_equal(oracle.pack_scales(s), w)
+    return s
+
+
+def check_bounded_copy(q, s, v, e, label):
+    """Codes q [n][m] and scale bytes s [n][m/32] (blocks of 32 along m) of
+    values within v +- e.  Returns the fractions of codes and of blocks that
+    the bound leaves open (values on an E4M3 rounding tie or a block amax on
+    a power of two, mostly where GELU(x) is x to within 1e-9)."""
+    n, m = v.shape
+    av = np.abs(v).reshape(n, m // 32, 32)
+    ae = e.reshape(n, m // 32, 32)
+    b_lo = oracle.scale_bytes(np.maximum(av - ae, 0.0).max(axis=2))
+    b_hi = oracle.scale_bytes((av + ae).max(axis=2))
+    bad = (s < b_lo) | (s > b_hi)
+    if bad.any():
+        i, j = np.argwhere(bad)[0]
+        raise AssertionError("%s: %d scale bytes outside their bound, first (%d,%d) got %d want [%d,%d]" % (
+            label, bad.sum(), i, j, s[i, j], b_lo[i, j], b_hi[i, j]))
+    X = np.repeat(oracle.e8m0_decode(s), 32, axis=1)
+    d = oracle.e4m3_decode(q)
+    assert not np.isnan(d).any(), label + ": NaN code"
+    d_lo = oracle.e4m3_decode(oracle.e4m3_encode((v - e) / X))
+    d_hi = oracle.e4m3_decode(oracle.e4m3_encode((v + e) / X))
+    bad = (d < d_lo) | (d > d_hi)
+    if bad.any():
+        i, j = np.argwhere(bad)[0]
+        raise AssertionError("%s: %d codes outside their bound, first (%d,%d) v=%g e=%g got %g want [%g,%g]" % (
+            label, bad.sum(), i, j, v[i, j], e[i, j], d[i, j], d_lo[i, j], d_hi[i, j]))
+    return float(np.mean(d_lo != d_hi)), float(np.mean(b_lo != b_hi))
+
+
+def check_gelu_result(got, v, e, flags, label, max_open=0.02):
+    R, C = v.shape
+    if flags & ROW:
+        s = unpack_words(got["s_row"], R) if flags & PACKED else got["s_row"]
+        f = check_bounded_copy(got["q_row"], s, v, e, label + " row")
+        assert max(f) <= max_open, "%s row: open fractions (codes, blocks) %s" % (label, f)
+    if flags & COL:
+        s = unpack_words(got["s_colT"], C) if flags & PACKED else got["s_colT"]
+        f = check_bounded_copy(got["q_colT"], s, np.ascontiguousarray(v.T), np.ascontiguousarray(e.T),
+                               label + " col")
+        assert max(f) <= max_open, "%s col: open fractions (codes, blocks) %s" % (label, f)
+    if flags & DB:
+        ref = v.sum(axis=0)
+        mag = np.abs(v).sum(axis=0)
+        depth = 8 + 2 + 3 + ((R + 127) // 128 + 7) // 8 + 3     # the fp32 addition chain of the kernel
+        tol = 1.01 * depth * ULP32 * (mag + e.sum(axis=0)) + e.sum(axis=0) + np.abs(ref) * ULP32 + 2.0 ** -126
+        err = np.abs(got["dbias"].astype(np.float64) - ref)
+        assert np.all(err <= tol), "%s: dbias off by %g" % (label, (err - tol).max())
+    if flags & AMAX:
+        a = float(got["amax"][0])
+        lo = float(np.maximum(np.abs(v) - e, 0.0).max(initial=0.0))
+        hi = float((np.abs(v) + e).max(initial=0.0))
+        assert lo <= a <= hi, "%s: amax %r outside [%r, %r]" % (label, a, lo, hi)
+
+
+def gelu_case(R, C, seed):
+    x = workloads.preact_bf16((R, C), seed)
+    return x, oracle.act_gelu(x), gelu_bound(x)
+
+
+def dgelu_case(R, C, seed):
+    g = workloads.wide_range_bf16((R, C), seed, u_lo=-30, u_hi=30, n_maxbf16=0, n_subnormal=0,
+                                  n_subnormal_blocks=0)
+    a = workloads.preact_bf16((R, C), seed + 1, floor=-10.0)
+    return g, a, oracle.dact_gelu(g, a), dgelu_bound(g, a)
+
+
+def test_gelu_bounds_cover_the_contract():
+    """The inputs stay where the fp32 results are normal numbers (the
+    contract), and the bounds are far below an E4M3 step (2^-4 relative)."""
+    x, v, e = gelu_case(256, 384, 1)
+    assert np.all((np.abs(v) >= 2.0 ** -126) | (v == 0)) and np.all(e <= 2.0 ** -10 * np.abs(v))
+    g, a, v, e = dgelu_case(256, 384, 2)
+    nz = v != 0
+    assert np.all(np.abs(v[nz]) >= 2.0 ** -126)
+
+
+@pytest.mark.parametrize("R,C", [(128, 128), (256, 384), (640, 256)])
+@pytest.mark.parametrize("flags", ACT_FLAGS)
+def test_gelu_quantize(R, C, flags):
+    x, v, e = gelu_case(R, C, 107 * R + C + flags)
+    label = "gelu R=%d C=%d flags=%d" % (R, C, flags)
+    log(label)
+    got = run_ex(x, flags | GELU)
+    check_gelu_result(got, v, e, flags, label)
+
+
+@pytest.mark.parametrize("R,C", [(128, 128), (256, 384), (640, 256)])
+@pytest.mark.parametrize("flags", ACT_FLAGS)
+def test_dgelu_quantize(R, C, flags):
+    g, a, v, e = dgelu_case(R, C, 109 * R + C + flags)
+    label = "dgelu R=%d C=%d flags=%d" % (R, C, flags)
+    log(label)
+    got = run_ex(g, flags | DGELU, act_bits=a)
+    check_gelu_result(got, v, e, flags, label)
+
+
+def test_gelu_ragged_rows_and_stride():
+    g, a, v, e = dgelu_case(200, 512, 11)
+    log("dgelu ragged")
+    got = run_ex(g, ROW | DB | AMAX | DGELU, ld=520, act_bits=a)
+    check_gelu_result(got, v, e, ROW | DB | AMAX, "dgelu ragged")
+    x, v, e = gelu_case(200, 512, 13)
+    log("gelu ragged")
+    got = run_ex(x, ROW | AMAX | GELU, ld=520)
+    check_gelu_result(got, v, e, ROW | AMAX, "gelu ragged")
+
+
+def test_gelu_special_values():
+    """Zero blocks (GELU(0) = 0: byte 0, codes 0), blocks far on the positive
+    side (GELU(x) = x to within 1e-15: the scale bytes of x itself),
+    saturation (GELU(31) = 31 = 1.9375 * 2^4 rounds past 448 * 2^-4)
+    and a zero activation input under a nonzero gradient (GELU'(0) = 1/2)."""
+    R, C = 128, 256
+    x = workloads.preact_bf16((R, C), 17)
+    x[:32, :32] = 0
+    x[32:64, 32:64] = workloads.f32_to_bf16_bits(np.linspace(8.0, 30.0, 1024, dtype=np.float32).reshape(32, 32))
+    x[64, 0:32] = workloads.f32_to_bf16_bits(np.full(32, 1.0, dtype=np.float32))
+    x[64, 5] = 0x41F8                      # 31.0
+    v, e = oracle.act_gelu(x), gelu_bound(x)
+    for flags in (ROW | COL | DB | AMAX, ROW | COL | PACKED):
+        log("gelu special flags=%d" % flags)
+        got = run_ex(x, flags | GELU)
+        check_gelu_result(got, v, e, flags, "gelu special")
+        if not flags & PACKED:
+            assert not got["q_row"][:32, :32].any() and not got["s_row"][:32, :1].any()
+            _, s = oracle.quantize_rowwise(x[32:64, 32:64])          # block amax 30: far from a power of 2
+            assert np.array_equal(got["s_row"][32:64, 1:2], s)
+            assert got["q_row"][64, 5] == 0x7E and got["s_row"][64, 0] == 127 - 4
+    g = workloads.wide_range_bf16((R, C), 19, u_lo=-10, u_hi=10, n_maxbf16=0, n_subnormal=0, n_subnormal_blocks=0)
+    a = workloads.preact_bf16((R, C), 21, floor=-10.0)
+    a[32:64, :64] = 0
+    v, e = oracle.dact_gelu(g, a), dgelu_bound(g, a)
+    for flags in (ROW | COL | DB | AMAX, ROW | COL | PACKED):
+        log("dgelu special flags=%d" % flags)
+        got = run_ex(g, flags | DGELU, act_bits=a)
+        check_gelu_result(got, v, e, flags, "dgelu special")
+        if not flags & PACKED:
+            q, s = oracle.quantize_rowwise_values(v[32:64, :64])   # g / 2 is exact
+            assert np.array_equal(got["q_row"][32:64, :64], q) and np.array_equal(got["s_row"][32:64, :2], s)
+
+
+@pytest.mark.parametrize("flags", [ROW | COL | DB | GELU, ROW | PACKED | DGELU])
+def test_gelu_noop(flags):
+    g, a, _, _ = dgelu_case(256, 256, 23)
+    got = run_ex(g, flags | AMAX, noop_value=1, act_bits=a if flags & DGELU else None)
+    for k, v in got.items():
+        if v.dtype == np.uint8:
+            assert np.all(v == 0xA5), k
+        elif v.dtype == np.uint32:
+            assert np.all(v == 0xFFFFFFFF), k
+        elif k == "dbias":
+            assert np.all(v == -5.0), k
+        else:
+            assert np.all(v == -7.0), k
+
+
+@pytest.mark.slow
+def test_full_mlp_gelu_quantize():
+    """A GELU MLP's two activation launches at full size (8192 x 14336, row +
+    col, packed scales): GELU of H (amax), and the backward of dA through H
+    with dbias."""
+    d = workloads.mlp_hidden()
+    h, da = d["H"], d["dA"]
+    log("full mlp gelu %s" % (h.shape,))
+    got = run_ex(h, ROW | COL | PACKED | AMAX | GELU)
+    check_gelu_result(got, oracle.act_gelu(h), gelu_bound(h), ROW | COL | PACKED | AMAX, "full gelu")
+    del got
+    log("full mlp dgelu %s" % (h.shape,))
+    got = run_ex(da, ROW | COL | PACKED | DB | DGELU, act_bits=h)
+    check_gelu_result(got, oracle.dact_gelu(da, h), dgelu_bound(da, h), ROW | COL | PACKED | DB, "full dgelu")

@@ -22,6 +22,10 @@ MoE workloads the MXFP8 quantize and GEMM pages discuss):
 * ``moe``       X BF16[16384x4096] ~ N(0,1) (seed 0); W BF16[8][14336x4096] ~
                 N(0,0.02) (seed 1); group sizes 32 * Multinomial(512, 1/8 each)
                 (seed 2) turned into int32 offsets[9].
+* ``preact``    GELU inputs: N(0,1) blocks scaled by 2^u, u in [-12, 2], with
+                1/16 of the blocks uniform in [-10, -3] and 1/16 uniform in
+                [3, 40], clipped below at -12 (where GELU stays inside fp32's
+                normal range); parity cases only.
 * ``stress``    A BF16[32768x8192]: N(0,1) with every rowwise 32-block scaled
                 by 2^u, u uniform integer in [-40, 40] (seed 0), plus 64 +-max
                 BF16 values, 4096 random +-subnormals and 16 all-subnormal
@@ -114,6 +118,29 @@ def wide_range_bf16(shape, seed: int, u_lo: int = -40, u_hi: int = 40,
         mant = rng.integers(1, 128, size=(n_subnormal_blocks, 32)).astype(np.uint16)
         flat.reshape(nblk, 32)[blk] = sign | mant
     return bits
+
+
+def preact_bf16(shape, seed: int, u_lo: int = -12, u_hi: int = 2, tail_frac: float = 1.0 / 16,
+                floor: float = -12.0) -> np.ndarray:
+    """Pre-activation-like values for GELU: N(0,1) with each rowwise 32-block
+    scaled by 2^u (u uniform integer in [u_lo, u_hi]); a fraction tail_frac
+    of the blocks is replaced by uniform values in [-10, -3] (GELU's negative
+    tail) and as many by uniform values in [3, 40] (where GELU is nearly the
+    identity); everything is clipped below at `floor`."""
+    rng = np.random.default_rng(seed)
+    r, c = shape
+    x = _normal_f32(rng, shape, 1.0)
+    xb = x.reshape(r * (c // 32), 32)
+    u = rng.integers(u_lo, u_hi + 1, size=r * (c // 32))
+    xb *= np.ldexp(np.float32(1.0), u)[:, None].astype(np.float32)
+    nblk = xb.shape[0]
+    k = int(round(tail_frac * nblk))
+    if k:
+        pick = rng.choice(nblk, size=2 * k, replace=False)
+        xb[pick[:k]] = rng.uniform(-10.0, -3.0, size=(k, 32)).astype(np.float32)
+        xb[pick[k:]] = rng.uniform(3.0, 40.0, size=(k, 32)).astype(np.float32)
+    np.maximum(x, np.float32(floor), out=x)
+    return f32_to_bf16_bits(x)
 
 
 def moe_offsets(total_tokens: int, groups: int, seed: int, align: int = 32) -> np.ndarray:
