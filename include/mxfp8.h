@@ -158,9 +158,10 @@ mxfp8_status mxfp8_quantize(const void *x, int64_t rows, int64_t cols, int64_t l
  *         one of MXFP8_ACT_SQRELU / MXFP8_DACT_SQRELU / MXFP8_ACT_GELU /
  *         MXFP8_DACT_GELU.  With an activation the quantized value v is the
  *         fp32 result of the activation (for squared ReLU each product of two
- *         BF16 values is exact in fp32; GELU uses the device erfcf / expf,
- *         within (8 + 3 a^2) fp32 ulp of GELU(a) and 8 ulp of |Phi(a)| +
- *         |a phi(a)| for its derivative); its block scale follows the same
+ *         BF16 values is exact in fp32; GELU is evaluated in fp32 from the
+ *         normal tail exp(-t^2/2) Q(t) with a fitted rational Q, within
+ *         (8 + 3 a^2) fp32 ulp of GELU(a) and 8 ulp of |Phi(a)| + |a phi(a)|
+ *         for its derivative); its block scale follows the same
  *         rule (exponent of the block amax - 8), codes are RNE of
  *         v / 2^(scale - 127) saturated to +-448.
  * s_row, s_colT  byte scales as in mxfp8_quantize, or (PACKED_SCALES) uint32

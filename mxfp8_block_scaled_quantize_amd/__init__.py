@@ -192,7 +192,7 @@ def quantize(x, rowwise=True, colwise=False, dbias=False, amax=False, packed=Fal
     act="sqrelu" quantizes relu(x)^2; act="dsqrelu" quantizes
     x * 2 relu(act_in) (x is the gradient, act_in the activation's input, a
     BF16 tensor of x's shape and strides); act="gelu" quantizes GELU(x) and
-    act="dgelu" x * GELU'(act_in) (exact erfc form, fp32)."""
+    act="dgelu" x * GELU'(act_in) (GELU(x) = x Phi(x), not the tanh approximation; fp32)."""
     import torch
     if not isinstance(x, torch.Tensor) or x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a BF16 [rows, cols] tensor with unit column stride")

@@ -94,8 +94,8 @@ __device__ __forceinline__ void fold_amax(const QuantOpts& o, uint32_t m) {
 // backward grad * 2 relu(a), GELU x Phi(x) or its backward grad * GELU'(a).
 // Values are fp32 and are quantized with the fp32 form of the scaled convert.
 // The squared-ReLU values are exact in fp32 (products of two BF16 values
-// inside its normal range); the GELU values come from the device library's
-// erfcf / expf (gelu_f32 in mx_device.h).
+// inside its normal range); the GELU values are within the error bounds
+// stated with gelu_f32 / dgelu_f32 in mx_device.h.
 enum { ACT_NONE = 0, ACT_SQRELU = 1, DACT_SQRELU = 2, ACT_GELU = 3, DACT_GELU = 4 };
 
 // relu of two BF16 values on their bits: every negative value (-0 included)
@@ -227,6 +227,8 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
       for (int i = 0; i < 8; i++)
         v[i] = make_uint4(relu_bf16x2(v[i].x), relu_bf16x2(v[i].y), relu_bf16x2(v[i].z), relu_bf16x2(v[i].w));
     }
+    // GELU (about 25 VALU operations a value) is recomputed too: keeping its
+    // 64 results for the column pass measured slower (fewer waves per SIMD).
     auto val = [&](int i, int k) -> float {
       const float xv = bf_half(v[i], k);
       if (ACT == ACT_SQRELU) return xv * xv;

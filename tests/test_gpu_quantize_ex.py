@@ -381,9 +381,12 @@ ULP32 = 2.0 ** -24
 
 def gelu_bound(x_bits):
     """|w - GELU(x)| <= (8 + 3 x^2) 2^-24 |GELU(x)|: twice the largest error
-    measured over every BF16 input for the erfc form in fp32."""
+    measured over every BF16 input of the kernel's fp32 GELU.  For |x| >= 16
+    the kernel's Phi(-|x|) is exactly 0 (exp(-128) underflows), so w is x or
+    -0: within one rounding of the exact value."""
     x = oracle.bf16_value(x_bits)
-    return (8.0 + 3.0 * x * x) * ULP32 * np.abs(oracle.gelu_f64(x))
+    g = np.abs(oracle.gelu_f64(x))
+    return np.where(np.abs(x) >= 16.0, ULP32 * g, (8.0 + 3.0 * x * x) * ULP32 * g)
 
 
 def dgelu_bound(g_bits, a_bits):
@@ -514,14 +517,19 @@ def test_gelu_ragged_rows_and_stride():
 def test_gelu_special_values():
     """Zero blocks (GELU(0) = 0: byte 0, codes 0), blocks far on the positive
     side (GELU(x) = x to within 1e-15: the scale bytes of x itself),
-    saturation (GELU(31) = 31 = 1.9375 * 2^4 rounds past 448 * 2^-4)
-    and a zero activation input under a nonzero gradient (GELU'(0) = 1/2)."""
+    saturation (GELU(31) = 31 = 1.9375 * 2^4 rounds past 448 * 2^-4), a zero
+    activation input under a nonzero gradient (GELU'(0) = 1/2), and blocks
+    of huge inputs (20 .. 3e38: GELU(x) = x and GELU'(a) = 1 exactly, their
+    negatives give zeros)."""
     R, C = 128, 256
     x = workloads.preact_bf16((R, C), 17)
     x[:32, :32] = 0
     x[32:64, 32:64] = workloads.f32_to_bf16_bits(np.linspace(8.0, 30.0, 1024, dtype=np.float32).reshape(32, 32))
     x[64, 0:32] = workloads.f32_to_bf16_bits(np.full(32, 1.0, dtype=np.float32))
     x[64, 5] = 0x41F8                      # 31.0
+    huge = workloads.f32_to_bf16_bits(np.geomspace(20.0, 3.0e38, 32).astype(np.float32))
+    x[96, 64:96] = huge                    # GELU(x) = x
+    x[97, 64:96] = huge | 0x8000           # GELU(x) = -0 (the exact value underflows)
     v, e = oracle.act_gelu(x), gelu_bound(x)
     for flags in (ROW | COL | DB | AMAX, ROW | COL | PACKED):
         log("gelu special flags=%d" % flags)
@@ -532,9 +540,14 @@ def test_gelu_special_values():
             _, s = oracle.quantize_rowwise(x[32:64, 32:64])          # block amax 30: far from a power of 2
             assert np.array_equal(got["s_row"][32:64, 1:2], s)
             assert got["q_row"][64, 5] == 0x7E and got["s_row"][64, 0] == 127 - 4
+            q, s = oracle.quantize_rowwise(huge[None, :])
+            assert np.array_equal(got["q_row"][96, 64:96], q[0]) and got["s_row"][96, 2] == s[0, 0]
+            assert got["s_row"][97, 2] == 0 and np.all(got["q_row"][97, 64:96] & 0x7F == 0)
     g = workloads.wide_range_bf16((R, C), 19, u_lo=-10, u_hi=10, n_maxbf16=0, n_subnormal=0, n_subnormal_blocks=0)
     a = workloads.preact_bf16((R, C), 21, floor=-10.0)
     a[32:64, :64] = 0
+    a[96, 64:96] = huge                    # GELU'(a) = 1: v = g
+    a[97, 64:96] = huge | 0x8000           # GELU'(a) = 0
     v, e = oracle.dact_gelu(g, a), dgelu_bound(g, a)
     for flags in (ROW | COL | DB | AMAX, ROW | COL | PACKED):
         log("dgelu special flags=%d" % flags)
@@ -543,6 +556,9 @@ def test_gelu_special_values():
         if not flags & PACKED:
             q, s = oracle.quantize_rowwise_values(v[32:64, :64])   # g / 2 is exact
             assert np.array_equal(got["q_row"][32:64, :64], q) and np.array_equal(got["s_row"][32:64, :2], s)
+            q, s = oracle.quantize_rowwise(g[96:97, 64:96])
+            assert np.array_equal(got["q_row"][96, 64:96], q[0]) and got["s_row"][96, 2] == s[0, 0]
+            assert got["s_row"][97, 2] == 0 and np.all(got["q_row"][97, 64:96] & 0x7F == 0)
 
 
 @pytest.mark.parametrize("flags", [ROW | COL | DB | GELU, ROW | PACKED | DGELU])
