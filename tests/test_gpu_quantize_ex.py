@@ -410,7 +410,7 @@ def unpack_words(p, dim):
 
 def check_bounded_copy(q, s, v, e, label):
     """Codes q [n][m] and scale bytes s [n][m/32] (blocks of 32 along m) of
-    values within v +- e.  Returns the fractions of codes and of blocks that
+    values within v +- e.  Returns the numbers of codes and of blocks that
     the bound leaves open (values on an E4M3 rounding tie or a block amax on
     a power of two, mostly where GELU(x) is x to within 1e-9)."""
     n, m = v.shape
@@ -433,20 +433,27 @@ def check_bounded_copy(q, s, v, e, label):
         i, j = np.argwhere(bad)[0]
         raise AssertionError("%s: %d codes outside their bound, first (%d,%d) v=%g e=%g got %g want [%g,%g]" % (
             label, bad.sum(), i, j, v[i, j], e[i, j], d[i, j], d_lo[i, j], d_hi[i, j]))
-    return float(np.mean(d_lo != d_hi)), float(np.mean(b_lo != b_hi))
+    return int(np.sum(d_lo != d_hi)), int(np.sum(b_lo != b_hi))
 
 
-def check_gelu_result(got, v, e, flags, label, max_open=0.02):
+def check_open(f, v, label, max_open=0.02):
+    """At most 2 % of the codes and of the blocks open (plus 2 codes and one
+    block, for tiny tensors)."""
+    n = v.size
+    assert f[0] <= max_open * n + 2 and f[1] <= max_open * n / 32 + 1, \
+        "%s: open (codes, blocks) %s of (%d, %d)" % (label, f, n, n // 32)
+
+
+def check_gelu_result(got, v, e, flags, label):
     R, C = v.shape
     if flags & ROW:
         s = unpack_words(got["s_row"], R) if flags & PACKED else got["s_row"]
-        f = check_bounded_copy(got["q_row"], s, v, e, label + " row")
-        assert max(f) <= max_open, "%s row: open fractions (codes, blocks) %s" % (label, f)
+        check_open(check_bounded_copy(got["q_row"], s, v, e, label + " row"), v, label + " row")
     if flags & COL:
         s = unpack_words(got["s_colT"], C) if flags & PACKED else got["s_colT"]
         f = check_bounded_copy(got["q_colT"], s, np.ascontiguousarray(v.T), np.ascontiguousarray(e.T),
                                label + " col")
-        assert max(f) <= max_open, "%s col: open fractions (codes, blocks) %s" % (label, f)
+        check_open(f, v, label + " col")
     if flags & DB:
         ref = v.sum(axis=0)
         mag = np.abs(v).sum(axis=0)

@@ -5,7 +5,8 @@ and grouped GEMMs with random group sizes (empty and non-multiple-of-32 groups,
 uncovered tails).  Each case is drawn from a fixed generator, so a failure
 names a reproducible case; the checks are the same as in the hand-picked
 tests (bit-exact codes and scales, dbias within its summation bound, GEMM
-within the stated tolerance)."""
+within the stated tolerance; GELU outputs within the bounded check of the
+GELU tests)."""
 
 import numpy as np
 import pytest
@@ -14,8 +15,8 @@ import mxfp8_block_scaled_quantize_amd as mx
 import oracle
 import workloads
 from gpu_util import bf16_to_f64, gemm_tolerance_check, log, need_gpu, to_dev_bf16, to_host
-from test_gpu_gemm import gemm_gpu, grouped_case, quantize_on_gpu, sqrelu_tolerance_check
-from test_gpu_quantize_ex import act_inputs, check_act_result, run_ex
+from test_gpu_gemm import gelu_tolerance_check, gemm_gpu, grouped_case, quantize_on_gpu, sqrelu_tolerance_check
+from test_gpu_quantize_ex import act_inputs, check_act_result, check_gelu_result, dgelu_case, gelu_case, run_ex
 
 pytestmark = pytest.mark.gpu
 
@@ -123,3 +124,51 @@ def test_random_grouped_gemm(case):
     if M == 0:
         pytest.skip("empty problem (covered by test_grouped_empty_total)")
     grouped_case(M, N, K, list(counts), seed, accumulate=epi == "accumulate", sqrelu=epi == "sqrelu")
+
+
+GELU, DGELU = mx.MXFP8_ACT_GELU, mx.MXFP8_DACT_GELU
+
+
+def gelu_quantize_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for (R, C, ld, flags, _, s) in quantize_cases(n, seed):
+        cases.append((R, C, ld, flags, [GELU, DGELU][rng.integers(0, 2)], s))
+    return cases
+
+
+@pytest.mark.parametrize("case", gelu_quantize_cases(24, 2025))
+def test_random_gelu_quantize(case):
+    R, C, ld, flags, act, seed = case
+    label = "random gelu quantize R=%d C=%d ld=%d flags=%d act=%d seed=%d" % case
+    log(label)
+    if act == GELU:
+        x, v, e = gelu_case(R, C, seed)
+        got = run_ex(x, flags | GELU, ld=ld)
+    else:
+        g, a, v, e = dgelu_case(R, C, seed)
+        got = run_ex(g, flags | DGELU, ld=ld, act_bits=a)
+    check_gelu_result(got, v, e, flags, label)
+
+
+@pytest.mark.parametrize("case", gemm_cases(12, 78))
+def test_random_gemm_gelu(case):
+    M, N, K, ldc, _, seed = case
+    log("random gemm gelu M=%d N=%d K=%d ldc=%d seed=%d" % (M, N, K, ldc, seed))
+    a = workloads.normal_bf16((M, K), seed)
+    b = workloads.normal_bf16((N, K), seed + 1, std=0.25)
+    qa, sa, pa = quantize_on_gpu(a)
+    qb, sb, pb = quantize_on_gpu(b)
+    oqa, osa = oracle.quantize_rowwise(a)
+    oqb, osb = oracle.quantize_rowwise(b)
+    c = gemm_gpu(qa, pa, qb, pb, ldc=ldc, canary=True, flags=mx.MXFP8_GEMM_GELU)
+    gelu_tolerance_check(c, oracle.gemm_tn(oqa, osa, oqb, osb), K, "gelu")
+
+
+@pytest.mark.parametrize("case", grouped_cases(8, 92))
+def test_random_grouped_gemm_gelu(case):
+    counts, tail, N, K, _, seed = case
+    M = sum(counts) + tail
+    if M == 0:
+        pytest.skip("empty problem (covered by test_grouped_empty_total)")
+    grouped_case(M, N, K, list(counts), seed, gelu=True)
