@@ -17,14 +17,14 @@ row+col, 1.09 GB) against the HBM peak; ``cpu_baseline`` is the CPU oracle
 running whole steps of the same workload on the host.  Per-launch times are
 reported as mean, median, min and max over the timed steps.
 
-``--workload dense|backward|moe|moe_sqrelu|linear|mlp`` measures the other
+``--workload dense|backward|moe|moe_sqrelu|linear|mlp|mlp_gelu`` measures the other
 workloads the same way: rowwise quantize and the TN GEMMs 8192x14336x4096 and
 8192^3; row+col+dbias quantize and the wgrad GEMM on the columnwise copies;
 the ragged grouped MoE GEMM (also with the squared-ReLU epilogue of an MoE
 first projection); one MXFP8 linear-layer training step (fprop, dgrad, wgrad
-accumulated into a BF16 main gradient); one squared-ReLU MLP training step
-(six GEMMs, the activation and its backward fused into the quantize
-launches).  They are reporting aids next to the default line.
+accumulated into a BF16 main gradient); one squared-ReLU (or GELU) MLP
+training step (six GEMMs, the activation and its backward fused into the
+quantize launches).  They are reporting aids next to the default line.
 """
 
 import argparse
@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="stress",
-                   choices=["stress", "dense", "backward", "moe", "moe_sqrelu", "linear", "mlp"])
+                   choices=["stress", "dense", "backward", "moe", "moe_sqrelu", "linear", "mlp", "mlp_gelu"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU-oracle time: whole oracle steps are repeated until reached "
@@ -219,31 +219,34 @@ def build_ops(workload, dev):
                 "row+col quantize of X, W, dY, fprop %dx%dx%d, dgrad %dx%dx%d on W's transposed copy, wgrad "
                 "%dx%dx%d on the transposed copies accumulated into a BF16 main gradient"
                 % (T, K, N, K, T, N, K, T, K, N, N, K, T))
-    elif workload == "mlp":
+    elif workload in ("mlp", "mlp_gelu"):
         lin = workloads.mlp()
         host = dict(lin, **workloads.mlp_hidden())
         T, D = lin["X"].shape
         F = lin["W1"].shape[0]
         w2, dy = lin["W2"], lin["dY"]
-        ACT, DACT = mx.MXFP8_ACT_SQRELU, mx.MXFP8_DACT_SQRELU
+        gelu = workload == "mlp_gelu"
+        ACT, DACT = ((mx.MXFP8_ACT_GELU, mx.MXFP8_DACT_GELU) if gelu
+                     else (mx.MXFP8_ACT_SQRELU, mx.MXFP8_DACT_SQRELU))
+        aname, dname, fname = (("GELU(H)", "dA*GELU'(H)", "GELU") if gelu else ("relu^2(H)", "dA*2relu(H)", "squared-ReLU"))
         h, da = [], []
         bx = quantize_op("X[%dx%d] row+col" % (T, D), lin["X"], ROW | COL, packed=True)
         bw1 = quantize_op("W1[%dx%d] row+col" % (F, D), lin["W1"], ROW | COL, packed=True)
         dominant = gemm_op(bx["q"], bx["p"], bw1["q"], bw1["p"], T, F, D, name="fc1 ", out=h)
-        ba = quantize_op("relu^2(H)[%dx%d] row+col" % (T, F), h[0], ROW | COL | ACT, packed=True)
+        ba = quantize_op("%s[%dx%d] row+col" % (aname, T, F), h[0], ROW | COL | ACT, packed=True)
         bw2 = quantize_op("W2[%dx%d] row+col" % (D, F), w2, ROW | COL, packed=True)
         gemm_op(ba["q"], ba["p"], bw2["q"], bw2["p"], T, D, F, name="fc2 ")
         bdy = quantize_op("dY[%dx%d] row+col" % (T, D), dy, ROW | COL, packed=True)
         gemm_op(bdy["q"], bdy["p"], bw2["qT"], bw2["pT"], T, F, D, name="fc2 dgrad ", out=da)
         gemm_op(bdy["qT"], bdy["pT"], ba["qT"], ba["pT"], D, F, T, name="fc2 wgrad ")
-        bdh = quantize_op("dH=dA*2relu(H)[%dx%d] row+col+dbias" % (T, F), da[0], ROW | COL | DB | DACT, packed=True,
+        bdh = quantize_op("dH=%s[%dx%d] row+col+dbias" % (dname, T, F), da[0], ROW | COL | DB | DACT, packed=True,
                           act_in=h[0])
         gemm_op(bdh["q"], bdh["p"], bw1["qT"], bw1["pT"], T, D, F, name="fc1 dgrad ")
         gemm_op(bdh["qT"], bdh["pT"], bx["qT"], bx["pT"], F, D, T, name="fc1 wgrad ")
-        desc = ("squared-ReLU MLP training step, tokens %d, d_model %d, d_ff %d: X N(0,1), W1 N(0,0.02), "
-                "W2 N(0,0.02), dY N(0,1); row+col quantize of X, W1, W2, dY; FC1 GEMM; relu^2 fused into the "
-                "quantize of its BF16 output; FC2 GEMM; FC2 dgrad and wgrad; the activation's backward fused "
-                "into the row+col+dbias quantize of FC2's dgrad output; FC1 dgrad and wgrad" % (T, D, F))
+        desc = ("%s MLP training step, tokens %d, d_model %d, d_ff %d: X N(0,1), W1 N(0,0.02), "
+                "W2 N(0,0.02), dY N(0,1); row+col quantize of X, W1, W2, dY; FC1 GEMM; the activation fused into "
+                "the quantize of its BF16 output; FC2 GEMM; FC2 dgrad and wgrad; the activation's backward fused "
+                "into the row+col+dbias quantize of FC2's dgrad output; FC1 dgrad and wgrad" % (fname, T, D, F))
     elif workload == "moe_sqrelu":
         d = workloads.moe()
         host = d
@@ -525,28 +528,31 @@ def oracle_step(workload, h):
             oracle.gemm_tn(qd, sd, qwT, swT, panel=P)
             oracle.gemm_tn(qdT, sdT, qxT, sxT, panel=P)
         return step, "row+col quantize of X, W, dY, scale packing, fp64 fprop, dgrad and wgrad"
-    if workload == "mlp":
+    if workload in ("mlp", "mlp_gelu"):
+        act, dact = ((oracle.act_gelu, oracle.dact_gelu) if workload == "mlp_gelu"
+                     else (oracle.act_sqrelu, oracle.dact_sqrelu))
+
         def step():
             qx, sx, qxT, sxT = both(h["X"])
             q1, s1, q1T, s1T = both(h["W1"])
             q2, s2, q2T, s2T = both(h["W2"])
             qy, sy, qyT, syT = both(h["dY"])
             oracle.gemm_tn(qx, sx, q1, s1, panel=P)                 # fc1
-            a = oracle.act_sqrelu(h["H"])
+            a = act(h["H"]).astype(np.float32)
             qa, sa = oracle.quantize_rowwise_values(a)
             qaT, saT = oracle.quantize_colwise_values(a)
             oracle.gemm_tn(qa, sa, q2, s2, panel=P)                 # fc2
             oracle.gemm_tn(qy, sy, q2T, s2T, panel=P)               # fc2 dgrad
             oracle.gemm_tn(qyT, syT, qaT, saT, panel=P)             # fc2 wgrad
-            g = oracle.dact_sqrelu(h["dA"], h["H"])
+            g = dact(h["dA"], h["H"]).astype(np.float32)
             qg, sg = oracle.quantize_rowwise_values(g)
             qgT, sgT = oracle.quantize_colwise_values(g)
             oracle.dbias_values(g)
             oracle.gemm_tn(qg, sg, q1T, s1T, panel=P)               # fc1 dgrad
             oracle.gemm_tn(qgT, sgT, qxT, sxT, panel=P)             # fc1 wgrad
-        return step, ("row+col quantize of X, W1, W2, dY, the relu^2 activation and its backward (on the "
+        return step, ("row+col quantize of X, W1, W2, dY, the %s activation and its backward (on the "
                       "full-size stand-ins for the GEMM outputs H and dA) quantized row+col (+dbias), six fp64 "
-                      "GEMMs")
+                      "GEMMs" % ("GELU" if workload == "mlp_gelu" else "relu^2"))
     raise ValueError(workload)
 
 

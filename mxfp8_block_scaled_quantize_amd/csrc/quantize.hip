@@ -227,13 +227,26 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
       for (int i = 0; i < 8; i++)
         v[i] = make_uint4(relu_bf16x2(v[i].x), relu_bf16x2(v[i].y), relu_bf16x2(v[i].z), relu_bf16x2(v[i].w));
     }
-    // GELU (about 25 VALU operations a value) is recomputed too: keeping its
-    // 64 results for the column pass measured slower (fewer waves per SIMD).
+    // GELU (about 20 VALU operations, one v_exp and one v_rcp a value) is
+    // evaluated once and its 64 results are kept for both passes.  Right
+    // after a GEMM, where an MLP runs it and the clock is power-limited, that
+    // is a third faster than recomputing (8192 x 14336 row + col: 116 against
+    // 175 us); alone at full clock recomputing is faster (103 against 121 us,
+    // more waves per SIMD), but that is not where the launch runs.
+    constexpr bool KEEP = ACT == ACT_GELU || ACT == DACT_GELU;
+    float fv[KEEP ? 8 : 1][8];
+    if constexpr (KEEP) {
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+#pragma unroll
+        for (int k = 0; k < 8; k++)
+          fv[i][k] = ACT == ACT_GELU ? gelu_f32(bf_half(v[i], k))
+                                     : bf_half(v[i], k) * dgelu_f32(bf_half(a[i], k));
+    }
     auto val = [&](int i, int k) -> float {
+      if (KEEP) return fv[KEEP ? i : 0][k];
       const float xv = bf_half(v[i], k);
       if (ACT == ACT_SQRELU) return xv * xv;
-      if (ACT == ACT_GELU) return gelu_f32(xv);
-      if (ACT == DACT_GELU) return xv * dgelu_f32(bf_half(a[i], k));
       return xv * bf_half(a[i], k);   // a holds 2 relu(a)
     };
     // |value| bits -> block amax bits (squared ReLU: from the max relu'd input)
@@ -270,7 +283,7 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
         if ((cg & 3) == 0) lds_sr[(32 * w + 8 * rg + i) * 4 + (cg >> 2)] = (uint8_t)byte;
       }
     }
-    if (ROW && (COL || DBIAS)) {
+    if (!KEEP && ROW && (COL || DBIAS)) {
       // Opaque to the optimiser: the column pass recomputes its values
       // instead of keeping the row pass's 64 fp32 results alive.
 #pragma unroll
