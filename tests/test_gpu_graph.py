@@ -21,8 +21,10 @@ AMAX, PACKED = mx.MXFP8_AMAX, mx.MXFP8_PACKED_SCALES
 class Chain:
     """Preallocated buffers of one chain: row+col+dbias+amax quantize of X and
     W into packed scales, dense GEMM X W^T, grouped GEMM of X's rows over two
-    experts (W's two row halves) and a dense wgrad-shaped GEMM of the
-    transposed copies."""
+    experts (W's two row halves), a dense wgrad-shaped GEMM of the transposed
+    copies, the dense GEMM again with the GELU epilogue, and GELU and its
+    backward fused into row+col quantizes of the GEMM output (the backward
+    with dbias, taking that output as both gradient and activation input)."""
 
     def __init__(self, torch, T, N, K):
         self.T, self.N, self.K = T, N, K
@@ -45,6 +47,17 @@ class Chain:
         self.c = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
         self.cg = torch.empty((T, half), dtype=torch.bfloat16, device=dev)
         self.cw = torch.empty((K, K), dtype=torch.bfloat16, device=dev)
+        self.cgelu = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+        for name in ("h", "dh"):
+            o = {"q": torch.empty((T, N), dtype=torch.uint8, device=dev),
+                 "p": torch.empty((N // 128, T), dtype=torch.int32, device=dev),
+                 "qT": torch.empty((N, T), dtype=torch.uint8, device=dev),
+                 "pT": torch.empty((T // 128, N), dtype=torch.int32, device=dev),
+                 "db": torch.empty((N,), dtype=torch.float32, device=dev),
+                 "amax": torch.empty((1,), dtype=torch.float32, device=dev)}
+            nws = mx.mxfp8_quantize_workspace_bytes(T, N, ROW | COL | DB)
+            o["ws"], o["nws"] = torch.empty((nws,), dtype=torch.uint8, device=dev), nws
+            self.out[name] = o
 
     def run(self):
         T, N, K = self.T, self.N, self.K
@@ -58,12 +71,19 @@ class Chain:
                                  mx.MXFP8_GEMM_SQRELU)
         # wgrad-shaped: [K x T] x [K x T]^T, reduction over the T tokens
         mx.mxfp8_gemm_ex(x["qT"], x["pT"], x["qT"], x["pT"], self.cw, K, K, K, T, 0)
+        mx.mxfp8_gemm_ex(x["q"], x["p"], w["q"], w["p"], self.cgelu, N, T, N, K, mx.MXFP8_GEMM_GELU)
+        h, dh = self.out["h"], self.out["dh"]
+        mx.mxfp8_quantize_ex(self.c, T, N, N, ROW | COL | AMAX | PACKED | mx.MXFP8_ACT_GELU, h["q"], h["p"],
+                             h["qT"], h["pT"], None, h["amax"], None, None, None, 0)
+        mx.mxfp8_quantize_ex(self.c, T, N, N, ROW | COL | DB | PACKED | mx.MXFP8_DACT_GELU, dh["q"], dh["p"],
+                             dh["qT"], dh["pT"], dh["db"], None, None, self.c, dh["ws"], dh["nws"])
 
     def snapshot(self):
-        snap = {"c": self.c.clone(), "cg": self.cg.clone(), "cw": self.cw.clone()}
+        snap = {"c": self.c.clone(), "cg": self.cg.clone(), "cw": self.cw.clone(), "cgelu": self.cgelu.clone()}
         for name, o in self.out.items():
             for k in ("q", "p", "qT", "pT", "db", "amax"):
-                snap[name + "." + k] = o[k].clone()
+                if not (name == "h" and k == "db") and not (name == "dh" and k == "amax"):
+                    snap[name + "." + k] = o[k].clone()
         return snap
 
 
@@ -133,7 +153,7 @@ def test_graph_replay_matches_eager():
                 o[k].fill_(-1)
             o["db"].fill_(-3.0)
             o["amax"].fill_(-7.0)
-        for t in (ch.c, ch.cg, ch.cw):
+        for t in (ch.c, ch.cg, ch.cw, ch.cgelu):
             t.fill_(float("nan"))
         torch.cuda.synchronize()
         log("replay %d" % rep)
