@@ -713,9 +713,11 @@ bool quantize_grids_fit(int64_t R, int64_t C, int64_t ldx, uint32_t flags) {
 
 // Tile configuration per copy set (measured on MI355X with the stress,
 // backward and columnwise-only shapes): 8 waves when the rowwise copy is
-// written, 4 for the columnwise copy alone.  Codes are written with cached
-// stores: non-temporal ones made the quantize launch alone slightly faster,
-// but cached codes make the GEMM that reads them next faster by more.
+// written, 4 for the columnwise copy alone (4-wave row + col tiles were 1-5 %
+// faster on 60-240 MB tensors, where the last round of 8-wave tiles is
+// partly empty, but 7 % slower on 1 GB and 3 % slower with dbias).  Inputs
+// are read and row codes written non-temporally; the transposed codes, which
+// a later wgrad reads, are written cached.
 template <bool ROW, bool COL, bool DBIAS, int ACT>
 static hipError_t launch_tiles(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q_row,
                                uint8_t* s_row, uint8_t* q_colT, uint8_t* s_colT, float* dbias_part,
