@@ -505,6 +505,22 @@ def test_full_dense_linear():
 
 
 @pytest.mark.slow
+def test_full_dense_linear_gelu_epilogue():
+    """The dense linear GEMM 8192x14336x4096 with the GELU epilogue (an MLP's
+    first projection written as GELU(X W^T)) on every entry, rms over the
+    whole output."""
+    d = workloads.dense_linear()
+    qa, _, pa = quantize_on_gpu(d["X"])
+    qb, _, pb = quantize_on_gpu(d["W"])
+    log("gelu epilogue 8192x14336x4096 (every entry)")
+    c = gemm_gpu(qa, pa, qb, pb, flags=mx.MXFP8_GEMM_GELU)
+    ref = oracle.gemm_tn(*oracle.quantize_rowwise(d["X"]), *oracle.quantize_rowwise(d["W"]), panel=PANEL)
+    rms = whole_output_rms(ref, panel=PANEL)
+    for r0 in range(0, ref.shape[0], PANEL):
+        gelu_tolerance_check(c[r0:r0 + PANEL], ref[r0:r0 + PANEL], 4096, label="gelu epilogue", rms=rms)
+
+
+@pytest.mark.slow
 def test_full_dense_square():
     d = workloads.dense_square()
     qa, _, pa = quantize_on_gpu(d["A"])
