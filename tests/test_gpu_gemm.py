@@ -180,12 +180,21 @@ def test_largest_k():
     gemm_tolerance_check(c[np.ix_(rows, cols)], ref, K, label="K=2^22")
 
 
-def test_k_zero_writes_zeros():
+@pytest.mark.parametrize("flags", [0, mx.MXFP8_GEMM_SQRELU, mx.MXFP8_GEMM_GELU])
+def test_k_zero_writes_zeros(flags):
+    """K = 0: the product is 0, and so are relu(0)^2 and GELU(0); the dense
+    and the grouped entry points write +0 everywhere they own."""
     torch = need_gpu()
     c = torch.full((64, 96), 3.0, dtype=torch.bfloat16, device="cuda")
-    mx.mxfp8_gemm(None, None, None, None, c, 96, 64, 96, 0)
+    mx.mxfp8_gemm_ex(None, None, None, None, c, 96, 64, 96, 0, flags)
     torch.cuda.synchronize()
-    assert torch.all(c == 0).item()
+    assert torch.all(c.view(torch.int16) == 0).item()
+    g = torch.full((64, 96), 3.0, dtype=torch.bfloat16, device="cuda")
+    off = to_dev(np.array([0, 20, 20, 50], dtype=np.int32))
+    mx.mxfp8_grouped_gemm_ex(None, None, None, None, off, 3, g, 96, 64, 96, 0, flags)
+    torch.cuda.synchronize()
+    gh = to_host(g)
+    assert np.all(gh[:50] == 0) and np.all(bf16_to_f64(gh[50:]) == 3.0)
 
 
 # ------------------------------------------------ accumulate (beta = 1)
