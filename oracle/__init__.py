@@ -273,6 +273,33 @@ def gelu_epilogue(r: np.ndarray) -> np.ndarray:
     return gelu_f64(r)
 
 
+# SwiGLU (the block-scale matmul and MoE grouped block-scale matmul forward
+# with a SwiGLU epilogue that "frost(gemm): Add Rubin kernel pipelines" lists
+# among its tests and benchmarks).  The pages give no formula or layout; the
+# reading is the standard gated form SwiGLU = SiLU(gate) * up with
+# SiLU(z) = z sigma(z) = z / (1 + exp(-z)), the GEMM's B holding the gate
+# projection in its first N rows and the up projection in the next N
+# (grouped: per expert), so C[m][n] = SiLU(R[m][n]) * R[m][N + n] for the
+# fp64 product R = A B^T over the 2N rows.
+
+def silu_f64(z) -> np.ndarray:
+    """SiLU(z) = z / (1 + exp(-z)) in float64 (exp overflow for z < -709
+    gives z / inf = -0, the correctly rounded value)."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu_epilogue(r: np.ndarray) -> np.ndarray:
+    """SwiGLU of a GEMM result over 2N columns [gate | up] -> [.., N]."""
+    r = np.asarray(r, dtype=np.float64)
+    n2 = r.shape[-1]
+    if n2 % 2:
+        raise ValueError("SwiGLU needs an even number of product columns")
+    n = n2 // 2
+    return silu_f64(r[..., :n]) * r[..., n:]
+
+
 def _check_f32(v: np.ndarray) -> np.ndarray:
     v = np.ascontiguousarray(v, dtype=np.float32)
     if v.ndim != 2 or v.shape[1] % MX_BLOCK:

@@ -693,6 +693,43 @@ def test_gelu_derivative_terms():
     assert np.array_equal(oracle.act_gelu(ab), oracle.gelu_f64(oracle.bf16_value(ab)))
 
 
+def test_silu_matches_torch_and_closed_forms():
+    """SiLU(z) = z sigma(z) against torch's float64 silu, the tabulated
+    logistic value sigma(1) = 0.7310585786300049, the identity
+    SiLU(z) - SiLU(-z) = z (sigma(z) + sigma(-z) = 1), the negative tail
+    SiLU(z) ~ z e^z, and no NaN at the overflow ends."""
+    import torch
+    rng = np.random.default_rng(64)
+    z = np.concatenate([rng.standard_normal(4000) * 4.0, np.linspace(-30, 30, 601)])
+    want = torch.nn.functional.silu(torch.from_numpy(z)).numpy()
+    assert np.all(np.abs(oracle.silu_f64(z) - want) <= 1e-15 * np.abs(want) + 1e-300)
+    assert abs(oracle.silu_f64(1.0) - 0.7310585786300049) <= 1e-16
+    assert oracle.silu_f64(0.0) == 0.0
+    y = rng.standard_normal(2000) * 20.0
+    assert np.all(np.abs(oracle.silu_f64(y) - oracle.silu_f64(-y) - y) <= 4 * np.spacing(np.abs(y)))
+    t = np.array([-40.0, -60.0, -100.0])
+    assert np.all(np.abs(oracle.silu_f64(t) / (t * np.exp(t)) - 1.0) <= 1e-15 + np.exp(t))
+    big = oracle.silu_f64(np.array([-1e300, -800.0, 800.0, 1e300]))
+    assert np.all(np.isfinite(big)) and big[0] == 0.0 and big[1] == 0.0 and big[2] == 800.0 and big[3] == 1e300
+
+
+def test_swiglu_epilogue_pairs_gate_and_up_columns():
+    """C[m][n] = SiLU(R[m][n]) * R[m][N + n]: checked on a hand example
+    (SiLU(0) = 0, SiLU(1) = sigma(1), up = 0) and against torch's float64 silu
+    on the two halves of a random product, including the grouped shape."""
+    import torch
+    r = np.array([[0.0, 1.0, 2.0, 5.0, -3.0, 0.0]])
+    got = oracle.swiglu_epilogue(r)
+    assert got.shape == (1, 3)
+    assert got[0, 0] == 0.0 and abs(got[0, 1] - (-3.0 * 0.7310585786300049)) <= 1e-15 and got[0, 2] == 0.0
+    rng = np.random.default_rng(65)
+    r = rng.standard_normal((3, 7, 64)) * 6.0
+    want = (torch.nn.functional.silu(torch.from_numpy(r[..., :32])) * torch.from_numpy(r[..., 32:])).numpy()
+    assert np.allclose(oracle.swiglu_epilogue(r), want, rtol=1e-15, atol=0)
+    with pytest.raises(ValueError):
+        oracle.swiglu_epilogue(np.zeros((2, 5)))
+
+
 def test_scale_bytes_array_matches_the_scalar_rule():
     rng = np.random.default_rng(63)
     a = np.abs(rng.standard_normal(3000)) * np.exp2(rng.integers(-140, 130, size=3000))
