@@ -285,21 +285,32 @@ mxfp8_status mxfp8_gemm(const uint8_t *a, const uint32_t *a_packed,
                                     FlyDSL review asks for ("Experimental FlyDSL GEMM
                                     backend for TE PyTorch (BF16/FP16/FP32/FP8/MXFP8)",
                                     review of the gelu / grad arguments) */
+#define MXFP8_GEMM_SWIGLU 8u     /* C[m][n] = bf16_rne( SiLU(g) * u ), g = the fp32 sum
+                                    over B row n, u = over B row N + n, SiLU(z) =
+                                    z / (1 + exp(-z)) in fp32: B holds 2N rows (the
+                                    gate projection, then the up projection; per
+                                    expert for the grouped GEMM), N is the output
+                                    width.  The block-scale matmul and MoE grouped
+                                    forward with a SwiGLU epilogue of "frost(gemm):
+                                    Add Rubin kernel pipelines" (its test and
+                                    benchmark list) */
 
 /*
  * mxfp8_gemm with options.  Defining passage: the accumulate option that the
  * FlyDSL backend still rejects (wgrad accumulation into an existing gradient,
  * "Experimental FlyDSL GEMM backend for TE PyTorch (BF16/FP16/FP32/FP8/MXFP8)",
  * review of the epilogue validation and of the fallback exceptions).
- * flags   0, MXFP8_GEMM_ACCUMULATE, MXFP8_GEMM_SQRELU or MXFP8_GEMM_GELU.
- *         With ACCUMULATE, C
+ * flags   0, MXFP8_GEMM_ACCUMULATE, MXFP8_GEMM_SQRELU, MXFP8_GEMM_GELU or
+ *         MXFP8_GEMM_SWIGLU.  With ACCUMULATE, C
  *         is read and the sum is rounded once (fp32 accumulator + the old BF16
  *         value, then BF16 round-to-nearest-even); K == 0 leaves C unchanged.
  *         With SQRELU the fp32 accumulator goes through relu(v)^2 before the
  *         BF16 rounding (the FC1 "squared_relu" epilogue of "gemm(cutedsl):
  *         add standalone Lightning W4A16 grouped GEMM - #811", section "API
  *         and compatibility impact"); K == 0 writes zeros.  GELU likewise
- *         (GELU(0) = 0).
+ *         (GELU(0) = 0).  With SWIGLU, b is [2N][K] and b_packed
+ *         [K/128][2N] (rows 0..N-1 the gate, N..2N-1 the up projection), C
+ *         is [M][N]; K == 0 writes zeros; N > 2^27 -> LIMIT.
  * Other arguments and errors as mxfp8_gemm; unknown flag bits or two flags
  * -> FLAGS.
  * mxfp8_gemm(...) is mxfp8_gemm_ex(..., 0, stream).
@@ -352,7 +363,10 @@ mxfp8_status mxfp8_grouped_gemm(const uint8_t *a, const uint32_t *a_packed,
                                 int64_t M_total, int64_t N, int64_t K, void *stream);
 
 /* mxfp8_grouped_gemm with options (flags as mxfp8_gemm_ex; rows outside every
- * group are neither read nor written). */
+ * group are neither read nor written).  With MXFP8_GEMM_SWIGLU each expert
+ * holds 2N rows: b is [G][2N][K], b_packed [K/128][G*2N] (expert g, row r is
+ * packed row 2gN + r), the gate projection in rows 0..N-1 of an expert and
+ * the up projection in rows N..2N-1; C is [M_total][N]. */
 mxfp8_status mxfp8_grouped_gemm_ex(const uint8_t *a, const uint32_t *a_packed,
                                    const uint8_t *b, const uint32_t *b_packed,
                                    const int32_t *offsets, int32_t G,

@@ -31,6 +31,7 @@ MXFP8_DACT_GELU = 256
 MXFP8_GEMM_ACCUMULATE = 1
 MXFP8_GEMM_SQRELU = 2
 MXFP8_GEMM_GELU = 4
+MXFP8_GEMM_SWIGLU = 8
 MXFP8_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 STATUS_NAMES = {0: "MXFP8_OK", 1: "MXFP8_ERR_NULL", 2: "MXFP8_ERR_SHAPE", 3: "MXFP8_ERR_MISALIGNED",
@@ -279,60 +280,69 @@ def pack_scales(s, stream=None):
     return out
 
 
-def _gemm_flags(accumulate, sqrelu, gelu):
-    if accumulate + sqrelu + gelu > 1:
-        raise ValueError("accumulate, sqrelu and gelu exclude each other")
+def _gemm_flags(accumulate, sqrelu, gelu, swiglu=False):
+    if accumulate + sqrelu + gelu + swiglu > 1:
+        raise ValueError("accumulate, sqrelu, gelu and swiglu exclude each other")
     return ((MXFP8_GEMM_ACCUMULATE if accumulate else 0) | (MXFP8_GEMM_SQRELU if sqrelu else 0)
-            | (MXFP8_GEMM_GELU if gelu else 0))
+            | (MXFP8_GEMM_GELU if gelu else 0) | (MXFP8_GEMM_SWIGLU if swiglu else 0))
 
 
-def gemm(a, a_packed, b, b_packed, out=None, accumulate=False, sqrelu=False, gelu=False, stream=None):
+def gemm(a, a_packed, b, b_packed, out=None, accumulate=False, sqrelu=False, gelu=False, swiglu=False,
+         stream=None):
     """C = dq(A) dq(B)^T in BF16 for E4M3 codes a [M, K], b [N, K]; with
     accumulate=True the product is added to `out` (beta = 1); with
     sqrelu=True C = relu(product)^2, with gelu=True C = GELU(product)
-    (formed in fp32, rounded once)."""
+    (formed in fp32, rounded once).  swiglu=True: b is [2N, K] (gate rows,
+    then up rows) and C [M, N] = SiLU(gate product) * up product."""
     import torch
     if not isinstance(a, torch.Tensor) or a.dim() != 2 or not isinstance(b, torch.Tensor) or b.dim() != 2:
         raise ValueError("a and b must be 2-D tensors of E4M3 codes")
     M, K = a.shape
-    N = b.shape[0]
+    NB = b.shape[0]
+    if swiglu and NB % 2:
+        raise ValueError("swiglu=True needs b with an even number of rows (gate rows, then up rows)")
+    N = NB // 2 if swiglu else NB
     dev = a.device
     _require(a, "a", torch.uint8)
-    _require(b, "b", torch.uint8, (N, K), dev)
+    _require(b, "b", torch.uint8, (NB, K), dev)
     _require(a_packed, "a_packed", torch.int32, (K // 128, M), dev)
-    _require(b_packed, "b_packed", torch.int32, (K // 128, N), dev)
+    _require(b_packed, "b_packed", torch.int32, (K // 128, NB), dev)
     if accumulate and out is None:
         raise ValueError("accumulate=True needs out")
     c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     if c.dtype != torch.bfloat16 or tuple(c.shape) != (M, N) or c.stride(1) != 1 or c.device != dev:
         raise ValueError("out must be a BF16 [M, N] tensor with unit column stride on the operands' device")
-    flags = _gemm_flags(accumulate, sqrelu, gelu)
+    flags = _gemm_flags(accumulate, sqrelu, gelu, swiglu)
     with torch.cuda.device(dev):
         mxfp8_gemm_ex(a, a_packed, b, b_packed, c, c.stride(0), M, N, K, flags, stream)
     return c
 
 
 def grouped_gemm(a, a_packed, b, b_packed, offsets, out=None, accumulate=False, sqrelu=False, gelu=False,
-                 stream=None):
+                 swiglu=False, stream=None):
     """Ragged grouped GEMM; b is [G, N, K]; rows outside every group keep `out`'s values;
-    sqrelu=True writes relu(product)^2 (an MoE block's first projection), gelu=True GELU(product)."""
+    sqrelu=True writes relu(product)^2 (an MoE block's first projection), gelu=True GELU(product);
+    swiglu=True: b is [G, 2N, K] (per expert gate rows, then up rows), C [M, N] = SiLU(gate) * up."""
     import torch
     if not isinstance(a, torch.Tensor) or a.dim() != 2 or not isinstance(b, torch.Tensor) or b.dim() != 3:
         raise ValueError("a must be 2-D [M, K] and b 3-D [G, N, K] tensors of E4M3 codes")
     M, K = a.shape
-    G, N, _ = b.shape
+    G, NB, _ = b.shape
+    if swiglu and NB % 2:
+        raise ValueError("swiglu=True needs experts with an even number of rows (gate rows, then up rows)")
+    N = NB // 2 if swiglu else NB
     dev = a.device
     _require(a, "a", torch.uint8)
-    _require(b, "b", torch.uint8, (G, N, K), dev)
+    _require(b, "b", torch.uint8, (G, NB, K), dev)
     _require(a_packed, "a_packed", torch.int32, (K // 128, M), dev)
-    _require(b_packed, "b_packed", torch.int32, (K // 128, G * N), dev)
+    _require(b_packed, "b_packed", torch.int32, (K // 128, G * NB), dev)
     _require(offsets, "offsets", torch.int32, (G + 1,), dev)
     if accumulate and out is None:
         raise ValueError("accumulate=True needs out")
     c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     if c.dtype != torch.bfloat16 or tuple(c.shape) != (M, N) or c.stride(1) != 1 or c.device != dev:
         raise ValueError("out must be a BF16 [M, N] tensor with unit column stride on the operands' device")
-    flags = _gemm_flags(accumulate, sqrelu, gelu)
+    flags = _gemm_flags(accumulate, sqrelu, gelu, swiglu)
     with torch.cuda.device(dev):
         mxfp8_grouped_gemm_ex(a, a_packed, b, b_packed, offsets, G, c, c.stride(0), M, N, K, flags, stream)
     return c

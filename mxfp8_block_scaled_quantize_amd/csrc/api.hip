@@ -82,14 +82,16 @@ mxfp8_status check_gemm_common(const uint8_t* a, const uint32_t* ap, const uint8
   return MXFP8_OK;
 }
 
-// GEMM options: known bits only, at most one of accumulate / relu^2 / GELU.
+// GEMM options: known bits only, at most one of accumulate / relu^2 / GELU / SwiGLU.
 bool gemm_flags_ok(uint32_t flags) {
-  constexpr uint32_t kAll = MXFP8_GEMM_ACCUMULATE | MXFP8_GEMM_SQRELU | MXFP8_GEMM_GELU;
+  constexpr uint32_t kAll = MXFP8_GEMM_ACCUMULATE | MXFP8_GEMM_SQRELU | MXFP8_GEMM_GELU | MXFP8_GEMM_SWIGLU;
   return !(flags & ~kAll) && __builtin_popcount(flags) <= 1;
 }
 int gemm_epilogue(uint32_t flags) {
-  return (flags & MXFP8_GEMM_SQRELU) ? 1 : (flags & MXFP8_GEMM_GELU) ? 2 : 0;
+  return (flags & MXFP8_GEMM_SQRELU) ? 1 : (flags & MXFP8_GEMM_GELU) ? 2 : (flags & MXFP8_GEMM_SWIGLU) ? 3 : 0;
 }
+// SwiGLU reads 2N rows of B: their scale-word offsets (8N bytes) stay below 2^31.
+constexpr int64_t kMaxSwigluN = int64_t(1) << 27;
 
 }  // namespace
 
@@ -183,8 +185,10 @@ mxfp8_status mxfp8_gemm_ex(const uint8_t* a, const uint32_t* a_packed, const uin
   if (!gemm_flags_ok(flags)) return MXFP8_ERR_FLAGS;
   const mxfp8_status st = check_gemm_common(a, a_packed, b, b_packed, c, ldc, M, N, K);
   if (st != MXFP8_OK) return st;
+  const bool swiglu = (flags & MXFP8_GEMM_SWIGLU) != 0;
+  if (swiglu && N > kMaxSwigluN) return MXFP8_ERR_LIMIT;
   if (M == 0 || N == 0) return MXFP8_OK;
-  if (!mx::gemm_grid_fits(M, N, 0, false)) return MXFP8_ERR_LIMIT;
+  if (!mx::gemm_grid_fits(M, N, 0, false, swiglu)) return MXFP8_ERR_LIMIT;
   return hip_status(mx::launch_gemm(a, a_packed, b, b_packed, static_cast<uint16_t*>(c), ldc, M, N, K, nullptr, 0,
                                     (flags & MXFP8_GEMM_ACCUMULATE) != 0, gemm_epilogue(flags),
                                     static_cast<hipStream_t>(stream)));
@@ -202,10 +206,12 @@ mxfp8_status mxfp8_grouped_gemm_ex(const uint8_t* a, const uint32_t* a_packed, c
   if (G < 1 || G > 65536) return MXFP8_ERR_SHAPE;
   const mxfp8_status st = check_gemm_common(a, a_packed, b, b_packed, c, ldc, M_total, N, K);
   if (st != MXFP8_OK) return st;
+  const bool swiglu = (flags & MXFP8_GEMM_SWIGLU) != 0;
+  if (swiglu && N > kMaxSwigluN) return MXFP8_ERR_LIMIT;
   if (M_total == 0 || N == 0) return MXFP8_OK;
   if (!offsets) return MXFP8_ERR_NULL;
   if (!aligned(offsets, 4)) return MXFP8_ERR_MISALIGNED;
-  if (!mx::gemm_grid_fits(M_total, N, G, true)) return MXFP8_ERR_LIMIT;
+  if (!mx::gemm_grid_fits(M_total, N, G, true, swiglu)) return MXFP8_ERR_LIMIT;
   return hip_status(mx::launch_gemm(a, a_packed, b, b_packed, static_cast<uint16_t*>(c), ldc, M_total, N, K,
                                     offsets, G, (flags & MXFP8_GEMM_ACCUMULATE) != 0, gemm_epilogue(flags),
                                     static_cast<hipStream_t>(stream)));

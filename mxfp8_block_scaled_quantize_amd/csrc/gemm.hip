@@ -63,6 +63,11 @@ constexpr int C_LDS_STRIDE = 2 * BN + 16;            // BF16 output tile row in 
 // The staged output tile (256 x 528 B = 135168 B) fills the ring exactly: a
 // wider row stride needs a larger ring.
 static_assert(BM * C_LDS_STRIDE <= LDS_BYTES, "output tile must fit in the ring");
+// SwiGLU epilogue: a tile covers 128 output columns (its 256 B rows are the
+// gate and up rows of those columns), staged as 256 x 272 B.
+constexpr int SW_TN = 128;
+constexpr int SW_LDS_STRIDE = 2 * SW_TN + 16;
+static_assert(BM * SW_LDS_STRIDE <= LDS_BYTES, "SwiGLU output tile must fit in the ring");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 constexpr uint32_t RSRC_FLAGS = 0x00020000u;         // raw buffer, 32-bit data format
 
@@ -99,6 +104,10 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA targets stay scalar
   const int wm = wave >> 1, wn = wave & 1;
+  // EPI 3 (SwiGLU): B holds 2N rows, gate rows [0, N) then up rows [N, 2N)
+  // (per group when grouped); a tile covers SW_TN output columns.
+  constexpr bool SW = EPI == 3;
+  constexpr int64_t BMUL = SW ? 2 : 1;
 
   // ---- tile selection: XCD-aware remap (each XCD gets a contiguous range of
   // ids), then groups of GROUP tiles along one dimension walked across the
@@ -177,13 +186,13 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
       tm -= total;
     }
     if (found < 0) return;  // whole workgroup leaves together
-    b_row0 = (int64_t)found * N;
+    b_row0 = (int64_t)found * N * BMUL;
   } else {
     m_lo = tm * BM;
     m_hi = M;
   }
-  const int64_t n0 = tn * BN;
-  const int64_t brows = GROUPED ? (int64_t)G * N : N;
+  const int64_t n0 = tn * (SW ? SW_TN : BN);
+  const int64_t brows = (GROUPED ? (int64_t)G : 1) * N * BMUL;
   const int rows_a = (int)((m_hi - m_lo) < BM ? (m_hi - m_lo) : BM);
   const int rows_b = (int)((N - n0) < BN ? (N - n0) : BN);
 
@@ -207,7 +216,18 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
   const int sp = 64 * wave + lane;
   const int srow = (sp & ~127) + 32 * (sp & 3) + ((sp & 127) >> 2);
   const int sra = srow < rows_a ? srow : rows_a - 1;
-  const int srb = srow < rows_b ? srow : rows_b - 1;
+  // SwiGLU: slab row srow lies in 64-row segment s = srow / 64, which holds
+  // the gate (s even) or up (s odd) rows of output columns n0 + 64 (s / 2) +
+  // [0, 64); rows past N are clamped to the half's last row (their data rows
+  // read as zero, so any scale will do).
+  int srb;
+  if (SW) {
+    const int s = srow >> 6;
+    const int64_t oc = n0 + 64 * (s >> 1) + (srow & 63);
+    srb = (int)((s & 1) * N + (oc < N ? oc : N - 1));
+  } else {
+    srb = srow < rows_b ? srow : rows_b - 1;
+  }
 
   const int nk = (int)(K / BK);
 
@@ -218,8 +238,22 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
   const uint32_t a_rec = (uint32_t)((int64_t)rows_a * K);
   const uint32_t b_rec = (uint32_t)((int64_t)rows_b * K);
   const __amdgpu_buffer_rsrc_t ra_v = __builtin_amdgcn_make_buffer_rsrc((void*)(A + m_lo * K), 0, (int)a_rec, RSRC_FLAGS);
-  const __amdgpu_buffer_rsrc_t rb_v =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(B + (b_row0 + n0) * K), 0, (int)b_rec, RSRC_FLAGS);
+  // B: the plain tile is rows b_row0 + n0 + [0, 256).  SwiGLU: wave w DMAs
+  // slab rows 64w + [0, 64) (segment w: gate rows for even w, up rows for odd
+  // w, of output columns n0 + 64 (w / 2) + [0, 64)); its resource starts 64w
+  // rows before that segment's first B row, so the shared row offsets (which
+  // include 64w rows) land on it, and ends after the segment's valid rows.
+  // Every access is at or after the segment's first row.
+  __amdgpu_buffer_rsrc_t rb_v;
+  if (SW) {
+    const int64_t oc0 = n0 + 64 * (wave >> 1);
+    const int64_t seg_rows = N - oc0 < 0 ? 0 : (N - oc0 < 64 ? N - oc0 : 64);
+    const int64_t src = b_row0 + (wave & 1) * N + oc0;
+    rb_v = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((uintptr_t)B + (uintptr_t)((src - 64 * wave) * K)), 0, (int)((64 * wave + seg_rows) * K), RSRC_FLAGS);
+  } else {
+    rb_v = __builtin_amdgcn_make_buffer_rsrc((void*)(B + (b_row0 + n0) * K), 0, (int)b_rec, RSRC_FLAGS);
+  }
   const __amdgpu_buffer_rsrc_t r_none = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, 0, RSRC_FLAGS);
   // DMA piece q of step s into SLOT: 0..7 A rows, 8..15 B rows, 16/17 the
   // scale words of A / B.  A step past the end gets zero-length buffer ranges.
@@ -241,8 +275,11 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(base + SA_OFF + 256 * wave), 4, 4u * (uint32_t)sra, 0,
                                                0, 0);
     } else {
-      const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(Bp + sv * brows + b_row0 + n0), 0, valid ? rows_b * 4 : 0, RSRC_FLAGS);
+      const __amdgpu_buffer_rsrc_t rsb =
+          SW ? __builtin_amdgcn_make_buffer_rsrc((void*)(Bp + sv * brows + b_row0), 0, valid ? (int)(8 * N) : 0,
+                                                 RSRC_FLAGS)
+             : __builtin_amdgcn_make_buffer_rsrc((void*)(Bp + sv * brows + b_row0 + n0), 0, valid ? rows_b * 4 : 0,
+                                                 RSRC_FLAGS);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(base + SB_OFF + 256 * wave), 4, 4u * (uint32_t)srb, 0,
                                                0, 0);
     }
@@ -385,10 +422,53 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
   // Lane-derived values are re-derived from the lane id here so that none of
   // them stays live (or spills) across the main loop.
   const int elane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const bool full_rows = m_lo + BM <= m_hi;
+  if constexpr (SW) {
+    // SwiGLU: blocks j = 0, 1 of a wave hold the gate and blocks j + 2 the up
+    // products of the same 64 output columns wn * 64 + [0, 64), so each output
+    // is SiLU(gate) * up of two registers of the lane, in fp32, rounded once.
+    {
+      const int lr = elane & 31, lg = elane >> 5;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int row = wm * 128 + 32 * i + lr;
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+          for (int g = 0; g < 4; g++) {
+            const int col = wn * 64 + 32 * j + 8 * g + 4 * lg;
+            float v[4];
+#pragma unroll
+            for (int t = 0; t < 4; t++) v[t] = silu_f32(acc[i][j][4 * g + t]) * acc[i][j + 2][4 * g + t];
+            const bf16x2 h0 = {(__bf16)v[0], (__bf16)v[1]};
+            const bf16x2 h1 = {(__bf16)v[2], (__bf16)v[3]};
+            *(__attribute__((address_space(3))) u32x2*)(smem + row * SW_LDS_STRIDE + 2 * col) =
+                u32x2{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1)};
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    wait_lgkm0();
+    lds_barrier();
+    // 16 chunks of 16 bytes per 256-byte output row: 16 rows per pass
+    const int ech = elane & 15;
+    const int erow0 = 4 * wave + (elane >> 4);
+    const int64_t ecol = n0 + 8 * ech;
+    if (ecol < N) {
+      u32x4 v[16];
+#pragma unroll
+      for (int k = 0; k < 16; k++) v[k] = *(lds_u32x4*)(smem + (erow0 + 16 * k) * SW_LDS_STRIDE + 16 * ech);
+#pragma unroll
+      for (int k = 0; k < 16; k++) {
+        const int64_t grow = m_lo + erow0 + 16 * k;
+        if (full_rows || grow < m_hi) store_nt16(Cm + grow * ldc + ecol, make_uint4(v[k].x, v[k].y, v[k].z, v[k].w));
+      }
+    }
+    return;
+  }
   const int ech = elane & 31;                    // 16-byte chunk of a tile row
   const int erow0 = 2 * wave + (elane >> 5);     // rows erow0 + 8 k
   const int64_t ecol = n0 + 8 * ech;
-  const bool full_rows = m_lo + BM <= m_hi;
   if (ACC) {
     // all 32 loads of a thread are issued before the first LDS write, so the
     // tile costs one memory latency (rows / columns outside C read as 0)
@@ -468,8 +548,8 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
   }
 }
 
-bool gemm_grid_fits(int64_t M, int64_t N, int32_t G, bool grouped) {
-  const int64_t tn = (N + BN - 1) / BN;
+bool gemm_grid_fits(int64_t M, int64_t N, int32_t G, bool grouped, bool swiglu) {
+  const int64_t tn = swiglu ? (N + SW_TN - 1) / SW_TN : (N + BN - 1) / BN;
   const int64_t tm = (M + BM - 1) / BM + (grouped ? (int64_t)G : 0);
   return grid_fits(tm, tn, 256);
 }
@@ -501,7 +581,7 @@ hipError_t launch_gemm(const uint8_t* a, const uint32_t* ap, const uint8_t* b, c
                        uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
                        const int32_t* offsets, int32_t G, bool accumulate, int epilogue, hipStream_t stream) {
   const bool grouped = offsets != nullptr;
-  const int64_t tiles_n = (N + BN - 1) / BN;
+  const int64_t tiles_n = epilogue == 3 ? (N + SW_TN - 1) / SW_TN : (N + BN - 1) / BN;
   const int64_t tiles_m = (M + BM - 1) / BM + (grouped ? (int64_t)G : 0);
   if (tiles_m * tiles_n == 0) return hipSuccess;
 #define MX_G_LAUNCH(GR, AC, EP) \
@@ -511,10 +591,12 @@ hipError_t launch_gemm(const uint8_t* a, const uint32_t* ap, const uint8_t* b, c
     return accumulate ? MX_G_LAUNCH(true, true, 0)
                       : epilogue == 1 ? MX_G_LAUNCH(true, false, 1)
                       : epilogue == 2 ? MX_G_LAUNCH(true, false, 2)
+                      : epilogue == 3 ? MX_G_LAUNCH(true, false, 3)
                                       : MX_G_LAUNCH(true, false, 0);
   return accumulate ? MX_G_LAUNCH(false, true, 0)
                     : epilogue == 1 ? MX_G_LAUNCH(false, false, 1)
                     : epilogue == 2 ? MX_G_LAUNCH(false, false, 2)
+                    : epilogue == 3 ? MX_G_LAUNCH(false, false, 3)
                                     : MX_G_LAUNCH(false, false, 0);
 #undef MX_G_LAUNCH
 }

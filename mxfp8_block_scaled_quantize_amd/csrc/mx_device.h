@@ -137,6 +137,13 @@ __device__ __forceinline__ float dgelu_f32(float a) {
   return fmaf(a * 0.39894228040143268f, e, a < 0.0f ? p : 1.0f - p);
 }
 
+// SiLU(z) = z sigma(z) = z / (1 + exp(-z)) in fp32: one v_exp_f32 and one
+// v_rcp_f32.  exp(-z) overflows to +inf below z = -88.7, where the result is
+// -0 (the exact value is below fp32's normal range there).
+__device__ __forceinline__ float silu_f32(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.44269504088896341f));
+}
+
 // Cross-lane max inside a quad of lanes via DPP quad permutes.
 __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
   uint32_t t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // lane ^ 1

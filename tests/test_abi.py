@@ -45,7 +45,7 @@ def test_header_constants_match_the_binding():
     import re
     text = open(HEADER).read()
     flags = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (MXFP8_[A-Z_]+) (\d+)u", text)}
-    assert len(flags) == 13, flags
+    assert len(flags) == 14, flags
     for name, value in flags.items():
         assert getattr(mx, name) == value, name
     binding = {n for n in dir(mx) if re.fullmatch(r"MXFP8_[A-Z_]+", n) and isinstance(getattr(mx, n), int)}
@@ -217,8 +217,13 @@ def test_grouped_gemm_validation(L):
 
 def test_gemm_ex_flags(L):
     G = L.mxfp8_gemm_ex
-    assert G(A16, A16, A16, A16, A16, 64, 64, 64, 128, 8, None) == FLAGS
+    assert G(A16, A16, A16, A16, A16, 64, 64, 64, 128, 16, None) == FLAGS
     assert G(A16, A16, A16, A16, A16, 64, 64, 64, 128, 3, None) == FLAGS   # accumulate and relu^2 together
+    assert G(A16, A16, A16, A16, A16, 64, 64, 64, 128, 9, None) == FLAGS   # accumulate and SwiGLU
+    assert G(A16, A16, A16, A16, A16, 64, 64, 64, 128, 12, None) == FLAGS  # GELU and SwiGLU
+    assert G(A16, A16, A16, A16, A16, 64, 64, 64, 100, 8, None) == SHAPE   # SwiGLU alone passes the flag check
+    assert G(A16, A16, A16, A16, A16, (1 << 27) + 32, 64, (1 << 27) + 32, 128, 8, None) == LIMIT
+    assert G(None, None, None, None, None, 64, 0, 64, 128, 8, None) == OK
     assert G(A16, A16, A16, A16, A16, 64, 64, 64, 128, 5, None) == FLAGS   # accumulate and GELU
     assert G(A16, A16, A16, A16, A16, 64, 64, 64, 128, 6, None) == FLAGS   # two epilogues
     assert G(A16, A16, A16, A16, A16, 64, 64, 64, 100, 4, None) == SHAPE   # GELU alone passes the flag check
@@ -227,7 +232,8 @@ def test_gemm_ex_flags(L):
     assert G(A16, A16, A16, A16, A16, 64, 64, 64, 100, 1, None) == SHAPE   # the dense checks still apply
     assert G(None, None, None, None, None, 64, 0, 64, 128, 1, None) == OK
     GG = L.mxfp8_grouped_gemm_ex
-    assert GG(A16, A16, A16, A16, A16, 4, A16, 64, 64, 64, 128, 8, None) == FLAGS
+    assert GG(A16, A16, A16, A16, A16, 4, A16, 64, 64, 64, 128, 16, None) == FLAGS
+    assert GG(A16, A16, A16, A16, A16, 4, A16, (1 << 27) + 32, 64, (1 << 27) + 32, 128, 8, None) == LIMIT
     assert GG(A16, A16, A16, A16, A16, 4, A16, 64, 64, 64, 128, 3, None) == FLAGS
     assert GG(A16, A16, A16, A16, A16, 4, A16, 64, 64, 64, 128, 6, None) == FLAGS
     assert GG(A16, A16, A16, A16, None, 4, None, 64, 0, 64, 128, 4, None) == OK

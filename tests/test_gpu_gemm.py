@@ -28,7 +28,7 @@ def quantize_on_gpu(bits, colwise=False):
 def gemm_gpu(qa, pa, qb, pb, ldc=None, canary=False, flags=0):
     torch = need_gpu()
     M, K = qa.shape
-    N = qb.shape[0]
+    N = qb.shape[0] // (2 if flags & mx.MXFP8_GEMM_SWIGLU else 1)   # SwiGLU: B holds gate and up rows
     ldc = N if ldc is None else ldc
     G = 1024 if canary else 0
     full = torch.full((M * ldc + 2 * G,), -12345, dtype=torch.int16, device="cuda")
@@ -180,10 +180,10 @@ def test_largest_k():
     gemm_tolerance_check(c[np.ix_(rows, cols)], ref, K, label="K=2^22")
 
 
-@pytest.mark.parametrize("flags", [0, mx.MXFP8_GEMM_SQRELU, mx.MXFP8_GEMM_GELU])
+@pytest.mark.parametrize("flags", [0, mx.MXFP8_GEMM_SQRELU, mx.MXFP8_GEMM_GELU, mx.MXFP8_GEMM_SWIGLU])
 def test_k_zero_writes_zeros(flags):
-    """K = 0: the product is 0, and so are relu(0)^2 and GELU(0); the dense
-    and the grouped entry points write +0 everywhere they own."""
+    """K = 0: the product is 0, and so are relu(0)^2, GELU(0) and SiLU(0) * 0;
+    the dense and the grouped entry points write +0 everywhere they own."""
     torch = need_gpu()
     c = torch.full((64, 96), 3.0, dtype=torch.bfloat16, device="cuda")
     mx.mxfp8_gemm_ex(None, None, None, None, c, 96, 64, 96, 0, flags)
@@ -257,15 +257,17 @@ def test_gemm_accumulate_k_zero_keeps_c():
 
 # --------------------------------------------------------- grouped GEMM
 
-def grouped_case(M, N, K, counts, seed, canary_rows=True, accumulate=False, sqrelu=False, gelu=False):
+def grouped_case(M, N, K, counts, seed, canary_rows=True, accumulate=False, sqrelu=False, gelu=False,
+                 swiglu=False):
     torch = need_gpu()
     G = len(counts)
+    NB = 2 * N if swiglu else N   # SwiGLU: per expert N gate rows, then N up rows
     x = workloads.normal_bf16((M, K), seed)
-    w = workloads.normal_bf16((G, N, K), seed + 1, std=0.02)
+    w = workloads.normal_bf16((G, NB, K), seed + 1, std=0.02)
     off = workloads.offsets_from_counts(counts)
     qx, sx, px = quantize_on_gpu(x)
-    wq = quantize_on_gpu(w.reshape(G * N, K))
-    qw = wq[0].view(G, N, K)
+    wq = quantize_on_gpu(w.reshape(G * NB, K))
+    qw = wq[0].view(G, NB, K)
     pw = wq[2]
     c_old = workloads.normal_bf16((M, N), seed + 2, std=2.0) if accumulate else None
     if accumulate:
@@ -273,7 +275,8 @@ def grouped_case(M, N, K, counts, seed, canary_rows=True, accumulate=False, sqre
     else:
         out = torch.full((M, N), -7.0, dtype=torch.bfloat16, device="cuda")
     log("grouped M=%d N=%d K=%d counts=%s accumulate=%d" % (M, N, K, list(counts), accumulate))
-    mx.grouped_gemm(qx, px, qw, pw, to_dev(off), out=out, accumulate=accumulate, sqrelu=sqrelu, gelu=gelu)
+    mx.grouped_gemm(qx, px, qw, pw, to_dev(off), out=out, accumulate=accumulate, sqrelu=sqrelu, gelu=gelu,
+                    swiglu=swiglu)
     torch.cuda.synchronize()
     c = to_host(out)
     oqx, osx = oracle.quantize_rowwise(x)
@@ -290,6 +293,8 @@ def grouped_case(M, N, K, counts, seed, canary_rows=True, accumulate=False, sqre
         sqrelu_tolerance_check(c[rows], ref, K, label="grouped sqrelu")
     elif gelu:
         gelu_tolerance_check(c[rows], ref, K, label="grouped gelu")
+    elif swiglu:
+        swiglu_tolerance_check(c[rows], ref, K, label="grouped swiglu")
     else:
         gemm_tolerance_check(c[rows], ref, K, label="grouped")
     if canary_rows and accumulate:
@@ -416,6 +421,77 @@ def test_gemm_gelu_epilogue_on_integers():
 
 def test_grouped_gelu_epilogue():
     grouped_case(1200, 96, 256, [5, 0, 131, 257, 600], 10, gelu=True)
+
+
+def swiglu_tolerance_check(gpu_bits, r, K, label="", rms=None):
+    """SwiGLU epilogue on a product r [.., 2N] = [gate | up]: the GPU forms
+    SiLU(g) * u from fp32 sums g, u with |g - R_g| <= t_g, |u - R_u| <= t_u (the
+    GEMM bound, rms over the whole 2N-wide product); |SiLU'| <= 1.1, so
+    |SiLU(g) u - SiLU(R_g) R_u| <= 1.1 t_g (|R_u| + t_u) + |SiLU(R_g)| t_u;
+    plus the fp32 SiLU and product, (16 + 2 |g|) 2^-24 of the result, and the
+    BF16 rounding, 2^-9 (doubled for margin)."""
+    gpu = bf16_to_f64(gpu_bits)
+    r = np.asarray(r, dtype=np.float64)
+    n = r.shape[1] // 2
+    if rms is None:
+        rms = np.sqrt(np.mean(r ** 2))
+    t = 8e-3 * np.abs(r) + 1e-3 * np.sqrt(K) * rms
+    rg, ru, tg, tu = r[:, :n], r[:, n:], t[:, :n], t[:, n:]
+    want = oracle.swiglu_epilogue(r)
+    m = (np.abs(oracle.silu_f64(rg)) + 1.1 * tg) * (np.abs(ru) + tu)
+    tol = 1.1 * tg * (np.abs(ru) + tu) + np.abs(oracle.silu_f64(rg)) * tu + 2.0 ** -8 * m \
+        + (16.0 + 2.0 * (np.abs(rg) + tg)) * 2.0 ** -24 * m
+    err = np.abs(gpu - want)
+    bad = ~(err <= tol)
+    assert not bad.any(), "%s: %d entries out of tolerance, worst %g vs %g" % (
+        label, bad.sum(), err[bad].max(), tol[bad][np.argmax(err[bad])])
+
+
+@pytest.mark.parametrize("M,N,K", [(32, 32, 128), (160, 96, 1024), (1000, 320, 256), (288, 288, 1152),
+                                   (300, 160, 640), (513, 384, 384)])
+def test_gemm_swiglu_epilogue(M, N, K):
+    """B = [gate; up] with 2N rows, C [M, N]; N not a multiple of 128 leaves
+    a partial 64-row segment (and empty ones) in the last tile."""
+    a = workloads.normal_bf16((M, K), 13 * M + K)
+    b = workloads.normal_bf16((2 * N, K), 17 * N + K, std=0.5)
+    qa, sa, pa = quantize_on_gpu(a)
+    qb, sb, pb = quantize_on_gpu(b)
+    log("swiglu epilogue M=%d N=%d K=%d" % (M, N, K))
+    c = gemm_gpu(qa, pa, qb, pb, ldc=N + 24, canary=True, flags=mx.MXFP8_GEMM_SWIGLU)
+    oqa, osa = oracle.quantize_rowwise(a)
+    oqb, osb = oracle.quantize_rowwise(b)
+    swiglu_tolerance_check(c, oracle.gemm_tn(oqa, osa, oqb, osb), K, "swiglu")
+
+
+def test_gemm_swiglu_epilogue_on_integers():
+    """Integer operands: the fp32 sums are exact, so the output is the BF16
+    rounding of the fp32 SiLU(R_g) R_u: between the BF16 roundings of the
+    exact value -+ its fp32 error bound (16 + 2 |R_g|) 2^-24 of it, which
+    coincide except on BF16 rounding ties.  Gate and up rows differ, so a swapped pair
+    or a gate paired with the wrong up column fails."""
+    rng = np.random.default_rng(15)
+    A = rng.integers(-1, 2, size=(160, 128))
+    B = rng.integers(-1, 2, size=(192, 128))     # N = 96: gate rows 0..95, up rows 96..191
+    ab = (A.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    bb = (B.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    qa, sa, pa = quantize_on_gpu(ab)
+    qb, sb, pb = quantize_on_gpu(bb)
+    log("swiglu integers")
+    c = bf16_to_f64(gemm_gpu(qa, pa, qb, pb, canary=True, flags=mx.MXFP8_GEMM_SWIGLU))
+    R = (A @ B.T).astype(np.float64)
+    v = oracle.swiglu_epilogue(R)
+    e = (16.0 + 2.0 * np.abs(R[:, :96])) * 2.0 ** -24 * np.abs(v)
+    lo = bf16_to_f64(workloads.f32_to_bf16_bits((v - e).astype(np.float32)))
+    hi = bf16_to_f64(workloads.f32_to_bf16_bits((v + e).astype(np.float32)))
+    ok = (c >= lo) & (c <= hi)
+    assert ok.all(), "%d of %d outside the rounding bracket" % ((~ok).sum(), ok.size)
+    # open: integer products on a BF16 tie (SiLU(g) = g to fp32 precision for large g)
+    assert (lo == hi).mean() > 0.9
+
+
+def test_grouped_swiglu_epilogue():
+    grouped_case(1200, 96, 256, [5, 0, 131, 257, 600], 11, swiglu=True)
+    grouped_case(700, 160, 384, [300, 0, 64, 336], 12, swiglu=True)
 
 
 def test_grouped_uniform_counts():
