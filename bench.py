@@ -17,11 +17,11 @@ row+col, 1.09 GB) against the HBM peak; ``cpu_baseline`` is the CPU oracle
 running whole steps of the same workload on the host.  Per-launch times are
 reported as mean, median, min and max over the timed steps.
 
-``--workload dense|backward|moe|moe_sqrelu|linear|mlp|mlp_gelu`` measures the other
+``--workload dense|backward|moe|moe_sqrelu|moe_swiglu|linear|mlp|mlp_gelu`` measures the other
 workloads the same way: rowwise quantize and the TN GEMMs 8192x14336x4096 and
 8192^3; row+col+dbias quantize and the wgrad GEMM on the columnwise copies;
-the ragged grouped MoE GEMM (also with the squared-ReLU epilogue of an MoE
-first projection); one MXFP8 linear-layer training step (fprop, dgrad, wgrad
+the ragged grouped MoE GEMM (also with the squared-ReLU or the SwiGLU
+epilogue of an MoE first projection); one MXFP8 linear-layer training step (fprop, dgrad, wgrad
 accumulated into a BF16 main gradient); one squared-ReLU (or GELU) MLP
 training step (six GEMMs, the activation and its backward fused into the
 quantize launches).  They are reporting aids next to the default line.
@@ -47,7 +47,8 @@ def parse():
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="stress",
-                   choices=["stress", "dense", "backward", "moe", "moe_sqrelu", "linear", "mlp", "mlp_gelu"])
+                   choices=["stress", "dense", "backward", "moe", "moe_sqrelu", "moe_swiglu", "linear", "mlp",
+                            "mlp_gelu"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU-oracle time: whole oracle steps are repeated until reached "
@@ -247,6 +248,26 @@ def build_ops(workload, dev):
                 "W2 N(0,0.02), dY N(0,1); row+col quantize of X, W1, W2, dY; FC1 GEMM; the activation fused into "
                 "the quantize of its BF16 output; FC2 GEMM; FC2 dgrad and wgrad; the activation's backward fused "
                 "into the row+col+dbias quantize of FC2's dgrad output; FC1 dgrad and wgrad" % (fname, T, D, F))
+    elif workload == "moe_swiglu":
+        d = workloads.moe()
+        host = d
+        G, NB, K = d["W"].shape
+        N = NB // 2
+        Mt = d["X"].shape[0]
+        bx = quantize_op("X[%dx%d]" % (Mt, K), d["X"], ROW, packed=True)
+        bw = quantize_op("W[%dx%dx%d]" % (G, NB, K), d["W"].reshape(G * NB, K), ROW, packed=True)
+        off = torch.from_numpy(d["offsets"]).to(dev)
+        c = torch.empty((Mt, N), dtype=torch.bfloat16, device=dev)
+        keep.extend([c, off])
+        tokens = int(d["offsets"][-1] - d["offsets"][0])
+        dominant = "grouped swiglu %dx%dx%d G=%d" % (Mt, NB, K, G)
+        ops.append(Op("gemm", dominant, lambda st: mx.mxfp8_grouped_gemm_ex(
+            bx["q"], bx["p"], bw["q"], bw["p"], off, G, c, N, Mt, N, K, mx.MXFP8_GEMM_SWIGLU, stream=st),
+            2.0 * tokens * NB * K))
+        desc = ("MoE first projection with the SwiGLU epilogue: X[%dx%d] and W[%d][%dx%d] (per expert %d gate rows, "
+                "then %d up rows) rowwise into packed scales, ragged grouped GEMM over %d experts (token counts %s) "
+                "writing SiLU(X W_gate^T) * (X W_up^T) [%dx%d]"
+                % (Mt, K, G, NB, K, N, N, G, np.diff(d["offsets"]).tolist(), Mt, N))
     elif workload == "moe_sqrelu":
         d = workloads.moe()
         host = d
@@ -509,7 +530,7 @@ def oracle_step(workload, h):
             oracle.gemm_tn(qdT, sdT, qxT, sxT, panel=P)
         return step, ("rowwise + columnwise quantize and dbias of dY[16384x4096], columnwise X, scale packing, "
                       "fp64 wgrad 4096x4096x16384")
-    if workload in ("moe", "moe_sqrelu"):
+    if workload in ("moe", "moe_sqrelu", "moe_swiglu"):
         def step():
             qx, sx = rowp(h["X"])
             ws = [rowp(w) for w in h["W"]]
@@ -517,8 +538,11 @@ def oracle_step(workload, h):
                                        h["offsets"], panel=P)
             if workload == "moe_sqrelu":
                 oracle.sqrelu_epilogue(c)
+            if workload == "moe_swiglu":
+                oracle.swiglu_epilogue(c)
+        epi = {"moe": "", "moe_sqrelu": " with the relu^2 epilogue", "moe_swiglu": " with the SwiGLU epilogue"}
         return step, ("rowwise quantize of X[16384x4096] and W[8][14336x4096], scale packing, fp64 grouped "
-                      "GEMM" + (" with the relu^2 epilogue" if workload == "moe_sqrelu" else ""))
+                      "GEMM" + epi[workload])
     if workload == "linear":
         def step():
             qx, sx, qxT, sxT = both(h["X"])

@@ -708,6 +708,26 @@ def test_full_moe_sqrelu():
 
 
 @pytest.mark.slow
+def test_full_moe_swiglu():
+    """The MoE first projection with the SwiGLU epilogue at full size: X
+    [16384 x 4096], each expert's 14336 rows as 7168 gate rows then 7168 up
+    rows, C [16384 x 7168] = SiLU(X W_gate^T) * (X W_up^T) per expert; every
+    entry, rms over the whole 14336-wide product."""
+    data = workloads.moe()
+    G, NB, K = data["W"].shape
+    N = NB // 2
+    x, w, off = data["X"], data["W"], data["offsets"]
+    qx, _, px = quantize_on_gpu(x)
+    wq = quantize_on_gpu(w.reshape(G * NB, K))
+    log("full moe swiglu %dx%dx%d G=%d (every entry)" % (x.shape[0], N, K, G))
+    c = to_host(mx.grouped_gemm(qx, px, wq[0].view(G, NB, K), wq[2], to_dev(off), swiglu=True))
+    ref = _moe_refs(x, w, off)
+    rms = whole_output_rms(ref, panel=PANEL)
+    for r0 in range(0, ref.shape[0], PANEL):
+        swiglu_tolerance_check(c[r0:r0 + PANEL], ref[r0:r0 + PANEL], K, label="moe swiglu", rms=rms)
+
+
+@pytest.mark.slow
 def test_full_linear_wgrad_accumulate():
     """The linear step's wgrad with accumulation at its full size
     (14336 x 4096, K = 8192 tokens) on the transposed copies, every entry."""

@@ -15,7 +15,8 @@ import mxfp8_block_scaled_quantize_amd as mx
 import oracle
 import workloads
 from gpu_util import bf16_to_f64, gemm_tolerance_check, log, need_gpu, to_dev_bf16, to_host
-from test_gpu_gemm import gelu_tolerance_check, gemm_gpu, grouped_case, quantize_on_gpu, sqrelu_tolerance_check
+from test_gpu_gemm import (gelu_tolerance_check, gemm_gpu, grouped_case, quantize_on_gpu, sqrelu_tolerance_check,
+                           swiglu_tolerance_check)
 from test_gpu_quantize_ex import act_inputs, check_act_result, check_gelu_result, dgelu_case, gelu_case, run_ex
 
 pytestmark = pytest.mark.gpu
@@ -172,3 +173,28 @@ def test_random_grouped_gemm_gelu(case):
     if M == 0:
         pytest.skip("empty problem (covered by test_grouped_empty_total)")
     grouped_case(M, N, K, list(counts), seed, gelu=True)
+
+
+@pytest.mark.parametrize("case", gemm_cases(12, 79))
+def test_random_gemm_swiglu(case):
+    """B = [gate; up] with 2N rows, C [M, N]: random M, N (a multiple of 32,
+    often not of 128), K and ldc."""
+    M, N, K, ldc, _, seed = case
+    log("random gemm swiglu M=%d N=%d K=%d ldc=%d seed=%d" % (M, N, K, ldc, seed))
+    a = workloads.normal_bf16((M, K), seed)
+    b = workloads.normal_bf16((2 * N, K), seed + 1, std=0.25)
+    qa, sa, pa = quantize_on_gpu(a)
+    qb, sb, pb = quantize_on_gpu(b)
+    oqa, osa = oracle.quantize_rowwise(a)
+    oqb, osb = oracle.quantize_rowwise(b)
+    c = gemm_gpu(qa, pa, qb, pb, ldc=ldc, canary=True, flags=mx.MXFP8_GEMM_SWIGLU)
+    swiglu_tolerance_check(c, oracle.gemm_tn(oqa, osa, oqb, osb), K, "swiglu")
+
+
+@pytest.mark.parametrize("case", grouped_cases(8, 93))
+def test_random_grouped_gemm_swiglu(case):
+    counts, tail, N, K, _, seed = case
+    M = sum(counts) + tail
+    if M == 0:
+        pytest.skip("empty problem (covered by test_grouped_empty_total)")
+    grouped_case(M, N, K, list(counts), seed, swiglu=True)
