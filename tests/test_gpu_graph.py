@@ -22,7 +22,8 @@ class Chain:
     """Preallocated buffers of one chain: row+col+dbias+amax quantize of X and
     W into packed scales, dense GEMM X W^T, grouped GEMM of X's rows over two
     experts (W's two row halves), a dense wgrad-shaped GEMM of the transposed
-    copies, the dense GEMM again with the GELU epilogue, and GELU and its
+    copies, the dense GEMM again with the GELU epilogue and with the SwiGLU
+    epilogue (W's rows read as N/2 gate rows then N/2 up rows), and GELU and its
     backward fused into row+col quantizes of the GEMM output (the backward
     with dbias, taking that output as both gradient and activation input)."""
 
@@ -48,6 +49,7 @@ class Chain:
         self.cg = torch.empty((T, half), dtype=torch.bfloat16, device=dev)
         self.cw = torch.empty((K, K), dtype=torch.bfloat16, device=dev)
         self.cgelu = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+        self.cswi = torch.empty((T, N // 2), dtype=torch.bfloat16, device=dev)
         for name in ("h", "dh"):
             o = {"q": torch.empty((T, N), dtype=torch.uint8, device=dev),
                  "p": torch.empty((N // 128, T), dtype=torch.int32, device=dev),
@@ -72,6 +74,7 @@ class Chain:
         # wgrad-shaped: [K x T] x [K x T]^T, reduction over the T tokens
         mx.mxfp8_gemm_ex(x["qT"], x["pT"], x["qT"], x["pT"], self.cw, K, K, K, T, 0)
         mx.mxfp8_gemm_ex(x["q"], x["p"], w["q"], w["p"], self.cgelu, N, T, N, K, mx.MXFP8_GEMM_GELU)
+        mx.mxfp8_gemm_ex(x["q"], x["p"], w["q"], w["p"], self.cswi, N // 2, T, N // 2, K, mx.MXFP8_GEMM_SWIGLU)
         h, dh = self.out["h"], self.out["dh"]
         mx.mxfp8_quantize_ex(self.c, T, N, N, ROW | COL | AMAX | PACKED | mx.MXFP8_ACT_GELU, h["q"], h["p"],
                              h["qT"], h["pT"], None, h["amax"], None, None, None, 0)
@@ -79,7 +82,8 @@ class Chain:
                              dh["qT"], dh["pT"], dh["db"], None, None, self.c, dh["ws"], dh["nws"])
 
     def snapshot(self):
-        snap = {"c": self.c.clone(), "cg": self.cg.clone(), "cw": self.cw.clone(), "cgelu": self.cgelu.clone()}
+        snap = {"c": self.c.clone(), "cg": self.cg.clone(), "cw": self.cw.clone(), "cgelu": self.cgelu.clone(),
+                "cswi": self.cswi.clone()}
         for name, o in self.out.items():
             for k in ("q", "p", "qT", "pT", "db", "amax"):
                 if not (name == "h" and k == "db") and not (name == "dh" and k == "amax"):
@@ -153,7 +157,7 @@ def test_graph_replay_matches_eager():
                 o[k].fill_(-1)
             o["db"].fill_(-3.0)
             o["amax"].fill_(-7.0)
-        for t in (ch.c, ch.cg, ch.cw, ch.cgelu):
+        for t in (ch.c, ch.cg, ch.cw, ch.cgelu, ch.cswi):
             t.fill_(float("nan"))
         torch.cuda.synchronize()
         log("replay %d" % rep)
