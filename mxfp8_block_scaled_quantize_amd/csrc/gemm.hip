@@ -34,6 +34,12 @@
 // resident on one XCD (ids are dealt round-robin to the 8 XCDs) form groups of
 // 4 tiles sharing A and B in that XCD's L2, with the XCDs splitting the larger
 // of M and N.
+//
+// Epilogues (template EPI): none, relu(acc)^2, GELU(acc), each applied to the
+// fp32 sum before the one BF16 rounding; SwiGLU, where B holds gate rows then
+// up rows and a tile covers 128 output columns whose gate and up sums end in
+// the same wave (see the SwiGLU DMA and epilogue below).  Accumulate (ACC)
+// adds the old C before the rounding.
 #include <atomic>
 
 #include "mx_device.h"
