@@ -1,12 +1,17 @@
-"""A squared-ReLU MLP training step chained through the library, as the MLP
-benchmark step runs it: row+col quantize of X, W1, W2, dY; FC1 GEMM; relu^2
-fused into the quantize of FC1's BF16 output H; FC2 GEMM; FC2 dgrad and
-wgrad; the activation's backward fused into the row+col+dbias quantize of
-FC2's dgrad output; FC1 dgrad and wgrad.
+"""A squared-ReLU MLP training step run through the library with the calls
+and layouts of the MLP benchmark step: row+col quantize of X, W1, W2, dY;
+FC1 GEMM; relu^2 fused into the quantize of a BF16 hidden tensor H; FC2 GEMM;
+FC2 dgrad and wgrad; the activation's backward fused into the
+row+col+dbias quantize of a BF16 gradient dA, which also reads H; FC1 dgrad
+and wgrad.
 
-Every stage is checked against the oracle on the GPU's own input to that
-stage (the BF16 output of the previous GEMM): quantize launches bit for bit,
-GEMMs within the GEMM tolerance, dbias within the summation bound."""
+The oracle runs the same step from the host tensors alone: its H and dA are
+its own GEMM outputs rounded to BF16.  Those are uploaded as the GPU's inputs
+to the activation launches, so every GPU stage is compared with the oracle on
+identical inputs (no oracle input or expected value comes from the GPU):
+quantize launches bit for bit, GEMMs within the GEMM tolerance, dbias within
+the summation bound; the GPU's own FC1 and FC2-dgrad outputs are checked
+against the oracle's H and dA within the GEMM tolerance."""
 
 import numpy as np
 import pytest
@@ -30,6 +35,11 @@ def check_quantized(got, v):
     return (q, s), (qT, sT)
 
 
+def bf16_of(r):
+    """The oracle's BF16 copy of an fp64 GEMM result (fp32, then RNE to BF16)."""
+    return workloads.f32_to_bf16_bits(np.asarray(r, dtype=np.float32))
+
+
 @pytest.mark.parametrize("T,D,F", [(256, 256, 384), (384, 512, 640)])
 def test_squared_relu_mlp_step(T, D, F):
     torch = need_gpu()
@@ -46,9 +56,12 @@ def test_squared_relu_mlp_step(T, D, F):
     (x_r, x_c) = check_quantized(qx, f32(x))
     (w1_r, w1_c) = check_quantized(qw1, f32(w1))
 
-    h = mx.gemm(qx["q_row"], qx["p_row"], qw1["q_row"], qw1["p_row"])
-    h_bits = to_host(h)
-    gemm_tolerance_check(h_bits, oracle.gemm_tn(*x_r, *w1_r), D, label="fc1")
+    # FC1: the GPU's output against the oracle's; the oracle's H feeds the rest
+    h_ref = oracle.gemm_tn(*x_r, *w1_r)
+    gemm_tolerance_check(to_host(mx.gemm(qx["q_row"], qx["p_row"], qw1["q_row"], qw1["p_row"])), h_ref, D,
+                         label="fc1")
+    h_bits = bf16_of(h_ref)
+    h = to_dev_bf16(h_bits)
 
     qa = mx.quantize(h, rowwise=True, colwise=True, packed=True, act="sqrelu")
     a_r, a_c = check_quantized(qa, oracle.act_sqrelu(h_bits))
@@ -60,13 +73,15 @@ def test_squared_relu_mlp_step(T, D, F):
 
     qdy = mx.quantize(to_dev_bf16(dy), rowwise=True, colwise=True, packed=True)
     dy_r, dy_c = check_quantized(qdy, f32(dy))
-    da = mx.gemm(qdy["q_row"], qdy["p_row"], qw2["q_colT"], qw2["p_colT"])
-    da_bits = to_host(da)
-    gemm_tolerance_check(da_bits, oracle.gemm_tn(*dy_r, *w2_c), D, label="fc2 dgrad")
+    da_ref = oracle.gemm_tn(*dy_r, *w2_c)
+    gemm_tolerance_check(to_host(mx.gemm(qdy["q_row"], qdy["p_row"], qw2["q_colT"], qw2["p_colT"])), da_ref, D,
+                         label="fc2 dgrad")
     dw2 = mx.gemm(qdy["q_colT"], qdy["p_colT"], qa["q_colT"], qa["p_colT"])
     gemm_tolerance_check(to_host(dw2), oracle.gemm_tn(*dy_c, *a_c), T, label="fc2 wgrad")
 
-    qdh = mx.quantize(da, rowwise=True, colwise=True, dbias=True, packed=True, act="dsqrelu", act_in=h)
+    da_bits = bf16_of(da_ref)
+    qdh = mx.quantize(to_dev_bf16(da_bits), rowwise=True, colwise=True, dbias=True, packed=True, act="dsqrelu",
+                      act_in=h)
     dh = oracle.dact_sqrelu(da_bits, h_bits)
     dh_r, dh_c = check_quantized(qdh, dh)
     ref = oracle.dbias_values(dh).astype(np.float64)
