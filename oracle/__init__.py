@@ -282,6 +282,19 @@ def gelu_epilogue(r: np.ndarray) -> np.ndarray:
 # (grouped: per expert), so C[m][n] = SiLU(R[m][n]) * R[m][N + n] for the
 # fp64 product R = A B^T over the 2N rows.
 
+def bias_add(r: np.ndarray, bias_bits: np.ndarray) -> np.ndarray:
+    """The bias epilogue of the GEMM (the fused bias that "Experimental FlyDSL
+    GEMM backend for TE PyTorch (BF16/FP16/FP32/FP8/MXFP8)" leaves as a TODO
+    and that te.Linear(bias=True) needs, review of the fallback exceptions):
+    R[m][n] + bias[n] in float64, the BF16 bias taken exactly, before any
+    activation epilogue and the output rounding.  r [.., C], bias [C]."""
+    b = bf16_value(np.asarray(bias_bits, dtype=np.uint16))
+    r = np.asarray(r, dtype=np.float64)
+    if b.shape != r.shape[-1:]:
+        raise ValueError("bias must have one value per product column")
+    return r + b
+
+
 def silu_f64(z) -> np.ndarray:
     """SiLU(z) = z / (1 + exp(-z)) in float64 (exp overflow for z < -709
     gives z / inf = -0, the correctly rounded value)."""

@@ -730,6 +730,20 @@ def test_swiglu_epilogue_pairs_gate_and_up_columns():
         oracle.swiglu_epilogue(np.zeros((2, 5)))
 
 
+def test_bias_add_broadcasts_one_value_per_column():
+    """R + bias[n]: zero bias is the identity; with a zero product the result
+    is the bias on every row (exact BF16 values, e.g. 0x3FC0 = 1.5 and
+    0xC080 = -4); a transposed bias (per row) is rejected."""
+    r = np.arange(12, dtype=np.float64).reshape(3, 4) - 5.0
+    assert np.array_equal(oracle.bias_add(r, np.zeros(4, dtype=np.uint16)), r)
+    b = np.array([0x3FC0, 0xC080, 0x0000, 0x8000], dtype=np.uint16)
+    got = oracle.bias_add(np.zeros((3, 4)), b)
+    assert np.array_equal(got, np.tile([1.5, -4.0, 0.0, 0.0], (3, 1)))
+    assert np.array_equal(oracle.bias_add(r, b)[:, 1], r[:, 1] - 4.0)
+    with pytest.raises(ValueError):
+        oracle.bias_add(r, np.zeros(3, dtype=np.uint16))
+
+
 def test_scale_bytes_array_matches_the_scalar_rule():
     rng = np.random.default_rng(63)
     a = np.abs(rng.standard_normal(3000)) * np.exp2(rng.integers(-140, 130, size=3000))
