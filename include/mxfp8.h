@@ -320,6 +320,29 @@ mxfp8_status mxfp8_gemm_ex(const uint8_t *a, const uint32_t *a_packed,
                            void *c, int64_t ldc,
                            int64_t M, int64_t N, int64_t K, uint32_t flags, void *stream);
 
+/*
+ * mxfp8_gemm_ex with a bias epilogue.  Defining passage: the fused bias that
+ * the FlyDSL backend leaves as a TODO, so that te.Linear(bias=True) fails on
+ * its first forward pass ("Experimental FlyDSL GEMM backend for TE PyTorch
+ * (BF16/FP16/FP32/FP8/MXFP8)", review of the fallback exceptions and of the
+ * epilogue validation).
+ *
+ *   C[m][n] = bf16_rne( epi( sum_k dq(A)[m][k] dq(B)[n][k] + bias[n] ) ),
+ *
+ * the BF16 bias added to the fp32 sum, epi the relu^2 / GELU epilogue or the
+ * identity.  With MXFP8_GEMM_SWIGLU the bias has 2N values, one per B row:
+ * C[m][n] = SiLU(g + bias[n]) * (u + bias[N + n]).
+ * bias    BF16 [N] ([2N] with SWIGLU), 16-byte aligned, not NULL.
+ * flags   0, MXFP8_GEMM_SQRELU, MXFP8_GEMM_GELU or MXFP8_GEMM_SWIGLU
+ *         (ACCUMULATE -> FLAGS).  K == 0 writes epi(bias).
+ * Other arguments and errors as mxfp8_gemm_ex; NULL for a NULL bias,
+ * MISALIGNED for a bias not 16-byte aligned.
+ */
+mxfp8_status mxfp8_gemm_bias(const uint8_t *a, const uint32_t *a_packed,
+                             const uint8_t *b, const uint32_t *b_packed,
+                             const void *bias, void *c, int64_t ldc,
+                             int64_t M, int64_t N, int64_t K, uint32_t flags, void *stream);
+
 /* ------------------------------------------------------------------------
  * Grouped (ragged expert) GEMM
  *
@@ -372,6 +395,16 @@ mxfp8_status mxfp8_grouped_gemm_ex(const uint8_t *a, const uint32_t *a_packed,
                                    const int32_t *offsets, int32_t G,
                                    void *c, int64_t ldc,
                                    int64_t M_total, int64_t N, int64_t K, uint32_t flags, void *stream);
+
+/* mxfp8_grouped_gemm_ex with the bias epilogue of mxfp8_gemm_bias, one bias
+ * per expert: bias BF16 [G][N] ([G][2N] with SWIGLU), expert g's bias at
+ * bias + g * N (g * 2N), 16-byte aligned.  Flags and errors as
+ * mxfp8_gemm_bias and mxfp8_grouped_gemm_ex. */
+mxfp8_status mxfp8_grouped_gemm_bias(const uint8_t *a, const uint32_t *a_packed,
+                                     const uint8_t *b, const uint32_t *b_packed,
+                                     const int32_t *offsets, int32_t G, const void *bias,
+                                     void *c, int64_t ldc,
+                                     int64_t M_total, int64_t N, int64_t K, uint32_t flags, void *stream);
 
 #ifdef __cplusplus
 }

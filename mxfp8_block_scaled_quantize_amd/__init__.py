@@ -39,7 +39,8 @@ STATUS_NAMES = {0: "MXFP8_OK", 1: "MXFP8_ERR_NULL", 2: "MXFP8_ERR_SHAPE", 3: "MX
 
 EXPORTED = ("mxfp8_status_string", "mxfp8_last_hip_error", "mxfp8_quantize_workspace_bytes",
             "mxfp8_quantize", "mxfp8_packed_scale_bytes", "mxfp8_pack_scales", "mxfp8_gemm",
-            "mxfp8_grouped_gemm", "mxfp8_gemm_ex", "mxfp8_grouped_gemm_ex", "mxfp8_quantize_ex",
+            "mxfp8_grouped_gemm", "mxfp8_gemm_ex", "mxfp8_grouped_gemm_ex", "mxfp8_gemm_bias",
+            "mxfp8_grouped_gemm_bias", "mxfp8_quantize_ex",
             "mxfp8_quantize_ex_noalloc")
 
 
@@ -88,6 +89,10 @@ def lib() -> ctypes.CDLL:
     L.mxfp8_gemm_ex.argtypes = [P, P, P, P, P, I64, I64, I64, I64, U32, P]
     L.mxfp8_grouped_gemm_ex.restype = ctypes.c_int
     L.mxfp8_grouped_gemm_ex.argtypes = [P, P, P, P, P, I32, P, I64, I64, I64, I64, U32, P]
+    L.mxfp8_gemm_bias.restype = ctypes.c_int
+    L.mxfp8_gemm_bias.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, U32, P]
+    L.mxfp8_grouped_gemm_bias.restype = ctypes.c_int
+    L.mxfp8_grouped_gemm_bias.argtypes = [P, P, P, P, P, I32, P, P, I64, I64, I64, I64, U32, P]
     _lib = L
     return L
 
@@ -173,6 +178,16 @@ def mxfp8_grouped_gemm(a, a_packed, b, b_packed, offsets, G, c, ldc, M_total, N,
 def mxfp8_gemm_ex(a, a_packed, b, b_packed, c, ldc, M, N, K, flags, stream=None):
     _check(lib().mxfp8_gemm_ex(_p(a), _p(a_packed), _p(b), _p(b_packed), _p(c), ldc, M, N, K, flags, _s(stream)),
            "mxfp8_gemm_ex")
+
+
+def mxfp8_gemm_bias(a, a_packed, b, b_packed, bias, c, ldc, M, N, K, flags, stream=None):
+    _check(lib().mxfp8_gemm_bias(_p(a), _p(a_packed), _p(b), _p(b_packed), _p(bias), _p(c), ldc, M, N, K, flags,
+                                 _s(stream)), "mxfp8_gemm_bias")
+
+
+def mxfp8_grouped_gemm_bias(a, a_packed, b, b_packed, offsets, G, bias, c, ldc, M_total, N, K, flags, stream=None):
+    _check(lib().mxfp8_grouped_gemm_bias(_p(a), _p(a_packed), _p(b), _p(b_packed), _p(offsets), G, _p(bias), _p(c),
+                                         ldc, M_total, N, K, flags, _s(stream)), "mxfp8_grouped_gemm_bias")
 
 
 def mxfp8_grouped_gemm_ex(a, a_packed, b, b_packed, offsets, G, c, ldc, M_total, N, K, flags, stream=None):
@@ -288,12 +303,14 @@ def _gemm_flags(accumulate, sqrelu, gelu, swiglu=False):
 
 
 def gemm(a, a_packed, b, b_packed, out=None, accumulate=False, sqrelu=False, gelu=False, swiglu=False,
-         stream=None):
+         bias=None, stream=None):
     """C = dq(A) dq(B)^T in BF16 for E4M3 codes a [M, K], b [N, K]; with
     accumulate=True the product is added to `out` (beta = 1); with
     sqrelu=True C = relu(product)^2, with gelu=True C = GELU(product)
     (formed in fp32, rounded once).  swiglu=True: b is [2N, K] (gate rows,
-    then up rows) and C [M, N] = SiLU(gate product) * up product."""
+    then up rows) and C [M, N] = SiLU(gate product) * up product.  bias (a
+    BF16 tensor with one value per row of b) is added to the fp32 product
+    before the activation (not with accumulate)."""
     import torch
     if not isinstance(a, torch.Tensor) or a.dim() != 2 or not isinstance(b, torch.Tensor) or b.dim() != 2:
         raise ValueError("a and b must be 2-D tensors of E4M3 codes")
@@ -313,16 +330,24 @@ def gemm(a, a_packed, b, b_packed, out=None, accumulate=False, sqrelu=False, gel
     if c.dtype != torch.bfloat16 or tuple(c.shape) != (M, N) or c.stride(1) != 1 or c.device != dev:
         raise ValueError("out must be a BF16 [M, N] tensor with unit column stride on the operands' device")
     flags = _gemm_flags(accumulate, sqrelu, gelu, swiglu)
+    if bias is not None:
+        if accumulate:
+            raise ValueError("bias and accumulate exclude each other")
+        _require(bias, "bias", torch.bfloat16, (NB,), dev)
     with torch.cuda.device(dev):
-        mxfp8_gemm_ex(a, a_packed, b, b_packed, c, c.stride(0), M, N, K, flags, stream)
+        if bias is not None:
+            mxfp8_gemm_bias(a, a_packed, b, b_packed, bias, c, c.stride(0), M, N, K, flags, stream)
+        else:
+            mxfp8_gemm_ex(a, a_packed, b, b_packed, c, c.stride(0), M, N, K, flags, stream)
     return c
 
 
 def grouped_gemm(a, a_packed, b, b_packed, offsets, out=None, accumulate=False, sqrelu=False, gelu=False,
-                 swiglu=False, stream=None):
+                 swiglu=False, bias=None, stream=None):
     """Ragged grouped GEMM; b is [G, N, K]; rows outside every group keep `out`'s values;
     sqrelu=True writes relu(product)^2 (an MoE block's first projection), gelu=True GELU(product);
-    swiglu=True: b is [G, 2N, K] (per expert gate rows, then up rows), C [M, N] = SiLU(gate) * up."""
+    swiglu=True: b is [G, 2N, K] (per expert gate rows, then up rows), C [M, N] = SiLU(gate) * up;
+    bias: BF16 [G, rows of an expert], added per expert before the activation."""
     import torch
     if not isinstance(a, torch.Tensor) or a.dim() != 2 or not isinstance(b, torch.Tensor) or b.dim() != 3:
         raise ValueError("a must be 2-D [M, K] and b 3-D [G, N, K] tensors of E4M3 codes")
@@ -343,6 +368,14 @@ def grouped_gemm(a, a_packed, b, b_packed, offsets, out=None, accumulate=False, 
     if c.dtype != torch.bfloat16 or tuple(c.shape) != (M, N) or c.stride(1) != 1 or c.device != dev:
         raise ValueError("out must be a BF16 [M, N] tensor with unit column stride on the operands' device")
     flags = _gemm_flags(accumulate, sqrelu, gelu, swiglu)
+    if bias is not None:
+        if accumulate:
+            raise ValueError("bias and accumulate exclude each other")
+        _require(bias, "bias", torch.bfloat16, (G, NB), dev)
     with torch.cuda.device(dev):
-        mxfp8_grouped_gemm_ex(a, a_packed, b, b_packed, offsets, G, c, c.stride(0), M, N, K, flags, stream)
+        if bias is not None:
+            mxfp8_grouped_gemm_bias(a, a_packed, b, b_packed, offsets, G, bias, c, c.stride(0), M, N, K, flags,
+                                    stream)
+        else:
+            mxfp8_grouped_gemm_ex(a, a_packed, b, b_packed, offsets, G, c, c.stride(0), M, N, K, flags, stream)
     return c

@@ -93,6 +93,31 @@ int gemm_epilogue(uint32_t flags) {
 // SwiGLU reads 2N rows of B: their scale-word offsets (8N bytes) stay below 2^31.
 constexpr int64_t kMaxSwigluN = int64_t(1) << 27;
 
+// Every GEMM entry point: flags, shapes, pointers, grid; then one launch.
+// Dense when offsets == nullptr and G == 0.  with_bias: the bias entry points
+// (a bias is required, accumulate is rejected).
+mxfp8_status gemm_entry(const uint8_t* a, const uint32_t* a_packed, const uint8_t* b, const uint32_t* b_packed,
+                        const int32_t* offsets, int32_t G, const void* bias, bool with_bias, void* c, int64_t ldc,
+                        int64_t M, int64_t N, int64_t K, uint32_t flags, void* stream) {
+  if (!gemm_flags_ok(flags)) return MXFP8_ERR_FLAGS;
+  if (with_bias && (flags & MXFP8_GEMM_ACCUMULATE)) return MXFP8_ERR_FLAGS;
+  const bool grouped = G > 0;
+  const mxfp8_status st = check_gemm_common(a, a_packed, b, b_packed, c, ldc, M, N, K);
+  if (st != MXFP8_OK) return st;
+  const bool swiglu = (flags & MXFP8_GEMM_SWIGLU) != 0;
+  if (swiglu && N > kMaxSwigluN) return MXFP8_ERR_LIMIT;
+  if (M == 0 || N == 0) return MXFP8_OK;
+  if (grouped && !offsets) return MXFP8_ERR_NULL;
+  if (grouped && !aligned(offsets, 4)) return MXFP8_ERR_MISALIGNED;
+  if (with_bias && !bias) return MXFP8_ERR_NULL;
+  if (with_bias && !aligned(bias, 16)) return MXFP8_ERR_MISALIGNED;
+  if (!mx::gemm_grid_fits(M, N, G, grouped, swiglu)) return MXFP8_ERR_LIMIT;
+  return hip_status(mx::launch_gemm(a, a_packed, b, b_packed, static_cast<uint16_t*>(c), ldc, M, N, K,
+                                    grouped ? offsets : nullptr, G, (flags & MXFP8_GEMM_ACCUMULATE) != 0,
+                                    gemm_epilogue(flags), with_bias ? static_cast<const uint16_t*>(bias) : nullptr,
+                                    static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -182,16 +207,7 @@ mxfp8_status mxfp8_pack_scales(const uint8_t* s, int64_t dim, int64_t k, int64_t
 
 mxfp8_status mxfp8_gemm_ex(const uint8_t* a, const uint32_t* a_packed, const uint8_t* b, const uint32_t* b_packed,
                            void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, uint32_t flags, void* stream) {
-  if (!gemm_flags_ok(flags)) return MXFP8_ERR_FLAGS;
-  const mxfp8_status st = check_gemm_common(a, a_packed, b, b_packed, c, ldc, M, N, K);
-  if (st != MXFP8_OK) return st;
-  const bool swiglu = (flags & MXFP8_GEMM_SWIGLU) != 0;
-  if (swiglu && N > kMaxSwigluN) return MXFP8_ERR_LIMIT;
-  if (M == 0 || N == 0) return MXFP8_OK;
-  if (!mx::gemm_grid_fits(M, N, 0, false, swiglu)) return MXFP8_ERR_LIMIT;
-  return hip_status(mx::launch_gemm(a, a_packed, b, b_packed, static_cast<uint16_t*>(c), ldc, M, N, K, nullptr, 0,
-                                    (flags & MXFP8_GEMM_ACCUMULATE) != 0, gemm_epilogue(flags),
-                                    static_cast<hipStream_t>(stream)));
+  return gemm_entry(a, a_packed, b, b_packed, nullptr, 0, nullptr, false, c, ldc, M, N, K, flags, stream);
 }
 
 mxfp8_status mxfp8_gemm(const uint8_t* a, const uint32_t* a_packed, const uint8_t* b, const uint32_t* b_packed,
@@ -199,28 +215,31 @@ mxfp8_status mxfp8_gemm(const uint8_t* a, const uint32_t* a_packed, const uint8_
   return mxfp8_gemm_ex(a, a_packed, b, b_packed, c, ldc, M, N, K, 0u, stream);
 }
 
+mxfp8_status mxfp8_gemm_bias(const uint8_t* a, const uint32_t* a_packed, const uint8_t* b, const uint32_t* b_packed,
+                             const void* bias, void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, uint32_t flags,
+                             void* stream) {
+  return gemm_entry(a, a_packed, b, b_packed, nullptr, 0, bias, true, c, ldc, M, N, K, flags, stream);
+}
+
 mxfp8_status mxfp8_grouped_gemm_ex(const uint8_t* a, const uint32_t* a_packed, const uint8_t* b,
                                    const uint32_t* b_packed, const int32_t* offsets, int32_t G, void* c, int64_t ldc,
                                    int64_t M_total, int64_t N, int64_t K, uint32_t flags, void* stream) {
-  if (!gemm_flags_ok(flags)) return MXFP8_ERR_FLAGS;
-  if (G < 1 || G > 65536) return MXFP8_ERR_SHAPE;
-  const mxfp8_status st = check_gemm_common(a, a_packed, b, b_packed, c, ldc, M_total, N, K);
-  if (st != MXFP8_OK) return st;
-  const bool swiglu = (flags & MXFP8_GEMM_SWIGLU) != 0;
-  if (swiglu && N > kMaxSwigluN) return MXFP8_ERR_LIMIT;
-  if (M_total == 0 || N == 0) return MXFP8_OK;
-  if (!offsets) return MXFP8_ERR_NULL;
-  if (!aligned(offsets, 4)) return MXFP8_ERR_MISALIGNED;
-  if (!mx::gemm_grid_fits(M_total, N, G, true, swiglu)) return MXFP8_ERR_LIMIT;
-  return hip_status(mx::launch_gemm(a, a_packed, b, b_packed, static_cast<uint16_t*>(c), ldc, M_total, N, K,
-                                    offsets, G, (flags & MXFP8_GEMM_ACCUMULATE) != 0, gemm_epilogue(flags),
-                                    static_cast<hipStream_t>(stream)));
+  if (G < 1 || G > 65536) return gemm_flags_ok(flags) ? MXFP8_ERR_SHAPE : MXFP8_ERR_FLAGS;
+  return gemm_entry(a, a_packed, b, b_packed, offsets, G, nullptr, false, c, ldc, M_total, N, K, flags, stream);
 }
 
 mxfp8_status mxfp8_grouped_gemm(const uint8_t* a, const uint32_t* a_packed, const uint8_t* b,
                                 const uint32_t* b_packed, const int32_t* offsets, int32_t G, void* c, int64_t ldc,
                                 int64_t M_total, int64_t N, int64_t K, void* stream) {
   return mxfp8_grouped_gemm_ex(a, a_packed, b, b_packed, offsets, G, c, ldc, M_total, N, K, 0u, stream);
+}
+
+mxfp8_status mxfp8_grouped_gemm_bias(const uint8_t* a, const uint32_t* a_packed, const uint8_t* b,
+                                     const uint32_t* b_packed, const int32_t* offsets, int32_t G, const void* bias,
+                                     void* c, int64_t ldc, int64_t M_total, int64_t N, int64_t K, uint32_t flags,
+                                     void* stream) {
+  if (G < 1 || G > 65536) return gemm_flags_ok(flags) ? MXFP8_ERR_SHAPE : MXFP8_ERR_FLAGS;
+  return gemm_entry(a, a_packed, b, b_packed, offsets, G, bias, true, c, ldc, M_total, N, K, flags, stream);
 }
 
 }  // extern "C"

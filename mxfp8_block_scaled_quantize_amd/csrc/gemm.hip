@@ -97,12 +97,13 @@ struct ic {
   static constexpr int value = V;
 };
 
-template <bool GROUPED, bool ACC, int EPI>
+template <bool GROUPED, bool ACC, int EPI, bool BIAS>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
                  const uint8_t* __restrict__ B, const uint32_t* __restrict__ Bp,
                  uint16_t* __restrict__ Cm, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                 const int32_t* __restrict__ offsets, int32_t G, int64_t tiles_m, int64_t tiles_n) {
+                 const int32_t* __restrict__ offsets, int32_t G, int64_t tiles_m, int64_t tiles_n,
+                 const uint16_t* __restrict__ bias) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
   lds_u8* smem = (lds_u8*)smem_raw;
 
@@ -429,12 +430,33 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
   // them stays live (or spills) across the main loop.
   const int elane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const bool full_rows = m_lo + BM <= m_hi;
+  // Four BF16 bias values at element offset `at` of the bias array, for the
+  // output columns col .. col + 3 (col % 4 == 0, N % 32 == 0: all four are
+  // inside N or none is); zeros past N.  One 8-byte load (the bias is
+  // 16-byte aligned).
+  auto bias4 = [&](int64_t at, int64_t col) -> u32x2 {
+    if (col < N) return *reinterpret_cast<const u32x2*>(bias + at);
+    return u32x2{0u, 0u};
+  };
   if constexpr (SW) {
     // SwiGLU: blocks j = 0, 1 of a wave hold the gate and blocks j + 2 the up
     // products of the same 64 output columns wn * 64 + [0, 64), so each output
     // is SiLU(gate) * up of two registers of the lane, in fp32, rounded once.
     {
       const int lr = elane & 31, lg = elane >> 5;
+      // BIAS: the gate bias of output column n is bias[n], the up bias
+      // bias[N + n] (per group: the bias rows follow B's rows).
+      u32x2 bgate[2][4], bup[2][4];
+      if (BIAS) {
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+          for (int g = 0; g < 4; g++) {
+            const int64_t col = n0 + wn * 64 + 32 * j + 8 * g + 4 * lg;
+            bgate[j][g] = bias4(b_row0 + col, col);
+            bup[j][g] = bias4(b_row0 + N + col, col);
+          }
+      }
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int row = wm * 128 + 32 * i + lr;
@@ -445,7 +467,14 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
             const int col = wn * 64 + 32 * j + 8 * g + 4 * lg;
             float v[4];
 #pragma unroll
-            for (int t = 0; t < 4; t++) v[t] = silu_f32(acc[i][j][4 * g + t]) * acc[i][j + 2][4 * g + t];
+            for (int t = 0; t < 4; t++) {
+              float gt = acc[i][j][4 * g + t], ut = acc[i][j + 2][4 * g + t];
+              if (BIAS) {
+                gt += bf16_half2(bgate[j][g], t);
+                ut += bf16_half2(bup[j][g], t);
+              }
+              v[t] = silu_f32(gt) * ut;
+            }
             const bf16x2 h0 = {(__bf16)v[0], (__bf16)v[1]};
             const bf16x2 h1 = {(__bf16)v[2], (__bf16)v[3]};
             *(__attribute__((address_space(3))) u32x2*)(smem + row * SW_LDS_STRIDE + 2 * col) =
@@ -494,6 +523,16 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
   }
   {
     const int lr = elane & 31, lg = elane >> 5;
+    u32x2 bv[4][4];   // BIAS: the bias of the lane's four columns per (j, g)
+    if (BIAS) {
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+          const int64_t gcol = n0 + wn * 128 + 32 * j + 8 * g + 4 * lg;
+          bv[j][g] = bias4(b_row0 + gcol, gcol);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int row = wm * 128 + 32 * i + lr;
@@ -512,6 +551,12 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
             v1 += __uint_as_float(o.x & 0xFFFF0000u);
             v2 += __uint_as_float(o.y << 16);
             v3 += __uint_as_float(o.y & 0xFFFF0000u);
+          }
+          if (BIAS) {   // the bias joins the fp32 sum before any activation
+            v0 += bf16_half2(bv[j][g], 0);
+            v1 += bf16_half2(bv[j][g], 1);
+            v2 += bf16_half2(bv[j][g], 2);
+            v3 += bf16_half2(bv[j][g], 3);
           }
           if (EPI == 1) {   // relu(acc)^2 in fp32, then the one BF16 rounding
             v0 = fmaxf(v0, 0.0f);
@@ -560,10 +605,11 @@ bool gemm_grid_fits(int64_t M, int64_t N, int32_t G, bool grouped, bool swiglu) 
   return grid_fits(tm, tn, 256);
 }
 
-template <bool GROUPED, bool ACC, int EPI>
+template <bool GROUPED, bool ACC, int EPI, bool BIAS>
 static hipError_t launch_gemm_t(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
                                 uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, const int32_t* offsets,
-                                int32_t G, int64_t tiles_m, int64_t tiles_n, hipStream_t stream) {
+                                int32_t G, int64_t tiles_m, int64_t tiles_n, const uint16_t* bias,
+                                hipStream_t stream) {
   // The dynamic-LDS opt-in is set once per device (bit d of the mask, for
   // device ids below 64; others set it on every launch), race-free across
   // host threads.
@@ -573,38 +619,51 @@ static hipError_t launch_gemm_t(const uint8_t* a, const uint32_t* ap, const uint
   if (e != hipSuccess) return e;
   const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
   if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<GROUPED, ACC, EPI>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<GROUPED, ACC, EPI, BIAS>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_done.fetch_or(bit, std::memory_order_release);
   }
-  hipLaunchKernelGGL((gemm_kernel<GROUPED, ACC, EPI>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), LDS_BYTES, stream,
-                     a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n);
+  hipLaunchKernelGGL((gemm_kernel<GROUPED, ACC, EPI, BIAS>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256),
+                     LDS_BYTES, stream, a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, bias);
   return hipGetLastError();
+}
+
+// One launch for an (epilogue, bias) pair of a dense or grouped GEMM.
+template <bool GROUPED>
+static hipError_t launch_gemm_g(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
+                                uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, const int32_t* offsets,
+                                int32_t G, int64_t tiles_m, int64_t tiles_n, bool accumulate, int epilogue,
+                                const uint16_t* bias, hipStream_t stream) {
+#define MX_G_LAUNCH(AC, EP, BI) \
+  launch_gemm_t<GROUPED, AC, EP, BI>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, bias, stream)
+  // accumulate, the epilogues and the bias: the API rejects accumulate
+  // together with any of the others
+  if (accumulate) return MX_G_LAUNCH(true, 0, false);
+  if (bias)
+    return epilogue == 1 ? MX_G_LAUNCH(false, 1, true)
+         : epilogue == 2 ? MX_G_LAUNCH(false, 2, true)
+         : epilogue == 3 ? MX_G_LAUNCH(false, 3, true)
+                         : MX_G_LAUNCH(false, 0, true);
+  return epilogue == 1 ? MX_G_LAUNCH(false, 1, false)
+       : epilogue == 2 ? MX_G_LAUNCH(false, 2, false)
+       : epilogue == 3 ? MX_G_LAUNCH(false, 3, false)
+                       : MX_G_LAUNCH(false, 0, false);
+#undef MX_G_LAUNCH
 }
 
 hipError_t launch_gemm(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
                        uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                       const int32_t* offsets, int32_t G, bool accumulate, int epilogue, hipStream_t stream) {
+                       const int32_t* offsets, int32_t G, bool accumulate, int epilogue, const uint16_t* bias,
+                       hipStream_t stream) {
   const bool grouped = offsets != nullptr;
   const int64_t tiles_n = epilogue == 3 ? (N + SW_TN - 1) / SW_TN : (N + BN - 1) / BN;
   const int64_t tiles_m = (M + BM - 1) / BM + (grouped ? (int64_t)G : 0);
   if (tiles_m * tiles_n == 0) return hipSuccess;
-#define MX_G_LAUNCH(GR, AC, EP) \
-  launch_gemm_t<GR, AC, EP>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, stream)
-  // accumulate and the epilogues are exclusive (the API rejects combinations)
-  if (grouped)
-    return accumulate ? MX_G_LAUNCH(true, true, 0)
-                      : epilogue == 1 ? MX_G_LAUNCH(true, false, 1)
-                      : epilogue == 2 ? MX_G_LAUNCH(true, false, 2)
-                      : epilogue == 3 ? MX_G_LAUNCH(true, false, 3)
-                                      : MX_G_LAUNCH(true, false, 0);
-  return accumulate ? MX_G_LAUNCH(false, true, 0)
-                    : epilogue == 1 ? MX_G_LAUNCH(false, false, 1)
-                    : epilogue == 2 ? MX_G_LAUNCH(false, false, 2)
-                    : epilogue == 3 ? MX_G_LAUNCH(false, false, 3)
-                                    : MX_G_LAUNCH(false, false, 0);
-#undef MX_G_LAUNCH
+  return grouped ? launch_gemm_g<true>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, accumulate,
+                                       epilogue, bias, stream)
+                 : launch_gemm_g<false>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, accumulate,
+                                        epilogue, bias, stream);
 }
 
 }  // namespace mx

@@ -46,6 +46,12 @@ __device__ __forceinline__ uint32_t abs_bits2(uint32_t w) { return w & 0x7FFF7FF
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// BF16 value t (0..3) of four packed in two dwords (little-endian), as fp32.
+__device__ __forceinline__ float bf16_half2(u32x2 w, int t) {
+  const uint32_t d = t < 2 ? w.x : w.y;
+  return (t & 1) ? bf_hi(d) : bf_lo(d);
+}
+
 // E8M0 byte of a block from the 15-bit magnitude pattern of its amax.
 // floor(log2 amax) - 8 + 127 is (biased exponent field - 8); subnormal or zero
 // amax (exponent field 0) and anything below 2^-118 clamp to byte 0.

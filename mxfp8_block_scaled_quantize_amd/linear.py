@@ -1,8 +1,10 @@
-"""MXFP8 linear layer (no bias) wired through the block-scaled GEMM.
+"""MXFP8 linear layer wired through the block-scaled GEMM.
 
-    fprop   y  = x W^T      TN GEMM: A = x rowwise [M][K],   B = W rowwise [N][K]
+    fprop   y  = x W^T + b  TN GEMM: A = x rowwise [M][K],   B = W rowwise [N][K],
+                            the optional BF16 bias b [N] added by the GEMM's bias epilogue
     dgrad   dx = dy W       TN GEMM: A = dy rowwise [M][N],  B = W columnwise copy [K][N]
     wgrad   dW = dy^T x     TN GEMM: A = dy columnwise copy [N][M], B = x columnwise copy [K][M]
+    bgrad   db = sum_m dy   the dbias fused into the quantization of dy (no extra pass)
 
 The columnwise copies are stored transposed, so every GEMM reduces over the
 contiguous dimension of both operands and runs on the same TN kernel; each
@@ -28,23 +30,29 @@ import torch
 from . import gemm, quantize
 
 
-def _quantize_both(t):
+def _quantize_both(t, dbias=False):
     # one pass writes both copies with their scales already in the GEMM's
-    # packed word layout (rows and columns are multiples of 128 here)
-    out = quantize(t, rowwise=True, colwise=True, packed=True)
-    return out["q_row"], out["p_row"], out["q_colT"], out["p_colT"]
+    # packed word layout (rows and columns are multiples of 128 here), and
+    # with dbias=True the fp32 column sums as well
+    out = quantize(t, rowwise=True, colwise=True, packed=True, dbias=dbias)
+    q = (out["q_row"], out["p_row"], out["q_colT"], out["p_colT"])
+    return q + (out["dbias"],) if dbias else q
 
 
 class MXFP8LinearFunction(torch.autograd.Function):
-    """apply(x, weight, fuse_wgrad_accumulation=False, weight_q=None):
+    """apply(x, weight, fuse_wgrad_accumulation=False, weight_q=None, bias=None):
     weight_q, when given, is the weight's quantization (q_row, p_row, q_colT,
     p_colT) as ``quantize(weight, rowwise=True, colwise=True, packed=True)``
-    returns it, made from the current value of ``weight``."""
+    returns it, made from the current value of ``weight``; bias, when given,
+    is a BF16 [N] tensor added by the GEMM (its gradient is the fp32 dbias of
+    dy's quantization, returned in the bias's dtype)."""
 
     @staticmethod
-    def forward(ctx, x, weight, fuse_wgrad_accumulation=False, weight_q=None):
+    def forward(ctx, x, weight, fuse_wgrad_accumulation=False, weight_q=None, bias=None):
         if x.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
             raise TypeError("MXFP8 linear takes BF16 input and weight")
+        if bias is not None and (bias.dtype != torch.bfloat16 or tuple(bias.shape) != (weight.shape[0],)):
+            raise ValueError("bias must be a BF16 tensor with one value per output feature")
         lead = x.shape[:-1]
         x2 = x.reshape(-1, x.shape[-1]).contiguous()
         M, K = x2.shape
@@ -58,8 +66,9 @@ class MXFP8LinearFunction(torch.autograd.Function):
         if weight_q is None:
             weight_q = _quantize_both(weight.contiguous())
         qw, pw, qwT, pwT = weight_q
-        y = gemm(qx, px, qw, pw)
+        y = gemm(qx, px, qw, pw, bias=None if bias is None else bias.contiguous())
         ctx.save_for_backward(qxT, pxT, qwT, pwT)
+        ctx.bias_dtype = None if bias is None else bias.dtype
         ctx.weight = weight
         ctx.fuse = fuse_wgrad_accumulation
         ctx.shape = (lead, M, K, N)
@@ -70,7 +79,8 @@ class MXFP8LinearFunction(torch.autograd.Function):
         qxT, pxT, qwT, pwT = ctx.saved_tensors
         lead, M, K, N = ctx.shape
         dy2 = dy.reshape(M, N).to(torch.bfloat16).contiguous()
-        qd, pd, qdT, pdT = _quantize_both(dy2)
+        want_db = ctx.bias_dtype is not None and ctx.needs_input_grad[4]
+        qd, pd, qdT, pdT, *db = _quantize_both(dy2, dbias=want_db)
         dx = None
         if ctx.needs_input_grad[0]:
             dx = gemm(qd, pd, qwT, pwT).view(*lead, K)
@@ -83,19 +93,24 @@ class MXFP8LinearFunction(torch.autograd.Function):
                 gemm(qdT, pdT, qxT, pxT, out=main, accumulate=True)
             else:
                 dw = gemm(qdT, pdT, qxT, pxT)
-        return dx, dw, None, None
+        dbias = db[0].to(ctx.bias_dtype) if want_db else None
+        return dx, dw, None, None, dbias
 
 
 class MXFP8Linear(torch.nn.Module):
-    """y = x W^T with MXFP8 block-scaled fprop, dgrad and wgrad (no bias)."""
+    """y = x W^T (+ b) with MXFP8 block-scaled fprop, dgrad and wgrad; the
+    optional BF16 bias is added by the fprop GEMM and its gradient comes from
+    the dbias fused into dy's quantization."""
 
-    def __init__(self, in_features, out_features, fuse_wgrad_accumulation=False, device=None):
+    def __init__(self, in_features, out_features, fuse_wgrad_accumulation=False, device=None, bias=False):
         super().__init__()
         self.in_features, self.out_features = in_features, out_features
         self.fuse_wgrad_accumulation = fuse_wgrad_accumulation
         w = torch.empty((out_features, in_features), dtype=torch.bfloat16, device=device)
         torch.nn.init.normal_(w, std=in_features ** -0.5)
         self.weight = torch.nn.Parameter(w)
+        self.bias = (torch.nn.Parameter(torch.zeros(out_features, dtype=torch.bfloat16, device=device))
+                     if bias else None)
         if fuse_wgrad_accumulation:
             self.weight.main_grad = torch.zeros_like(w)
         self._wq_key = None
@@ -113,4 +128,5 @@ class MXFP8Linear(torch.nn.Module):
         return self._wq
 
     def forward(self, x):
-        return MXFP8LinearFunction.apply(x, self.weight, self.fuse_wgrad_accumulation, self.quantized_weight())
+        return MXFP8LinearFunction.apply(x, self.weight, self.fuse_wgrad_accumulation, self.quantized_weight(),
+                                         self.bias)

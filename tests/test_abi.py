@@ -242,6 +242,27 @@ def test_gemm_ex_flags(L):
     assert GG(A16, A16, A16, A16, None, 4, None, 64, 0, 64, 128, 1, None) == OK
 
 
+def test_gemm_bias_validation(L):
+    """The bias entry points apply the _ex rules, require a 16-byte aligned
+    bias pointer, and reject accumulate (the bias belongs to a fresh output)."""
+    B = L.mxfp8_gemm_bias
+    assert B(A16, A16, A16, A16, None, A16, 64, 64, 64, 128, 0, None) == NULL
+    assert B(A16, A16, A16, A16, A16 + 2, A16, 64, 64, 64, 128, 0, None) == MISALIGNED
+    assert B(A16, A16, A16, A16, A16, A16, 64, 64, 64, 128, 1, None) == FLAGS        # accumulate
+    assert B(A16, A16, A16, A16, A16, A16, 64, 64, 64, 128, 16, None) == FLAGS
+    assert B(A16, A16, A16, A16, A16, A16, 64, 64, 64, 100, 4, None) == SHAPE         # K % 128
+    assert B(A16, A16, A16, A16, None, A16, 64, 0, 64, 128, 0, None) == OK           # empty: nothing read
+    assert B(A16, A16, A16, A16, A16, A16, (1 << 27) + 32, 64, (1 << 27) + 32, 128, 8, None) == LIMIT
+    GB = L.mxfp8_grouped_gemm_bias
+    assert GB(A16, A16, A16, A16, A16, 0, A16, A16, 64, 64, 64, 128, 0, None) == SHAPE
+    assert GB(A16, A16, A16, A16, A16, 0, A16, A16, 64, 64, 64, 128, 16, None) == FLAGS
+    assert GB(A16, A16, A16, A16, A16, 4, None, A16, 64, 64, 64, 128, 0, None) == NULL
+    assert GB(A16, A16, A16, A16, A16, 4, A16 + 8, A16, 64, 64, 64, 128, 2, None) == MISALIGNED
+    assert GB(A16, A16, A16, A16, A16, 4, A16, A16, 64, 64, 64, 128, 1, None) == FLAGS
+    assert GB(A16, A16, A16, A16, None, 4, A16, A16, 64, 64, 64, 128, 0, None) == NULL  # offsets
+    assert GB(A16, A16, A16, A16, None, 4, None, A16, 64, 0, 64, 128, 0, None) == OK
+
+
 def test_binding_raises_on_error(L):
     with pytest.raises(mx.MXFP8Error) as ei:
         mx.mxfp8_quantize(A16, 64, 48, 64, ROW, A16, A16, stream=0)

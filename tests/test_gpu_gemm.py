@@ -258,7 +258,7 @@ def test_gemm_accumulate_k_zero_keeps_c():
 # --------------------------------------------------------- grouped GEMM
 
 def grouped_case(M, N, K, counts, seed, canary_rows=True, accumulate=False, sqrelu=False, gelu=False,
-                 swiglu=False):
+                 swiglu=False, bias=False):
     torch = need_gpu()
     G = len(counts)
     NB = 2 * N if swiglu else N   # SwiGLU: per expert N gate rows, then N up rows
@@ -275,8 +275,9 @@ def grouped_case(M, N, K, counts, seed, canary_rows=True, accumulate=False, sqre
     else:
         out = torch.full((M, N), -7.0, dtype=torch.bfloat16, device="cuda")
     log("grouped M=%d N=%d K=%d counts=%s accumulate=%d" % (M, N, K, list(counts), accumulate))
+    bb = workloads.normal_bf16((G, NB), seed + 3, std=0.5) if bias else None   # one bias row per expert
     mx.grouped_gemm(qx, px, qw, pw, to_dev(off), out=out, accumulate=accumulate, sqrelu=sqrelu, gelu=gelu,
-                    swiglu=swiglu)
+                    swiglu=swiglu, bias=None if bb is None else to_dev_bf16(bb))
     torch.cuda.synchronize()
     c = to_host(out)
     oqx, osx = oracle.quantize_rowwise(x)
@@ -289,12 +290,19 @@ def grouped_case(M, N, K, counts, seed, canary_rows=True, accumulate=False, sqre
     ref = oracle.grouped_gemm_tn(oqx, osx, qwo, swo, off, rows=rows)
     if accumulate:
         ref = ref + bf16_to_f64(c_old[rows])
+    t = None
+    if bias:
+        t = product_bound(ref, K)
+        grp = np.searchsorted(off, rows, side="right") - 1                  # expert of each covered row
+        ref = ref + bf16_to_f64(bb)[grp]                                     # R + bias[g] (exact)
     if sqrelu:
-        sqrelu_tolerance_check(c[rows], ref, K, label="grouped sqrelu")
+        sqrelu_tolerance_check(c[rows], ref, K, label="grouped sqrelu", t=t)
     elif gelu:
-        gelu_tolerance_check(c[rows], ref, K, label="grouped gelu")
+        gelu_tolerance_check(c[rows], ref, K, label="grouped gelu", t=t)
     elif swiglu:
-        swiglu_tolerance_check(c[rows], ref, K, label="grouped swiglu")
+        swiglu_tolerance_check(c[rows], ref, K, label="grouped swiglu", t=t)
+    elif bias:
+        bias_tolerance_check(c[rows], ref, t, label="grouped bias")
     else:
         gemm_tolerance_check(c[rows], ref, K, label="grouped")
     if canary_rows and accumulate:
@@ -303,16 +311,17 @@ def grouped_case(M, N, K, counts, seed, canary_rows=True, accumulate=False, sqre
         assert np.all(bf16_to_f64(c[~covered]) == -7.0), "rows outside the groups were written"
 
 
-def sqrelu_tolerance_check(gpu_bits, r, K, label="", rms=None):
+def sqrelu_tolerance_check(gpu_bits, r, K, label="", rms=None, t=None):
     """relu(R)^2 epilogue: the GPU forms relu(acc)^2 from its fp32 sum acc,
     |acc - R| <= t = 8e-3 |R| + 1e-3 sqrt(K) rms(R) (the GEMM bound), so
     |relu(acc)^2 - relu(R)^2| <= t (2|R| + t), plus the one BF16 rounding,
     2^-9 (|R| + t)^2 (doubled for margin)."""
     gpu = bf16_to_f64(gpu_bits)
     r = np.asarray(r, dtype=np.float64)
-    if rms is None:
-        rms = np.sqrt(np.mean(r ** 2))
-    t = 8e-3 * np.abs(r) + 1e-3 * np.sqrt(K) * rms
+    if t is None:   # (a bias test passes the bound of the unbiased product)
+        if rms is None:
+            rms = np.sqrt(np.mean(r ** 2))
+        t = 8e-3 * np.abs(r) + 1e-3 * np.sqrt(K) * rms
     tol = t * (2 * np.abs(r) + t) + 2.0 ** -8 * (np.abs(r) + t) ** 2
     err = np.abs(gpu - oracle.sqrelu_epilogue(r))
     bad = ~(err <= tol)
@@ -359,16 +368,17 @@ def test_grouped_sqrelu_epilogue():
 GELU_MIN = -0.16997   # min GELU, at x = -0.7518 (GELU(-0.75179) = -0.169971)
 
 
-def gelu_tolerance_check(gpu_bits, r, K, label="", rms=None):
+def gelu_tolerance_check(gpu_bits, r, K, label="", rms=None, t=None):
     """GELU(R) epilogue: the GPU applies GELU to its fp32 sum acc with
     |acc - R| <= t (the GEMM bound); |GELU'| <= 1.13 everywhere, so the exact
     GELU moves by at most 1.13 t; the fp32 GELU adds (8 + 3 acc^2) 2^-24 of
     its value, and the BF16 rounding 2^-9 (doubled for margin)."""
     gpu = bf16_to_f64(gpu_bits)
     r = np.asarray(r, dtype=np.float64)
-    if rms is None:
-        rms = np.sqrt(np.mean(r ** 2))
-    t = 8e-3 * np.abs(r) + 1e-3 * np.sqrt(K) * rms
+    if t is None:
+        if rms is None:
+            rms = np.sqrt(np.mean(r ** 2))
+        t = 8e-3 * np.abs(r) + 1e-3 * np.sqrt(K) * rms
     g = oracle.gelu_epilogue(r)
     mag = np.abs(g) + 1.13 * t
     tol = 1.13 * t + 2.0 ** -8 * mag + (8.0 + 3.0 * (np.abs(r) + t) ** 2) * 2.0 ** -24 * mag
@@ -423,7 +433,7 @@ def test_grouped_gelu_epilogue():
     grouped_case(1200, 96, 256, [5, 0, 131, 257, 600], 10, gelu=True)
 
 
-def swiglu_tolerance_check(gpu_bits, r, K, label="", rms=None):
+def swiglu_tolerance_check(gpu_bits, r, K, label="", rms=None, t=None):
     """SwiGLU epilogue on a product r [.., 2N] = [gate | up]: the GPU forms
     SiLU(g) * u from fp32 sums g, u with |g - R_g| <= t_g, |u - R_u| <= t_u (the
     GEMM bound, rms over the whole 2N-wide product); |SiLU'| <= 1.1, so
@@ -433,9 +443,10 @@ def swiglu_tolerance_check(gpu_bits, r, K, label="", rms=None):
     gpu = bf16_to_f64(gpu_bits)
     r = np.asarray(r, dtype=np.float64)
     n = r.shape[1] // 2
-    if rms is None:
-        rms = np.sqrt(np.mean(r ** 2))
-    t = 8e-3 * np.abs(r) + 1e-3 * np.sqrt(K) * rms
+    if t is None:
+        if rms is None:
+            rms = np.sqrt(np.mean(r ** 2))
+        t = 8e-3 * np.abs(r) + 1e-3 * np.sqrt(K) * rms
     rg, ru, tg, tu = r[:, :n], r[:, n:], t[:, :n], t[:, n:]
     want = oracle.swiglu_epilogue(r)
     m = (np.abs(oracle.silu_f64(rg)) + 1.1 * tg) * (np.abs(ru) + tu)
@@ -492,6 +503,107 @@ def test_gemm_swiglu_epilogue_on_integers():
 def test_grouped_swiglu_epilogue():
     grouped_case(1200, 96, 256, [5, 0, 131, 257, 600], 11, swiglu=True)
     grouped_case(700, 160, 384, [300, 0, 64, 336], 12, swiglu=True)
+
+
+# ------------------------------------------------------------ bias epilogue
+
+def product_bound(r, K):
+    """The GEMM bound t on an (unbiased) product r, rms over all of r."""
+    r = np.asarray(r, dtype=np.float64)
+    return 8e-3 * np.abs(r) + 1e-3 * np.sqrt(K) * np.sqrt(np.mean(r ** 2))
+
+
+def bias_tolerance_check(gpu_bits, ref_b, t, label=""):
+    """|gpu - (R + b)| <= t (the bound of R) + the BF16 rounding of the
+    biased value, 2^-9 |R + b| (doubled for margin)."""
+    err = np.abs(bf16_to_f64(gpu_bits) - ref_b)
+    tol = t + 2.0 ** -8 * (np.abs(ref_b) + t)
+    bad = ~(err <= tol)
+    assert not bad.any(), "%s: %d entries out of tolerance, worst %g" % (label, bad.sum(), err[bad].max())
+
+
+BIAS_EPI = {"plain": 0, "sqrelu": mx.MXFP8_GEMM_SQRELU, "gelu": mx.MXFP8_GEMM_GELU, "swiglu": mx.MXFP8_GEMM_SWIGLU}
+
+
+@pytest.mark.parametrize("epi", ["plain", "sqrelu", "gelu", "swiglu"])
+@pytest.mark.parametrize("M,N,K", [(160, 96, 512), (300, 288, 256), (64, 32, 128)])
+def test_gemm_bias_epilogue(M, N, K, epi):
+    """C = epi(A B^T + bias) with a BF16 bias per B row (2N values for SwiGLU:
+    gate, then up) of the same size as the products, so some sums cancel;
+    padded ldc with canaries around C."""
+    torch = need_gpu()
+    NB = 2 * N if epi == "swiglu" else N
+    a = workloads.normal_bf16((M, K), 19 * M + K)
+    b = workloads.normal_bf16((NB, K), 23 * N + K, std=0.25)
+    bias = workloads.normal_bf16((NB,), 29 * N + M, std=2.0)
+    qa, sa, pa = quantize_on_gpu(a)
+    qb, sb, pb = quantize_on_gpu(b)
+    log("bias epilogue %s M=%d N=%d K=%d" % (epi, M, N, K))
+    ldc, G = N + 16, 1024
+    full = torch.full((M * ldc + 2 * G,), -12345, dtype=torch.int16, device="cuda")
+    c = full[G:G + M * ldc].view(torch.bfloat16)
+    mx.mxfp8_gemm_bias(qa, pa, qb, pb, to_dev_bf16(bias), c, ldc, M, N, K, BIAS_EPI[epi])
+    torch.cuda.synchronize()
+    h = to_host(full.view(torch.bfloat16))
+    canary = np.uint16(-12345 & 0xFFFF)
+    assert np.all(h[:G] == canary) and np.all(h[-G:] == canary)
+    inner = h[G:G + M * ldc].reshape(M, ldc)
+    assert np.all(inner[:, N:] == canary), "columns beyond N written"
+    got = inner[:, :N]
+    oqa, osa = oracle.quantize_rowwise(a)
+    oqb, osb = oracle.quantize_rowwise(b)
+    r = oracle.gemm_tn(oqa, osa, oqb, osb)
+    t = product_bound(r, K)
+    rb = oracle.bias_add(r, bias)
+    if epi == "plain":
+        bias_tolerance_check(got, rb, t, "bias")
+    elif epi == "sqrelu":
+        sqrelu_tolerance_check(got, rb, K, "bias sqrelu", t=t)
+    elif epi == "gelu":
+        gelu_tolerance_check(got, rb, K, "bias gelu", t=t)
+    else:
+        swiglu_tolerance_check(got, rb, K, "bias swiglu", t=t)
+
+
+def test_gemm_bias_exact_on_integers():
+    """Integer operands and an integer bias: R + b is exact in fp32 and BF16
+    (|R + b| < 256), so the output equals it exactly; a bias taken from the
+    wrong column, row or half fails."""
+    rng = np.random.default_rng(16)
+    A = rng.integers(-1, 2, size=(96, 128))
+    B = rng.integers(-1, 2, size=(64, 128))
+    bias = rng.integers(-100, 101, size=64).astype(np.float32)
+    to_bits = lambda v: (np.asarray(v, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    qa, sa, pa = quantize_on_gpu(to_bits(A))
+    qb, sb, pb = quantize_on_gpu(to_bits(B))
+    log("bias integers")
+    torch = need_gpu()
+    c = torch.empty((96, 64), dtype=torch.bfloat16, device="cuda")
+    mx.mxfp8_gemm_bias(qa, pa, qb, pb, to_dev_bf16(to_bits(bias)), c, 64, 96, 64, 128, 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_to_f64(to_host(c)), (A @ B.T + bias[None, :]).astype(np.float64))
+
+
+def test_grouped_bias_epilogue():
+    grouped_case(1200, 96, 256, [5, 0, 131, 257, 600], 13, bias=True)
+    grouped_case(700, 160, 384, [300, 0, 64, 336], 14, bias=True, swiglu=True)
+    grouped_case(900, 128, 256, [400, 200, 300], 15, bias=True, gelu=True)
+
+
+@pytest.mark.parametrize("epi", ["plain", "gelu", "swiglu"])
+def test_bias_with_k_zero_writes_the_epilogue_of_the_bias(epi):
+    """K = 0: C = epi(bias) on every row (SwiGLU: SiLU(gate bias) * up bias)."""
+    torch = need_gpu()
+    N = 96
+    NB = 2 * N if epi == "swiglu" else N
+    bias = workloads.normal_bf16((NB,), 33, std=2.0)
+    c = torch.full((40, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    mx.mxfp8_gemm_bias(None, None, None, None, to_dev_bf16(bias), c, N, 40, N, 0, BIAS_EPI[epi])
+    torch.cuda.synchronize()
+    bv = bf16_to_f64(bias)[None, :]
+    want = {"plain": bv, "gelu": oracle.gelu_epilogue(bv), "swiglu": oracle.swiglu_epilogue(bv)}[epi]
+    got = bf16_to_f64(to_host(c))
+    assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 1e-30)
 
 
 def test_grouped_uniform_counts():

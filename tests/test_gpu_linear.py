@@ -137,3 +137,61 @@ def test_linear_module_reuses_weight_quantization_until_the_weight_changes(monke
     qx, sx = oracle.quantize_rowwise(x1)
     qw, sw = oracle.quantize_rowwise(w2)
     gemm_tolerance_check(to_host(y), oracle.gemm_tn(qx, sx, qw, sw), K, label="forward after update")
+
+
+def _bias_checks(y, db, x, w, dy, bias, label):
+    """y = x W^T + b against the oracle's product plus the bias (the GEMM bound
+    of the unbiased product, plus the BF16 rounding of the biased value);
+    the bias gradient against the oracle's column sums of dy (the fp32 dbias
+    bound of the quantize tests, plus its rounding to BF16, 2^-9 doubled)."""
+    from test_gpu_quantize import dbias_depth
+    y_ref, _, _ = _refs(x, w, dy)
+    t = 8e-3 * np.abs(y_ref) + 1e-3 * np.sqrt(K) * np.sqrt(np.mean(y_ref ** 2))
+    want = oracle.bias_add(y_ref, bias)
+    err = np.abs(bf16_to_f64(to_host(y)) - want)
+    tol = t + 2.0 ** -8 * (np.abs(want) + t)
+    assert np.all(err <= tol), "%s fprop: %d entries out of tolerance" % (label, np.sum(err > tol))
+    ref = oracle.dbias(dy).astype(np.float64)
+    mag = np.abs(bf16_to_f64(dy)).sum(axis=0)
+    tol = 1.01 * dbias_depth(M) * 2.0 ** -24 * mag + np.abs(ref) * 2.0 ** -24 + 2.0 ** -126
+    tol = tol + 2.0 ** -8 * (np.abs(ref) + tol)
+    err = np.abs(bf16_to_f64(to_host(db)) - ref)
+    assert np.all(err <= tol), "%s dbias off by %g" % (label, err.max())
+
+
+def test_linear_with_bias():
+    """The bias goes through the GEMM's bias epilogue in fprop and its gradient
+    through the dbias fused into dy's quantization; dgrad and wgrad are the
+    same as without a bias."""
+    torch = need_gpu()
+    from mxfp8_block_scaled_quantize_amd.linear import MXFP8LinearFunction
+    x, w, dy = _inputs(36)
+    bias = workloads.normal_bf16((N,), 37, std=1.0)
+    log("linear with bias M=%d K=%d N=%d" % (M, K, N))
+    xt = to_dev_bf16(x).requires_grad_(True)
+    wt = to_dev_bf16(w).requires_grad_(True)
+    bt = to_dev_bf16(bias).requires_grad_(True)
+    y = MXFP8LinearFunction.apply(xt, wt, False, None, bt)
+    y.backward(to_dev_bf16(dy))
+    torch.cuda.synchronize()
+    assert bt.grad.dtype == torch.bfloat16 and tuple(bt.grad.shape) == (N,)
+    _bias_checks(y.detach(), bt.grad, x, w, dy, bias, "function")
+    _, dx_ref, dw_ref = _refs(x, w, dy)
+    gemm_tolerance_check(to_host(xt.grad), dx_ref, N, label="dgrad with bias")
+    gemm_tolerance_check(to_host(wt.grad), dw_ref, M, label="wgrad with bias")
+
+
+def test_linear_module_with_bias():
+    torch = need_gpu()
+    import mxfp8_block_scaled_quantize_amd.linear as lin
+    x, w, dy = _inputs(38)
+    bias = workloads.normal_bf16((N,), 39, std=1.0)
+    layer = lin.MXFP8Linear(K, N, device="cuda", bias=True)
+    with torch.no_grad():
+        layer.weight.copy_(to_dev_bf16(w))
+        layer.bias.copy_(to_dev_bf16(bias))
+    log("linear module with bias")
+    y = layer(to_dev_bf16(x))
+    y.backward(to_dev_bf16(dy))
+    torch.cuda.synchronize()
+    _bias_checks(y.detach(), layer.bias.grad, x, w, dy, bias, "module")

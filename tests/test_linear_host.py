@@ -71,3 +71,27 @@ def test_module_weight_cache_key(monkeypatch):
     assert len(calls) == 2
     layer.weight.data = torch.zeros((256, 128), dtype=torch.bfloat16)   # new storage
     assert layer.quantized_weight() is not again and len(calls) == 3
+
+
+def test_bias_is_checked_before_any_launch():
+    """A bias must be BF16 with one value per output feature; the GEMM helpers
+    refuse a bias together with accumulate (host checks only)."""
+    import mxfp8_block_scaled_quantize_amd as mx
+    x = torch.zeros((128, 128), dtype=torch.bfloat16)
+    w = torch.zeros((256, 128), dtype=torch.bfloat16)
+    for bad in (torch.zeros(256), torch.zeros(128, dtype=torch.bfloat16), torch.zeros((1, 256), dtype=torch.bfloat16)):
+        with pytest.raises(ValueError, match="bias"):
+            MXFP8LinearFunction.apply(x, w, False, None, bad)
+    a = torch.zeros((64, 128), dtype=torch.uint8)
+    p = torch.zeros((1, 64), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        mx.gemm(a, p, a, p, out=torch.zeros((64, 64), dtype=torch.bfloat16), accumulate=True,
+                bias=torch.zeros(64, dtype=torch.bfloat16))
+
+
+def test_module_with_bias_has_a_bias_parameter():
+    import mxfp8_block_scaled_quantize_amd.linear as lin
+    layer = lin.MXFP8Linear(128, 256, bias=True)
+    assert layer.bias is not None and layer.bias.dtype == torch.bfloat16 and tuple(layer.bias.shape) == (256,)
+    assert {n for n, _ in layer.named_parameters()} == {"weight", "bias"}
+    assert lin.MXFP8Linear(128, 256).bias is None
