@@ -525,21 +525,20 @@ def bias_tolerance_check(gpu_bits, ref_b, t, label=""):
 BIAS_EPI = {"plain": 0, "sqrelu": mx.MXFP8_GEMM_SQRELU, "gelu": mx.MXFP8_GEMM_GELU, "swiglu": mx.MXFP8_GEMM_SWIGLU}
 
 
-@pytest.mark.parametrize("epi", ["plain", "sqrelu", "gelu", "swiglu"])
-@pytest.mark.parametrize("M,N,K", [(160, 96, 512), (300, 288, 256), (64, 32, 128)])
-def test_gemm_bias_epilogue(M, N, K, epi):
+def bias_case(M, N, K, epi, seed, ldc=None):
     """C = epi(A B^T + bias) with a BF16 bias per B row (2N values for SwiGLU:
     gate, then up) of the same size as the products, so some sums cancel;
-    padded ldc with canaries around C."""
+    ldc padding and canaries around C."""
     torch = need_gpu()
     NB = 2 * N if epi == "swiglu" else N
-    a = workloads.normal_bf16((M, K), 19 * M + K)
-    b = workloads.normal_bf16((NB, K), 23 * N + K, std=0.25)
-    bias = workloads.normal_bf16((NB,), 29 * N + M, std=2.0)
+    a = workloads.normal_bf16((M, K), seed)
+    b = workloads.normal_bf16((NB, K), seed + 1, std=0.25)
+    bias = workloads.normal_bf16((NB,), seed + 2, std=2.0)
     qa, sa, pa = quantize_on_gpu(a)
     qb, sb, pb = quantize_on_gpu(b)
-    log("bias epilogue %s M=%d N=%d K=%d" % (epi, M, N, K))
-    ldc, G = N + 16, 1024
+    log("bias epilogue %s M=%d N=%d K=%d ldc=%s seed=%d" % (epi, M, N, K, ldc, seed))
+    ldc = N + 16 if ldc is None else ldc
+    G = 1024
     full = torch.full((M * ldc + 2 * G,), -12345, dtype=torch.int16, device="cuda")
     c = full[G:G + M * ldc].view(torch.bfloat16)
     mx.mxfp8_gemm_bias(qa, pa, qb, pb, to_dev_bf16(bias), c, ldc, M, N, K, BIAS_EPI[epi])
@@ -563,6 +562,12 @@ def test_gemm_bias_epilogue(M, N, K, epi):
         gelu_tolerance_check(got, rb, K, "bias gelu", t=t)
     else:
         swiglu_tolerance_check(got, rb, K, "bias swiglu", t=t)
+
+
+@pytest.mark.parametrize("epi", ["plain", "sqrelu", "gelu", "swiglu"])
+@pytest.mark.parametrize("M,N,K", [(160, 96, 512), (300, 288, 256), (64, 32, 128)])
+def test_gemm_bias_epilogue(M, N, K, epi):
+    bias_case(M, N, K, epi, 19 * M + 23 * N + K)
 
 
 def test_gemm_bias_exact_on_integers():

@@ -15,8 +15,8 @@ import mxfp8_block_scaled_quantize_amd as mx
 import oracle
 import workloads
 from gpu_util import bf16_to_f64, gemm_tolerance_check, log, need_gpu, to_dev_bf16, to_host
-from test_gpu_gemm import (gelu_tolerance_check, gemm_gpu, grouped_case, quantize_on_gpu, sqrelu_tolerance_check,
-                           swiglu_tolerance_check)
+from test_gpu_gemm import (bias_case, gelu_tolerance_check, gemm_gpu, grouped_case, quantize_on_gpu,
+                           sqrelu_tolerance_check, swiglu_tolerance_check)
 from test_gpu_quantize_ex import act_inputs, check_act_result, check_gelu_result, dgelu_case, gelu_case, run_ex
 
 pytestmark = pytest.mark.gpu
@@ -198,3 +198,24 @@ def test_random_grouped_gemm_swiglu(case):
     if M == 0:
         pytest.skip("empty problem (covered by test_grouped_empty_total)")
     grouped_case(M, N, K, list(counts), seed, swiglu=True)
+
+
+EPIS = ["plain", "sqrelu", "gelu", "swiglu"]
+
+
+@pytest.mark.parametrize("case", gemm_cases(12, 80))
+def test_random_gemm_bias(case):
+    """The bias epilogue under each activation, random M, N, K and ldc."""
+    M, N, K, ldc, _, seed = case
+    bias_case(M, N, K, EPIS[seed % 4], seed, ldc=ldc)
+
+
+@pytest.mark.parametrize("case", grouped_cases(8, 94))
+def test_random_grouped_gemm_bias(case):
+    counts, tail, N, K, _, seed = case
+    M = sum(counts) + tail
+    if M == 0:
+        pytest.skip("empty problem (covered by test_grouped_empty_total)")
+    epi = EPIS[seed % 4]
+    grouped_case(M, N, K, list(counts), seed, bias=True, sqrelu=epi == "sqrelu", gelu=epi == "gelu",
+                 swiglu=epi == "swiglu")
