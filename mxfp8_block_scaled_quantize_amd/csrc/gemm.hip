@@ -39,7 +39,8 @@
 // fp32 sum before the one BF16 rounding; SwiGLU, where B holds gate rows then
 // up rows and a tile covers 128 output columns whose gate and up sums end in
 // the same wave (see the SwiGLU DMA and epilogue below).  Accumulate (ACC)
-// adds the old C before the rounding.
+// adds the old C before the rounding; BIAS adds a BF16 value per B row (per
+// expert row for the grouped GEMM) to the fp32 sum before the activation.
 #include <atomic>
 
 #include "mx_device.h"

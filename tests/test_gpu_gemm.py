@@ -45,22 +45,27 @@ def gemm_gpu(qa, pa, qb, pb, ldc=None, canary=False, flags=0):
 
 # ------------------------------------------------------------- packing
 
-@pytest.mark.parametrize("dim,K", [(32, 128), (96, 512), (1000, 4096), (64, 128 * 67)])
+@pytest.mark.parametrize("dim,K", [(32, 128), (96, 512), (1000, 4096), (64, 128 * 67), (264, 2560), (1004, 1024),
+                                   (16384, 4096)])
 def test_pack_scales_bit_exact(dim, K):
+    """Both kernel forms: 4-byte accesses (K / 128 or dim not a multiple of 4,
+    or a source stride not a multiple of 16) and 16-byte accesses (partial row
+    and word tiles included)."""
     torch = need_gpu()
     rng = np.random.default_rng(dim + K)
     s = rng.integers(0, 256, size=(dim, K // 32)).astype(np.uint8)
     log("pack dim=%d K=%d" % (dim, K))
     got = to_host(mx.pack_scales(to_dev(s)))
     assert np.array_equal(got, oracle.pack_scales(s))
-    # strided source (ld_s > K/32)
-    wide = np.zeros((dim, K // 32 + 12), dtype=np.uint8)
-    wide[:, :K // 32] = s
-    ws = to_dev(wide)
-    out = torch.empty((K // 128, dim), dtype=torch.int32, device="cuda")
-    mx.mxfp8_pack_scales(ws, dim, K, wide.shape[1], out)
-    torch.cuda.synchronize()
-    assert np.array_equal(to_host(out), oracle.pack_scales(s))
+    # strided sources (ld_s > K/32; + 12 keeps the 4-byte form, + 16 allows the 16-byte one)
+    for extra in (12, 16):
+        wide = np.zeros((dim, K // 32 + extra), dtype=np.uint8)
+        wide[:, :K // 32] = s
+        ws = to_dev(wide)
+        out = torch.empty((K // 128, dim), dtype=torch.int32, device="cuda")
+        mx.mxfp8_pack_scales(ws, dim, K, wide.shape[1], out)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(out), oracle.pack_scales(s)), extra
 
 
 # -------------------------------------------------------- dense GEMM
