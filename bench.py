@@ -55,6 +55,10 @@ def parse():
                         "(at least one whole step runs)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain 256 MiB device copy (reference for HBM byte counters)")
+    p.add_argument("--mfma-calibration", action="store_true",
+                   help="also time the scaled FP8 MFMA fed from registers only (libmxfp8_calib.so), in launches "
+                        "of the dominant GEMM's FLOPs, as many as the timed steps: the rate a GEMM that still "
+                        "moves its operands could at most reach on this GPU at this power")
     return p.parse_args()
 
 
@@ -480,10 +484,77 @@ def main():
                        "separate pass after them (%d steps); ms = mean, with median, min and max; "
                        "short_launch_blocks: the same launches as timed in the steps" % min(args.steps, 10),
     }
+    if args.mfma_calibration:
+        result["mfma_calibration"] = mfma_calibration(torch, stream, dominant, dom.work, args.steps, args.warmup,
+                                                      achieved)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.workload, host, total_flops, args.cpu_seconds)
 
     print(json.dumps(result))
+
+
+def mfma_calibration(torch, stream, label, flops_per_launch, launches, warmup, gemm_tflops):
+    """The register-only MFMA kernel of libmxfp8_calib.so (GEMM-shaped
+    workgroups: 4 waves, 256 accumulators and 128 operand registers each,
+    random E4M3 codes) with the GEMM's grid: one workgroup per 256 x 256 tile
+    of an M x N x K label, each running the tile's K / 64 rounds of 16 MFMAs
+    per wave (other labels: 1024 workgroups and the GEMM's FLOPs).  Timed with
+    HIP events per launch on the bench stream."""
+    import re
+    import ctypes
+
+    import numpy as np
+
+    from mxfp8_block_scaled_quantize_amd.build import CALIB_PATH
+    L = ctypes.CDLL(CALIB_PATH)
+    P = ctypes.c_void_p
+    L.mxfp8_calib_mfma_ceiling.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, P]
+    L.mxfp8_calib_mfma_ceiling.restype = ctypes.c_int
+    words = L.mxfp8_calib_code_words()
+    g = torch.Generator().manual_seed(11)
+    c = torch.randint(0, 254, (4 * words,), generator=g, dtype=torch.int32)
+    c = torch.where(c >= 0x7F, c + 1, c).to(torch.uint8)          # every E4M3 code except the NaNs
+    codes = c.view(torch.int32).to("cuda")
+    scales = torch.full((128,), 0x77777777, dtype=torch.int32, device="cuda")   # 2^-8: sums stay finite
+    m = re.fullmatch(r"(\d+)x(\d+)x(\d+)", label)
+    if m:
+        M, N, K = (int(v) for v in m.groups())
+        blocks = ((M + 255) // 256) * ((N + 255) // 256)
+        iters = max(1, K // 128)
+    else:
+        blocks = 1024
+        iters = max(1, int(round(flops_per_launch / (blocks * 4 * 32 * 2.0 * 32 * 32 * 64))))
+    per_iter = blocks * 4 * 32 * 2.0 * 32 * 32 * 64
+    out = torch.empty((blocks * 256,), dtype=torch.float32, device="cuda")
+
+    def launch():
+        rc = L.mxfp8_calib_mfma_ceiling(codes.data_ptr(), scales.data_ptr(), out.data_ptr(), blocks, iters,
+                                        stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError("calibration launch failed (hipError %d)" % rc)
+
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(launches):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError("calibration sums are not finite")
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    tf = per_iter * iters / (ms * 1e-3) / 1e12
+    return {"kernel": "mfma_ceiling_kernel (register-only scaled FP8 MFMA)", "blocks": blocks, "iters": iters,
+            "flops_per_launch": per_iter * iters, "launches": launches, "ms": round(float(np.mean(ms)), 4),
+            "ms_median": round(float(np.median(ms)), 4), "tflops": round(float(np.mean(tf)), 1),
+            "tflops_at_median": round(per_iter * iters / (float(np.median(ms)) * 1e-3) / 1e12, 1),
+            "frac_fp8_peak": round(float(np.mean(tf)) / FP8_PEAK_TFLOPS, 4),
+            "gemm_over_ceiling": round(gemm_tflops / float(np.mean(tf)), 4)}
 
 
 def oracle_step(workload, h):

@@ -1,4 +1,6 @@
-"""Build libmxfp8.so (gfx950 HIP kernels + C ABI) in-tree with hipcc."""
+"""Build libmxfp8.so (gfx950 HIP kernels + C ABI) in-tree with hipcc, and
+libmxfp8_calib.so, the benchmark's measurement aid (the register-only MFMA
+rate; not part of the library)."""
 
 from __future__ import annotations
 
@@ -10,7 +12,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libmxfp8.so")
+CALIB_PATH = os.path.join(HERE, "libmxfp8_calib.so")
 SOURCES = ["api.hip", "quantize.hip", "pack_scales.hip", "gemm.hip"]
+CALIB_SOURCES = ["calib.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-FP32 VALU forms are disabled for all device code; hipcc's host pass
@@ -24,7 +28,7 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     procs = []
     objs = []
-    for src in SOURCES:
+    for src in SOURCES + CALIB_SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
         cmd = [HIPCC, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
@@ -41,9 +45,11 @@ def build(verbose: bool = False) -> str:
             sys.stderr.write(text + "\n")
     if failed:
         raise RuntimeError("hipcc compilation failed")
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB_PATH)
+    n = len(SOURCES)
+    for path, parts in ((LIB_PATH, objs[:n]), (CALIB_PATH, objs[n:])):
+        tmp = path + ".tmp%d" % os.getpid()
+        subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *parts, "-o", tmp])
+        os.replace(tmp, path)
     return LIB_PATH
 
 

@@ -286,3 +286,13 @@ def test_noalloc_quantize_validation(L):
     assert L.mxfp8_quantize_workspace_bytes(1025 * 128, 2048, ROW | DB) > limit
     assert qn(rows=1025 * 128, cols=2048, ld=2048, flags=ROW | DB) == WORKSPACE
     assert qn(rows=1025 * 128, cols=2048, ld=2048, flags=ROW | COL | DB) == WORKSPACE
+
+
+def test_calibration_library_is_separate(L):
+    """The benchmark's register-only MFMA kernel lives in its own library, so
+    the product library exports exactly what include/mxfp8.h declares."""
+    from mxfp8_block_scaled_quantize_amd.build import CALIB_PATH
+    cal = ctypes.CDLL(CALIB_PATH)
+    cal.mxfp8_calib_mfma_ceiling
+    assert cal.mxfp8_calib_code_words() == 4096
+    assert not hasattr(ctypes.CDLL(mx.LIB_PATH), "mxfp8_calib_mfma_ceiling")
