@@ -55,10 +55,10 @@ def parse():
                         "(at least one whole step runs)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain 256 MiB device copy (reference for HBM byte counters)")
-    p.add_argument("--mfma-calibration", action="store_true",
-                   help="also time the scaled FP8 MFMA fed from registers only (libmxfp8_calib.so), in launches "
-                        "of the dominant GEMM's FLOPs, as many as the timed steps: the rate a GEMM that still "
-                        "moves its operands could at most reach on this GPU at this power")
+    p.add_argument("--no-mfma-calibration", action="store_true",
+                   help="skip the reference run of the scaled FP8 MFMA fed from registers only (libmxfp8_calib.so) "
+                        "on the dominant GEMM's tile grid, as many launches as timed steps, after the timed region: "
+                        "the rate a GEMM that still moves its operands could at most reach on this GPU at this power")
     return p.parse_args()
 
 
@@ -484,7 +484,7 @@ def main():
                        "separate pass after them (%d steps); ms = mean, with median, min and max; "
                        "short_launch_blocks: the same launches as timed in the steps" % min(args.steps, 10),
     }
-    if args.mfma_calibration:
+    if not args.no_mfma_calibration:
         result["mfma_calibration"] = mfma_calibration(torch, stream, dominant, dom.work, args.steps, args.warmup,
                                                       achieved)
     if not args.no_cpu_baseline:
@@ -506,6 +506,8 @@ def mfma_calibration(torch, stream, label, flops_per_launch, launches, warmup, g
     import numpy as np
 
     from mxfp8_block_scaled_quantize_amd.build import CALIB_PATH
+    if not os.path.exists(CALIB_PATH):
+        return {"skipped": "libmxfp8_calib.so is not built (build() makes it)"}
     L = ctypes.CDLL(CALIB_PATH)
     P = ctypes.c_void_p
     L.mxfp8_calib_mfma_ceiling.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, P]
