@@ -497,9 +497,10 @@ def mfma_calibration(torch, stream, label, flops_per_launch, launches, warmup, g
     """The register-only MFMA kernel of libmxfp8_calib.so (GEMM-shaped
     workgroups: 4 waves, 256 accumulators and 128 operand registers each,
     random E4M3 codes) with the GEMM's grid: one workgroup per 256 x 256 tile
-    of an M x N x K label, each running the tile's K / 64 rounds of 16 MFMAs
-    per wave (other labels: 1024 workgroups and the GEMM's FLOPs).  Timed with
-    HIP events per launch on the bench stream."""
+    of the label's M x N x K (for a grouped GEMM, M is all routed rows, i.e.
+    the dense grid of the same FLOPs), each running the tile's K / 64 rounds
+    of 16 MFMAs per wave.  Timed with HIP events per launch on the bench
+    stream."""
     import re
     import ctypes
 
@@ -518,7 +519,7 @@ def mfma_calibration(torch, stream, label, flops_per_launch, launches, warmup, g
     c = torch.where(c >= 0x7F, c + 1, c).to(torch.uint8)          # every E4M3 code except the NaNs
     codes = c.view(torch.int32).to("cuda")
     scales = torch.full((128,), 0x77777777, dtype=torch.int32, device="cuda")   # 2^-8: sums stay finite
-    m = re.fullmatch(r"(\d+)x(\d+)x(\d+)", label)
+    m = re.search(r"(\d+)x(\d+)x(\d+)", label)
     if m:
         M, N, K = (int(v) for v in m.groups())
         blocks = ((M + 255) // 256) * ((N + 255) // 256)
