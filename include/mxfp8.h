@@ -406,6 +406,45 @@ mxfp8_status mxfp8_grouped_gemm_bias(const uint8_t *a, const uint32_t *a_packed,
                                      void *c, int64_t ldc,
                                      int64_t M_total, int64_t N, int64_t K, uint32_t flags, void *stream);
 
+/*
+ * GEMM with an MXFP8 output: the output quantization that the FlyDSL backend
+ * rejects ("Experimental FlyDSL GEMM backend for TE PyTorch
+ * (BF16/FP16/FP32/FP8/MXFP8)", review of the fallback exceptions: a quantizer
+ * for the GEMM output, reachable from te.Linear's output quantization
+ * parameters, and of the epilogue validation, which raises for it).
+ *
+ * The output of mxfp8_gemm_bias (bias given) or mxfp8_gemm_ex (bias NULL)
+ * with the same flags, i.e. the BF16 values C that those would write, is
+ * written as its rowwise MXFP8 copy instead: codes q_out[m][n] and, per row
+ * and 32-column block, the scale byte of the quantizer's rowwise rule, in the
+ * packed word layout of the GEMM operands, so the result is the A operand of
+ * a following GEMM.  The codes and scales equal those of mxfp8_quantize_ex
+ * (ROWWISE | PACKED_SCALES) applied to C.
+ * q_out         E4M3 codes [M][ldq]; ldq >= N, ldq % 16 == 0, 16-byte aligned.
+ * q_out_packed  uint32 [N/128][M] (word (t, m): scale bytes of blocks
+ *               4t .. 4t+3 of row m), 4-byte aligned, not NULL.
+ * bias          as mxfp8_gemm_bias, or NULL for none.
+ * N             the output columns (SWIGLU: B holds 2N rows); N % 128 == 0.
+ * flags         0, MXFP8_GEMM_SQRELU, MXFP8_GEMM_GELU or MXFP8_GEMM_SWIGLU
+ *               (ACCUMULATE -> FLAGS).
+ * Other arguments and errors as mxfp8_gemm_ex.
+ */
+mxfp8_status mxfp8_gemm_mxfp8_out(const uint8_t *a, const uint32_t *a_packed,
+                                  const uint8_t *b, const uint32_t *b_packed, const void *bias,
+                                  uint8_t *q_out, int64_t ldq, uint32_t *q_out_packed,
+                                  int64_t M, int64_t N, int64_t K, uint32_t flags, void *stream);
+
+/* The grouped GEMM (mxfp8_grouped_gemm_ex / mxfp8_grouped_gemm_bias, bias per
+ * expert or NULL) with the MXFP8 output of mxfp8_gemm_mxfp8_out: q_out
+ * [M_total][ldq], q_out_packed [N/128][M_total]; rows outside every group are
+ * not written (codes nor scale words). */
+mxfp8_status mxfp8_grouped_gemm_mxfp8_out(const uint8_t *a, const uint32_t *a_packed,
+                                          const uint8_t *b, const uint32_t *b_packed,
+                                          const int32_t *offsets, int32_t G, const void *bias,
+                                          uint8_t *q_out, int64_t ldq, uint32_t *q_out_packed,
+                                          int64_t M_total, int64_t N, int64_t K, uint32_t flags,
+                                          void *stream);
+
 #ifdef __cplusplus
 }
 #endif

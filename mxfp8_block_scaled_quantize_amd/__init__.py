@@ -40,7 +40,7 @@ STATUS_NAMES = {0: "MXFP8_OK", 1: "MXFP8_ERR_NULL", 2: "MXFP8_ERR_SHAPE", 3: "MX
 EXPORTED = ("mxfp8_status_string", "mxfp8_last_hip_error", "mxfp8_quantize_workspace_bytes",
             "mxfp8_quantize", "mxfp8_packed_scale_bytes", "mxfp8_pack_scales", "mxfp8_gemm",
             "mxfp8_grouped_gemm", "mxfp8_gemm_ex", "mxfp8_grouped_gemm_ex", "mxfp8_gemm_bias",
-            "mxfp8_grouped_gemm_bias", "mxfp8_quantize_ex",
+            "mxfp8_grouped_gemm_bias", "mxfp8_gemm_mxfp8_out", "mxfp8_grouped_gemm_mxfp8_out", "mxfp8_quantize_ex",
             "mxfp8_quantize_ex_noalloc")
 
 
@@ -93,6 +93,10 @@ def lib() -> ctypes.CDLL:
     L.mxfp8_gemm_bias.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, U32, P]
     L.mxfp8_grouped_gemm_bias.restype = ctypes.c_int
     L.mxfp8_grouped_gemm_bias.argtypes = [P, P, P, P, P, I32, P, P, I64, I64, I64, I64, U32, P]
+    L.mxfp8_gemm_mxfp8_out.restype = ctypes.c_int
+    L.mxfp8_gemm_mxfp8_out.argtypes = [P, P, P, P, P, P, I64, P, I64, I64, I64, U32, P]
+    L.mxfp8_grouped_gemm_mxfp8_out.restype = ctypes.c_int
+    L.mxfp8_grouped_gemm_mxfp8_out.argtypes = [P, P, P, P, P, I32, P, P, I64, P, I64, I64, I64, U32, P]
     _lib = L
     return L
 
@@ -188,6 +192,18 @@ def mxfp8_gemm_bias(a, a_packed, b, b_packed, bias, c, ldc, M, N, K, flags, stre
 def mxfp8_grouped_gemm_bias(a, a_packed, b, b_packed, offsets, G, bias, c, ldc, M_total, N, K, flags, stream=None):
     _check(lib().mxfp8_grouped_gemm_bias(_p(a), _p(a_packed), _p(b), _p(b_packed), _p(offsets), G, _p(bias), _p(c),
                                          ldc, M_total, N, K, flags, _s(stream)), "mxfp8_grouped_gemm_bias")
+
+
+def mxfp8_gemm_mxfp8_out(a, a_packed, b, b_packed, bias, q_out, ldq, q_out_packed, M, N, K, flags, stream=None):
+    _check(lib().mxfp8_gemm_mxfp8_out(_p(a), _p(a_packed), _p(b), _p(b_packed), _p(bias), _p(q_out), ldq,
+                                      _p(q_out_packed), M, N, K, flags, _s(stream)), "mxfp8_gemm_mxfp8_out")
+
+
+def mxfp8_grouped_gemm_mxfp8_out(a, a_packed, b, b_packed, offsets, G, bias, q_out, ldq, q_out_packed, M_total, N,
+                                 K, flags, stream=None):
+    _check(lib().mxfp8_grouped_gemm_mxfp8_out(_p(a), _p(a_packed), _p(b), _p(b_packed), _p(offsets), G, _p(bias),
+                                              _p(q_out), ldq, _p(q_out_packed), M_total, N, K, flags, _s(stream)),
+           "mxfp8_grouped_gemm_mxfp8_out")
 
 
 def mxfp8_grouped_gemm_ex(a, a_packed, b, b_packed, offsets, G, c, ldc, M_total, N, K, flags, stream=None):
@@ -303,14 +319,16 @@ def _gemm_flags(accumulate, sqrelu, gelu, swiglu=False):
 
 
 def gemm(a, a_packed, b, b_packed, out=None, accumulate=False, sqrelu=False, gelu=False, swiglu=False,
-         bias=None, stream=None):
+         bias=None, mxfp8_out=False, stream=None):
     """C = dq(A) dq(B)^T in BF16 for E4M3 codes a [M, K], b [N, K]; with
     accumulate=True the product is added to `out` (beta = 1); with
     sqrelu=True C = relu(product)^2, with gelu=True C = GELU(product)
     (formed in fp32, rounded once).  swiglu=True: b is [2N, K] (gate rows,
     then up rows) and C [M, N] = SiLU(gate product) * up product.  bias (a
     BF16 tensor with one value per row of b) is added to the fp32 product
-    before the activation (not with accumulate)."""
+    before the activation (not with accumulate).  mxfp8_out=True returns C's
+    rowwise MXFP8 copy instead, as (codes uint8 [M, N], packed scale words
+    int32 [N / 128, M]) (N % 128 == 0; not with accumulate or out)."""
     import torch
     if not isinstance(a, torch.Tensor) or a.dim() != 2 or not isinstance(b, torch.Tensor) or b.dim() != 2:
         raise ValueError("a and b must be 2-D tensors of E4M3 codes")
@@ -334,6 +352,9 @@ def gemm(a, a_packed, b, b_packed, out=None, accumulate=False, sqrelu=False, gel
         if accumulate:
             raise ValueError("bias and accumulate exclude each other")
         _require(bias, "bias", torch.bfloat16, (NB,), dev)
+    if mxfp8_out:
+        return _mx_out(M, N, dev, accumulate, out, lambda q, p: mxfp8_gemm_mxfp8_out(
+            a, a_packed, b, b_packed, bias, q, N, p, M, N, K, flags, stream))
     with torch.cuda.device(dev):
         if bias is not None:
             mxfp8_gemm_bias(a, a_packed, b, b_packed, bias, c, c.stride(0), M, N, K, flags, stream)
@@ -342,12 +363,28 @@ def gemm(a, a_packed, b, b_packed, out=None, accumulate=False, sqrelu=False, gel
     return c
 
 
+def _mx_out(M, N, dev, accumulate, out, call):
+    """Allocate the MXFP8 output of a GEMM and run `call(codes, packed)`."""
+    import torch
+    if accumulate or out is not None:
+        raise ValueError("mxfp8_out=True writes fresh outputs: no accumulate, no out")
+    if N % 128:
+        raise ValueError("mxfp8_out=True needs N % 128 == 0 (whole packed scale words)")
+    q = torch.zeros((M, N), dtype=torch.uint8, device=dev)
+    p = torch.zeros((N // 128, M), dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        call(q, p)
+    return q, p
+
+
 def grouped_gemm(a, a_packed, b, b_packed, offsets, out=None, accumulate=False, sqrelu=False, gelu=False,
-                 swiglu=False, bias=None, stream=None):
+                 swiglu=False, bias=None, mxfp8_out=False, stream=None):
     """Ragged grouped GEMM; b is [G, N, K]; rows outside every group keep `out`'s values;
     sqrelu=True writes relu(product)^2 (an MoE block's first projection), gelu=True GELU(product);
     swiglu=True: b is [G, 2N, K] (per expert gate rows, then up rows), C [M, N] = SiLU(gate) * up;
-    bias: BF16 [G, rows of an expert], added per expert before the activation."""
+    bias: BF16 [G, rows of an expert], added per expert before the activation; mxfp8_out=True:
+    (codes [M, N], packed scale words [N / 128, M]) as for gemm, rows outside every group left
+    unwritten (zero in freshly allocated outputs)."""
     import torch
     if not isinstance(a, torch.Tensor) or a.dim() != 2 or not isinstance(b, torch.Tensor) or b.dim() != 3:
         raise ValueError("a must be 2-D [M, K] and b 3-D [G, N, K] tensors of E4M3 codes")
@@ -364,14 +401,17 @@ def grouped_gemm(a, a_packed, b, b_packed, offsets, out=None, accumulate=False, 
     _require(offsets, "offsets", torch.int32, (G + 1,), dev)
     if accumulate and out is None:
         raise ValueError("accumulate=True needs out")
-    c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    if c.dtype != torch.bfloat16 or tuple(c.shape) != (M, N) or c.stride(1) != 1 or c.device != dev:
-        raise ValueError("out must be a BF16 [M, N] tensor with unit column stride on the operands' device")
     flags = _gemm_flags(accumulate, sqrelu, gelu, swiglu)
     if bias is not None:
         if accumulate:
             raise ValueError("bias and accumulate exclude each other")
         _require(bias, "bias", torch.bfloat16, (G, NB), dev)
+    if mxfp8_out:
+        return _mx_out(M, N, dev, accumulate, out, lambda q, p: mxfp8_grouped_gemm_mxfp8_out(
+            a, a_packed, b, b_packed, offsets, G, bias, q, N, p, M, N, K, flags, stream))
+    c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if c.dtype != torch.bfloat16 or tuple(c.shape) != (M, N) or c.stride(1) != 1 or c.device != dev:
+        raise ValueError("out must be a BF16 [M, N] tensor with unit column stride on the operands' device")
     with torch.cuda.device(dev):
         if bias is not None:
             mxfp8_grouped_gemm_bias(a, a_packed, b, b_packed, offsets, G, bias, c, c.stride(0), M, N, K, flags,

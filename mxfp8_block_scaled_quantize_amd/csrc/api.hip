@@ -67,8 +67,10 @@ mxfp8_status check_quantize(const void* x, int64_t rows, int64_t cols, int64_t l
   return MXFP8_OK;
 }
 
+// c / ldc: the output and its row stride in elements of out_bytes bytes (2 for
+// BF16, 1 for MXFP8 codes); rows must start 16-byte aligned.
 mxfp8_status check_gemm_common(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
-                               const void* c, int64_t ldc, int64_t M, int64_t N, int64_t K) {
+                               const void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, int out_bytes = 2) {
   if (M < 0 || N < 0 || K < 0) return MXFP8_ERR_SHAPE;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim || ldc > kMaxDim) return MXFP8_ERR_LIMIT;
   if (K > kMaxGemmK) return MXFP8_ERR_LIMIT;
@@ -76,7 +78,7 @@ mxfp8_status check_gemm_common(const uint8_t* a, const uint32_t* ap, const uint8
   if (M == 0 || N == 0) return MXFP8_OK;
   if (!c) return MXFP8_ERR_NULL;
   if (K > 0 && (!a || !ap || !b || !bp)) return MXFP8_ERR_NULL;
-  if (!aligned(c, 16) || ldc % 8) return MXFP8_ERR_MISALIGNED;
+  if (!aligned(c, 16) || (ldc * out_bytes) % 16) return MXFP8_ERR_MISALIGNED;
   if (K > 0 && (!aligned(a, 16) || !aligned(b, 16) || !aligned(ap, 4) || !aligned(bp, 4)))
     return MXFP8_ERR_MISALIGNED;
   return MXFP8_OK;
@@ -95,15 +97,19 @@ constexpr int64_t kMaxSwigluN = int64_t(1) << 27;
 
 // Every GEMM entry point: flags, shapes, pointers, grid; then one launch.
 // Dense when offsets == nullptr and G == 0.  with_bias: the bias entry points
-// (a bias is required, accumulate is rejected).
+// (a bias is required, accumulate is rejected).  mxo.q set: the MXFP8-output
+// entry points (c unused; the bias is optional, accumulate is rejected).
 mxfp8_status gemm_entry(const uint8_t* a, const uint32_t* a_packed, const uint8_t* b, const uint32_t* b_packed,
                         const int32_t* offsets, int32_t G, const void* bias, bool with_bias, void* c, int64_t ldc,
-                        int64_t M, int64_t N, int64_t K, uint32_t flags, void* stream) {
+                        int64_t M, int64_t N, int64_t K, uint32_t flags, void* stream,
+                        mx::MxOut mxo = mx::MxOut{nullptr, 0, nullptr}, bool mx_out = false) {
   if (!gemm_flags_ok(flags)) return MXFP8_ERR_FLAGS;
-  if (with_bias && (flags & MXFP8_GEMM_ACCUMULATE)) return MXFP8_ERR_FLAGS;
+  if ((with_bias || mx_out) && (flags & MXFP8_GEMM_ACCUMULATE)) return MXFP8_ERR_FLAGS;
   const bool grouped = G > 0;
-  const mxfp8_status st = check_gemm_common(a, a_packed, b, b_packed, c, ldc, M, N, K);
+  const mxfp8_status st = mx_out ? check_gemm_common(a, a_packed, b, b_packed, mxo.q, mxo.ldq, M, N, K, 1)
+                                 : check_gemm_common(a, a_packed, b, b_packed, c, ldc, M, N, K);
   if (st != MXFP8_OK) return st;
+  if (mx_out && N % 128) return MXFP8_ERR_SHAPE;   // whole packed scale words per row
   const bool swiglu = (flags & MXFP8_GEMM_SWIGLU) != 0;
   if (swiglu && N > kMaxSwigluN) return MXFP8_ERR_LIMIT;
   if (M == 0 || N == 0) return MXFP8_OK;
@@ -111,11 +117,13 @@ mxfp8_status gemm_entry(const uint8_t* a, const uint32_t* a_packed, const uint8_
   if (grouped && !aligned(offsets, 4)) return MXFP8_ERR_MISALIGNED;
   if (with_bias && !bias) return MXFP8_ERR_NULL;
   if (with_bias && !aligned(bias, 16)) return MXFP8_ERR_MISALIGNED;
+  if (mx_out && !mxo.qp) return MXFP8_ERR_NULL;
+  if (mx_out && !aligned(mxo.qp, 4)) return MXFP8_ERR_MISALIGNED;
   if (!mx::gemm_grid_fits(M, N, G, grouped, swiglu)) return MXFP8_ERR_LIMIT;
   return hip_status(mx::launch_gemm(a, a_packed, b, b_packed, static_cast<uint16_t*>(c), ldc, M, N, K,
                                     grouped ? offsets : nullptr, G, (flags & MXFP8_GEMM_ACCUMULATE) != 0,
                                     gemm_epilogue(flags), with_bias ? static_cast<const uint16_t*>(bias) : nullptr,
-                                    static_cast<hipStream_t>(stream)));
+                                    mx_out ? mxo : mx::MxOut{nullptr, 0, nullptr}, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -240,6 +248,23 @@ mxfp8_status mxfp8_grouped_gemm_bias(const uint8_t* a, const uint32_t* a_packed,
                                      void* stream) {
   if (G < 1 || G > 65536) return gemm_flags_ok(flags) ? MXFP8_ERR_SHAPE : MXFP8_ERR_FLAGS;
   return gemm_entry(a, a_packed, b, b_packed, offsets, G, bias, true, c, ldc, M_total, N, K, flags, stream);
+}
+
+mxfp8_status mxfp8_gemm_mxfp8_out(const uint8_t* a, const uint32_t* a_packed, const uint8_t* b,
+                                  const uint32_t* b_packed, const void* bias, uint8_t* q_out, int64_t ldq,
+                                  uint32_t* q_out_packed, int64_t M, int64_t N, int64_t K, uint32_t flags,
+                                  void* stream) {
+  return gemm_entry(a, a_packed, b, b_packed, nullptr, 0, bias, bias != nullptr, nullptr, 0, M, N, K, flags, stream,
+                    mx::MxOut{q_out, ldq, q_out_packed}, true);
+}
+
+mxfp8_status mxfp8_grouped_gemm_mxfp8_out(const uint8_t* a, const uint32_t* a_packed, const uint8_t* b,
+                                          const uint32_t* b_packed, const int32_t* offsets, int32_t G,
+                                          const void* bias, uint8_t* q_out, int64_t ldq, uint32_t* q_out_packed,
+                                          int64_t M_total, int64_t N, int64_t K, uint32_t flags, void* stream) {
+  if (G < 1 || G > 65536) return gemm_flags_ok(flags) ? MXFP8_ERR_SHAPE : MXFP8_ERR_FLAGS;
+  return gemm_entry(a, a_packed, b, b_packed, offsets, G, bias, bias != nullptr, nullptr, 0, M_total, N, K, flags,
+                    stream, mx::MxOut{q_out, ldq, q_out_packed}, true);
 }
 
 }  // extern "C"

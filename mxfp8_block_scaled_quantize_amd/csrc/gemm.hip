@@ -41,6 +41,9 @@
 // the same wave (see the SwiGLU DMA and epilogue below).  Accumulate (ACC)
 // adds the old C before the rounding; BIAS adds a BF16 value per B row (per
 // expert row for the grouped GEMM) to the fp32 sum before the activation.
+// MXO writes the output as MXFP8 instead of BF16: the staged BF16 tile (the
+// values the BF16 output would hold) is quantized row by row in 32-column
+// blocks on its way out, with the scales as packed words [N/128][M].
 #include <atomic>
 
 #include "mx_device.h"
@@ -98,13 +101,37 @@ struct ic {
   static constexpr int value = V;
 };
 
-template <bool GROUPED, bool ACC, int EPI, bool BIAS>
+// MXFP8 output of one 16-byte chunk of a staged BF16 output row: four
+// consecutive lanes hold a 32-column block, sixteen consecutive lanes (a DPP
+// row) the 128 columns of one packed scale word.  The block amax is the
+// integer max of the BF16 magnitudes over the quad, the scale byte and the
+// codes follow the quantizer's rowwise rule (the same device functions), and
+// the first lane of each 16-lane row assembles the word from the bytes of
+// lanes +4, +8, +12.  Every lane of a 16-lane row must execute this (the
+// reductions read the other lanes); row_ok only gates the stores.
+__device__ __forceinline__ void mx_out_chunk(u32x4 v, bool row_ok, uint8_t* q, uint32_t* word, bool word_lane) {
+  uint32_t m = pk_max_u16(pk_max_u16(abs_bits2(v.x), abs_bits2(v.y)), pk_max_u16(abs_bits2(v.z), abs_bits2(v.w)));
+  m = max(m & 0xFFFFu, m >> 16);
+  m = quad_max(m);
+  const uint32_t byte = scale_byte_from_amax(m);
+  const uint2 o = quantize8(make_uint4(v.x, v.y, v.z, v.w), byte);
+  const uint32_t b1 = (uint32_t)__shfl_down((int)byte, 4u, 16);
+  const uint32_t b2 = (uint32_t)__shfl_down((int)byte, 8u, 16);
+  const uint32_t b3 = (uint32_t)__shfl_down((int)byte, 12u, 16);
+  if (row_ok) {
+    *reinterpret_cast<uint2*>(q) = o;
+    if (word_lane) *word = byte | (b1 << 8) | (b2 << 16) | (b3 << 24);
+  }
+}
+
+template <bool GROUPED, bool ACC, int EPI, bool BIAS, bool MXO>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
                  const uint8_t* __restrict__ B, const uint32_t* __restrict__ Bp,
                  uint16_t* __restrict__ Cm, int64_t ldc, int64_t M, int64_t N, int64_t K,
                  const int32_t* __restrict__ offsets, int32_t G, int64_t tiles_m, int64_t tiles_n,
-                 const uint16_t* __restrict__ bias) {
+                 const uint16_t* __restrict__ bias, uint8_t* __restrict__ Q, int64_t ldq,
+                 uint32_t* __restrict__ Qp) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
   lds_u8* smem = (lds_u8*)smem_raw;
 
@@ -497,7 +524,10 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
 #pragma unroll
       for (int k = 0; k < 16; k++) {
         const int64_t grow = m_lo + erow0 + 16 * k;
-        if (full_rows || grow < m_hi) store_nt16(Cm + grow * ldc + ecol, make_uint4(v[k].x, v[k].y, v[k].z, v[k].w));
+        if constexpr (MXO)   // a 16-lane row is one output row's 128 columns: one scale word
+          mx_out_chunk(v[k], full_rows || grow < m_hi, Q + grow * ldq + ecol, Qp + (n0 >> 7) * M + grow, ech == 0);
+        else if (full_rows || grow < m_hi)
+          store_nt16(Cm + grow * ldc + ecol, make_uint4(v[k].x, v[k].y, v[k].z, v[k].w));
       }
     }
     return;
@@ -594,7 +624,11 @@ void gemm_kernel(const uint8_t* __restrict__ A, const uint32_t* __restrict__ Ap,
 #pragma unroll
       for (int k = 0; k < 16; k++) {
         const int64_t grow = m_lo + erow0 + 8 * (kb + k);
-        if (full_rows || grow < m_hi) store_nt16(Cm + grow * ldc + ecol, make_uint4(v[k].x, v[k].y, v[k].z, v[k].w));
+        if constexpr (MXO)   // lanes 16 t .. 16 t + 15 of a row: scale word n0 / 128 + t
+          mx_out_chunk(v[k], full_rows || grow < m_hi, Q + grow * ldq + ecol,
+                       Qp + ((n0 >> 7) + (ech >> 4)) * M + grow, (ech & 15) == 0);
+        else if (full_rows || grow < m_hi)
+          store_nt16(Cm + grow * ldc + ecol, make_uint4(v[k].x, v[k].y, v[k].z, v[k].w));
       }
     }
   }
@@ -606,10 +640,10 @@ bool gemm_grid_fits(int64_t M, int64_t N, int32_t G, bool grouped, bool swiglu) 
   return grid_fits(tm, tn, 256);
 }
 
-template <bool GROUPED, bool ACC, int EPI, bool BIAS>
+template <bool GROUPED, bool ACC, int EPI, bool BIAS, bool MXO>
 static hipError_t launch_gemm_t(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
                                 uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, const int32_t* offsets,
-                                int32_t G, int64_t tiles_m, int64_t tiles_n, const uint16_t* bias,
+                                int32_t G, int64_t tiles_m, int64_t tiles_n, const uint16_t* bias, MxOut mxo,
                                 hipStream_t stream) {
   // The dynamic-LDS opt-in is set once per device (bit d of the mask, for
   // device ids below 64; others set it on every launch), race-free across
@@ -620,27 +654,31 @@ static hipError_t launch_gemm_t(const uint8_t* a, const uint32_t* ap, const uint
   if (e != hipSuccess) return e;
   const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
   if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<GROUPED, ACC, EPI, BIAS>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<GROUPED, ACC, EPI, BIAS, MXO>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_done.fetch_or(bit, std::memory_order_release);
   }
-  hipLaunchKernelGGL((gemm_kernel<GROUPED, ACC, EPI, BIAS>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256),
-                     LDS_BYTES, stream, a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, bias);
+  hipLaunchKernelGGL((gemm_kernel<GROUPED, ACC, EPI, BIAS, MXO>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256),
+                     LDS_BYTES, stream, a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, bias, mxo.q,
+                     mxo.ldq, mxo.qp);
   return hipGetLastError();
 }
 
-// One launch for an (epilogue, bias) pair of a dense or grouped GEMM.
-template <bool GROUPED>
-static hipError_t launch_gemm_g(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
+// One launch for an (epilogue, bias, output format) choice of a dense or
+// grouped GEMM.
+template <bool GROUPED, bool MXO>
+static hipError_t launch_gemm_o(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
                                 uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, const int32_t* offsets,
                                 int32_t G, int64_t tiles_m, int64_t tiles_n, bool accumulate, int epilogue,
-                                const uint16_t* bias, hipStream_t stream) {
+                                const uint16_t* bias, MxOut mxo, hipStream_t stream) {
 #define MX_G_LAUNCH(AC, EP, BI) \
-  launch_gemm_t<GROUPED, AC, EP, BI>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, bias, stream)
+  launch_gemm_t<GROUPED, AC, EP, BI, MXO>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, bias, mxo, \
+                                          stream)
   // accumulate, the epilogues and the bias: the API rejects accumulate
-  // together with any of the others
-  if (accumulate) return MX_G_LAUNCH(true, 0, false);
+  // together with any of the others, and with the MXFP8 output
+  if constexpr (!MXO)
+    if (accumulate) return MX_G_LAUNCH(true, 0, false);
   if (bias)
     return epilogue == 1 ? MX_G_LAUNCH(false, 1, true)
          : epilogue == 2 ? MX_G_LAUNCH(false, 2, true)
@@ -653,18 +691,29 @@ static hipError_t launch_gemm_g(const uint8_t* a, const uint32_t* ap, const uint
 #undef MX_G_LAUNCH
 }
 
+template <bool GROUPED>
+static hipError_t launch_gemm_g(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
+                                uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, const int32_t* offsets,
+                                int32_t G, int64_t tiles_m, int64_t tiles_n, bool accumulate, int epilogue,
+                                const uint16_t* bias, MxOut mxo, hipStream_t stream) {
+  return mxo.q ? launch_gemm_o<GROUPED, true>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n,
+                                               accumulate, epilogue, bias, mxo, stream)
+               : launch_gemm_o<GROUPED, false>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n,
+                                                accumulate, epilogue, bias, mxo, stream);
+}
+
 hipError_t launch_gemm(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
                        uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
                        const int32_t* offsets, int32_t G, bool accumulate, int epilogue, const uint16_t* bias,
-                       hipStream_t stream) {
+                       MxOut mxo, hipStream_t stream) {
   const bool grouped = offsets != nullptr;
   const int64_t tiles_n = epilogue == 3 ? (N + SW_TN - 1) / SW_TN : (N + BN - 1) / BN;
   const int64_t tiles_m = (M + BM - 1) / BM + (grouped ? (int64_t)G : 0);
   if (tiles_m * tiles_n == 0) return hipSuccess;
   return grouped ? launch_gemm_g<true>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, accumulate,
-                                       epilogue, bias, stream)
+                                       epilogue, bias, mxo, stream)
                  : launch_gemm_g<false>(a, ap, b, bp, c, ldc, M, N, K, offsets, G, tiles_m, tiles_n, accumulate,
-                                        epilogue, bias, stream);
+                                        epilogue, bias, mxo, stream);
 }
 
 }  // namespace mx

@@ -43,15 +43,24 @@ hipError_t launch_pack_scales(const uint8_t* s, int64_t dim, int64_t k, int64_t 
                               hipStream_t stream);
 bool pack_scales_grid_fits(int64_t dim, int64_t k);
 
+// MXFP8 output of the GEMM (rowwise copy): codes q [M][ldq] bytes and packed
+// scale words qp [N/128][M]; q == nullptr selects the BF16 output c.
+struct MxOut {
+  uint8_t* q;
+  int64_t ldq;
+  uint32_t* qp;
+};
+
 // Dense (offsets == nullptr) or grouped GEMM; accumulate adds the product to C; epilogue 1 writes
 // relu(product)^2, 2 writes GELU(product), 3 writes SiLU(gate) * up with B holding 2N rows (gate rows,
 // then up rows; per group when grouped) and N the output columns (none together with accumulate).
 // bias (optional, BF16, one value per B row, per group when grouped) is added to the fp32 sum before
-// the epilogue (not together with accumulate).
+// the epilogue (not together with accumulate).  mxo.q set: the output is written as MXFP8 (N % 128 == 0,
+// not together with accumulate) instead of to c.
 hipError_t launch_gemm(const uint8_t* a, const uint32_t* ap, const uint8_t* b, const uint32_t* bp,
                        uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
                        const int32_t* offsets, int32_t G, bool accumulate, int epilogue, const uint16_t* bias,
-                       hipStream_t stream);
+                       MxOut mxo, hipStream_t stream);
 bool gemm_grid_fits(int64_t M, int64_t N, int32_t G, bool grouped, bool swiglu);
 
 }  // namespace mx

@@ -263,6 +263,32 @@ def test_gemm_bias_validation(L):
     assert GB(A16, A16, A16, A16, None, 4, None, A16, 64, 0, 64, 128, 0, None) == OK
 
 
+def test_gemm_mxfp8_out_validation(L):
+    """The MXFP8-output GEMMs: the _ex rules with a byte-element output (row
+    stride a multiple of 16 bytes), whole packed scale words (N % 128), a
+    packed-scale pointer, an optional bias, and no accumulate."""
+    X = L.mxfp8_gemm_mxfp8_out
+    assert X(A16, A16, A16, A16, None, A16, 128, A16, 64, 128, 128, 1, None) == FLAGS      # accumulate
+    assert X(A16, A16, A16, A16, None, A16, 128, A16, 64, 128, 128, 16, None) == FLAGS
+    assert X(A16, A16, A16, A16, None, A16, 96, A16, 64, 96, 128, 0, None) == SHAPE       # N % 128
+    assert X(A16, A16, A16, A16, None, A16, 64, A16, 64, 128, 128, 0, None) == SHAPE      # ldq < N
+    assert X(A16, A16, A16, A16, None, None, 128, A16, 64, 128, 128, 0, None) == NULL     # codes
+    assert X(A16, A16, A16, A16, None, A16, 128, None, 64, 128, 128, 0, None) == NULL     # packed scales
+    assert X(A16, A16, A16, A16, None, A16, 136, A16, 64, 128, 128, 0, None) == MISALIGNED   # ldq % 16
+    assert X(A16, A16, A16, A16, None, A16 + 8, 128, A16, 64, 128, 128, 0, None) == MISALIGNED
+    assert X(A16, A16, A16, A16, None, A16, 128, A16 + 2, 64, 128, 128, 0, None) == MISALIGNED
+    assert X(A16, A16, A16, A16, A16 + 2, A16, 128, A16, 64, 128, 128, 0, None) == MISALIGNED   # bias
+    assert X(A16, A16, A16, A16, None, None, 128, None, 0, 128, 128, 0, None) == OK       # empty
+    assert X(A16, A16, A16, A16, None, A16, (1 << 27) + 128, A16, 64, (1 << 27) + 128, 128, 8, None) == LIMIT
+    XG = L.mxfp8_grouped_gemm_mxfp8_out
+    assert XG(A16, A16, A16, A16, A16, 0, None, A16, 128, A16, 64, 128, 128, 0, None) == SHAPE
+    assert XG(A16, A16, A16, A16, A16, 4, None, A16, 128, A16, 64, 128, 128, 1, None) == FLAGS
+    assert XG(A16, A16, A16, A16, None, 4, None, A16, 128, A16, 64, 128, 128, 0, None) == NULL   # offsets
+    assert XG(A16, A16, A16, A16, A16, 4, None, A16, 128, None, 64, 128, 128, 0, None) == NULL
+    assert XG(A16, A16, A16, A16, A16, 4, None, A16, 160, A16, 64, 160, 128, 0, None) == SHAPE   # N % 128
+    assert XG(A16, A16, A16, A16, None, 4, None, None, 128, None, 0, 128, 128, 0, None) == OK
+
+
 def test_binding_raises_on_error(L):
     with pytest.raises(mx.MXFP8Error) as ei:
         mx.mxfp8_quantize(A16, 64, 48, 64, ROW, A16, A16, stream=0)
