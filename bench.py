@@ -17,14 +17,16 @@ row+col, 1.09 GB) against the HBM peak; ``cpu_baseline`` is the CPU oracle
 running whole steps of the same workload on the host.  Per-launch times are
 reported as mean, median, min and max over the timed steps.
 
-``--workload dense|backward|moe|moe_sqrelu|moe_swiglu|linear|mlp|mlp_gelu`` measures the other
+``--workload dense|backward|moe|moe_sqrelu|moe_swiglu|linear|mlp|mlp_gelu|mlp_fwd`` measures the other
 workloads the same way: rowwise quantize and the TN GEMMs 8192x14336x4096 and
 8192^3; row+col+dbias quantize and the wgrad GEMM on the columnwise copies;
 the ragged grouped MoE GEMM (also with the squared-ReLU or the SwiGLU
 epilogue of an MoE first projection); one MXFP8 linear-layer training step (fprop, dgrad, wgrad
 accumulated into a BF16 main gradient); one squared-ReLU (or GELU) MLP
 training step (six GEMMs, the activation and its backward fused into the
-quantize launches).  They are reporting aids next to the default line.
+quantize launches); the GELU MLP's inference forward (FC1 writing its GELU
+output as MXFP8, FC2 reading it).  They are reporting aids next to the
+default line.
 """
 
 import argparse
@@ -48,7 +50,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="stress",
                    choices=["stress", "dense", "backward", "moe", "moe_sqrelu", "moe_swiglu", "linear", "mlp",
-                            "mlp_gelu"])
+                            "mlp_gelu", "mlp_fwd"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU-oracle time: whole oracle steps are repeated until reached "
@@ -252,6 +254,30 @@ def build_ops(workload, dev):
                 "W2 N(0,0.02), dY N(0,1); row+col quantize of X, W1, W2, dY; FC1 GEMM; the activation fused into "
                 "the quantize of its BF16 output; FC2 GEMM; FC2 dgrad and wgrad; the activation's backward fused "
                 "into the row+col+dbias quantize of FC2's dgrad output; FC1 dgrad and wgrad" % (fname, T, D, F))
+    elif workload == "mlp_fwd":
+        lin = workloads.mlp()
+        host = lin
+        T, D = lin["X"].shape
+        F = lin["W1"].shape[0]
+        # inference: the weights are quantized once, before the steps
+        w1 = mx.quantize(upload(lin["W1"]), rowwise=True, packed=True)
+        w2 = mx.quantize(upload(lin["W2"]), rowwise=True, packed=True)
+        keep.extend([w1, w2])
+        bx = quantize_op("X[%dx%d]" % (T, D), lin["X"], ROW, packed=True)
+        hq = torch.empty((T, F), dtype=torch.uint8, device=dev)
+        hp = torch.empty((F // 128, T), dtype=torch.int32, device=dev)
+        y = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+        keep.extend([hq, hp, y])
+        dominant = "fc1 gelu mxfp8-out %dx%dx%d" % (T, F, D)
+        ops.append(Op("gemm", dominant, lambda st: mx.mxfp8_gemm_mxfp8_out(
+            bx["q"], bx["p"], w1["q_row"], w1["p_row"], None, hq, F, hp, T, F, D, mx.MXFP8_GEMM_GELU, stream=st),
+            2.0 * T * F * D))
+        ops.append(Op("gemm", "fc2 %dx%dx%d" % (T, D, F), lambda st: mx.mxfp8_gemm_ex(
+            hq, hp, w2["q_row"], w2["p_row"], y, D, T, D, F, 0, stream=st), 2.0 * T * D * F))
+        desc = ("GELU MLP inference forward, tokens %d, d_model %d, d_ff %d: X N(0,1), W1 and W2 N(0,0.02) "
+                "quantized once before the steps; per step the rowwise quantize of X into packed scales, FC1 "
+                "GEMM with the GELU epilogue writing its output as MXFP8 (rowwise codes + packed scale words), "
+                "FC2 GEMM on those codes with BF16 output" % (T, D, F))
     elif workload == "moe_swiglu":
         d = workloads.moe()
         host = d
@@ -626,6 +652,18 @@ def oracle_step(workload, h):
             oracle.gemm_tn(qd, sd, qwT, swT, panel=P)
             oracle.gemm_tn(qdT, sdT, qxT, sxT, panel=P)
         return step, "row+col quantize of X, W, dY, scale packing, fp64 fprop, dgrad and wgrad"
+    if workload == "mlp_fwd":
+        q1, s1 = rowp(h["W1"])
+        q2, s2 = rowp(h["W2"])
+
+        def step():
+            qx, sx = rowp(h["X"])
+            hv = oracle.gelu_epilogue(oracle.gemm_tn(qx, sx, q1, s1, panel=P)).astype(np.float32)
+            qh, sh = oracle.quantize_rowwise_values(hv)
+            oracle.pack_scales(sh)
+            oracle.gemm_tn(qh, sh, q2, s2, panel=P)
+        return step, ("rowwise quantize of X with scale packing, fp64 FC1 GEMM, GELU, rowwise quantize of the "
+                      "result with scale packing, fp64 FC2 GEMM (weights quantized once, outside the steps)")
     if workload in ("mlp", "mlp_gelu"):
         act, dact = ((oracle.act_gelu, oracle.dact_gelu) if workload == "mlp_gelu"
                      else (oracle.act_sqrelu, oracle.dact_sqrelu))

@@ -182,3 +182,19 @@ def test_helper_returns_codes_and_words():
     q, p = mx.gemm(qa, pa, qb, pb, gelu=True, mxfp8_out=True)
     (fq, fp), _, _ = fused_and_unfused(qa, pa, qb, pb, M, N, K, "gelu")
     assert np.array_equal(to_host(q), fq) and np.array_equal(words(p), fp)
+
+
+def test_full_size_mlp_fc1_gelu():
+    """The GELU MLP's first projection at full size (8192 x 14336 x 4096, the
+    inference-forward workload of bench.py): fused output equals the quantized
+    BF16 output on every entry (the BF16 GELU output itself is checked
+    against the oracle in test_gpu_gemm.py)."""
+    need_gpu()
+    lin = workloads.mlp()
+    T, D = lin["X"].shape
+    F = lin["W1"].shape[0]
+    qx, _, px = quantize_on_gpu(lin["X"])
+    qw, _, pw = quantize_on_gpu(lin["W1"])
+    log("mxfp8 out full size fc1 gelu %dx%dx%d" % (T, F, D))
+    (q, p), (rq, rp), _ = fused_and_unfused(qx, px, qw, pw, T, F, D, "gelu")
+    assert np.array_equal(q, rq) and np.array_equal(p, rp)
