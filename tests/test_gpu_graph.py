@@ -26,7 +26,8 @@ class Chain:
     epilogue (W's rows read as N/2 gate rows then N/2 up rows), and GELU and its
     backward fused into row+col quantizes of the GEMM output (the backward
     with dbias, taking that output as both gradient and activation input), and
-    the grouped GEMM with a per-expert bias and the SwiGLU epilogue."""
+    the grouped GEMM with a per-expert bias and the SwiGLU epilogue, and the
+    dense GEMM with the GELU epilogue writing MXFP8 (codes + packed scales)."""
 
     def __init__(self, torch, T, N, K):
         self.T, self.N, self.K = T, N, K
@@ -53,6 +54,8 @@ class Chain:
         self.cswi = torch.empty((T, N // 2), dtype=torch.bfloat16, device=dev)
         self.bias = to_dev_bf16(workloads.normal_bf16((2, N // 2), 5, std=1.0))   # a bias row per expert
         self.cbias = torch.empty((T, N // 4), dtype=torch.bfloat16, device=dev)
+        self.qmx = torch.empty((T, N), dtype=torch.uint8, device=dev)
+        self.pmx = torch.empty((N // 128, T), dtype=torch.int32, device=dev)
         for name in ("h", "dh"):
             o = {"q": torch.empty((T, N), dtype=torch.uint8, device=dev),
                  "p": torch.empty((N // 128, T), dtype=torch.int32, device=dev),
@@ -81,6 +84,8 @@ class Chain:
         # W's N rows as two experts of N/2 rows, each N/4 gate rows then N/4 up rows, with their own bias rows
         mx.mxfp8_grouped_gemm_bias(x["q"], x["p"], w["q"], w["p"], self.offsets, 2, self.bias, self.cbias, N // 4,
                                    T, N // 4, K, mx.MXFP8_GEMM_SWIGLU)
+        mx.mxfp8_gemm_mxfp8_out(x["q"], x["p"], w["q"], w["p"], None, self.qmx, N, self.pmx, T, N, K,
+                                mx.MXFP8_GEMM_GELU)
         h, dh = self.out["h"], self.out["dh"]
         mx.mxfp8_quantize_ex(self.c, T, N, N, ROW | COL | AMAX | PACKED | mx.MXFP8_ACT_GELU, h["q"], h["p"],
                              h["qT"], h["pT"], None, h["amax"], None, None, None, 0)
@@ -89,7 +94,8 @@ class Chain:
 
     def snapshot(self):
         snap = {"c": self.c.clone(), "cg": self.cg.clone(), "cw": self.cw.clone(), "cgelu": self.cgelu.clone(),
-                "cswi": self.cswi.clone(), "cbias": self.cbias.clone()}
+                "cswi": self.cswi.clone(), "cbias": self.cbias.clone(), "qmx": self.qmx.clone(),
+                "pmx": self.pmx.clone()}
         for name, o in self.out.items():
             for k in ("q", "p", "qT", "pT", "db", "amax"):
                 if not (name == "h" and k == "db") and not (name == "dh" and k == "amax"):
@@ -165,6 +171,8 @@ def test_graph_replay_matches_eager():
             o["amax"].fill_(-7.0)
         for t in (ch.c, ch.cg, ch.cw, ch.cgelu, ch.cswi, ch.cbias):
             t.fill_(float("nan"))
+        ch.qmx.fill_(0xA5)
+        ch.pmx.fill_(-1)
         torch.cuda.synchronize()
         log("replay %d" % rep)
         g.replay()

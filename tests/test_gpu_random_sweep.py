@@ -219,3 +219,31 @@ def test_random_grouped_gemm_bias(case):
     epi = EPIS[seed % 4]
     grouped_case(M, N, K, list(counts), seed, bias=True, sqrelu=epi == "sqrelu", gelu=epi == "gelu",
                  swiglu=epi == "swiglu")
+
+
+def mxout_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        M = int(rng.integers(1, 700))
+        N = 128 * int(rng.integers(1, 6))
+        K = 128 * int(rng.integers(1, 9))
+        ldq = N + 16 * int(rng.integers(0, 3))
+        cases.append((M, N, K, ldq, EPIS[int(rng.integers(0, 4))], bool(rng.integers(0, 2)),
+                      int(rng.integers(0, 1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("case", mxout_cases(12, 81))
+def test_random_gemm_mxfp8_out(case):
+    """The MXFP8-output GEMM equals the rowwise packed quantize of the BF16
+    output, random shapes, row strides, epilogues and biases."""
+    from test_gpu_gemm_mxout import fused_and_unfused
+    M, N, K, ldq, epi, with_bias, seed = case
+    log("random mxfp8 out M=%d N=%d K=%d ldq=%d %s bias=%d seed=%d" % case)
+    NB = 2 * N if epi == "swiglu" else N
+    qa, _, pa = quantize_on_gpu(workloads.normal_bf16((M, K), seed))
+    qb, _, pb = quantize_on_gpu(workloads.normal_bf16((NB, K), seed + 1, std=0.25))
+    bias = to_dev_bf16(workloads.normal_bf16((NB,), seed + 2, std=1.0)) if with_bias else None
+    (q, p), (rq, rp), _ = fused_and_unfused(qa, pa, qb, pb, M, N, K, epi, bias, ldq=ldq)
+    assert np.array_equal(q, rq) and np.array_equal(p, rp)
