@@ -107,7 +107,7 @@ struct ic {
 // integer max of the BF16 magnitudes over the quad, the scale byte and the
 // codes follow the quantizer's rowwise rule (the same device functions), and
 // the first lane of each 16-lane row assembles the word from the bytes of
-// lanes +4, +8, +12.  Every lane of a 16-lane row must execute this (the
+// lanes +4, +8, +12 (DPP row shifts).  Every lane of a 16-lane row must execute this (the
 // reductions read the other lanes); row_ok only gates the stores.
 __device__ __forceinline__ void mx_out_chunk(u32x4 v, bool row_ok, uint8_t* q, uint32_t* word, bool word_lane) {
   uint32_t m = pk_max_u16(pk_max_u16(abs_bits2(v.x), abs_bits2(v.y)), pk_max_u16(abs_bits2(v.z), abs_bits2(v.w)));
@@ -115,9 +115,10 @@ __device__ __forceinline__ void mx_out_chunk(u32x4 v, bool row_ok, uint8_t* q, u
   m = quad_max(m);
   const uint32_t byte = scale_byte_from_amax(m);
   const uint2 o = quantize8(make_uint4(v.x, v.y, v.z, v.w), byte);
-  const uint32_t b1 = (uint32_t)__shfl_down((int)byte, 4u, 16);
-  const uint32_t b2 = (uint32_t)__shfl_down((int)byte, 8u, 16);
-  const uint32_t b3 = (uint32_t)__shfl_down((int)byte, 12u, 16);
+  // DPP row_shl:n (lane i reads lane i + n of its 16-lane row)
+  const uint32_t b1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)byte, 0x104, 0xF, 0xF, true);
+  const uint32_t b2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)byte, 0x108, 0xF, 0xF, true);
+  const uint32_t b3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)byte, 0x10C, 0xF, 0xF, true);
   if (row_ok) {
     *reinterpret_cast<uint2*>(q) = o;
     if (word_lane) *word = byte | (b1 << 8) | (b2 << 16) | (b3 << 24);
