@@ -4,7 +4,8 @@
  * MXFP8 block-scaled quantization (BF16 -> E4M3 codes + one E8M0 scale per
  * 32 consecutive elements along the reduction direction, rowwise and
  * columnwise, optional fused dbias) and the block-scaled MXFP8 GEMM
- * (fp32 accumulation, BF16 output; dense and ragged grouped).
+ * (fp32 accumulation, BF16 output or its rowwise MXFP8 copy; dense and
+ * ragged grouped; optional accumulate, bias and activation epilogues).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -23,7 +24,8 @@
  *    available from mxfp8_last_hip_error()).
  *  - Empty problems (a zero dimension) are valid no-ops, except that
  *    outputs that are mathematically defined (a dbias over zero rows, a GEMM
- *    with K = 0) are written as zeros.
+ *    with K = 0) are written: zeros, or the epilogue of the bias for a GEMM
+ *    with a bias.
  *
  * Numerics (OCP MX reading of the pages: the block size, E8M0 scales, E4M3
  * data and the rowwise / columnwise / dbias options come from the page
@@ -251,10 +253,12 @@ mxfp8_status mxfp8_pack_scales(const uint8_t *s, int64_t dim, int64_t k, int64_t
  * Block-scaled GEMM (TN)
  *
  * Defining passage: MXFP8 x MXFP8 -> BF16 on the gfx950 scaled FP8 MFMA,
- * with only alpha = 1 and beta = 0 supported (no accumulate, bias or output
- * epilogue), TN layout with both operands K-major ("Experimental FlyDSL GEMM
- * backend for TE PyTorch (BF16/FP16/FP32/FP8/MXFP8)", Summary and the review
- * of the epilogue validation).
+ * where the FlyDSL backend supports only alpha = 1 and beta = 0 (no
+ * accumulate, bias or output quantization), TN layout with both operands
+ * K-major ("Experimental FlyDSL GEMM backend for TE PyTorch
+ * (BF16/FP16/FP32/FP8/MXFP8)", Summary and the review of the epilogue
+ * validation).  mxfp8_gemm is that operation; the _ex, _bias and _mxfp8_out
+ * entry points below add the options the review finds missing.
  *
  *   C[m][n] = bf16_rne( sum_k dq(A)[m][k] * dq(B)[n][k] ),  fp32 accumulation.
  * ------------------------------------------------------------------------ */
