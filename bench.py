@@ -17,7 +17,7 @@ row+col, 1.09 GB) against the HBM peak; ``cpu_baseline`` is the CPU oracle
 running whole steps of the same workload on the host.  Per-launch times are
 reported as mean, median, min and max over the timed steps.
 
-``--workload dense|backward|moe|moe_sqrelu|moe_swiglu|linear|mlp|mlp_gelu|mlp_fwd`` measures the other
+``--workload dense|backward|moe|moe_sqrelu|moe_swiglu|linear|mlp|mlp_gelu|mlp_fwd|moe_fwd`` measures the other
 workloads the same way: rowwise quantize and the TN GEMMs 8192x14336x4096 and
 8192^3; row+col+dbias quantize and the wgrad GEMM on the columnwise copies;
 the ragged grouped MoE GEMM (also with the squared-ReLU or the SwiGLU
@@ -25,7 +25,8 @@ epilogue of an MoE first projection); one MXFP8 linear-layer training step (fpro
 accumulated into a BF16 main gradient); one squared-ReLU (or GELU) MLP
 training step (six GEMMs, the activation and its backward fused into the
 quantize launches); the GELU MLP's inference forward (FC1 writing its GELU
-output as MXFP8, FC2 reading it).  They are reporting aids next to the
+output as MXFP8, FC2 reading it) and the MoE block's (the grouped first
+projection writing its SwiGLU output as MXFP8 for the grouped second).  They are reporting aids next to the
 default line.
 """
 
@@ -50,7 +51,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="stress",
                    choices=["stress", "dense", "backward", "moe", "moe_sqrelu", "moe_swiglu", "linear", "mlp",
-                            "mlp_gelu", "mlp_fwd"])
+                            "mlp_gelu", "mlp_fwd", "moe_fwd"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU-oracle time: whole oracle steps are repeated until reached "
@@ -278,6 +279,37 @@ def build_ops(workload, dev):
                 "quantized once before the steps; per step the rowwise quantize of X into packed scales, FC1 "
                 "GEMM with the GELU epilogue writing its output as MXFP8 (rowwise codes + packed scale words), "
                 "FC2 GEMM on those codes with BF16 output" % (T, D, F))
+    elif workload == "moe_fwd":
+        d = workloads.moe()
+        w2h = workloads.moe_fc2()["W2"]
+        host = dict(d, W2=w2h)
+        G, NB, K = d["W"].shape
+        N = NB // 2
+        D = w2h.shape[1]
+        Mt = d["X"].shape[0]
+        # inference: the expert weights are quantized once, before the steps
+        w1 = mx.quantize(upload(d["W"].reshape(G * NB, K)), rowwise=True, packed=True)
+        w2 = mx.quantize(upload(w2h.reshape(G * D, N)), rowwise=True, packed=True)
+        keep.extend([w1, w2])
+        bx = quantize_op("X[%dx%d]" % (Mt, K), d["X"], ROW, packed=True)
+        off = torch.from_numpy(d["offsets"]).to(dev)
+        hq = torch.empty((Mt, N), dtype=torch.uint8, device=dev)
+        hp = torch.empty((N // 128, Mt), dtype=torch.int32, device=dev)
+        y = torch.empty((Mt, D), dtype=torch.bfloat16, device=dev)
+        keep.extend([off, hq, hp, y])
+        tokens = int(d["offsets"][-1] - d["offsets"][0])
+        dominant = "grouped fc1 swiglu mxfp8-out %dx%dx%d G=%d" % (Mt, NB, K, G)
+        ops.append(Op("gemm", dominant, lambda st: mx.mxfp8_grouped_gemm_mxfp8_out(
+            bx["q"], bx["p"], w1["q_row"], w1["p_row"], off, G, None, hq, N, hp, Mt, N, K, mx.MXFP8_GEMM_SWIGLU,
+            stream=st), 2.0 * tokens * NB * K))
+        ops.append(Op("gemm", "grouped fc2 %dx%dx%d G=%d" % (Mt, D, N, G), lambda st: mx.mxfp8_grouped_gemm_ex(
+            hq, hp, w2["q_row"], w2["p_row"], off, G, y, D, Mt, D, N, 0, stream=st), 2.0 * tokens * D * N))
+        desc = ("MoE block inference forward over %d experts (token counts %s): X[%dx%d] N(0,1); W1[%d][%dx%d] "
+                "(per expert %d gate rows, then %d up rows) and W2[%d][%dx%d] N(0,0.02) quantized once before the "
+                "steps; per step the rowwise quantize of X into packed scales, the grouped first projection with "
+                "the SwiGLU epilogue writing MXFP8 [%dx%d], the grouped second projection on those codes with "
+                "BF16 output [%dx%d]" % (G, np.diff(d["offsets"]).tolist(), Mt, K, G, NB, K, N, N, G, D, N, Mt, N,
+                                         Mt, D))
     elif workload == "moe_swiglu":
         d = workloads.moe()
         host = d
@@ -652,6 +684,22 @@ def oracle_step(workload, h):
             oracle.gemm_tn(qd, sd, qwT, swT, panel=P)
             oracle.gemm_tn(qdT, sdT, qxT, sxT, panel=P)
         return step, "row+col quantize of X, W, dY, scale packing, fp64 fprop, dgrad and wgrad"
+    if workload == "moe_fwd":
+        G = h["W"].shape[0]
+        w1 = [rowp(w) for w in h["W"]]
+        w2 = [rowp(w) for w in h["W2"]]
+        q1, s1 = np.stack([q for q, _ in w1]), np.stack([s for _, s in w1])
+        q2, s2 = np.stack([q for q, _ in w2]), np.stack([s for _, s in w2])
+
+        def step():
+            qx, sx = rowp(h["X"])
+            hv = oracle.swiglu_epilogue(oracle.grouped_gemm_tn(qx, sx, q1, s1, h["offsets"], panel=P))
+            qh, sh = oracle.quantize_rowwise_values(np.nan_to_num(hv).astype(np.float32))
+            oracle.pack_scales(sh)
+            oracle.grouped_gemm_tn(qh, sh, q2, s2, h["offsets"], panel=P)
+        return step, ("rowwise quantize of X with scale packing, fp64 grouped first projection, SwiGLU, rowwise "
+                      "quantize of the result with scale packing, fp64 grouped second projection (expert weights "
+                      "quantized once, outside the steps)")
     if workload == "mlp_fwd":
         q1, s1 = rowp(h["W1"])
         q2, s2 = rowp(h["W2"])

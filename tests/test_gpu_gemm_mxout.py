@@ -198,3 +198,21 @@ def test_full_size_mlp_fc1_gelu():
     log("mxfp8 out full size fc1 gelu %dx%dx%d" % (T, F, D))
     (q, p), (rq, rp), _ = fused_and_unfused(qx, px, qw, pw, T, F, D, "gelu")
     assert np.array_equal(q, rq) and np.array_equal(p, rp)
+
+
+def test_full_size_moe_fc1_swiglu():
+    """The MoE block's first projection at full size (16384 routed rows, 8
+    experts of 7168 gate + 7168 up rows, K = 4096, the moe_fwd workload of
+    bench.py): the grouped fused output equals the quantized BF16 output on
+    every entry (the BF16 SwiGLU output is checked against the oracle in
+    test_gpu_gemm.py)."""
+    need_gpu()
+    d = workloads.moe()
+    G, NB, K = d["W"].shape
+    M = d["X"].shape[0]
+    qx, _, px = quantize_on_gpu(d["X"])
+    wq = quantize_on_gpu(d["W"].reshape(G * NB, K))
+    log("mxfp8 out full size moe fc1 swiglu %dx%dx%d G=%d" % (M, NB, K, G))
+    (q, p), (rq, rp), _ = fused_and_unfused(qx, px, wq[0].view(G, NB, K), wq[2], M, NB // 2, K, "swiglu",
+                                            offsets=to_dev(d["offsets"]), G=G)
+    assert np.array_equal(q, rq) and np.array_equal(p, rp)

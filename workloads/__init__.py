@@ -208,6 +208,12 @@ def moe(empty_groups: bool = False):
     return {"X": x, "W": w, "offsets": off}
 
 
+def moe_fc2():
+    """The MoE block's second projection: per expert W2 [4096][7168] (d_model
+    x the SwiGLU output width of the first projection), N(0, 0.02)."""
+    return {"W2": normal_bf16((8, 4096, 7168), 5, std=0.02)}
+
+
 def stress():
     return {"A": wide_range_bf16((32768, 8192), 0),
             "B": wide_range_bf16((8192, 8192), 1, n_maxbf16=0)}
