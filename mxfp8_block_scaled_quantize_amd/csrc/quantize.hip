@@ -21,8 +21,13 @@
 //  - dbias partial sums are reduced lane -> wave -> workgroup and written once
 //    per (row tile, column); a second kernel sums the row tiles.
 //
+//  - with a fused activation (squared ReLU, GELU or their backward) the tile
+//    kernel quantizes the fp32 activation values by the same block rule.
+//
 // Flat kernel: the rowwise copy of a contiguous input is one stream of
-// 32-element blocks (see quantize_rowwise_flat_kernel).
+// 32-element blocks (see quantize_rowwise_flat_kernel).  Panel kernel: the
+// rowwise copy with its scales written as packed words (see
+// quantize_rowwise_packed_kernel).
 #include <mutex>
 
 #include "mx_device.h"
@@ -207,11 +212,12 @@ __global__ __launch_bounds__(64 * QW) void quantize_tile_kernel(
 
   uint32_t lane_amax = 0;
   if constexpr (ACT != ACT_NONE) {
-    // ---- activation path.  relu is applied to the BF16 bits in place.  The
-    // fp32 value of row i, column k of the lane is recomputed where it is
-    // needed (keeping 64 fp32 values live would halve the waves per SIMD).
-    // Squared ReLU: max r^2 = (max r)^2, so block amaxes come from integer
-    // maxima of the relu'd BF16 bits, as in the plain path.
+    // ---- activation path.  relu is applied to the BF16 bits in place.  For
+    // the squared ReLU and its backward the fp32 value of row i, column k of
+    // the lane is recomputed where it is needed (a few operations; keeping 64
+    // fp32 values live would halve the waves per SIMD); GELU keeps them (see
+    // below).  Squared ReLU: max r^2 = (max r)^2, so block amaxes come from
+    // integer maxima of the relu'd BF16 bits, as in the plain path.
     constexpr bool DACT = ACT == DACT_SQRELU || ACT == DACT_GELU;
     uint4 a[8];
     if (ACT == DACT_SQRELU) {
