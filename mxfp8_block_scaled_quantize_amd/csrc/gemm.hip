@@ -648,15 +648,24 @@ static hipError_t launch_gemm_t(const uint8_t* a, const uint32_t* ap, const uint
                                 hipStream_t stream) {
   // The dynamic-LDS opt-in is set once per device (bit d of the mask, for
   // device ids below 64; others set it on every launch), race-free across
-  // host threads.
+  // host threads.  The device is the stream's (the current device for the
+  // null stream), made current while the attribute is set.
   static std::atomic<uint64_t> attr_done{0};
   int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
   if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<GROUPED, ACC, EPI, BIAS, MXO>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
     if (e != hipSuccess) return e;
     attr_done.fetch_or(bit, std::memory_order_release);
   }
