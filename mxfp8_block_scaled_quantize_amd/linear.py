@@ -22,7 +22,9 @@ three GEMMs reduces over one of them).
 and quantizes the weight again only when the parameter changes: its storage,
 shape or version counter (every in-place update, an optimizer step included,
 bumps the counter).  Micro-batches between two weight updates reuse one
-quantization.
+quantization.  When no gradient is needed (grad mode off, or no input that
+requires one) the module's forward quantizes the input rowwise only: the
+columnwise copies exist for dgrad and wgrad.
 """
 
 import torch
@@ -39,6 +41,37 @@ def _quantize_both(t, dbias=False):
     return q + (out["dbias"],) if dbias else q
 
 
+def _check_linear(x, weight, bias):
+    """dtype and shape rules of the MXFP8 linear layer; returns the leading
+    shape, the input as a contiguous [M, K] matrix, M, K and N."""
+    if x.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise TypeError("MXFP8 linear takes BF16 input and weight")
+    if bias is not None and (bias.dtype != torch.bfloat16 or tuple(bias.shape) != (weight.shape[0],)):
+        raise ValueError("bias must be a BF16 tensor with one value per output feature")
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, x.shape[-1]).contiguous()
+    M, K = x2.shape
+    N = weight.shape[0]
+    if weight.shape[1] != K:
+        raise ValueError("weight is [%d, %d], input has %d features" % (weight.shape[0], weight.shape[1], K))
+    if M % 128 or N % 128 or K % 128:
+        raise ValueError("MXFP8 linear needs tokens, in- and out-features to be multiples of 128 "
+                         "(got M=%d, K=%d, N=%d)" % (M, K, N))
+    return lead, x2, M, K, N
+
+
+def mxfp8_linear_inference(x, weight, weight_q=None, bias=None):
+    """y = x W^T (+ b) without autograd: the input is quantized rowwise only
+    (into packed scales) and the fprop GEMM reads the weight's rowwise copy
+    (weight_q as for MXFP8LinearFunction, else quantized here)."""
+    lead, x2, M, K, N = _check_linear(x, weight, bias)
+    xq = quantize(x2, rowwise=True, packed=True)
+    if weight_q is None:
+        weight_q = _quantize_both(weight.contiguous())
+    y = gemm(xq["q_row"], xq["p_row"], weight_q[0], weight_q[1], bias=None if bias is None else bias.contiguous())
+    return y.view(*lead, N)
+
+
 class MXFP8LinearFunction(torch.autograd.Function):
     """apply(x, weight, fuse_wgrad_accumulation=False, weight_q=None, bias=None):
     weight_q, when given, is the weight's quantization (q_row, p_row, q_colT,
@@ -49,19 +82,7 @@ class MXFP8LinearFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, x, weight, fuse_wgrad_accumulation=False, weight_q=None, bias=None):
-        if x.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
-            raise TypeError("MXFP8 linear takes BF16 input and weight")
-        if bias is not None and (bias.dtype != torch.bfloat16 or tuple(bias.shape) != (weight.shape[0],)):
-            raise ValueError("bias must be a BF16 tensor with one value per output feature")
-        lead = x.shape[:-1]
-        x2 = x.reshape(-1, x.shape[-1]).contiguous()
-        M, K = x2.shape
-        N = weight.shape[0]
-        if weight.shape[1] != K:
-            raise ValueError("weight is [%d, %d], input has %d features" % (weight.shape[0], weight.shape[1], K))
-        if M % 128 or N % 128 or K % 128:
-            raise ValueError("MXFP8 linear needs tokens, in- and out-features to be multiples of 128 "
-                             "(got M=%d, K=%d, N=%d)" % (M, K, N))
+        lead, x2, M, K, N = _check_linear(x, weight, bias)
         qx, px, qxT, pxT = _quantize_both(x2)
         if weight_q is None:
             weight_q = _quantize_both(weight.contiguous())
@@ -128,5 +149,8 @@ class MXFP8Linear(torch.nn.Module):
         return self._wq
 
     def forward(self, x):
+        params = [self.weight] + ([self.bias] if self.bias is not None else [])
+        if not (torch.is_grad_enabled() and (x.requires_grad or any(p.requires_grad for p in params))):
+            return mxfp8_linear_inference(x, self.weight, self.quantized_weight(), self.bias)
         return MXFP8LinearFunction.apply(x, self.weight, self.fuse_wgrad_accumulation, self.quantized_weight(),
                                          self.bias)

@@ -195,3 +195,40 @@ def test_linear_module_with_bias():
     y.backward(to_dev_bf16(dy))
     torch.cuda.synchronize()
     _bias_checks(y.detach(), layer.bias.grad, x, w, dy, bias, "module")
+
+
+def test_linear_module_inference_quantizes_the_input_rowwise_only(monkeypatch):
+    """Without grad the module quantizes the input rowwise only (no columnwise
+    copy: nothing reads it) and its output equals the autograd path's bit for
+    bit (the same codes reach the same GEMM) and the oracle within the bound."""
+    torch = need_gpu()
+    import mxfp8_block_scaled_quantize_amd.linear as lin
+    calls = []
+    real = lin.quantize
+
+    def recording(t, **kw):
+        calls.append((tuple(t.shape), bool(kw.get("colwise"))))
+        return real(t, **kw)
+
+    monkeypatch.setattr(lin, "quantize", recording)
+    x, w, dy = _inputs(40)
+    bias = workloads.normal_bf16((N,), 41, std=1.0)
+    layer = lin.MXFP8Linear(K, N, device="cuda", bias=True)
+    with torch.no_grad():
+        layer.weight.copy_(to_dev_bf16(w))
+        layer.bias.copy_(to_dev_bf16(bias))
+    log("linear module inference")
+    xt = to_dev_bf16(x)
+    with torch.no_grad():
+        y_inf = layer(xt)
+    torch.cuda.synchronize()
+    assert calls == [((N, K), True), ((M, K), False)], calls     # W's two copies (cached), x rowwise only
+    y_train = layer(xt)                                           # grad mode: the weight requires grad
+    torch.cuda.synchronize()
+    assert calls[2:] == [((M, K), True)], calls
+    assert torch.equal(y_inf.view(torch.int16), y_train.detach().view(torch.int16))
+    y_ref, _, _ = _refs(x, w, dy)
+    t = 8e-3 * np.abs(y_ref) + 1e-3 * np.sqrt(K) * np.sqrt(np.mean(y_ref ** 2))
+    want = oracle.bias_add(y_ref, bias)
+    err = np.abs(bf16_to_f64(to_host(y_inf)) - want)
+    assert np.all(err <= t + 2.0 ** -8 * (np.abs(want) + t))
