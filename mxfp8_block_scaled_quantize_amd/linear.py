@@ -22,9 +22,11 @@ three GEMMs reduces over one of them).
 and quantizes the weight again only when the parameter changes: its storage,
 shape or version counter (every in-place update, an optimizer step included,
 bumps the counter).  Micro-batches between two weight updates reuse one
-quantization.  When no gradient is needed (grad mode off, or no input that
-requires one) the module's forward quantizes the input rowwise only: the
-columnwise copies exist for dgrad and wgrad.
+quantization.  Only the copies a GEMM will read are made: without any
+gradient (grad mode off, or no input that requires one) the module's forward
+quantizes the input rowwise only; x's columnwise copy is made only when the
+weight needs a gradient, dy's rowwise copy only for dgrad and its columnwise
+copy only for wgrad.
 """
 
 import torch
@@ -39,6 +41,14 @@ def _quantize_both(t, dbias=False):
     out = quantize(t, rowwise=True, colwise=True, packed=True, dbias=dbias)
     q = (out["q_row"], out["p_row"], out["q_colT"], out["p_colT"])
     return q + (out["dbias"],) if dbias else q
+
+
+def _quantize_copies(t, row, col, dbias=False):
+    """Only the copies a later GEMM reads (at least one of them; dbias needs a
+    copy too): (q_row, p_row, q_colT, p_colT, dbias), None where not made."""
+    row = row or not col
+    out = quantize(t, rowwise=row, colwise=col, packed=True, dbias=dbias)
+    return out.get("q_row"), out.get("p_row"), out.get("q_colT"), out.get("p_colT"), out.get("dbias")
 
 
 def _check_linear(x, weight, bias):
@@ -83,7 +93,8 @@ class MXFP8LinearFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, weight, fuse_wgrad_accumulation=False, weight_q=None, bias=None):
         lead, x2, M, K, N = _check_linear(x, weight, bias)
-        qx, px, qxT, pxT = _quantize_both(x2)
+        # x's columnwise copy only feeds wgrad
+        qx, px, qxT, pxT, _ = _quantize_copies(x2, True, ctx.needs_input_grad[1])
         if weight_q is None:
             weight_q = _quantize_both(weight.contiguous())
         qw, pw, qwT, pwT = weight_q
@@ -101,7 +112,10 @@ class MXFP8LinearFunction(torch.autograd.Function):
         lead, M, K, N = ctx.shape
         dy2 = dy.reshape(M, N).to(torch.bfloat16).contiguous()
         want_db = ctx.bias_dtype is not None and ctx.needs_input_grad[4]
-        qd, pd, qdT, pdT, *db = _quantize_both(dy2, dbias=want_db)
+        if not (ctx.needs_input_grad[0] or ctx.needs_input_grad[1] or want_db):
+            return None, None, None, None, None
+        # dy's rowwise copy feeds dgrad, its columnwise copy wgrad
+        qd, pd, qdT, pdT, db = _quantize_copies(dy2, ctx.needs_input_grad[0], ctx.needs_input_grad[1], want_db)
         dx = None
         if ctx.needs_input_grad[0]:
             dx = gemm(qd, pd, qwT, pwT).view(*lead, K)
@@ -114,7 +128,7 @@ class MXFP8LinearFunction(torch.autograd.Function):
                 gemm(qdT, pdT, qxT, pxT, out=main, accumulate=True)
             else:
                 dw = gemm(qdT, pdT, qxT, pxT)
-        dbias = db[0].to(ctx.bias_dtype) if want_db else None
+        dbias = db.to(ctx.bias_dtype) if want_db else None
         return dx, dw, None, None, dbias
 
 

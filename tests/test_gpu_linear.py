@@ -232,3 +232,39 @@ def test_linear_module_inference_quantizes_the_input_rowwise_only(monkeypatch):
     want = oracle.bias_add(y_ref, bias)
     err = np.abs(bf16_to_f64(to_host(y_inf)) - want)
     assert np.all(err <= t + 2.0 ** -8 * (np.abs(want) + t))
+
+
+@pytest.mark.parametrize("frozen", ["weight", "input"])
+def test_linear_makes_only_the_copies_its_gradients_read(monkeypatch, frozen):
+    """A frozen weight: x is quantized rowwise only and dy rowwise only (dgrad);
+    an input that needs no gradient: dy is quantized columnwise only (wgrad).
+    The gradients that are computed match the oracle."""
+    torch = need_gpu()
+    import mxfp8_block_scaled_quantize_amd.linear as lin
+    calls = []
+    real = lin.quantize
+
+    def recording(t, **kw):
+        calls.append((tuple(t.shape), bool(kw.get("rowwise", True)), bool(kw.get("colwise"))))
+        return real(t, **kw)
+
+    monkeypatch.setattr(lin, "quantize", recording)
+    x, w, dy = _inputs(42)
+    xt = to_dev_bf16(x).requires_grad_(frozen == "weight")
+    wt = to_dev_bf16(w).requires_grad_(frozen == "input")
+    log("linear frozen %s" % frozen)
+    wq = lin._quantize_both(wt.detach())
+    del calls[:]
+    y = lin.MXFP8LinearFunction.apply(xt, wt, False, wq)
+    y.backward(to_dev_bf16(dy))
+    torch.cuda.synchronize()
+    y_ref, dx_ref, dw_ref = _refs(x, w, dy)
+    gemm_tolerance_check(to_host(y.detach()), y_ref, K, label="fprop")
+    if frozen == "weight":
+        assert calls == [((M, K), True, False), ((M, N), True, False)], calls
+        assert wt.grad is None
+        gemm_tolerance_check(to_host(xt.grad), dx_ref, N, label="dgrad")
+    else:
+        assert calls == [((M, K), True, True), ((M, N), False, True)], calls
+        assert xt.grad is None
+        gemm_tolerance_check(to_host(wt.grad), dw_ref, M, label="wgrad")
