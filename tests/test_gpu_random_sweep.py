@@ -6,7 +6,10 @@ uncovered tails).  Each case is drawn from a fixed generator, so a failure
 names a reproducible case; the checks are the same as in the hand-picked
 tests (bit-exact codes and scales, dbias within its summation bound, GEMM
 within the stated tolerance; GELU outputs within the bounded check of the
-GELU tests)."""
+GELU tests).  MXFP8_SWEEP_SCALE=k in the environment multiplies every case
+count by k."""
+
+import os
 
 import numpy as np
 import pytest
@@ -20,6 +23,10 @@ from test_gpu_gemm import (bias_case, gelu_tolerance_check, gemm_gpu, grouped_ca
 from test_gpu_quantize_ex import act_inputs, check_act_result, check_gelu_result, dgelu_case, gelu_case, run_ex
 
 pytestmark = pytest.mark.gpu
+
+# MXFP8_SWEEP_SCALE=k runs k times as many cases of every sweep (the first
+# ones are the default cases: each generator draws its cases in order).
+SCALE = max(1, int(os.environ.get("MXFP8_SWEEP_SCALE", "1")))
 
 ROW, COL, DB = mx.MXFP8_ROWWISE, mx.MXFP8_COLWISE, mx.MXFP8_DBIAS
 AMAX, PACKED = mx.MXFP8_AMAX, mx.MXFP8_PACKED_SCALES
@@ -44,7 +51,7 @@ def quantize_cases(n, seed):
     return cases
 
 
-@pytest.mark.parametrize("case", quantize_cases(48, 2024))
+@pytest.mark.parametrize("case", quantize_cases(48 * SCALE, 2024))
 def test_random_quantize(case):
     R, C, ld, flags, act, seed = case
     label = "random quantize R=%d C=%d ld=%d flags=%d act=%d seed=%d" % case
@@ -75,7 +82,7 @@ def gemm_cases(n, seed):
     return cases
 
 
-@pytest.mark.parametrize("case", gemm_cases(32, 77))
+@pytest.mark.parametrize("case", gemm_cases(32 * SCALE, 77))
 def test_random_gemm(case):
     torch = need_gpu()
     M, N, K, ldc, epi, seed = case
@@ -118,7 +125,7 @@ def grouped_cases(n, seed):
     return cases
 
 
-@pytest.mark.parametrize("case", grouped_cases(20, 91))
+@pytest.mark.parametrize("case", grouped_cases(20 * SCALE, 91))
 def test_random_grouped_gemm(case):
     counts, tail, N, K, epi, seed = case
     M = sum(counts) + tail
@@ -138,7 +145,7 @@ def gelu_quantize_cases(n, seed):
     return cases
 
 
-@pytest.mark.parametrize("case", gelu_quantize_cases(24, 2025))
+@pytest.mark.parametrize("case", gelu_quantize_cases(24 * SCALE, 2025))
 def test_random_gelu_quantize(case):
     R, C, ld, flags, act, seed = case
     label = "random gelu quantize R=%d C=%d ld=%d flags=%d act=%d seed=%d" % case
@@ -152,7 +159,7 @@ def test_random_gelu_quantize(case):
     check_gelu_result(got, v, e, flags, label)
 
 
-@pytest.mark.parametrize("case", gemm_cases(12, 78))
+@pytest.mark.parametrize("case", gemm_cases(12 * SCALE, 78))
 def test_random_gemm_gelu(case):
     M, N, K, ldc, _, seed = case
     log("random gemm gelu M=%d N=%d K=%d ldc=%d seed=%d" % (M, N, K, ldc, seed))
@@ -166,7 +173,7 @@ def test_random_gemm_gelu(case):
     gelu_tolerance_check(c, oracle.gemm_tn(oqa, osa, oqb, osb), K, "gelu")
 
 
-@pytest.mark.parametrize("case", grouped_cases(8, 92))
+@pytest.mark.parametrize("case", grouped_cases(8 * SCALE, 92))
 def test_random_grouped_gemm_gelu(case):
     counts, tail, N, K, _, seed = case
     M = sum(counts) + tail
@@ -175,7 +182,7 @@ def test_random_grouped_gemm_gelu(case):
     grouped_case(M, N, K, list(counts), seed, gelu=True)
 
 
-@pytest.mark.parametrize("case", gemm_cases(12, 79))
+@pytest.mark.parametrize("case", gemm_cases(12 * SCALE, 79))
 def test_random_gemm_swiglu(case):
     """B = [gate; up] with 2N rows, C [M, N]: random M, N (a multiple of 32,
     often not of 128), K and ldc."""
@@ -191,7 +198,7 @@ def test_random_gemm_swiglu(case):
     swiglu_tolerance_check(c, oracle.gemm_tn(oqa, osa, oqb, osb), K, "swiglu")
 
 
-@pytest.mark.parametrize("case", grouped_cases(8, 93))
+@pytest.mark.parametrize("case", grouped_cases(8 * SCALE, 93))
 def test_random_grouped_gemm_swiglu(case):
     counts, tail, N, K, _, seed = case
     M = sum(counts) + tail
@@ -203,14 +210,14 @@ def test_random_grouped_gemm_swiglu(case):
 EPIS = ["plain", "sqrelu", "gelu", "swiglu"]
 
 
-@pytest.mark.parametrize("case", gemm_cases(12, 80))
+@pytest.mark.parametrize("case", gemm_cases(12 * SCALE, 80))
 def test_random_gemm_bias(case):
     """The bias epilogue under each activation, random M, N, K and ldc."""
     M, N, K, ldc, _, seed = case
     bias_case(M, N, K, EPIS[seed % 4], seed, ldc=ldc)
 
 
-@pytest.mark.parametrize("case", grouped_cases(8, 94))
+@pytest.mark.parametrize("case", grouped_cases(8 * SCALE, 94))
 def test_random_grouped_gemm_bias(case):
     counts, tail, N, K, _, seed = case
     M = sum(counts) + tail
@@ -234,7 +241,7 @@ def mxout_cases(n, seed):
     return cases
 
 
-@pytest.mark.parametrize("case", mxout_cases(12, 81))
+@pytest.mark.parametrize("case", mxout_cases(12 * SCALE, 81))
 def test_random_gemm_mxfp8_out(case):
     """The MXFP8-output GEMM equals the rowwise packed quantize of the BF16
     output, random shapes, row strides, epilogues and biases."""
