@@ -1,0 +1,83 @@
+"""Tensors beyond 2^32 elements: the quantizer's row+col+dbias launch with
+packed scales on a [69632 x 65536] BF16 tensor (4.56 G elements, 9.1 GB), the
+GEMM reading its rowwise codes as an A operand of 4.56 GB (K = 65536), and
+the two rowwise-only quantize kernels on the same tensor.
+Element offsets above 2^32 must be formed in 64 bits everywhere.
+
+The tensor repeats one seeded 4096 x 4096 tile of the input generators (the
+repetition is done by torch on the device), so every row and column of it is
+known on the host: sampled rows and columns on both sides of element 2^32 are
+compared with the oracle bit for bit, dbias within its summation bound, and
+sampled GEMM rows within the GEMM tolerance."""
+
+import numpy as np
+import pytest
+
+import mxfp8_block_scaled_quantize_amd as mx
+import oracle
+import workloads
+from gpu_util import bf16_to_f64, gemm_tolerance_check, log, need_gpu, to_dev_bf16, to_host
+from test_gpu_quantize import dbias_depth
+from test_gpu_quantize_ex import unpack_words
+
+pytestmark = pytest.mark.gpu
+
+T = 4096
+R, C = 69632, 65536          # R * C = 4.56e9 > 2^32; row 65536 starts at element 2^32
+
+
+def test_quantize_and_gemm_beyond_2_pow_32_elements():
+    torch = need_gpu()
+    free, _ = torch.cuda.mem_get_info()
+    if free < 40 * 2 ** 30:
+        pytest.skip("needs about 24 GB of device memory (40 GB free asked for)")
+    tile = workloads.normal_bf16((T, T), 77)
+    log("large quantize R=%d C=%d (%.2e elements)" % (R, C, float(R) * C))
+    x = to_dev_bf16(tile).repeat(R // T, C // T)
+    assert x.shape == (R, C)
+    out = mx.quantize(x, rowwise=True, colwise=True, dbias=True, packed=True)
+    torch.cuda.synchronize()
+    rows = [0, 4095, 65535, 65536, 65537, R - 1]
+    for r in rows:
+        q, s = oracle.quantize_rowwise(np.tile(tile[r % T], C // T)[None, :])
+        assert np.array_equal(to_host(out["q_row"][r]), q[0]), r
+        got_s = unpack_words(to_host(out["p_row"][:, r:r + 1]), 1)
+        assert np.array_equal(got_s, s), r
+    cols = [0, 4097, C // 2 + 31, C - 1]
+    for c in cols:
+        qT, sT = oracle.quantize_colwise(np.tile(tile[:, c % T], R // T)[:, None])
+        assert np.array_equal(to_host(out["q_colT"][c]), qT[0]), c
+        got_s = unpack_words(to_host(out["p_colT"][:, c:c + 1]), 1)
+        assert np.array_equal(got_s, sT), c
+    # dbias: R / T copies of each tile column sum, within the kernel's summation bound
+    ref = (R // T) * oracle.dbias(tile).astype(np.float64)
+    ref = np.tile(ref, C // T)
+    mag = np.tile((R // T) * np.abs(bf16_to_f64(tile)).sum(axis=0), C // T)
+    tol = 1.01 * dbias_depth(R) * 2.0 ** -24 * mag + np.abs(ref) * 2.0 ** -23 + 2.0 ** -126
+    err = np.abs(to_host(out["dbias"]).astype(np.float64) - ref)
+    assert np.all(err <= tol), "dbias off by %g" % (err - tol).max()
+    # the GEMM with that rowwise copy as A (M = 69632, K = 65536: 4.56 GB of codes)
+    N = 256
+    b = workloads.normal_bf16((N, C), 78, std=0.02)
+    qb = mx.quantize(to_dev_bf16(b), rowwise=True, packed=True)
+    log("large gemm M=%d N=%d K=%d" % (R, N, C))
+    y = mx.gemm(out["q_row"], out["p_row"], qb["q_row"], qb["p_row"])
+    torch.cuda.synchronize()
+    oqb, osb = oracle.quantize_rowwise(b)
+    for r in rows:
+        oqa, osa = oracle.quantize_rowwise(np.tile(tile[r % T], C // T)[None, :])
+        ref = oracle.gemm_tn(oqa, osa, oqb, osb)
+        gemm_tolerance_check(to_host(y[r:r + 1]), ref, C, label="row %d" % r)
+    del out, y
+    # the two rowwise-only kernels: the flat stream (byte scales) and the
+    # panel kernel (packed scale words)
+    for packed in (False, True):
+        log("large rowwise quantize packed=%d" % packed)
+        o = mx.quantize(x, rowwise=True, packed=packed)
+        torch.cuda.synchronize()
+        for r in rows:
+            q, s = oracle.quantize_rowwise(np.tile(tile[r % T], C // T)[None, :])
+            assert np.array_equal(to_host(o["q_row"][r]), q[0]), (packed, r)
+            got_s = unpack_words(to_host(o["p_row"][:, r:r + 1]), 1) if packed else to_host(o["s_row"][r:r + 1])
+            assert np.array_equal(got_s, s), (packed, r)
+        del o
