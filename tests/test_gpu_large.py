@@ -1,4 +1,4 @@
-"""Tensors beyond 2^32 elements: the quantizer's row+col+dbias launch with
+"""Tensors beyond 2^32 elements or bytes: the quantizer's row+col+dbias launch with
 packed scales on a [69632 x 65536] BF16 tensor (4.56 G elements, 9.1 GB), the
 GEMM reading its rowwise codes as an A operand of 4.56 GB (K = 65536), and
 the two rowwise-only quantize kernels on the same tensor.
@@ -81,3 +81,37 @@ def test_quantize_and_gemm_beyond_2_pow_32_elements():
             got_s = unpack_words(to_host(o["p_row"][:, r:r + 1]), 1) if packed else to_host(o["s_row"][r:r + 1])
             assert np.array_equal(got_s, s), (packed, r)
         del o
+
+
+def test_grouped_gemm_with_experts_past_2_pow_32_bytes():
+    """64 experts of 8192 x 8192 codes (4.3 GB of B: the last experts start
+    past byte 2^32), 256 rows each: sampled rows of several experts, the last
+    included, against the oracle with that expert's weights (every expert's
+    weights differ: expert g's row j is row (j + 61 g) mod 4096 of the tile,
+    repeated along K)."""
+    torch = need_gpu()
+    free, _ = torch.cuda.mem_get_info()
+    if free < 40 * 2 ** 30:
+        pytest.skip("needs about 14 GB of device memory (40 GB free asked for)")
+    G, N, K, per = 64, 8192, 8192, 256
+    M = G * per
+    tile = workloads.normal_bf16((T, T), 79, std=0.02)
+    base = to_dev_bf16(tile).repeat(N // T, K // T)                    # [8192, 8192]
+    w = torch.stack([torch.roll(base, shifts=-61 * g, dims=0) for g in range(G)])   # [64, 8192, 8192]
+    del base
+    log("large grouped gemm G=%d N=%d K=%d" % (G, N, K))
+    wq = mx.quantize(w.view(G * N, K), rowwise=True, packed=True)
+    del w
+    x = workloads.normal_bf16((M, K), 80)
+    xq = mx.quantize(to_dev_bf16(x), rowwise=True, packed=True)
+    off = torch.arange(0, M + 1, per, dtype=torch.int32, device="cuda")
+    y = mx.grouped_gemm(xq["q_row"], xq["p_row"], wq["q_row"].view(G, N, K), wq["p_row"], off)
+    torch.cuda.synchronize()
+    cols = np.arange(0, N, 97)
+    for g in (0, 31, 62, 63):
+        wg = np.tile(tile[(np.arange(N) + 61 * g) % T][cols], (1, K // T))     # the sampled weight rows
+        oqw, osw = oracle.quantize_rowwise(wg)
+        for r in (g * per, g * per + per - 1):
+            oqx, osx = oracle.quantize_rowwise(x[r:r + 1])
+            ref = oracle.gemm_tn(oqx, osx, oqw, osw)
+            gemm_tolerance_check(to_host(y[r:r + 1])[:, cols], ref, K, label="expert %d row %d" % (g, r))
