@@ -115,3 +115,37 @@ def test_grouped_gemm_with_experts_past_2_pow_32_bytes():
             oqx, osx = oracle.quantize_rowwise(x[r:r + 1])
             ref = oracle.gemm_tn(oqx, osx, oqw, osw)
             gemm_tolerance_check(to_host(y[r:r + 1])[:, cols], ref, K, label="expert %d row %d" % (g, r))
+
+
+def test_gemm_output_past_2_pow_32_elements():
+    """C [69632 x 65536] (4.56 G outputs, 9.1 GB of BF16) with K = 128, and the
+    same GEMM writing MXFP8 (4.56 GB of codes): sampled rows on both sides of
+    element 2^32 against the oracle's product; the MXFP8 rows must equal the
+    library's rowwise quantization of the BF16 rows of the first launch (the
+    output quantizer's contract: a consistency check between entry points)."""
+    torch = need_gpu()
+    free, _ = torch.cuda.mem_get_info()
+    if free < 40 * 2 ** 30:
+        pytest.skip("needs about 15 GB of device memory (40 GB free asked for)")
+    M, N, K = R, C, 128
+    a = workloads.normal_bf16((M, K), 81)
+    b = workloads.normal_bf16((N, K), 82, std=0.25)
+    qa = mx.quantize(to_dev_bf16(a), rowwise=True, packed=True)
+    qb = mx.quantize(to_dev_bf16(b), rowwise=True, packed=True)
+    log("large gemm output M=%d N=%d K=%d" % (M, N, K))
+    y = mx.gemm(qa["q_row"], qa["p_row"], qb["q_row"], qb["p_row"])
+    torch.cuda.synchronize()
+    oqb, osb = oracle.quantize_rowwise(b)
+    rows = [0, 65535, 65536, M - 1]
+    want = {}
+    for r in rows:
+        oqa, osa = oracle.quantize_rowwise(a[r:r + 1])
+        gemm_tolerance_check(to_host(y[r:r + 1]), oracle.gemm_tn(oqa, osa, oqb, osb), K, label="row %d" % r)
+        rq = mx.quantize(y[r:r + 1].contiguous(), rowwise=True, packed=True)   # the quantizer on the BF16 row
+        want[r] = (to_host(rq["q_row"]), to_host(rq["p_row"]))
+    del y
+    q, p = mx.gemm(qa["q_row"], qa["p_row"], qb["q_row"], qb["p_row"], mxfp8_out=True)
+    torch.cuda.synchronize()
+    for r in rows:
+        assert np.array_equal(to_host(q[r:r + 1]), want[r][0]), r
+        assert np.array_equal(to_host(p[:, r:r + 1]), want[r][1]), r
