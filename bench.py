@@ -58,6 +58,9 @@ def parse():
                         "(at least one whole step runs)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain 256 MiB device copy (reference for HBM byte counters)")
+    p.add_argument("--no-vendor-reference", action="store_true",
+                   help="skip the reference run of PyTorch's MXFP8 GEMM (torch._scaled_mm with E8M0 block scales, "
+                        "hipBLASLt on ROCm) on the dominant GEMM's shape, after the timed region")
     p.add_argument("--no-mfma-calibration", action="store_true",
                    help="skip the reference run of the scaled FP8 MFMA fed from registers only (libmxfp8_calib.so) "
                         "on the dominant GEMM's tile grid, as many launches as timed steps, after the timed region: "
@@ -542,6 +545,9 @@ def main():
                        "separate pass after them (%d steps); ms = mean, with median, min and max; "
                        "short_launch_blocks: the same launches as timed in the steps" % min(args.steps, 10),
     }
+    if not args.no_vendor_reference:
+        result["vendor_reference"] = vendor_reference(torch, stream, dominant, dom.work, args.steps, args.warmup,
+                                                      achieved)
     if not args.no_mfma_calibration:
         result["mfma_calibration"] = mfma_calibration(torch, stream, dominant, dom.work, args.steps, args.warmup,
                                                       achieved)
@@ -549,6 +555,57 @@ def main():
         result["cpu_baseline"] = cpu_baseline(args.workload, host, total_flops, args.cpu_seconds)
 
     print(json.dumps(result))
+
+
+def vendor_reference(torch, stream, label, flops_per_launch, launches, warmup, gemm_tflops):
+    """PyTorch's own MXFP8 GEMM on the dominant GEMM's M x N x K (for a grouped
+    GEMM: all routed rows as one dense GEMM of the same FLOPs): torch._scaled_mm
+    with E4M3 operands and E8M0 scales per 32-element block (hipBLASLt on
+    ROCm), BF16 output, random codes and unit scales, timed with HIP events per
+    launch on the bench stream.  A reference only: nothing of this library
+    runs in it."""
+    import re
+
+    import numpy as np
+
+    m = re.search(r"(\d+)x(\d+)x(\d+)", label)
+    M, N, K = (int(v) for v in m.groups())
+    if "grouped" in label or "swiglu" in label:
+        N = int(round(flops_per_launch / (2.0 * M * K)))   # the dense shape of the same FLOPs
+    if not hasattr(torch, "float8_e8m0fnu"):
+        return {"skipped": "this PyTorch has no float8_e8m0fnu"}
+    g = torch.Generator(device="cuda").manual_seed(7)
+    try:
+        with torch.cuda.stream(stream):
+            a = torch.randn((M, K), device="cuda", generator=g).to(torch.float8_e4m3fn)
+            b = torch.randn((N, K), device="cuda", generator=g).to(torch.float8_e4m3fn)
+            sa = torch.full((M, K // 32), 127, dtype=torch.uint8, device="cuda").view(torch.float8_e8m0fnu)
+            sb = torch.full((N, K // 32), 127, dtype=torch.uint8, device="cuda").view(torch.float8_e8m0fnu)
+
+            def launch():
+                return torch._scaled_mm(a, b.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+
+            for _ in range(warmup):
+                launch()
+            torch.cuda.synchronize()
+            ev = []
+            for _ in range(launches):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                launch()
+                e1.record(stream)
+                ev.append((e0, e1))
+            torch.cuda.synchronize()
+    except Exception as e:   # not supported by this PyTorch / hipBLASLt build
+        return {"skipped": "torch._scaled_mm with MX block scales failed: %s" % repr(e)[:200]}
+    ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    return {"kernel": "torch._scaled_mm, E4M3 x E4M3 with E8M0 scales per 32 (hipBLASLt), BF16 out, no epilogue",
+            "shape": "%dx%dx%d" % (M, N, K), "launches": launches, "ms": round(float(np.mean(ms)), 4),
+            "ms_median": round(float(np.median(ms)), 4), "tflops": round(float(np.mean(tf)), 1),
+            "frac_fp8_peak": round(float(np.mean(tf)) / FP8_PEAK_TFLOPS, 4),
+            "this_library_over_vendor": round(gemm_tflops / float(np.mean(tf)), 3)}
 
 
 def mfma_calibration(torch, stream, label, flops_per_launch, launches, warmup, gemm_tflops):
