@@ -545,11 +545,13 @@ def main():
                        "separate pass after them (%d steps); ms = mean, with median, min and max; "
                        "short_launch_blocks: the same launches as timed in the steps" % min(args.steps, 10),
     }
-    if not args.no_vendor_reference:
-        result["vendor_reference"] = vendor_reference(torch, stream, dominant, dom.work, args.steps, args.warmup,
-                                                      achieved)
+    # the register-only MFMA reference first, right after the timed region (as
+    # the GEMM ran), then the vendor GEMM
     if not args.no_mfma_calibration:
         result["mfma_calibration"] = mfma_calibration(torch, stream, dominant, dom.work, args.steps, args.warmup,
+                                                      achieved)
+    if not args.no_vendor_reference:
+        result["vendor_reference"] = vendor_reference(torch, stream, dominant, dom.work, args.steps, args.warmup,
                                                       achieved)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.workload, host, total_flops, args.cpu_seconds)
