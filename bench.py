@@ -587,6 +587,18 @@ def vendor_reference(torch, stream, label, flops_per_launch, launches, warmup, g
             def launch():
                 return torch._scaled_mm(a, b.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
 
+            # hipBLASLt's algorithm query has been seen to return INVALID_VALUE
+            # now and then for a shape it serves otherwise (a status, no
+            # fault): the first call is tried up to three times
+            failures = []
+            while True:
+                try:
+                    launch()
+                    break
+                except RuntimeError as e:
+                    failures.append(repr(e)[:120])
+                    if len(failures) == 3:
+                        raise
             for _ in range(warmup):
                 launch()
             torch.cuda.synchronize()
@@ -607,7 +619,8 @@ def vendor_reference(torch, stream, label, flops_per_launch, launches, warmup, g
             "shape": "%dx%dx%d" % (M, N, K), "launches": launches, "ms": round(float(np.mean(ms)), 4),
             "ms_median": round(float(np.median(ms)), 4), "tflops": round(float(np.mean(tf)), 1),
             "frac_fp8_peak": round(float(np.mean(tf)) / FP8_PEAK_TFLOPS, 4),
-            "this_library_over_vendor": round(gemm_tflops / float(np.mean(tf)), 3)}
+            "this_library_over_vendor": round(gemm_tflops / float(np.mean(tf)), 3),
+            "first_call_failures": len(failures)}
 
 
 def mfma_calibration(torch, stream, label, flops_per_launch, launches, warmup, gemm_tflops):
