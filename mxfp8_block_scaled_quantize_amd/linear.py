@@ -73,11 +73,13 @@ def _check_linear(x, weight, bias):
 def mxfp8_linear_inference(x, weight, weight_q=None, bias=None):
     """y = x W^T (+ b) without autograd: the input is quantized rowwise only
     (into packed scales) and the fprop GEMM reads the weight's rowwise copy
-    (weight_q as for MXFP8LinearFunction, else quantized here)."""
+    (weight_q as for MXFP8LinearFunction, else the rowwise copy is made
+    here)."""
     lead, x2, M, K, N = _check_linear(x, weight, bias)
     xq = quantize(x2, rowwise=True, packed=True)
-    if weight_q is None:
-        weight_q = _quantize_both(weight.contiguous())
+    if weight_q is None:   # only the rowwise copy is read here
+        wq = quantize(weight.contiguous(), rowwise=True, packed=True)
+        weight_q = (wq["q_row"], wq["p_row"])
     y = gemm(xq["q_row"], xq["p_row"], weight_q[0], weight_q[1], bias=None if bias is None else bias.contiguous())
     return y.view(*lead, N)
 

@@ -95,3 +95,22 @@ def test_module_with_bias_has_a_bias_parameter():
     assert layer.bias is not None and layer.bias.dtype == torch.bfloat16 and tuple(layer.bias.shape) == (256,)
     assert {n for n, _ in layer.named_parameters()} == {"weight", "bias"}
     assert lin.MXFP8Linear(128, 256).bias is None
+
+
+def test_inference_without_a_cached_weight_quantizes_rowwise_only(monkeypatch):
+    """mxfp8_linear_inference with no weight quantization given makes only
+    the rowwise copies of x and W (host logic: quantize and gemm are stubs)."""
+    import mxfp8_block_scaled_quantize_amd.linear as lin
+    calls = []
+
+    def stub_quantize(t, **kw):
+        calls.append((tuple(t.shape), kw.get("rowwise"), bool(kw.get("colwise"))))
+        return {"q_row": t, "p_row": t}
+
+    monkeypatch.setattr(lin, "quantize", stub_quantize)
+    monkeypatch.setattr(lin, "gemm", lambda a, pa, b, pb, bias=None: torch.zeros((a.shape[0], b.shape[0])))
+    x = torch.zeros((128, 256), dtype=torch.bfloat16)
+    w = torch.zeros((384, 256), dtype=torch.bfloat16)
+    y = lin.mxfp8_linear_inference(x, w)
+    assert tuple(y.shape) == (128, 384)
+    assert calls == [((128, 256), True, False), ((384, 256), True, False)], calls
