@@ -322,3 +322,41 @@ def test_calibration_library_is_separate(L):
     cal.mxfp8_calib_mfma_ceiling
     assert cal.mxfp8_calib_code_words() == 4096
     assert not hasattr(ctypes.CDLL(mx.LIB_PATH), "mxfp8_calib_mfma_ceiling")
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/mxfp8.h compiles as C99 with warnings as errors, and a C program
+    linked against libmxfp8.so calls it without Python: status strings, sizes
+    and host-side validation (nothing reaches the GPU)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    if not os.path.exists(mx.LIB_PATH):
+        mxbuild.build()
+    src = tmp_path / "abi.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <string.h>
+#include "mxfp8.h"
+int main(void) {
+    void *p = (void *)0x10000;   /* never dereferenced: every call below fails validation */
+    if (strncmp(mxfp8_status_string(MXFP8_ERR_SHAPE), "MXFP8_ERR_SHAPE", 15) != 0) return 1;
+    if (mxfp8_packed_scale_bytes(96, 512) != 4 * 96 * 4) return 2;
+    if (mxfp8_quantize(p, 64, 48, 64, MXFP8_ROWWISE, p, p, NULL, NULL, NULL, NULL, 0, NULL) != MXFP8_ERR_SHAPE)
+        return 3;
+    if (mxfp8_gemm_ex(p, p, p, p, p, 64, 64, 64, 128, MXFP8_GEMM_ACCUMULATE | MXFP8_GEMM_GELU, NULL)
+        != MXFP8_ERR_FLAGS) return 4;
+    if (mxfp8_gemm_mxfp8_out(p, p, p, p, NULL, p, 96, p, 64, 96, 128, 0, NULL) != MXFP8_ERR_SHAPE) return 5;
+    if (mxfp8_grouped_gemm(p, p, p, p, p, 0, p, 64, 64, 64, 128, NULL) != MXFP8_ERR_SHAPE) return 6;
+    puts("c abi ok");
+    return 0;
+}
+''')
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(mx.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe), "-L", libdir, "-l:libmxfp8.so", "-Wl,-rpath," + libdir],
+                   check=True, capture_output=True, text=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and "c abi ok" in r.stdout, (r.returncode, r.stdout, r.stderr)
